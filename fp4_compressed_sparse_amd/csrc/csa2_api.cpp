@@ -1,0 +1,535 @@
+// C ABI of the CSA2 gfx950 library: host-side validation, workspace layout, launch
+// sequencing and optional per-kernel event timing.  Validation runs before any HIP call,
+// so every error path is reachable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/csa2.h"
+#include "csa2_internal.h"
+
+using namespace csa2;
+
+namespace {
+
+thread_local std::string g_err;
+
+csa2_status fail(csa2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// ---------------------------------------------------------------- kernel timing
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t e0, e1;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<TimedLaunch> pending;
+  std::vector<std::string> names;
+  std::vector<int64_t> launches;
+  std::vector<double> ms;
+};
+Timing g_timing;
+
+hipEvent_t timing_event() {
+  if (g_timing.used == g_timing.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_timing.pool.push_back(e);
+  }
+  return g_timing.pool[g_timing.used++];
+}
+
+// Launch `fn` (returning hipError_t) on `s`, bracketed by events when timing is on.
+template <class F>
+csa2_status timed(const char* name, hipStream_t s, F&& fn) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_timing.on) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    e0 = timing_event();
+    e1 = timing_event();
+    if (e0) (void)hipEventRecord(e0, s);
+  }
+  hipError_t err = fn();
+  if (err != hipSuccess) return fail(CSA2_ERR_HIP, "%s launch: %s", name, hipGetErrorString(err));
+  if (e0 && e1) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    (void)hipEventRecord(e1, s);
+    g_timing.pending.push_back({name, e0, e1});
+  }
+  return CSA2_OK;
+}
+
+// ---------------------------------------------------------------- validation helpers
+#define REQ(ptr, what)                                                    \
+  do {                                                                    \
+    if (!(ptr)) return fail(CSA2_ERR_NULL, "%s: %s is NULL", fn, what);   \
+    if (misaligned(ptr))                                                  \
+      return fail(CSA2_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, what); \
+  } while (0)
+
+#define FORBID(ptr, what)                                                          \
+  do {                                                                             \
+    if (ptr) return fail(CSA2_ERR_MODE, "%s: %s must be NULL here", fn, what);     \
+  } while (0)
+
+constexpr int64_t kMaxPagesTotal = (int64_t(1) << 25) - 1;   // physical rows fit in int32
+
+csa2_status check_paging(const char* fn, int32_t B, int32_t max_pages, int32_t n_pages) {
+  if (B < 1) return fail(CSA2_ERR_SHAPE, "%s: B=%d must be >= 1", fn, B);
+  if (max_pages < 1 || (int64_t)max_pages * CSA2_PAGE > INT32_MAX)
+    return fail(CSA2_ERR_SHAPE, "%s: max_pages=%d out of range", fn, max_pages);
+  if (n_pages < 1 || n_pages > kMaxPagesTotal)
+    return fail(CSA2_ERR_SHAPE, "%s: n_pages=%d out of range [1, %lld]", fn, n_pages,
+                (long long)kMaxPagesTotal);
+  return CSA2_OK;
+}
+
+size_t index_ws_bytes(int32_t T, int32_t max_pages) {
+  return round_up((size_t)T * (size_t)max_pages * CSA2_PAGE * sizeof(uint32_t));
+}
+
+size_t attn_ws_bytes(int32_t T, int32_t H, int32_t K) {
+  int S, per;
+  attn_plan(T, H, K, &S, &per);
+  if (S <= 1) return 0;
+  return round_up((size_t)T * S * H * CSA2_D_LAT * sizeof(float)) +
+         round_up((size_t)T * S * H * sizeof(float));
+}
+
+csa2_status check_ws(const char* fn, void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return CSA2_OK;
+  if (!ws) return fail(CSA2_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign)
+    return fail(CSA2_ERR_WORKSPACE, "%s: workspace must be %zu-byte aligned", fn, kWsAlign);
+  if (ws_bytes < need)
+    return fail(CSA2_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  return CSA2_OK;
+}
+
+// ---------------------------------------------------------------- index + top-k
+csa2_status validate_index(const csa2_index_args* a) {
+  const char* fn = "csa2_index_topk";
+  if (!a) return fail(CSA2_ERR_NULL, "%s: args is NULL", fn);
+  if (a->T < 0) return fail(CSA2_ERR_SHAPE, "%s: T=%d < 0", fn, a->T);
+  if (a->H_I < 1 || a->H_I > CSA2_MAX_H_I)
+    return fail(CSA2_ERR_SHAPE, "%s: H_I=%d outside [1, %d]", fn, a->H_I, CSA2_MAX_H_I);
+  if (a->K < 1 || a->K > CSA2_MAX_K)
+    return fail(CSA2_ERR_SHAPE, "%s: K=%d outside [1, %d]", fn, a->K, CSA2_MAX_K);
+  csa2_status st = check_paging(fn, a->B, a->max_pages, a->n_pages);
+  if (st) return st;
+  if (a->T == 0) return CSA2_OK;
+  REQ(a->q_idx, "q_idx");
+  REQ(a->w_idx, "w_idx");
+  REQ(a->k_idx, "k_idx");
+  REQ(a->page_table, "page_table");
+  REQ(a->seq_id, "seq_id");
+  REQ(a->n_vis, "n_vis");
+  REQ(a->idx_out, "idx_out");
+  return CSA2_OK;
+}
+
+csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {
+  if (a->T == 0) return CSA2_OK;
+  const int64_t E = (int64_t)a->max_pages * CSA2_PAGE;
+  IdxScoreParams sp;
+  sp.T = a->T;
+  sp.H_I = a->H_I;
+  sp.max_pages = a->max_pages;
+  sp.chunks = (int)((E + kIdxChunk - 1) / kIdxChunk);
+  sp.key_stride = E;
+  sp.q_idx = static_cast<const uint16_t*>(a->q_idx);
+  sp.w_idx = a->w_idx;
+  sp.k_idx = static_cast<const uint16_t*>(a->k_idx);
+  sp.page_table = a->page_table;
+  sp.seq_id = a->seq_id;
+  sp.n_vis = a->n_vis;
+  sp.keys = static_cast<uint32_t*>(ws);
+  csa2_status st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
+  if (st) return st;
+  TopkParams tp;
+  tp.T = a->T;
+  tp.K = a->K;
+  tp.key_stride = E;
+  tp.keys = sp.keys;
+  tp.n_vis = a->n_vis;
+  tp.idx_out = a->idx_out;
+  return timed("topk", s, [&] { return launch_topk(tp, s); });
+}
+
+// ---------------------------------------------------------------- attention
+csa2_status validate_attn(const csa2_attn_args* a) {
+  const char* fn = "csa2_sparse_attn_fp4";
+  if (!a) return fail(CSA2_ERR_NULL, "%s: args is NULL", fn);
+  if (a->T < 0) return fail(CSA2_ERR_SHAPE, "%s: T=%d < 0", fn, a->T);
+  if (!(a->H == 16 || a->H == 32 || a->H == 64 || a->H == 128))
+    return fail(CSA2_ERR_SHAPE, "%s: H=%d must be 16, 32, 64 or 128", fn, a->H);
+  if (a->K < 1 || a->K > CSA2_MAX_K)
+    return fail(CSA2_ERR_SHAPE, "%s: K=%d outside [1, %d]", fn, a->K, CSA2_MAX_K);
+  csa2_status st = check_paging(fn, a->B, a->max_pages, a->n_pages);
+  if (st) return st;
+  if (!std::isfinite(a->sm_scale)) return fail(CSA2_ERR_SHAPE, "%s: sm_scale not finite", fn);
+  const bool swa = a->q_swa != nullptr;
+  if (swa) {
+    if (a->H_kv < 1 || a->H % a->H_kv != 0)
+      return fail(CSA2_ERR_SHAPE, "%s: H_kv=%d must divide H=%d", fn, a->H_kv, a->H);
+    const int G = a->H / a->H_kv;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8))
+      return fail(CSA2_ERR_SHAPE, "%s: H/H_kv=%d must be 1, 2, 4 or 8", fn, G);
+    if (a->L_swa < 1) return fail(CSA2_ERR_SHAPE, "%s: L_swa=%d < 1", fn, a->L_swa);
+    if (!std::isfinite(a->sm_scale_swa))
+      return fail(CSA2_ERR_SHAPE, "%s: sm_scale_swa not finite", fn);
+  }
+  if (a->T == 0) return CSA2_OK;
+  REQ(a->q, "q");
+  REQ(a->kv_lat, "kv_lat");
+  REQ(a->kv_scl, "kv_scl");
+  REQ(a->kv_rope, "kv_rope");
+  REQ(a->page_table, "page_table");
+  REQ(a->seq_id, "seq_id");
+  REQ(a->idx, "idx");
+  REQ(a->o, "o");
+  REQ(a->lse, "lse");
+  if (swa) {
+    REQ(a->swa_k, "swa_k");
+    REQ(a->swa_v, "swa_v");
+    REQ(a->swa_start, "swa_start");
+    REQ(a->swa_len, "swa_len");
+    REQ(a->o_swa, "o_swa");
+    REQ(a->lse_swa, "lse_swa");
+  } else {
+    FORBID(a->swa_k, "swa_k (no q_swa)");
+    FORBID(a->swa_v, "swa_v (no q_swa)");
+    FORBID(a->swa_start, "swa_start (no q_swa)");
+    FORBID(a->swa_len, "swa_len (no q_swa)");
+    FORBID(a->o_swa, "o_swa (no q_swa)");
+    FORBID(a->lse_swa, "lse_swa (no q_swa)");
+  }
+  return CSA2_OK;
+}
+
+csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
+  if (a->T == 0) return CSA2_OK;
+  int S, per;
+  attn_plan(a->T, a->H, a->K, &S, &per);
+  AttnParams ap;
+  ap.T = a->T;
+  ap.H = a->H;
+  ap.K = a->K;
+  ap.max_pages = a->max_pages;
+  ap.splits = S;
+  ap.per_split = per;
+  ap.sm_scale_log2 = a->sm_scale * 1.4426950408889634f;
+  ap.q = static_cast<const uint16_t*>(a->q);
+  ap.kv_lat = a->kv_lat;
+  ap.kv_scl = a->kv_scl;
+  ap.kv_rope = static_cast<const uint16_t*>(a->kv_rope);
+  ap.page_table = a->page_table;
+  ap.seq_id = a->seq_id;
+  ap.idx = a->idx;
+  ap.o = a->o;
+  ap.lse = a->lse;
+  ap.o_part = nullptr;
+  ap.lse_part = nullptr;
+  if (S > 1) {
+    char* w = static_cast<char*>(ws);
+    ap.o_part = reinterpret_cast<float*>(w);
+    ap.lse_part = reinterpret_cast<float*>(
+        w + round_up((size_t)a->T * S * a->H * CSA2_D_LAT * sizeof(float)));
+  }
+  csa2_status st = timed("sparse_attn", s, [&] { return launch_sparse_attn(ap, s); });
+  if (st) return st;
+  if (S > 1) {
+    MergeParams mp{a->T, a->H, S, ap.o_part, ap.lse_part, a->o, a->lse};
+    st = timed("attn_merge", s, [&] { return launch_attn_merge(mp, s); });
+    if (st) return st;
+  }
+  if (a->q_swa) {
+    SwaParams wp;
+    wp.T = a->T;
+    wp.H = a->H;
+    wp.H_kv = a->H_kv;
+    wp.L_swa = a->L_swa;
+    wp.sm_scale_log2 = a->sm_scale_swa * 1.4426950408889634f;
+    wp.q_swa = static_cast<const uint16_t*>(a->q_swa);
+    wp.k = static_cast<const uint16_t*>(a->swa_k);
+    wp.v = static_cast<const uint16_t*>(a->swa_v);
+    wp.seq_id = a->seq_id;
+    wp.start = a->swa_start;
+    wp.len = a->swa_len;
+    wp.o = a->o_swa;
+    wp.lse = a->lse_swa;
+    st = timed("swa", s, [&] { return launch_swa(wp, s); });
+    if (st) return st;
+  }
+  return CSA2_OK;
+}
+
+// ---------------------------------------------------------------- layer group
+csa2_status validate_group(const csa2_layer_desc* L, int32_t n_layers, const csa2_group_args* g,
+                           csa2_index_args* ia, csa2_attn_args* aa) {
+  const char* fn = "csa2_layer_group";
+  if (!g) return fail(CSA2_ERR_NULL, "%s: group args is NULL", fn);
+  if (!L) return fail(CSA2_ERR_NULL, "%s: layer array is NULL", fn);
+  if (n_layers < 1) return fail(CSA2_ERR_SHAPE, "%s: n_layers=%d < 1", fn, n_layers);
+  if (L[0].mode != CSA2_FULL) return fail(CSA2_ERR_MODE, "%s: layer 0 must be Full", fn);
+  for (int i = 0; i < n_layers; ++i) {
+    const csa2_layer_desc& d = L[i];
+    char what[96];
+    if (d.mode != CSA2_FULL && d.mode != CSA2_REINDEX && d.mode != CSA2_REUSE)
+      return fail(CSA2_ERR_MODE, "%s: layer %d has unknown mode %d", fn, i, d.mode);
+    const bool own_idx = d.mode != CSA2_REUSE, own_kv = d.mode == CSA2_FULL;
+#define LAYER_REQ(field)                                            \
+    do {                                                            \
+      snprintf(what, sizeof(what), "layer %d " #field, i);          \
+      if (g->T > 0) REQ(d.field, what);                             \
+    } while (0)
+#define LAYER_FORBID(field)                                         \
+    do {                                                            \
+      snprintf(what, sizeof(what), "layer %d " #field, i);          \
+      FORBID(d.field, what);                                        \
+    } while (0)
+    LAYER_REQ(q);
+    LAYER_REQ(o);
+    LAYER_REQ(lse);
+    if (own_idx) {
+      LAYER_REQ(q_idx);
+      LAYER_REQ(w_idx);
+      LAYER_REQ(k_idx);
+      LAYER_REQ(idx_out);
+    } else {
+      LAYER_FORBID(q_idx);
+      LAYER_FORBID(w_idx);
+      LAYER_FORBID(k_idx);
+      LAYER_FORBID(idx_out);
+    }
+    if (own_kv) {
+      LAYER_REQ(kv_lat);
+      LAYER_REQ(kv_scl);
+      LAYER_REQ(kv_rope);
+    } else {
+      LAYER_FORBID(kv_lat);
+      LAYER_FORBID(kv_scl);
+      LAYER_FORBID(kv_rope);
+    }
+#undef LAYER_REQ
+#undef LAYER_FORBID
+  }
+  // shapes through the per-op validators (first layer's pointers stand in)
+  *ia = csa2_index_args{g->T, g->B, g->H_I, g->K, g->max_pages, g->n_pages, L[0].q_idx,
+                        L[0].w_idx, L[0].k_idx, g->page_table, g->seq_id, g->n_vis,
+                        L[0].idx_out};
+  csa2_status st = validate_index(ia);
+  if (st) return st;
+  for (int i = 0; i < n_layers; ++i) {
+    aa[i] = csa2_attn_args{};
+    aa[i].T = g->T;
+    aa[i].B = g->B;
+    aa[i].H = g->H;
+    aa[i].K = g->K;
+    aa[i].max_pages = g->max_pages;
+    aa[i].n_pages = g->n_pages;
+    aa[i].q = L[i].q;
+    aa[i].page_table = g->page_table;
+    aa[i].seq_id = g->seq_id;
+    aa[i].sm_scale = g->sm_scale;
+    aa[i].o = L[i].o;
+    aa[i].lse = L[i].lse;
+    aa[i].H_kv = g->H_kv;
+    aa[i].L_swa = g->L_swa;
+    aa[i].q_swa = L[i].q_swa;
+    if (L[i].q_swa) {
+      aa[i].swa_k = L[i].swa_k;
+      aa[i].swa_v = L[i].swa_v;
+      aa[i].swa_start = g->swa_start;
+      aa[i].swa_len = g->swa_len;
+      aa[i].sm_scale_swa = g->sm_scale_swa;
+      aa[i].o_swa = L[i].o_swa;
+      aa[i].lse_swa = L[i].lse_swa;
+    }
+    // resolve KV (nearest Full at or before i) and indices (nearest Full/Reindex)
+    int kv = i, ix = i;
+    while (L[kv].mode != CSA2_FULL) --kv;
+    while (L[ix].mode == CSA2_REUSE) --ix;
+    aa[i].kv_lat = L[kv].kv_lat;
+    aa[i].kv_scl = L[kv].kv_scl;
+    aa[i].kv_rope = L[kv].kv_rope;
+    aa[i].idx = L[ix].idx_out;
+    st = validate_attn(&aa[i]);
+    if (st) {
+      std::string m = g_err;
+      return fail(st, "layer %d: %s", i, m.c_str());
+    }
+  }
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_index_topk(const csa2_index_args* a, void* ws, size_t ws_bytes, void* stream) {
+  csa2_status st = validate_index(a);
+  if (st) return st;
+  st = check_ws("csa2_index_topk", ws, ws_bytes, a->T ? index_ws_bytes(a->T, a->max_pages) : 0);
+  if (st) return st;
+  return run_index(a, ws, static_cast<hipStream_t>(stream));
+}
+
+csa2_status csa2_sparse_attn_fp4(const csa2_attn_args* a, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  csa2_status st = validate_attn(a);
+  if (st) return st;
+  st = check_ws("csa2_sparse_attn_fp4", ws, ws_bytes, a->T ? attn_ws_bytes(a->T, a->H, a->K) : 0);
+  if (st) return st;
+  return run_attn(a, ws, static_cast<hipStream_t>(stream));
+}
+
+csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
+                             const csa2_group_args* g, void* ws, size_t ws_bytes, void* stream) {
+  csa2_index_args ia;
+  if (n_layers > 64) return fail(CSA2_ERR_SHAPE, "csa2_layer_group: n_layers=%d > 64", n_layers);
+  csa2_attn_args aa[64];
+  csa2_status st = validate_group(L, n_layers, g, &ia, aa);
+  if (st) return st;
+  if (g->T == 0) return CSA2_OK;
+  st = check_ws("csa2_layer_group", ws, ws_bytes,
+                csa2_workspace_bytes(CSA2_OP_LAYER_GROUP, g));
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n_layers; ++i) {
+    if (L[i].mode != CSA2_REUSE) {
+      ia.q_idx = L[i].q_idx;
+      ia.w_idx = L[i].w_idx;
+      ia.k_idx = L[i].k_idx;
+      ia.idx_out = L[i].idx_out;
+      st = run_index(&ia, ws, s);
+      if (st) return st;
+    }
+    st = run_attn(&aa[i], ws, s);
+    if (st) return st;
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
+                                const int64_t* dst_row, void* stream) {
+  const char* fn = "csa2_mxfp4_quantize";
+  if (rows < 0) return fail(CSA2_ERR_SHAPE, "%s: rows=%lld < 0", fn, (long long)rows);
+  if (rows > (int64_t)0xffffffff * 4)
+    return fail(CSA2_ERR_SHAPE, "%s: rows=%lld too large", fn, (long long)rows);
+  if (rows == 0) return CSA2_OK;
+  REQ(x, "x");
+  REQ(lat, "lat");
+  REQ(scl, "scl");
+  if (dst_row && misaligned(dst_row))
+    return fail(CSA2_ERR_ALIGN, "%s: dst_row is not 16-byte aligned", fn);
+  QuantParams p{rows, x, lat, scl, dst_row};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed("mxfp4_quantize", s, [&] { return launch_quantize(p, s); });
+}
+
+size_t csa2_workspace_bytes(int32_t op, const void* args) {
+  if (!args) return 0;
+  switch (op) {
+    case CSA2_OP_INDEX_TOPK: {
+      const csa2_index_args* a = static_cast<const csa2_index_args*>(args);
+      if (a->T <= 0 || a->max_pages <= 0) return 0;
+      return index_ws_bytes(a->T, a->max_pages);
+    }
+    case CSA2_OP_SPARSE_ATTN: {
+      const csa2_attn_args* a = static_cast<const csa2_attn_args*>(args);
+      if (a->T <= 0 || a->K <= 0 || a->H <= 0) return 0;
+      return attn_ws_bytes(a->T, a->H, a->K);
+    }
+    case CSA2_OP_LAYER_GROUP: {
+      const csa2_group_args* g = static_cast<const csa2_group_args*>(args);
+      if (g->T <= 0 || g->max_pages <= 0 || g->K <= 0 || g->H <= 0) return 0;
+      const size_t a = index_ws_bytes(g->T, g->max_pages);
+      const size_t b = attn_ws_bytes(g->T, g->H, g->K);
+      return a > b ? a : b;
+    }
+    default:
+      return 0;
+  }
+}
+
+const char* csa2_last_error(void) { return g_err.c_str(); }
+
+const char* csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_ERR_NULL: return "CSA2_ERR_NULL";
+    case CSA2_ERR_SHAPE: return "CSA2_ERR_SHAPE";
+    case CSA2_ERR_ALIGN: return "CSA2_ERR_ALIGN";
+    case CSA2_ERR_MODE: return "CSA2_ERR_MODE";
+    case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE";
+    case CSA2_ERR_UNSUPPORTED: return "CSA2_ERR_UNSUPPORTED";
+    case CSA2_ERR_HIP: return "CSA2_ERR_HIP";
+  }
+  return "CSA2_ERR_UNKNOWN";
+}
+
+int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+csa2_status csa2_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return CSA2_OK;
+}
+
+int32_t csa2_timing_read(char* names_64, int64_t* launches, double* total_ms, int32_t max) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (const TimedLaunch& tl : g_timing.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(tl.e1) != hipSuccess) continue;
+    if (hipEventElapsedTime(&ms, tl.e0, tl.e1) != hipSuccess) continue;
+    size_t k = 0;
+    while (k < g_timing.names.size() && g_timing.names[k] != tl.name) ++k;
+    if (k == g_timing.names.size()) {
+      g_timing.names.emplace_back(tl.name);
+      g_timing.launches.push_back(0);
+      g_timing.ms.push_back(0.0);
+    }
+    g_timing.launches[k] += 1;
+    g_timing.ms[k] += ms;
+  }
+  g_timing.pending.clear();
+  g_timing.used = 0;
+  int32_t n = 0;
+  for (size_t k = 0; k < g_timing.names.size() && n < max; ++k, ++n) {
+    if (names_64) {
+      memset(names_64 + 64 * n, 0, 64);
+      strncpy(names_64 + 64 * n, g_timing.names[k].c_str(), 63);
+    }
+    if (launches) launches[n] = g_timing.launches[k];
+    if (total_ms) total_ms[n] = g_timing.ms[k];
+  }
+  g_timing.names.clear();
+  g_timing.launches.clear();
+  g_timing.ms.clear();
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal declarations of the CSA2 gfx950 library: kernel parameter blocks, launchers
+// and small device helpers.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kLat = 512;        // latent channels (E2M1 codes, 2 per byte)
+constexpr int kLatBytes = 256;
+constexpr int kScl = 16;         // E8M0 scale bytes per entry (one per 32 channels)
+constexpr int kRope = 64;        // rope channels (bf16)
+constexpr int kDq = 576;
+constexpr int kDidx = 64;
+constexpr int kDswa = 128;
+constexpr int kPage = 64;
+
+// ---------------------------------------------------------------- parameter blocks
+struct IdxScoreParams {
+  int T, H_I, max_pages, chunks;       // chunks = blocks per row
+  int64_t key_stride;                  // u32 keys per row in the workspace
+  const uint16_t* q_idx;               // [T, H_I, 64]
+  const float* w_idx;                  // [T, H_I]
+  const uint16_t* k_idx;               // [n_pages*64, 64]
+  const int32_t* page_table;
+  const int32_t* seq_id;
+  const int32_t* n_vis;
+  uint32_t* keys;                      // [T, key_stride] order-preserving keys
+};
+
+struct TopkParams {
+  int T, K;
+  int64_t key_stride;
+  const uint32_t* keys;
+  const int32_t* n_vis;
+  int32_t* idx_out;                    // [T, K]
+};
+
+struct AttnParams {
+  int T, H, K, max_pages, splits, per_split;   // per_split: idx slots per split
+  float sm_scale_log2;                          // sm_scale * log2(e)
+  const uint16_t* q;                            // [T, H, 576]
+  const uint8_t* kv_lat;
+  const uint8_t* kv_scl;
+  const uint16_t* kv_rope;
+  const int32_t* page_table;
+  const int32_t* seq_id;
+  const int32_t* idx;                           // [T, K]
+  float* o;                                     // final [T, H, 512] when splits == 1
+  float* lse;
+  float* o_part;                                // [T, splits, H, 512] when splits > 1
+  float* lse_part;                              // [T, splits, H]
+};
+
+struct MergeParams {
+  int T, H, splits;
+  const float* o_part;
+  const float* lse_part;
+  float* o;
+  float* lse;
+};
+
+struct SwaParams {
+  int T, H, H_kv, L_swa;
+  float sm_scale_log2;
+  const uint16_t* q_swa;               // [T, H, 128]
+  const uint16_t* k;                   // [B, L_swa, H_kv, 128]
+  const uint16_t* v;
+  const int32_t* seq_id;
+  const int32_t* start;
+  const int32_t* len;
+  float* o;                            // [T, H, 128]
+  float* lse;                          // [T, H]
+};
+
+struct QuantParams {
+  int64_t rows;
+  const float* x;                      // [rows, 512]
+  uint8_t* lat;
+  uint8_t* scl;
+  const int64_t* dst_row;              // may be null
+};
+
+// ---------------------------------------------------------------- launch geometry
+constexpr int kIdxChunk = 1024;        // entries scored per workgroup
+constexpr int kTopkThreads = 1024;
+
+// Split plan of the attention launch: `splits` workgroups per row, each covering
+// `per_split` (a multiple of 32, <= 2048) consecutive index slots.
+void attn_plan(int T, int H, int K, int* splits, int* per_split);
+
+// ---------------------------------------------------------------- launchers
+// Each launcher enqueues one kernel on `s` and returns hipGetLastError().
+hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s);
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_swa(const SwaParams& p, hipStream_t s);
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+
+}  // namespace csa2

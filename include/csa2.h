@@ -1,0 +1,219 @@
+/*
+ * csa2.h -- C ABI of the CSA2 (Compressed Sparse Attention 2) decode/prefill hot path
+ * for AMD MI355X (gfx950).
+ *
+ * What the path computes (sources cited by page and section):
+ *   [summary] picx.dev whiteboard summary "DeepSeek-V4.1-Flash: Pushing the Limits of KV
+ *             Cache Compression", Methodology > Architecture Components:
+ *             item 2 (CSA2: Full / Reindex / Reuse modes), item 5 (FP4 main KV cache);
+ *             Introduction (global branch + local sliding-window branch).
+ *   [blog]    cyber-feed.org repost of the blog article of the same title, introduction
+ *             (sparse attention covering the whole context combined with SWA).
+ * Per query row: an indexer scores the visible compressed entries, a Top-K selects a
+ * set, the attention gathers the selected entries from an MXFP4 cache (E2M1 codes, one
+ * E8M0 scale per 32 channels), dequantizes them in registers and runs softmax attention
+ * over them; a bf16 sliding-window branch attends over the last tokens.  Readings of the
+ * points the pages leave open (indexer form, scale format, tie-break, branch outputs):
+ *   score[t, j] = sum_h w_idx[t, h] * max(0, q_idx[t, h, :] . k_idx[j, :])
+ *   Top-K order: descending score, ascending index; output ascending, -1 padded
+ *   global key  = [dequant(latent) (512) ; rope (64)], value = dequant(latent) (512),
+ *                 shared by all heads; logit = sm_scale * q . key
+ *   the two branches are returned separately as (o, lse) pairs.
+ *
+ * Conventions (all entry points):
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     No host synchronisation, no allocation: the caller owns all memory, including
+ *     the workspace, whose size csa2_workspace_bytes() returns.
+ *   - "device" pointers are device memory and must be 16-byte aligned.
+ *   - bf16 tensors are raw 16-bit patterns; all layouts are dense row-major.
+ *   - Paged caches: 64 entries per page; entry j of sequence b lives in physical row
+ *     page_table[b * max_pages + j / 64] * 64 + j % 64 of every per-entry plane.
+ *   - Arguments are validated on the host before any HIP call; a failure returns a
+ *     status and sets a thread-local message (csa2_last_error) and launches nothing.
+ *     Device contents are preconditions, not checked: indices in [0, n_vis) or -1,
+ *     page-table entries of visible entries in [0, n_pages), finite inputs.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+#define CSA2_D_LAT 512   /* latent channels per entry (MXFP4) */
+#define CSA2_D_ROPE 64   /* rope channels per entry (bf16) */
+#define CSA2_D_Q 576     /* query head dim of the global branch */
+#define CSA2_D_IDX 64    /* indexer query/key dim (bf16) */
+#define CSA2_D_SWA 128   /* sliding-window head dim (bf16) */
+#define CSA2_PAGE 64     /* entries per page */
+#define CSA2_MAX_H_I 16  /* indexer heads */
+#define CSA2_MAX_K 65536 /* Top-K size */
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
+  CSA2_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  CSA2_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  CSA2_ERR_MODE = 4,        /* bad layer-group schedule or a buffer the mode forbids */
+  CSA2_ERR_WORKSPACE = 5,   /* workspace NULL/misaligned or smaller than required */
+  CSA2_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  CSA2_ERR_HIP = 7          /* a HIP call failed; csa2_last_error has HIP's message */
+} csa2_status;
+
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+
+/* Operation codes for csa2_workspace_bytes. */
+enum { CSA2_OP_INDEX_TOPK = 1, CSA2_OP_SPARSE_ATTN = 2, CSA2_OP_LAYER_GROUP = 3 };
+
+/* Indexer scoring + Top-K ([summary] Architecture Components, item 2: Full and Reindex
+ * layers compute fresh Top-K indices from the indexer key).
+ * For each row t: scores the entries j < n_vis[t] of sequence seq_id[t], selects
+ * min(K, n_vis[t]) of them by (score desc, index asc) and writes them to
+ * idx_out[t, 0:K] in ascending order, -1 in the unused tail. */
+typedef struct csa2_index_args {
+  int32_t T;          /* query rows, >= 0 */
+  int32_t B;          /* sequences (rows of page_table), >= 1 */
+  int32_t H_I;        /* indexer heads, 1..16 */
+  int32_t K;          /* selected entries per row, 1..CSA2_MAX_K */
+  int32_t max_pages;  /* page_table row stride; n_vis[t] <= max_pages * 64 */
+  int32_t n_pages;    /* physical pages in k_idx */
+  const void* q_idx;           /* device bf16 [T, H_I, 64] */
+  const float* w_idx;          /* device f32  [T, H_I] */
+  const void* k_idx;           /* device bf16 [n_pages, 64, 64] (one 64-d key per entry) */
+  const int32_t* page_table;   /* device i32  [B, max_pages] */
+  const int32_t* seq_id;       /* device i32  [T], in [0, B) */
+  const int32_t* n_vis;        /* device i32  [T], visible entries, 0..max_pages*64 */
+  int32_t* idx_out;            /* device i32  [T, K] (output) */
+} csa2_index_args;
+
+/* Sparse global attention over the selected FP4 entries plus the bf16 sliding-window
+ * branch ([summary] Architecture Components, items 2 and 5; Introduction).
+ * Global branch, per row t and head h (entries of sequence seq_id[t]):
+ *   logit_j = sm_scale * (q[t,h,0:512] . v_j + q[t,h,512:576] . rope_j),  j in idx[t,:],
+ *   v_j = e2m1(code) * 2^(scale - 127)  (low nibble = even channel),
+ *   o[t,h,:] = sum_j softmax(logit)_j v_j,  lse[t,h] = log sum_j exp(logit_j);
+ *   no valid index: o = 0, lse = -inf.
+ * SWA branch (skipped when q_swa is NULL, then every SWA pointer must be NULL):
+ *   keys/values at positions [swa_start[t], swa_start[t] + swa_len[t]) of sequence
+ *   seq_id[t], KV head h * H_kv / H, logit = sm_scale_swa * q_swa . k;
+ *   o_swa = softmax-weighted values (128-d), lse_swa; empty window: 0 / -inf.
+ * Numerics: q.k in bf16 MFMA with fp32 accumulation; the probability-value product in
+ * fp16 MFMA with fp32 accumulation (dequantized values are exact in fp16 for scale
+ * bytes 104..140, i.e. |v| <= 49152 -- the pages bound KV magnitudes by ~22.6);
+ * softmax and outputs in fp32. */
+typedef struct csa2_attn_args {
+  int32_t T;          /* query rows */
+  int32_t B;          /* sequences */
+  int32_t H;          /* query heads: 16, 32, 64 or 128 */
+  int32_t K;          /* index slots per row, 1..CSA2_MAX_K */
+  int32_t max_pages;
+  int32_t n_pages;
+  const void* q;               /* device bf16 [T, H, 576] */
+  const uint8_t* kv_lat;       /* device u8   [n_pages, 64, 256] E2M1 codes */
+  const uint8_t* kv_scl;       /* device u8   [n_pages, 64, 16]  E8M0 scales */
+  const void* kv_rope;         /* device bf16 [n_pages, 64, 64] */
+  const int32_t* page_table;   /* device i32  [B, max_pages] */
+  const int32_t* seq_id;       /* device i32  [T] */
+  const int32_t* idx;          /* device i32  [T, K] entry indices or -1 */
+  float sm_scale;              /* logit scale, e.g. 1/sqrt(576) */
+  float* o;                    /* device f32 [T, H, 512] (output) */
+  float* lse;                  /* device f32 [T, H]      (output, natural log) */
+  /* sliding-window branch */
+  int32_t H_kv;                /* SWA KV heads, H % H_kv == 0, H / H_kv <= 8 */
+  int32_t L_swa;               /* SWA buffer positions per sequence */
+  const void* q_swa;           /* device bf16 [T, H, 128] or NULL */
+  const void* swa_k;           /* device bf16 [B, L_swa, H_kv, 128] */
+  const void* swa_v;           /* device bf16 [B, L_swa, H_kv, 128] */
+  const int32_t* swa_start;    /* device i32 [T] */
+  const int32_t* swa_len;      /* device i32 [T], window length, start+len <= L_swa */
+  float sm_scale_swa;          /* e.g. 1/sqrt(128) */
+  float* o_swa;                /* device f32 [T, H, 128] (output) */
+  float* lse_swa;              /* device f32 [T, H]      (output) */
+} csa2_attn_args;
+
+/* One layer of a Full / Reindex / Reuse group ([summary] Architecture Components,
+ * item 2).  Full: own main KV planes + own indexer (q_idx, w_idx, k_idx) -> idx_out.
+ * Reindex: main KV of the nearest preceding Full layer, own indexer -> idx_out.
+ * Reuse: main KV of the nearest preceding Full layer and the indices of the nearest
+ * preceding Full/Reindex layer; it must leave every indexer/KV/idx_out field NULL.
+ * Every layer has its own q, SWA caches and outputs. */
+typedef struct csa2_layer_desc {
+  int32_t mode;                /* csa2_mode */
+  const void* q;               /* bf16 [T, H, 576] */
+  const void* q_swa;           /* bf16 [T, H, 128] or NULL (then no SWA for this layer) */
+  const void* q_idx;           /* bf16 [T, H_I, 64]  (Full, Reindex) */
+  const float* w_idx;          /* f32  [T, H_I]      (Full, Reindex) */
+  const void* k_idx;           /* bf16 [n_pages, 64, 64] (Full, Reindex) */
+  const uint8_t* kv_lat;       /* Full only */
+  const uint8_t* kv_scl;       /* Full only */
+  const void* kv_rope;         /* Full only */
+  const void* swa_k;           /* bf16 [B, L_swa, H_kv, 128] */
+  const void* swa_v;
+  int32_t* idx_out;            /* i32 [T, K] (Full, Reindex; output) */
+  float* o;                    /* f32 [T, H, 512] */
+  float* lse;                  /* f32 [T, H] */
+  float* o_swa;                /* f32 [T, H, 128] */
+  float* lse_swa;              /* f32 [T, H] */
+} csa2_layer_desc;
+
+/* Shapes and per-row metadata shared by the layers of a group. */
+typedef struct csa2_group_args {
+  int32_t T, B, H, H_I, K, H_kv, L_swa, max_pages, n_pages;
+  const int32_t* page_table;   /* [B, max_pages] */
+  const int32_t* seq_id;       /* [T] */
+  const int32_t* n_vis;        /* [T] */
+  const int32_t* swa_start;    /* [T] */
+  const int32_t* swa_len;      /* [T] */
+  float sm_scale, sm_scale_swa;
+} csa2_group_args;
+
+/* Indexer scoring + Top-K.  Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, a). */
+csa2_status csa2_index_topk(const csa2_index_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse FP4 global attention + SWA.  Workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, a)
+ * (may be 0, then ws may be NULL). */
+csa2_status csa2_sparse_attn_fp4(const csa2_attn_args* a, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* A Full/Reindex/Reuse layer group, layers run in order on `stream`; L[0] must be Full.
+ * Workspace: csa2_workspace_bytes(CSA2_OP_LAYER_GROUP, g). */
+csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
+                             const csa2_group_args* g, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* MXFP4 cache write ([summary] Architecture Components, item 5): quantizes `rows` fp32
+ * latent rows x [rows, 512] into physical rows dst_row[r] of the planes
+ * lat [*, 256] and scl [*, 16] (OCP MX: shared exponent floor(log2 max|x|) - 2 over each
+ * 32-channel block, clamped to [-127, 127]; elements rounded to E2M1 to nearest, ties to
+ * the even code, saturating at 6; sign kept on zeros).  dst_row NULL = rows 0..rows-1.
+ * Inputs must be finite. */
+csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
+                                const int64_t* dst_row, void* stream);
+
+/* Workspace bytes for an operation; args points to the op's argument struct
+ * (csa2_index_args, csa2_attn_args or csa2_group_args).  Returns 0 for NULL args. */
+size_t csa2_workspace_bytes(int32_t op, const void* args);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* csa2_last_error(void);
+const char* csa2_status_string(csa2_status s);
+int32_t csa2_abi_version(void);
+
+/* Kernel timing: while enabled, the library records a HIP event pair on the launch
+ * stream around every kernel it launches and accumulates the elapsed time per kernel
+ * name.  csa2_timing_read synchronizes on the recorded events, returns the number of
+ * distinct kernels (at most `max`) with their names (NUL-terminated, 64 bytes each),
+ * launch counts and total milliseconds, and resets the totals. */
+csa2_status csa2_timing_enable(int32_t on);
+int32_t csa2_timing_read(char* names_64, int64_t* launches, double* total_ms, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -126,6 +126,11 @@ class Workload:
     shuffle: bool = True
     prefill: bool = False
     modes: list = field(default_factory=lambda: [FULL])
+    # explicit per-row metadata (ragged test cases); None = the workload's own rule
+    seq_id_rows: np.ndarray | None = None
+    n_vis_rows: np.ndarray | None = None
+    swa_start_rows: np.ndarray | None = None
+    swa_len_rows: np.ndarray | None = None
 
     @property
     def P(self) -> int:
@@ -137,11 +142,15 @@ class Workload:
 
     # ---- per-row metadata -------------------------------------------------
     def seq_id(self) -> np.ndarray:
+        if self.seq_id_rows is not None:
+            return np.asarray(self.seq_id_rows, np.int32)
         if self.prefill:
             return np.zeros(self.T, dtype=np.int32)
         return (np.arange(self.T, dtype=np.int64) % self.B).astype(np.int32)
 
     def n_vis(self) -> np.ndarray:
+        if self.n_vis_rows is not None:
+            return np.asarray(self.n_vis_rows, np.int32)
         if self.prefill:
             # Entry j (raw tokens 4j..4j+3) is visible once its block is complete.
             prefix = self.E - self.T // 4
@@ -150,11 +159,15 @@ class Workload:
         return np.full(self.T, self.E, dtype=np.int32)
 
     def swa_start(self) -> np.ndarray:
+        if self.swa_start_rows is not None:
+            return np.asarray(self.swa_start_rows, np.int32)
         if self.prefill:
             return np.arange(self.T, dtype=np.int32)
         return np.full(self.T, self.L_swa - self.n_win, dtype=np.int32)
 
     def swa_len(self) -> np.ndarray:
+        if self.swa_len_rows is not None:
+            return np.asarray(self.swa_len_rows, np.int32)
         return np.full(self.T, self.n_win, dtype=np.int32)
 
     def page_table(self) -> np.ndarray:

@@ -1,0 +1,248 @@
+"""GPU parity: the gfx950 library (through its C ABI) against the CPU oracle.
+
+Each case prints its name before running so a failure on the GPU names the case.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+import csa2_testlib as tl
+from oracle import oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    from fp4_compressed_sparse_amd import csa2 as c
+    return c
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def W(**kw):
+    base = dict(name="t", B=2, T=2, E=1024, H=64, H_I=8, K=256, H_kv=64, L_swa=128, seed=77,
+                hot="uniform", n_hot=10, shuffle=True)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+SMALL = {
+    "cfg1_decode_1x4k_h16": synth.workload(1),
+    "ragged_b3_t5_h64_gqa4": W(B=3, T=5, E=1536, K=512, H_kv=16, L_swa=200,
+                               seq_id_rows=[0, 1, 2, 1, 0], n_vis_rows=[1536, 700, 33, 1100, 1],
+                               swa_start_rows=[0, 72, 199, 10, 5],
+                               swa_len_rows=[128, 128, 1, 0, 77]),
+    "k_not_tile_multiple_h32_gqa8": W(B=2, T=3, E=640, H=32, H_I=3, K=100, H_kv=4, L_swa=64,
+                                      seq_id_rows=[1, 0, 1], n_vis_rows=[640, 99, 350],
+                                      swa_start_rows=[0, 0, 3], swa_len_rows=[64, 17, 61]),
+    "h128_hi16_k64": W(B=1, T=2, E=512, H=128, H_I=16, K=64, H_kv=128, L_swa=128, n_hot=4),
+    "h16_shuffled_b4_k2048": W(B=4, T=4, E=4096, H=16, H_I=4, K=2048, H_kv=16),
+    "many_splits_b1_k2048_h64": W(B=1, T=1, E=8192, H=64, H_I=8, K=2048, H_kv=64),
+}
+
+
+def test_quantize_bit_exact(csa2, dev):
+    _say("quantize_bit_exact")
+    rng = np.random.default_rng(1)
+    rows = 512
+    x = synth.normal_f32(5, 1, 0, rows * 512).reshape(rows, 512)
+    mult = (2.0 ** rng.integers(-30, 30, size=(rows, 16))).astype(np.float32)
+    x = (x.reshape(rows, 16, 32) * mult[:, :, None]).reshape(rows, 512).astype(np.float32)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 7.5], np.float32)
+    for r in range(rows):
+        blk = rng.integers(0, 16)
+        sc = np.float32(2.0 ** rng.integers(-8, 8))
+        x[r, blk * 32: blk * 32 + 10] = ties * sc * rng.choice([-1, 1], 10)
+    x[0, :32] = 0.0
+    x[0, 3] = -0.0
+    x[1, :32] = np.float32(1e-40) * np.arange(32)            # subnormal block
+    x[2, 32:64] = np.float32(3e38) * rng.choice([-1, 1], 32)  # near the float maximum
+    lat_ref, scl_ref = orc.mxfp4_quantize(x)
+    xd = torch.from_numpy(x).to(dev)
+    lat = torch.zeros((rows, 256), dtype=torch.uint8, device=dev)
+    scl = torch.zeros((rows, 16), dtype=torch.uint8, device=dev)
+    csa2.mxfp4_quantize(xd, lat, scl)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lat.cpu().numpy(), lat_ref)
+    np.testing.assert_array_equal(scl.cpu().numpy(), scl_ref)
+    # scattered destination rows
+    perm = rng.permutation(rows + 7)[:rows]
+    lat2 = torch.zeros((rows + 7, 256), dtype=torch.uint8, device=dev)
+    scl2 = torch.zeros((rows + 7, 16), dtype=torch.uint8, device=dev)
+    csa2.mxfp4_quantize(xd, lat2, scl2, torch.from_numpy(perm.astype(np.int64)).to(dev))
+    np.testing.assert_array_equal(lat2.cpu().numpy()[perm], lat_ref)
+    np.testing.assert_array_equal(scl2.cpu().numpy()[perm], scl_ref)
+
+
+def _index_parity(csa2, dev, w, name):
+    _say("index_topk", name)
+    d = tl.DeviceWorkload(w, dev)
+    L = d.layers[0]
+    idx = csa2.index_topk(L["q_idx"], L["w_idx"], L["k_idx"], d.page_table, d.seq_id, d.n_vis,
+                          w.K)
+    torch.cuda.synchronize()
+    h = tl.HostWorkload(w)
+    rows = np.arange(w.T)
+    tl.check_topk(idx.cpu().numpy(), h.scores(0, rows), w.K, w.n_vis())
+    return d, h, idx
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_index_topk_parity(csa2, dev, name):
+    _index_parity(csa2, dev, SMALL[name], name)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_sparse_attn_parity(csa2, dev, name):
+    w = SMALL[name]
+    d, h, idx = _index_parity(csa2, dev, w, name)
+    _say("sparse_attn", name)
+    L = d.layers[0]
+    o, lse, ow, lw = csa2.sparse_attn_fp4(L["q"], L["kv_lat"], L["kv_scl"], L["kv_rope"],
+                                          d.page_table, d.seq_id, idx, q_swa=L["q_swa"],
+                                          swa_k=L["swa_k"], swa_v=L["swa_v"],
+                                          swa_start=d.swa_start, swa_len=d.swa_len)
+    torch.cuda.synchronize()
+    rows = np.arange(w.T)
+    ref = h.attn_on(idx.cpu().numpy(), 0, rows)
+    res = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy(), "o_swa": ow.cpu().numpy(),
+           "lse_swa": lw.cpu().numpy()}
+    tl.check_attn(res, ref)
+
+
+def test_attn_arbitrary_index_lists(csa2, dev):
+    """Holes, empty rows, unsorted lists and repeated entries (the attention is defined for
+    any index list; the oracle runs on the same list)."""
+    _say("attn_arbitrary_index_lists")
+    w = W(B=2, T=4, E=1024, K=96, H=64, seq_id_rows=[0, 1, 1, 0])
+    d = tl.DeviceWorkload(w, dev)
+    h = tl.HostWorkload(w)
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, 1024, size=(4, 96)).astype(np.int32)
+    idx[0, ::3] = -1                 # holes
+    idx[1, :] = -1                   # empty row
+    idx[2, 40:] = -1                 # ragged tail
+    idx[3, 10:20] = idx[3, 0]        # repeated entry
+    L = d.layers[0]
+    o, lse = csa2.sparse_attn_fp4(L["q"], L["kv_lat"], L["kv_scl"], L["kv_rope"], d.page_table,
+                                  d.seq_id, torch.from_numpy(idx).to(dev))
+    torch.cuda.synchronize()
+    ref = h.attn_on(idx, 0, np.arange(4))
+    res = {"o": o.cpu().numpy(), "lse": lse.cpu().numpy()}
+    tl.check_attn(res, ref, swa=False)
+    assert np.all(res["o"][1] == 0) and np.all(np.isneginf(res["lse"][1]))
+
+
+def test_topk_all_equal_scores(csa2, dev):
+    """Every entry scores the same: the lowest K indices win, in order."""
+    _say("topk_all_equal_scores")
+    E, K = 4096, 300
+    key = torch.from_numpy(synth.normal_bf16(9, 1, 0, 64).view(np.int16)).to(dev)
+    k_idx = key.view(1, 1, 64).expand(E // 64, 64, 64).contiguous().view(torch.bfloat16)
+    q = torch.from_numpy(synth.normal_bf16(9, 2, 0, 2 * 64).view(np.int16)).to(dev).view(
+        torch.bfloat16).view(2, 1, 64)
+    wv = torch.ones((2, 1), dtype=torch.float32, device=dev)
+    pt = torch.arange(E // 64, dtype=torch.int32, device=dev).view(1, -1)
+    sid = torch.zeros(2, dtype=torch.int32, device=dev)
+    nv = torch.tensor([E, 1000], dtype=torch.int32, device=dev)
+    idx = csa2.index_topk(q, wv, k_idx, pt, sid, nv, K).cpu().numpy()
+    np.testing.assert_array_equal(idx[0], np.arange(K))
+    np.testing.assert_array_equal(idx[1], np.arange(K))
+
+
+def test_empty_rows_and_windows(csa2, dev):
+    _say("empty_rows_and_windows")
+    w = W(B=2, T=3, E=512, K=64, H=16, H_I=2, H_kv=16, seq_id_rows=[0, 1, 0],
+          n_vis_rows=[0, 512, 5], swa_start_rows=[0, 0, 0], swa_len_rows=[0, 128, 0])
+    d = tl.DeviceWorkload(w, dev)
+    res = d.run_layer_group()[0]
+    assert np.all(res["idx"][0] == -1)
+    np.testing.assert_array_equal(res["idx"][2], np.r_[np.arange(5), -np.ones(59, np.int32)])
+    assert np.all(res["o"][0] == 0) and np.all(np.isneginf(res["lse"][0]))
+    assert np.all(res["o_swa"][0] == 0) and np.all(np.isneginf(res["lse_swa"][0]))
+    assert np.all(res["o_swa"][2] == 0) and np.all(np.isneginf(res["lse_swa"][2]))
+    h = tl.HostWorkload(w)
+    rows = np.arange(3)
+    tl.check_topk(res["idx"], h.scores(0, rows), w.K, w.n_vis())
+    tl.check_attn(res, h.attn_on(res["idx"], 0, rows))
+    # T = 0 is a no-op
+    L = d.layers[0]
+    z = csa2.index_topk(L["q_idx"][:0], L["w_idx"][:0], L["k_idx"], d.page_table,
+                        d.seq_id[:0], d.n_vis[:0], w.K)
+    assert z.shape == (0, w.K)
+
+
+def _group_case(csa2, dev, w, rows, name):
+    _say("layer_group", name)
+    d = tl.DeviceWorkload(w, dev)
+    res = d.run_layer_group()
+    torch.cuda.synchronize()
+    h = tl.HostWorkload(w)
+    ref = h.run_layer_group(rows)
+    nb = 0
+    for li in range(len(w.modes)):
+        nb += tl.check_topk(res[li]["idx"], ref[li]["scores"], w.K, w.n_vis(), rows=rows)
+        oref = h.attn_on(res[li]["idx"][rows], li, rows)
+        tl.check_attn(res[li], oref, rows=rows)
+    # Reuse borrows Reindex's indices; Reindex's differ from Full's (independent indexers)
+    if w.modes == [0, 1, 2]:
+        np.testing.assert_array_equal(res[2]["idx"], res[1]["idx"])
+        assert not np.array_equal(res[1]["idx"], res[0]["idx"])
+    return d, res, nb
+
+
+def test_layer_group_full_reindex_reuse(csa2, dev):
+    w = W(name="group_small", B=4, T=4, E=2048, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
+          modes=[0, 1, 2])
+    _group_case(csa2, dev, w, np.arange(4), "group_small")
+
+
+def test_determinism(csa2, dev):
+    _say("determinism")
+    w = W(B=4, T=8, E=4096, K=1024, H=64, seq_id_rows=[0, 1, 2, 3, 3, 2, 1, 0])
+    d = tl.DeviceWorkload(w, dev)
+    a = d.run_layer_group()[0]
+    b = d.run_layer_group()[0]
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# ---------------------------------------------------------------- full sizes
+def test_full_size_decode_64x128k_sampled(csa2, dev):
+    """The headline decode workload (64 rows, 32768 entries each, K=2048, H=64) in the same
+    launch configuration the benchmark times; the oracle checks sampled rows, and every
+    row's selection is checked for validity."""
+    w = synth.workload(2)
+    rows = np.array([0, 1, 17, 42, 63])
+    d, res, _ = _group_case(csa2, dev, w, rows, w.name)
+    idx = res[0]["idx"]
+    assert np.all(np.diff(idx, axis=1) > 0) and idx.min() >= 0 and idx.max() < w.E
+
+
+def test_full_size_decode_4x1m(csa2, dev):
+    w = synth.workload(4)
+    _group_case(csa2, dev, w, np.arange(4), w.name)
+
+
+def test_full_size_group_32x256k_sampled(csa2, dev):
+    w = synth.workload(3)
+    _group_case(csa2, dev, w, np.array([0, 13, 31]), w.name)
+
+
+def test_full_size_prefill_4096_sampled(csa2, dev):
+    w = synth.workload(5)
+    rows = np.unique(np.r_[[0, 1, 2, 3, 4095], np.arange(0, 4096, 64)])
+    _group_case(csa2, dev, w, rows, w.name)
