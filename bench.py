@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 decode hot path on one MI355X.
+
+Workload (the headline decode case): 64 query rows, each with its own 128K-token context
+compressed 4:1 into 32,768 MXFP4 entries (512-d E2M1 latent + per-32 E8M0 scales + 64-d
+bf16 rope, paged in 64-entry pages through a shuffled page table), 64 query heads of dim
+576, an 8-head x 64 bf16 indexer, Top-K = 2048, and a bf16 sliding window of 128 tokens
+with 64 KV heads of dim 128.  Seeded synthetic N(0,1) data, 1% hot indexer keys.
+
+One step = one Full-mode CSA2 layer through csa2_layer_group: indexer scoring, Top-K,
+FP4 gather attention (+ split merge) and the SWA branch, inputs resident in HBM.
+Prints one JSON line (metric: decode query-tokens/s), with the dominant kernel's roofline
+(algorithmic bytes / its average duration, from HIP events on the launch stream) and the
+CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1..5: which named workload (2 = the headline decode)")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="query rows of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------- inputs
+class Inputs:
+    """Device-resident inputs of one workload, built from the seeded generator; the MXFP4
+    planes are written by the library's own quantizer."""
+
+    def __init__(self, w, dev):
+        import numpy as np
+        import torch
+        from fp4_compressed_sparse_amd import csa2
+        self.w, self.dev, self.csa2 = w, dev, csa2
+        pt = w.page_table()
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        b16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+        self.page_table = t(pt.astype(np.int32))
+        self.seq_id, self.n_vis = t(w.seq_id()), t(w.n_vis())
+        self.swa_start, self.swa_len = t(w.swa_start()), t(w.swa_len())
+        rows_per_page = 64
+        self.layers = []
+        for li, m in enumerate(w.modes):
+            L = {"mode": m, "q": b16(w.q(li)), "q_swa": b16(w.q_swa(li)),
+                 "swa_k": b16(w.swa_k(li)), "swa_v": b16(w.swa_v(li))}
+            if m in (0, 1):
+                L["q_idx"], L["w_idx"] = b16(w.q_idx(li)), t(w.w_idx(li))
+                kidx = torch.empty((w.n_pages, rows_per_page, 64), dtype=torch.bfloat16,
+                                   device=dev)
+                for b in range(w.B):
+                    kidx.view(-1, 64)[t(w.physical_rows(b, pt))] = b16(w.k_idx_seq(b, li))
+                L["k_idx"] = kidx
+                L["idx_out"] = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+            if m == 0:
+                lat = torch.empty((w.n_pages, 64, 256), dtype=torch.uint8, device=dev)
+                scl = torch.empty((w.n_pages, 64, 16), dtype=torch.uint8, device=dev)
+                rope = torch.empty((w.n_pages, 64, 64), dtype=torch.bfloat16, device=dev)
+                for b in range(w.B):
+                    dst = t(w.physical_rows(b, pt))
+                    csa2.mxfp4_quantize(t(w.latent_seq(b, li)), lat, scl, dst)
+                    rope.view(-1, 64)[dst] = b16(w.rope_seq(b, li))
+                L["kv_lat"], L["kv_scl"], L["kv_rope"] = lat, scl, rope
+            L["o"] = torch.empty((w.T, w.H, 512), dtype=torch.float32, device=dev)
+            L["lse"] = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+            L["o_swa"] = torch.empty((w.T, w.H, 128), dtype=torch.float32, device=dev)
+            L["lse_swa"] = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+            self.layers.append(L)
+        self.g = csa2.group_args(w.T, w.B, w.H, w.H_I, w.K, w.H_kv, w.L_swa, w.P, w.n_pages,
+                                 self.page_table, self.seq_id, self.n_vis, self.swa_start,
+                                 self.swa_len)
+        self.descs = [csa2.layer_desc(
+            L["mode"], L["q"], L["o"], L["lse"], q_swa=L["q_swa"], q_idx=L.get("q_idx"),
+            w_idx=L.get("w_idx"), k_idx=L.get("k_idx"), kv_lat=L.get("kv_lat"),
+            kv_scl=L.get("kv_scl"), kv_rope=L.get("kv_rope"), swa_k=L["swa_k"],
+            swa_v=L["swa_v"], idx_out=L.get("idx_out"), o_swa=L["o_swa"],
+            lse_swa=L["lse_swa"]) for L in self.layers]
+        need = csa2.workspace_bytes(csa2.OP_LAYER_GROUP, self.g)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def step(self):
+        self.csa2.layer_group(self.descs, self.g, workspace=self.ws)
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+def algorithmic_bytes(w):
+    """Bytes each kernel class must move per step (what the method itself reads/writes,
+    not what an implementation re-reads): per row, the indexer-key scan n_vis x 128 B, the
+    gather of the selected entries K x 400 B, the SWA window n_win x H_kv x 128 x 2 x 2 B,
+    plus queries and fp32 outputs.  Returned per kernel name of the library."""
+    import numpy as np
+    nv = w.n_vis().astype(np.int64)
+    sel = np.minimum(nv, w.K)
+    n_idx_layers = sum(1 for m in w.modes if m in (0, 1))
+    n_layers = len(w.modes)
+    idx_score = n_idx_layers * (int(nv.sum()) * 128 + w.T * w.H_I * (64 * 2 + 4))
+    topk = n_idx_layers * w.T * w.K * 4
+    attn = n_layers * (int(sel.sum()) * 400 + w.T * w.H * (576 * 2 + 512 * 4 + 4))
+    win = w.swa_len().astype(np.int64)
+    swa = n_layers * (int(win.sum()) * w.H_kv * 128 * 2 * 2 + w.T * w.H * (128 * 2 + 128 * 4 + 4))
+    return {"idx_score": idx_score, "topk": topk, "sparse_attn": attn, "swa": swa}
+
+
+def kernel_source_sha(name):
+    src = {"idx_score": "k_index.hip", "topk": "k_index.hip", "sparse_attn": "k_attn.hip",
+           "attn_merge": "k_attn.hip", "swa": "k_swa.hip"}.get(name)
+    if src is None:
+        return None
+    path = os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", src)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(workload_name, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there
+    is none for this kernel or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("source_sha") != kernel_source_sha(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, rows):
+    """The CPU oracle as it stands, on `rows` query rows of the same workload: indexer
+    scoring, Top-K, sparse FP4 attention and SWA (inputs prepared beforehand)."""
+    import numpy as np
+    from oracle import oracle as orc
+    pt = w.page_table()
+    lat_l, scl_l = [], []
+    for b in range(w.B):
+        l, s = orc.mxfp4_quantize(w.latent_seq(b))
+        lat_l.append(l)
+        scl_l.append(s)
+    lat = w.to_physical(lambda b: lat_l[b], pt)
+    scl = w.to_physical(lambda b: scl_l[b], pt)
+    rope = w.to_physical(w.rope_seq, pt)
+    kidx = w.to_physical(w.k_idx_seq, pt)
+    q, q_swa, q_idx, w_idx = w.q(), w.q_swa(), w.q_idx(), w.w_idx()
+    swa_k, swa_v = w.swa_k(), w.swa_v()
+    sel_rows = np.linspace(0, w.T - 1, rows).round().astype(np.int32)
+    sel_rows = np.unique(sel_rows)
+    t0 = time.perf_counter()
+    idx = orc.index_topk(w.K, w.P, q_idx, w_idx, kidx, pt, w.seq_id(), w.n_vis(),
+                         rows=sel_rows)
+    idx_full = -np.ones((w.T, w.K), np.int32)
+    idx_full[sel_rows] = idx
+    orc.sparse_attn(w.P, q, lat, scl, rope, pt, w.seq_id(), idx_full, rows=sel_rows)
+    orc.swa_attn(q_swa, swa_k, swa_v, w.seq_id(), w.swa_start(), w.swa_len(), rows=sel_rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(sel_rows) / dt, 3), "unit": "query-tokens/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{len(sel_rows)} of {w.T} query rows of one step (indexer scores over "
+                      f"all {w.E} entries, Top-K, FP4 sparse attention, SWA), fp64, "
+                      f"{dt:.2f} s wall"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the hot path shards by sequence with no "
+              f"exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy:
+        n = 1 << 28                          # 1 GiB of fp32 read + 1 GiB written per copy
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(max(args.steps, 1)):
+            torch.add(x, 0.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                          "launches": max(args.steps, 1)}))
+        return
+
+    from fp4_compressed_sparse_amd import csa2
+    w = synth.workload(args.workload)
+    t_build = time.perf_counter()
+    inp = Inputs(w, dev)
+    torch.cuda.synchronize()
+    t_build = time.perf_counter() - t_build
+    print(f"[bench] {w.name}: inputs built in {t_build:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        inp.step()
+    torch.cuda.synchronize()
+    csa2.timing_read()                       # drop anything recorded so far
+    csa2.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        inp.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    csa2.timing_enable(False)
+    kt = csa2.timing_read()
+    print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr,
+          flush=True)
+
+    ms_step = elapsed * 1e3 / args.steps
+    qtok_s = w.T / (ms_step * 1e-3)
+    algo = algorithmic_bytes(w)
+    step_bytes = sum(algo.values())
+    kernels = {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in kt.items()}
+    for k, v in kernels.items():
+        if k in algo:
+            per_launch = algo[k] / (v["launches"] / args.steps)
+            v["algo_bytes"] = per_launch
+            v["gbs"] = round(per_launch / (v["avg_us"] * 1e-6) / 1e9, 1)
+    dominant = max(kt, key=lambda k: kt[k][1])
+    dk = kernels[dominant]
+    achieved = dk.get("gbs")
+    traffic = counter_traffic(w.name, dominant)
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                "traffic": traffic,
+                "algo_bytes_per_launch": dk.get("algo_bytes"), "avg_us": dk["avg_us"]}
+
+    result = {
+        "metric": "decode query-tokens/s and achieved HBM GB/s (% peak) at 128K ctx, Top-K 2048",
+        "value": round(qtok_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+bf16 (bf16/fp16 MFMA, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.T, "context_tokens": 4 * w.E,
+                   "entries_per_seq": w.E, "top_k": w.K, "heads": w.H, "head_dim": 576,
+                   "indexer_heads": w.H_I, "swa_window": w.n_win, "swa_kv_heads": w.H_kv,
+                   "kv_format": "MXFP4 (E2M1, E8M0 per 32) latent 512 + bf16 rope 64",
+                   "layers": ["full", "reindex", "reuse"][:len(w.modes)] if len(w.modes) > 1
+                   else ["full"], "parallelism": "single GPU"},
+        "step_algo_bytes": step_bytes,
+        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if args.cpu_rows > 0:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, w.T))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

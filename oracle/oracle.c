@@ -22,6 +22,9 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -359,6 +362,15 @@ void csa2o_swa_attn(int H, int H_kv, int L_swa, const uint16_t* q_swa, const uin
     free(l);
     free(v);
   }
+}
+
+/* Threads the oracle's parallel loops use (1 without OpenMP). */
+int csa2o_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* ------------------------------------------------------------------------- */

@@ -58,6 +58,7 @@ def lib():
                                         i32, vp, vp]
         L.csa2o_swa_attn.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, f64, vp, i32, vp,
                                      vp]
+        L.csa2o_num_threads.restype = i32
         L.csa2o_footprint_bytes_per_token.restype = f64
         L.csa2o_footprint_bytes_per_token.argtypes = [vp, i32, i32, i32, i32, i32, i32]
         _lib = L
@@ -211,6 +212,10 @@ def layer_group(layers, K, max_pages, page_table, seq_id, n_vis, swa_start, swa_
         results.append({"idx_all": idx_all, "idx": idx_all[rows_], "o": o, "lse": lse,
                         "o_swa": o_w, "lse_swa": lse_w})
     return results
+
+
+def num_threads() -> int:
+    return lib().csa2o_num_threads()
 
 
 def footprint_bytes_per_token(modes, lat_bytes=256, scale_bytes=16, rope_bytes=128,
