@@ -13,6 +13,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -56,6 +57,27 @@ __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f
 
 __device__ __forceinline__ u32x4 ld_global_16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 16-byte load from an address held as an integer, kept in the global address space (a
+// generic pointer would become a flat load, which also counts against LDS waits).
+__device__ __forceinline__ u32x4 ld_global_16_addr(uint64_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(a);
+}
+
+// Wait until every vector memory load issued so far has returned.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (Hillis-Steele within
+// each 16-lane row by row_shr 1, 2, 4, 8, then row_bcast 15 / 31 carry the row totals).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

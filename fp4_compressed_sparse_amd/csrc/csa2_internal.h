@@ -83,7 +83,7 @@ struct QuantParams {
 };
 
 // ---------------------------------------------------------------- launch geometry
-constexpr int kIdxChunk = 1024;        // entries scored per workgroup
+constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
 constexpr int kTopkThreads = 1024;
 
 // Split plan of the attention launch: `splits` workgroups per row, each covering

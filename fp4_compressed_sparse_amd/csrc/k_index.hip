@@ -9,23 +9,61 @@
 // accumulation, streaming each sequence's paged indexer keys once.
 //
 // Top-K: the K largest scores, ties to the lowest index, emitted in ascending index
-// order, -1 padded.  Radix select over order-preserving u32 keys (4 passes of 8 bits)
-// finds the K-th key tau and how many keys equal to tau to keep; an ordered block-wide
-// scan then compacts the selected indices in index order.
+// order, -1 padded.  Radix select over order-preserving u32 keys (digits of 12, 12 and
+// 8 bits) finds the K-th key tau and how many keys equal to tau to keep; an ordered
+// block-wide scan then compacts the selected indices in index order.  Rows of up to 64K
+// entries are read once into registers; longer rows are streamed per pass.
 #include "csa2_internal.h"
 #include "csa2_device.h"
 
 namespace csa2 {
 
 constexpr int kIdxWaves = 4;
-constexpr int kIdxPerWave = kIdxChunk / kIdxWaves;   // 256 entries per wave
-constexpr int kIdxUnroll = 4;                         // 16-entry groups in flight per wave
+constexpr int kIdxPerWave = kIdxChunk / kIdxWaves;   // entries per wave (whole pages)
+constexpr int kIdxPagesPerWave = kIdxPerWave / kPage;
+static_assert(kIdxPagesPerWave <= 64, "one page-table entry per lane");
 
-// One workgroup scores kIdxChunk consecutive entries of one row; each wave takes 256 of
-// them, 16 per MFMA pair.  MFMA A = q_idx (rows = heads, zero-padded to 16), B = keys
-// (columns = entries).  The 64 key channels are split over the two MFMAs and the four
-// lane groups g as channels [16g, 16g+8) and [16g+8, 16g+16); q uses the same split, so
-// each lane loads 32 contiguous key bytes.
+// Keys of one 64-entry page for the MFMA B operand: group u (entries 16u .. 16u+15 of the
+// page), lane (g, n) holds entry 16u + n, channels [16g, 16g+8) and [16g+8, 16g+16).
+__device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, int valid,
+                                              int n, int g, u32x4 (&kb)[8]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (16 * u + n < valid) {
+      const uint16_t* kp = k_idx + ((int64_t)page * kPage + 16 * u + n) * kDidx + 16 * g;
+      kb[2 * u] = ld_global_16(kp);
+      kb[2 * u + 1] = ld_global_16(kp + 8);
+    } else {
+      kb[2 * u] = u32x4{0u, 0u, 0u, 0u};
+      kb[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Score one page: MFMA A = q_idx (rows = heads, zero-padded to 16), B = keys (columns =
+// entries); the result lane (g, n) holds heads 4g..4g+3 of entry n.
+__device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa1,
+                                               const float (&w)[4], const u32x4 (&kb)[8],
+                                               int valid, int n, int g, uint32_t* keys) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa0), as_bf16x8(kb[2 * u]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa1), as_bf16x8(kb[2 * u + 1]), acc, 0, 0, 0);
+    float s = w[0] * fmaxf(acc[0], 0.f);
+    s += w[1] * fmaxf(acc[1], 0.f);
+    s += w[2] * fmaxf(acc[2], 0.f);
+    s += w[3] * fmaxf(acc[3], 0.f);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (g == 0 && 16 * u + n < valid) keys[16 * u + n] = float_key(s);
+  }
+}
+
+// One workgroup scores kIdxChunk consecutive entries of one row, each wave a run of whole
+// pages.  The wave resolves its pages' physical numbers once (one page-table entry per
+// lane, broadcast by shuffle) and keeps the next page's 8 KB of keys in flight while it
+// scores the current one.
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
   const int t = blockIdx.x / p.chunks;
   const int c = blockIdx.x - t * p.chunks;
@@ -34,8 +72,12 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
   const int j_begin = c * kIdxChunk + wave * kIdxPerWave;
   if (j_begin >= nv) return;                 // wave-uniform; no block barriers below
   const int j_end = min(j_begin + kIdxPerWave, nv);
+  const int npages = (j_end - j_begin + kPage - 1) / kPage;
   const int b = p.seq_id[t];
   const int n = lane & 15, g = lane >> 4;
+
+  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages + j_begin / kPage;
+  const int my_page = (lane < npages) ? pt[lane] : 0;
 
   u32x4 qa0 = {0u, 0u, 0u, 0u}, qa1 = {0u, 0u, 0u, 0u};
   if (n < p.H_I) {
@@ -49,164 +91,310 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
     const int h = 4 * g + i;
     w[i] = (h < p.H_I) ? p.w_idx[(int64_t)t * p.H_I + h] : 0.f;
   }
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
+  uint32_t* keys = p.keys + (int64_t)t * p.key_stride + j_begin;
 
-  for (int j0 = j_begin; j0 < j_end; j0 += 16 * kIdxUnroll) {
-    u32x4 kb0[kIdxUnroll], kb1[kIdxUnroll];
-#pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      const int j = j0 + 16 * u + n;
-      if (j < j_end) {
-        const int64_t row = (int64_t)pt[j >> 6] * kPage + (j & 63);
-        const uint16_t* kp = p.k_idx + row * kDidx + 16 * g;
-        kb0[u] = ld_global_16(kp);
-        kb1[u] = ld_global_16(kp + 8);
-      } else {
-        kb0[u] = u32x4{0u, 0u, 0u, 0u};
-        kb1[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa0), as_bf16x8(kb0[u]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa1), as_bf16x8(kb1[u]), acc, 0, 0, 0);
-      // lane holds heads 4g..4g+3 of entry n
-      float s = w[0] * fmaxf(acc[0], 0.f);
-      s += w[1] * fmaxf(acc[1], 0.f);
-      s += w[2] * fmaxf(acc[2], 0.f);
-      s += w[3] * fmaxf(acc[3], 0.f);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      const int j = j0 + 16 * u + n;
-      if (g == 0 && j < j_end) keys[j] = float_key(s);
-    }
+  const int span = j_end - j_begin;           // valid entries of page pi: span - 64*pi
+  auto valid_in = [&](int pi) { return min(kPage, span - kPage * pi); };
+  u32x4 bufA[8], bufB[8];
+  idx_load_page(p.k_idx, __shfl(my_page, 0), valid_in(0), n, g, bufA);
+  for (int pi = 0; pi < npages; pi += 2) {
+    if (pi + 1 < npages) idx_load_page(p.k_idx, __shfl(my_page, pi + 1), valid_in(pi + 1), n, g, bufB);
+    idx_score_page(qa0, qa1, w, bufA, valid_in(pi), n, g, keys + kPage * pi);
+    if (pi + 2 < npages) idx_load_page(p.k_idx, __shfl(my_page, pi + 2), valid_in(pi + 2), n, g, bufA);
+    if (pi + 1 < npages)
+      idx_score_page(qa0, qa1, w, bufB, valid_in(pi + 1), n, g, keys + kPage * (pi + 1));
   }
 }
 
-// One workgroup (1024 threads) per row.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  constexpr int NWAVE = kTopkThreads / 64;
-  __shared__ uint32_t hist[NWAVE][256];
-  __shared__ uint32_t s_digit, s_remaining;
-  __shared__ uint32_t wave_tot[NWAVE];
+// ---------------------------------------------------------------- Top-K
+// Radix select over 32-bit keys in three digit passes (bits 31..20, 19..8, 7..0).  The
+// shared helpers below work on one row per workgroup of kTopkThreads threads.
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kHistBins = 4096;
 
+struct TopkShared {
+  uint32_t hist[kHistBins];
+  uint32_t wave_tot[kTopkWaves];
+  uint32_t digit, remaining;
+};
+
+// Given the histogram of the current digit (among keys matching the prefix so far) and
+// `remaining` = rank (1-based, from the top) of the wanted key among them, find the digit
+// holding that key and the rank left inside it.  Thread t owns bins 4t .. 4t+3.
+__device__ __forceinline__ void topk_find_digit(TopkShared& sh, uint32_t remaining) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = sh.hist[4 * tid + e];
+  const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+  uint32_t suf = tot;                              // inclusive suffix sum within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(suf, o);
+    if (lane + o < 64) suf += y;
+  }
+  if (lane == 0) sh.wave_tot[wave] = suf;
+  __syncthreads();
+  uint32_t above = suf - tot;                      // keys in bins of higher threads
+  for (int w = wave + 1; w < kTopkWaves; ++w) above += sh.wave_tot[w];
+#pragma unroll
+  for (int e = 3; e >= 0; --e) {
+    if (above < remaining && above + c[e] >= remaining) {
+      sh.digit = (uint32_t)(4 * tid + e);
+      sh.remaining = remaining - above;
+    }
+    above += c[e];
+  }
+  __syncthreads();
+}
+
+// Ordered compaction of one 4096-key tile: thread t holds keys 4t..4t+3 of the tile
+// (valid[e] marks keys below n).  Output position of a selected key i:
+// (#keys > tau before i) + min(#keys == tau before i, need_eq).
+__device__ __forceinline__ void topk_emit_tile(TopkShared& sh, const uint32_t kv[4],
+                                               const bool valid[4], int i0, uint32_t tau,
+                                               uint32_t need_eq, uint32_t& gt_base,
+                                               uint32_t& eq_base, int32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    cg += (valid[e] && kv[e] > tau);
+    ce += (valid[e] && kv[e] == tau);
+  }
+  const uint32_t packed = cg | (ce << 16);
+  uint32_t incl = packed;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t wave_off = 0u, tile_tot = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t x = sh.wave_tot[w];
+    wave_off += (w < wave) ? x : 0u;
+    tile_tot += x;
+  }
+  const uint32_t excl = wave_off + incl - packed;
+  uint32_t gtb = gt_base + (excl & 0xffffu);
+  uint32_t eqb = eq_base + (excl >> 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (!valid[e]) continue;
+    if (kv[e] > tau) {
+      out[gtb + min(eqb, need_eq)] = i0 + e;
+      ++gtb;
+    } else if (kv[e] == tau) {
+      if (eqb < need_eq) out[gtb + eqb] = i0 + e;
+      ++eqb;
+    }
+  }
+  gt_base += tile_tot & 0xffffu;
+  eq_base += tile_tot >> 16;
+  __syncthreads();                                 // wave_tot is reused by the next tile
+}
+
+__device__ __forceinline__ uint32_t topk_digit(uint32_t k, int pass) {
+  return pass == 0 ? (k >> 20) : (pass == 1 ? ((k >> 8) & 0xfffu) : (k & 0xffu));
+}
+__device__ __forceinline__ uint32_t topk_prefix_mask(int pass) {
+  return pass == 0 ? 0u : (pass == 1 ? 0xfff00000u : 0xffffff00u);
+}
+__device__ __forceinline__ uint32_t topk_place(uint32_t d, int pass) {
+  return pass == 0 ? (d << 20) : (pass == 1 ? (d << 8) : d);
+}
+
+// Exclusive prefix sum over the wave of small per-lane counts (< 2^BITS) and the wave
+// total, from one ballot per count bit (no LDS traffic).
+template <int BITS>
+__device__ __forceinline__ uint32_t wave_prefix_small(uint32_t v, uint32_t& total) {
+  const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
+  uint32_t pre = 0u, tot = 0u;
+#pragma unroll
+  for (int bit = 0; bit < BITS; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1u);
+    pre += (uint32_t)__popcll(m & below) << bit;
+    tot += (uint32_t)__popcll(m) << bit;
+  }
+  total = tot;
+  return pre;
+}
+
+// Wave 0 locates the digit holding the `remaining`-th key (from the top) in a 4096-bin
+// histogram: lane l first sums bins 64l .. 64l+63, a suffix scan over lanes picks the
+// lane whose range holds the rank, then the wave scans that lane's 64 bins in parallel.
+__device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_t remaining,
+                                                   uint32_t* s_digit, uint32_t* s_rem) {
+  const int lane = threadIdx.x & 63;
+  const u32x4* h4 = reinterpret_cast<const u32x4*>(hist + 64 * lane);
+  uint32_t tot = 0u;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const u32x4 v = h4[q];
+    tot += v[0] + v[1] + v[2] + v[3];
+  }
+  // suffix sums: keys in lanes >= l
+  const uint32_t incl = wave_incl_scan(tot);
+  const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t suf = all - incl + tot;
+  const uint32_t above = suf - tot;
+  const uint64_t hit = __ballot(above < remaining && suf >= remaining);
+  const int L = (int)__builtin_ctzll(hit);                     // exactly one lane
+  const uint32_t above_L = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+  const uint32_t rem2 = remaining - above_L;
+  // bins of lane L, highest first: lane l takes bin 64L + 63 - l
+  const uint32_t c = hist[64 * L + 63 - lane];
+  const uint32_t incl2 = wave_incl_scan(c);                    // keys in bins above, incl.
+  const uint64_t hit2 = __ballot(incl2 - c < rem2 && incl2 >= rem2);
+  const int l2 = (int)__builtin_ctzll(hit2);
+  if (lane == l2) {
+    *s_digit = (uint32_t)(64 * L + 63 - l2);
+    *s_rem = rem2 - (incl2 - c);
+  }
+}
+
+// Rows of at most 4096 * NR keys: thread t keeps keys [4NR t, 4NR (t+1)) in registers,
+// so the row is read from memory once and one block-wide scan orders the output.
+template <int NR>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
+  constexpr int KPT = 4 * NR;                        // keys per thread
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
+  __shared__ uint32_t s_digit, s_rem;
+  __shared__ uint32_t s_wtot[kTopkWaves];
   const int t = blockIdx.x;
   const int n = p.n_vis[t];
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
-  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
   if (n <= K) {                       // every visible entry is selected
     for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
     return;
   }
-
-  // ---- radix select of the K-th largest key
-  uint32_t prefix = 0u, pmask = 0u, remaining = (uint32_t)K;
-  const int n4 = n >> 2;
-  const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < NWAVE * 256; i += kTopkThreads) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n4; i += kTopkThreads) {
-      const u32x4 v = k4[i];
+  // keys below n are >= float_key(-inf) > 0; 0 marks the slots past n
+  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
+  const int i0 = KPT * tid;
+  uint32_t kv[KPT];
+  if (i0 + KPT <= n) {
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(keys + i0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((v[e] & pmask) == prefix) atomicAdd(&hist[wave][(v[e] >> shift) & 255u], 1u);
+    for (int r = 0; r < NR; ++r) {
+      const u32x4 v = k4[r];
+      kv[4 * r] = v[0]; kv[4 * r + 1] = v[1]; kv[4 * r + 2] = v[2]; kv[4 * r + 3] = v[3];
     }
-    for (int i = 4 * n4 + tid; i < n; i += kTopkThreads) {
-      const uint32_t v = keys[i];
-      if ((v & pmask) == prefix) atomicAdd(&hist[wave][(v >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t cnt[4];
+  } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t s = 0u;
-        for (int w = 0; w < NWAVE; ++w) s += hist[w][4 * lane + e];
-        cnt[e] = s;
-      }
-      const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-      uint32_t suf = tot;                                // inclusive suffix sum over lanes
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(suf, o);
-        if (lane + o < 64) suf += y;
-      }
-      uint32_t above = suf - tot;                        // keys in higher lanes' bins
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        if (above < remaining && above + cnt[e] >= remaining) {
-          s_digit = (uint32_t)(4 * lane + e);
-          s_remaining = remaining - above;
-        }
-        above += cnt[e];
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    pmask |= 255u << shift;
-    remaining = s_remaining;
+    for (int e = 0; e < KPT; ++e) kv[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
   }
-  const uint32_t tau = prefix;        // K-th largest key
-  const uint32_t need_eq = remaining; // keys equal to tau to keep (lowest indices first)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hist[0][4 * tid + e] = 0u;
+  __syncthreads();
+
+  uint32_t prefix = 0u, remaining = (uint32_t)K;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const uint32_t pmask = topk_prefix_mask(pass);
+    uint32_t* h = hist[pass & 1];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+      if (kv[e] != 0u && (kv[e] & pmask) == prefix) atomicAdd(&h[topk_digit(kv[e], pass)], 1u);
+    // the other buffer is free: clear it for the next pass
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hist[(pass + 1) & 1][4 * tid + e] = 0u;
+    __syncthreads();
+    if (wave == 0) topk_find_digit_w0(h, remaining, &s_digit, &s_rem);
+    __syncthreads();
+    prefix |= topk_place(s_digit, pass);
+    remaining = s_rem;
+  }
+  const uint32_t tau = prefix, need_eq = remaining;
 
   // ---- ordered compaction: position = (#greater before) + min(#equal before, need_eq)
+  uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    cg += (kv[e] > tau);
+    ce += (kv[e] == tau);
+  }
+  uint32_t wg, we;
+  const uint32_t pg = wave_prefix_small<7>(cg, wg);
+  const uint32_t pe = wave_prefix_small<7>(ce, we);
+  if (lane == 0) s_wtot[wave] = wg | (we << 16);
+  __syncthreads();
+  uint32_t off = 0u;
+  for (int w = 0; w < wave; ++w) off += s_wtot[w];
+  uint32_t gtb = (off & 0xffffu) + pg;
+  uint32_t eqb = (off >> 16) + pe;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (kv[e] > tau) {
+      out[gtb + min(eqb, need_eq)] = i0 + e;
+      ++gtb;
+    } else if (kv[e] == tau) {
+      if (eqb < need_eq) out[gtb + eqb] = i0 + e;
+      ++eqb;
+    }
+  }
+}
+
+// Rows of any length: every digit pass and the compaction stream the row's keys.
+__global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p) {
+  __shared__ TopkShared sh;
+  const int t = blockIdx.x;
+  const int n = p.n_vis[t];
+  const int K = p.K;
+  int32_t* out = p.idx_out + (int64_t)t * K;
+  const int tid = threadIdx.x;
+  if (n <= K) {
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
+  const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
+  uint32_t prefix = 0u, remaining = (uint32_t)K;
+  for (int pass = 0; pass < 3; ++pass) {
+    const uint32_t pmask = topk_prefix_mask(pass);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
+    __syncthreads();
+    for (int i0 = 4 * tid; i0 < n; i0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+      if (i0 + 3 < n) {
+        const u32x4 v = k4[i0 >> 2];
+        kv[0] = v[0]; kv[1] = v[1]; kv[2] = v[2]; kv[3] = v[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < n && (kv[e] & pmask) == prefix)
+          atomicAdd(&sh.hist[topk_digit(kv[e], pass)], 1u);
+    }
+    __syncthreads();
+    topk_find_digit(sh, remaining);
+    prefix |= topk_place(sh.digit, pass);
+    remaining = sh.remaining;
+  }
   uint32_t gt_base = 0u, eq_base = 0u;
   for (int base = 0; base < n; base += 4 * kTopkThreads) {
     const int i0 = base + 4 * tid;
     uint32_t kv[4];
+    bool valid[4];
     if (i0 + 3 < n) {
       const u32x4 v = k4[i0 >> 2];
-      kv[0] = v[0]; kv[1] = v[1]; kv[2] = v[2]; kv[3] = v[3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { kv[e] = v[e]; valid[e] = true; }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kv[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
-    }
-    uint32_t cg = 0u, ce = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool valid = i0 + e < n;
-      cg += (valid && kv[e] > tau);
-      ce += (valid && kv[e] == tau);
-    }
-    const uint32_t packed = cg | (ce << 16);
-    uint32_t incl = packed;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    uint32_t wave_off = 0u, tile_tot = 0u;
-    for (int w = 0; w < NWAVE; ++w) {
-      const uint32_t x = wave_tot[w];
-      wave_off += (w < wave) ? x : 0u;
-      tile_tot += x;
-    }
-    const uint32_t excl = wave_off + incl - packed;
-    uint32_t gtb = gt_base + (excl & 0xffffu);
-    uint32_t eqb = eq_base + (excl >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i0 + e >= n) break;
-      if (kv[e] > tau) {
-        out[gtb + min(eqb, need_eq)] = i0 + e;
-        ++gtb;
-      } else if (kv[e] == tau) {
-        if (eqb < need_eq) out[gtb + eqb] = i0 + e;
-        ++eqb;
+      for (int e = 0; e < 4; ++e) {
+        valid[e] = i0 + e < n;
+        kv[e] = valid[e] ? keys[i0 + e] : 0u;
       }
     }
-    gt_base += tile_tot & 0xffffu;
-    eq_base += tile_tot >> 16;
-    __syncthreads();
+    topk_emit_tile(sh, kv, valid, i0, prefix, remaining, gt_base, eq_base, out);
   }
 }
 
@@ -217,7 +405,14 @@ hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)p.T), dim3(kTopkThreads), 0, s, p);
+  // key_stride bounds every row's n_vis; pick the register-resident variant that holds it
+  const int64_t nr = (p.key_stride + 4 * kTopkThreads - 1) / (4 * kTopkThreads);
+  const dim3 grid((unsigned)p.T), block(kTopkThreads);
+  if (nr <= 2) hipLaunchKernelGGL(topk_reg_kernel<2>, grid, block, 0, s, p);
+  else if (nr <= 4) hipLaunchKernelGGL(topk_reg_kernel<4>, grid, block, 0, s, p);
+  else if (nr <= 8) hipLaunchKernelGGL(topk_reg_kernel<8>, grid, block, 0, s, p);
+  else if (nr <= 16) hipLaunchKernelGGL(topk_reg_kernel<16>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
