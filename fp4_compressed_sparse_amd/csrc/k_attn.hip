@@ -8,27 +8,27 @@
 // Every head of a row shares each entry (MLA-style latent): key = [latent ; rope] (576),
 // value = latent (512).
 //
-// One workgroup per (row, split of the K index slots).  Waves are (head group of 32 heads
-// -- 16 when H = 16 --, half); with H = 64 that is 4 waves.
+// One workgroup per (row, split of the K index slots) with four waves (one per SIMD).
+// Wave w is the "score wave" of heads 16w'.. (w' = w for H = 64; fewer heads per wave for
+// smaller H) and the "value wave" of latent channels 128w .. 128w+127 for every head.
 //   gather  : the split's physical rows are resolved once into LDS.  Each 32-entry tile
 //             (8 KB codes, 4 KB rope, 0.5 KB scales) is fetched with coalesced 16-byte loads
-//             into registers three tiles ahead, then written to LDS with an XOR swizzle of
+//             into registers two tiles ahead, then written to LDS with an XOR swizzle of
 //             the 16-byte slots so the operand reads below are bank-conflict free.
-//   QK^T    : S^T[32 entries x 32 heads], split over the two waves of a head group by
-//             channel half (288 of 576).  The latent part runs on the MXFP4 matrix path
-//             (v_mfma_scale 16x16x128, A = the cached E2M1 codes with their own E8M0
-//             block scales, dequantized inside the MFMA); the query enters as two fp8
-//             (E4M3) parts with per-32-channel E8M0 scales, hi + lo, which reproduce the
-//             bf16 query exactly.  The rope part is a bf16 MFMA.  The two partial sums
-//             meet in LDS, so both waves hold the full S^T tile.
-//   softmax : online, per head, log2 domain, fp32; the running maximum is raised only
-//             when a tile exceeds it by more than 2^8 (fp16 P stays below 256).
-//   PV      : O^T[256 channels x 32 heads] += V^T P^T on fp16 MFMA 16x16x32, fp32
-//             accumulation; each wave owns one channel half.  V^T is dequantized once per
-//             tile into LDS, channel-major, with entries stored in the order the P^T
-//             operand already has in registers (the S^T result rows of a lane), so every
-//             V^T operand is one 16-byte LDS read.  fp16 rather than bf16 for P: bf16
-//             rounding of P alone would put the output's relative error near 1.7e-3.
+//   QK^T    : S^T[32 entries x 16 heads] per score wave over all 576 channels.  The latent
+//             part runs on the MXFP4 matrix path (v_mfma_scale 16x16x128: A = the cached
+//             E2M1 codes with their own E8M0 block scales, dequantized inside the MFMA);
+//             the query enters as two fp8 (E4M3) parts with per-32-channel E8M0 scales,
+//             hi + lo, which reproduce the bf16 query exactly.  The rope part is bf16 MFMA.
+//   softmax : online, per head, log2 domain, fp32, in the score wave; the running maximum
+//             is raised only when a tile exceeds it by more than 2^8 (fp16 P <= 256).  The
+//             wave publishes P (fp16) and, when it raised a maximum, the rescale factors.
+//   PV      : O^T[128 channels x 64 heads] += V^T P^T per value wave on fp16 MFMA 16x16x32
+//             with fp32 accumulation; each V^T operand (one 16-byte LDS read) feeds the
+//             four 16-head blocks.  V^T is dequantized once per tile into LDS (fp16,
+//             channel-major, entries in the order the P^T operand has in registers), one
+//             tile ahead, alongside the PV of the current tile.  fp16 rather than bf16 for
+//             P: bf16 rounding of P alone would put the output's relative error near 1.7e-3.
 // Splits write normalized partial outputs plus log2-sum-exp; a merge kernel combines them.
 #include "csa2_internal.h"
 #include "csa2_device.h"
@@ -37,17 +37,17 @@ namespace csa2 {
 
 constexpr int kTE = 32;              // entries per tile
 constexpr int kMaxPerSplit = 2048;   // idx slots per split (LDS row table size)
-constexpr int kNPre = 3;             // tiles in flight in registers
+constexpr int kNPre = 2;             // tiles in flight in registers
 // raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16]
 constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 12800;
 constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rope, 1 scales
 constexpr int kVtStride = 80;        // LDS bytes per V^T channel row (32 fp16 + 16 pad)
 
 void attn_plan(int T, int H, int K, int* splits, int* per_split) {
-  (void)H;
+  const int groups = H > 64 ? H / 64 : 1;                    // 64-head workgroups per split
   const int min_s = (K + kMaxPerSplit - 1) / kMaxPerSplit;
   const int max_s = max(1, (K + 2 * kTE - 1) / (2 * kTE));   // >= 2 tiles per split
-  int s = (T > 0) ? (256 + T - 1) / T : 1;
+  int s = (T > 0) ? (256 + T * groups - 1) / (T * groups) : 1;
   s = min(s, max_s);
   s = max(s, min_s);
   // whole tiles per split; the split count follows from the rounded slot count
@@ -66,19 +66,23 @@ __device__ __forceinline__ int vt_pos(int e) {
   return (e < 16) ? (8 * (e >> 2) + (e & 3)) : (8 * ((e - 16) >> 2) + 4 + (e & 3));
 }
 
-template <int NHG, int NB>   // NHG head groups of 16*NB heads; waves = 2 * NHG
-__global__ __launch_bounds__(128 * NHG) void sparse_attn_kernel(AttnParams p) {
-  constexpr int HG = 16 * NB;                                 // heads per group
-  constexpr int NW = 2 * NHG;
+template <int NHB>   // 16-head blocks per workgroup: 1, 2 or 4 (blockIdx.y picks 64-head groups)
+__global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
+  constexpr int NW = 4;
   constexpr int NT = 64 * NW;
-  constexpr int CPW = (kChunks + NW - 1) / NW;                // load units per wave
-  constexpr int VT_ITEMS = (kTE / 4) * (kLat / 8);            // (entry quad, channel octet)
-  constexpr int VT_PER_T = (VT_ITEMS + NT - 1) / NT;
+  constexpr int SPW = (NHB + NW - 1) / NW;          // 16-head blocks scored per wave
+  constexpr int CPW = (kChunks + NW - 1) / NW;       // load units per wave
+  constexpr int VT_PER_T = (kTE / 4) * (kLat / 8) / NT;
+  constexpr float kMInit = -1.0e30f;                 // running max before any valid entry
 
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kLat * kVtStride];
-  __shared__ __attribute__((aligned(16))) f32x4 s_part[NW][2 * NB][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLat * kVtStride];
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[NHB][64];      // P^T operands
+  __shared__ float s_alpha[NHB][16];                                // rescale factors
+  __shared__ float s_l[NHB][16];
+  __shared__ uint32_t s_raised[2];                // per tile parity: blocks that raised
   __shared__ int32_t s_rows[kMaxPerSplit];
+  __shared__ uint32_t s_tmask[kMaxPerSplit / kTE];
 
   const int t = blockIdx.x / p.splits;
   const int sp = blockIdx.x - t * p.splits;
@@ -86,10 +90,11 @@ __global__ __launch_bounds__(128 * NHG) void sparse_attn_kernel(AttnParams p) {
   const int nslots = max(min(k0 + p.per_split, p.K) - k0, 0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int hg = wave >> 1, half = wave & 1;       // head group; channel half
+  const int h0 = 16 * NHB * blockIdx.y;            // first head of this workgroup
   const int ntiles = (nslots + kTE - 1) / kTE;
 
-  // ---- resolve the split's physical rows once (-1 = empty slot)
+  // ---- resolve the split's physical rows once (-1 = empty slot); one validity bit per
+  //      entry of each tile
   {
     const int b = p.seq_id[t];
     const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
@@ -101,26 +106,109 @@ __global__ __launch_bounds__(128 * NHG) void sparse_attn_kernel(AttnParams p) {
         if (j >= 0) row = pt[j >> 6] * kPage + (j & 63);
       }
       s_rows[i] = row;
+      const uint64_t bal = __ballot(row >= 0);      // 64 slots = two tiles per wave step
+      if (lane == 0) s_tmask[i >> 5] = (uint32_t)bal;
+      if (lane == 32) s_tmask[i >> 5] = (uint32_t)(bal >> 32);
     }
+    if (tid < 2) s_raised[tid] = 0u;
   }
+  __syncthreads();                                   // s_rows ready
 
-  // ---- query operands of this wave (heads HG*hg + 16nb + n, channel half `half`)
-  // Latent part, per 128-channel chunk kk of the half: the scaled MFMA pairs A lane group
-  // gA (one 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16),
-  // byte p%16 + 16(gA>>1).  So B lane (g, n) carries channels 32(4kk + g/2) + 16(g&1) + [0,16)
+  // ---- gather: load unit j of a tile = 1 KB, lane l moves 16 bytes
+  //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
+  //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
+  //   j == 12    : scales of entry l (lanes < 32)
+  // Wave w owns units j = w + 4c.  Every wave issues CPW loads per tile without branches
+  // (dead units, empty slots and tiles past the end read the zero row), so the compiler
+  // can count the loads in flight.
+  const uint8_t* const lat_base = p.kv_lat;
+  const uint8_t* const rope_base = reinterpret_cast<const uint8_t*>(p.kv_rope);
+  const uint8_t* const scl_base = p.kv_scl;
+  auto unit_entry = [&](int j) {
+    return j < 8 ? 4 * j + (lane >> 4) : (j < 12 ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
+  };
+  auto load_tile = [&](int tile, u32x4 (&r)[CPW]) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int j = wave + NW * c;
+      const int row = (tile < ntiles && j < kChunks) ? s_rows[tile * kTE + unit_entry(j)] : -1;
+      const uint8_t* src;
+      if (j < 8) src = lat_base + (int64_t)row * kLatBytes + 16 * (lane & 15);
+      else if (j < 12) src = rope_base + (int64_t)row * (2 * kRope) + 16 * (lane & 7);
+      else src = scl_base + (int64_t)row * kScl;
+      const bool live = row >= 0 && (j < 12 || lane < 32);
+      r[c] = ld_global_16_addr(live ? reinterpret_cast<uint64_t>(src)
+                                    : reinterpret_cast<uint64_t>(g_zero_row));
+    }
+  };
+  auto store_tile = [&](const u32x4 (&r)[CPW], uint8_t* raw) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int j = wave + NW * c;
+      if (j < 8) {
+        const int e = 4 * j + (lane >> 4);
+        *reinterpret_cast<u32x4*>(raw + kRawLat + 256 * e + 16 * ((lane & 15) ^ (e & 15))) = r[c];
+      } else if (j < 12) {
+        const int e = 8 * (j - 8) + (lane >> 3);
+        *reinterpret_cast<u32x4*>(raw + kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7))) = r[c];
+      } else if (j == 12 && lane < 32) {
+        *reinterpret_cast<u32x4*>(raw + kRawScl + 16 * lane) = r[c];
+      }
+    }
+  };
+  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`
+  auto build_vt = [&](const uint8_t* raw, uint8_t* vtb) {
+#pragma unroll
+    for (int r = 0; r < VT_PER_T; ++r) {
+      const int it = tid + NT * r;
+      const int eq = it & 7;                       // entries 4eq .. 4eq+3
+      const int co = it >> 3;                      // channels 8co .. 8co+7
+      uint32_t hv[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * eq + k;
+        const int slot = (co >> 2) ^ (e & 15);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+            raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
+        const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);
+        fp4x8_to_f16_pairs(w, sc, hv[k]);
+      }
+      uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
+        lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
+        lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
+        hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
+        hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
+        *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
+        *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
+      }
+    }
+  };
+
+  u32x4 stg[kNPre][CPW];
+#pragma unroll
+  for (int b = 0; b < kNPre; ++b) load_tile(b, stg[b]);
+
+  // ---- query operands of this wave's score blocks, prepared while the first tiles fly.
+  // Latent part, per 128-channel chunk kk: the scaled MFMA pairs A lane group gA (one
+  // 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16), byte
+  // p%16 + 16(gA>>1).  So B lane (g, n) carries channels 32(4kk + g/2) + 16(g&1) + [0,16)
   // in bytes 0..15 and the same run of block 4kk + g/2 + 2 in bytes 16..31; it supplies the
   // E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2 max|q|) - 7,
   // and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every bf16 value within
   // 2^9 of the block maximum, and within 2^-16 of it below that.
-  i32x8 qhi[NB][2], qlo[NB][2];
-  int qsc[NB][2];
-  u32x4 qrope[NB];
+  i32x8 qhi[SPW][4], qlo[SPW][4];
+  int qsc[SPW][4];
+  u32x4 qrope[SPW][2];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const uint16_t* qp = p.q + ((int64_t)t * p.H + HG * hg + 16 * nb + n) * kDq;
+  for (int sb = 0; sb < SPW; ++sb) {
+    const int hb = wave + NW * sb;                   // 16-head block scored by this wave
+    const int h = h0 + 16 * (hb < NHB ? hb : 0) + n;
+    const uint16_t* qp = p.q + ((int64_t)t * p.H + h) * kDq;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int kk = 2 * half + k2;
+    for (int kk = 0; kk < 4; ++kk) {
       const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
       float x[2][16];
 #pragma unroll
@@ -150,7 +238,7 @@ __global__ __launch_bounds__(128 * NHG) void sparse_attn_kernel(AttnParams p) {
       // g = 1: run 0 of lane g = 3, g = 2: run 1 of lane g = 0)
       const int x0o = __shfl_xor(X[0], 32), x1o = __shfl_xor(X[1], 32);
       const int Xs = (g == 0) ? X[0] : (g == 3) ? X[1] : (g == 1) ? x0o : x1o;
-      qsc[nb][k2] = Xs + 127;
+      qsc[sb][kk] = Xs + 127;
       i32x8 hi, lo;
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
@@ -160,97 +248,46 @@ __global__ __launch_bounds__(128 * NHG) void sparse_attn_kernel(AttnParams p) {
           float y[4], r[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = x[run][4 * d + e] * inv;
-          int h = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-          h = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], h, true);
-          r[0] = y[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0);
-          r[1] = y[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1);
-          r[2] = y[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2);
-          r[3] = y[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3);
-          int l = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-          l = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], l, true);
-          hi[4 * run + d] = h;
-          lo[4 * run + d] = l;
+          int hh = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          hh = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], hh, true);
+          r[0] = y[0] - __builtin_amdgcn_cvt_f32_fp8(hh, 0);
+          r[1] = y[1] - __builtin_amdgcn_cvt_f32_fp8(hh, 1);
+          r[2] = y[2] - __builtin_amdgcn_cvt_f32_fp8(hh, 2);
+          r[3] = y[3] - __builtin_amdgcn_cvt_f32_fp8(hh, 3);
+          int ll = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+          ll = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], ll, true);
+          hi[4 * run + d] = hh;
+          lo[4 * run + d] = ll;
         }
       }
-      qhi[nb][k2] = hi;
-      qlo[nb][k2] = lo;
+      qhi[sb][kk] = hi;
+      qlo[sb][kk] = lo;
     }
-    qrope[nb] = ld_global_16(qp + kLat + 32 * half + 8 * g);
+    qrope[sb][0] = ld_global_16(qp + kLat + 8 * g);
+    qrope[sb][1] = ld_global_16(qp + kLat + 32 + 8 * g);
   }
 
-  f32x4 acc[16][NB];
-  float m_run[NB], l_run[NB];
+  // O^T accumulators of this value wave: channels 128 wave + 16 c + 4g + i, head 16 hb + n
+  f32x4 acc[8][NHB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
+    for (int c = 0; c < 8; ++c) acc[c][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[SPW], l_run[SPW];
+#pragma unroll
+  for (int sb = 0; sb < SPW; ++sb) {
+    m_run[sb] = kMInit;
+    l_run[sb] = 0.f;
   }
 
-  wait_vmem_all();                                   // Q operands are in registers
-  __syncthreads();                                   // s_rows ready
-
-  // ---- gather: load unit j of a tile = 1 KB, lane l moves 16 bytes
-  //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
-  //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
-  //   j == 12    : scales of entry l (lanes < 32)
-  // Wave w owns units j = w + NW c.  Per unit the plane base, row stride, entry, source
-  // offset and swizzled LDS slot are fixed for the whole kernel: resolve them once.
-  const uint64_t zero_addr = reinterpret_cast<uint64_t>(g_zero_row);
-  uint64_t u_base[CPW];
-  int u_stride[CPW], u_entry[CPW], u_off[CPW], u_dst[CPW];
-  bool u_live[CPW];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int j = wave + NW * c;
-    u_live[c] = j < kChunks && (j < 12 || lane < 32);
-    if (j < 8) {
-      const int e = 4 * j + (lane >> 4);
-      u_base[c] = reinterpret_cast<uint64_t>(p.kv_lat);
-      u_stride[c] = kLatBytes;
-      u_entry[c] = e;
-      u_off[c] = 16 * (lane & 15);
-      u_dst[c] = kRawLat + 256 * e + 16 * ((lane & 15) ^ (e & 15));
-    } else if (j < 12) {
-      const int e = 8 * (j - 8) + (lane >> 3);
-      u_base[c] = reinterpret_cast<uint64_t>(p.kv_rope);
-      u_stride[c] = 2 * kRope;
-      u_entry[c] = e;
-      u_off[c] = 16 * (lane & 7);
-      u_dst[c] = kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7));
-    } else {
-      u_base[c] = reinterpret_cast<uint64_t>(p.kv_scl);
-      u_stride[c] = kScl;
-      u_entry[c] = lane & 31;
-      u_off[c] = 0;
-      u_dst[c] = kRawScl + 16 * (lane & 31);
-    }
-  }
-  u32x4 stg[kNPre][CPW];
-  // every wave issues exactly CPW loads per tile, without branches (dead units and empty
-  // slots read the zero row), so the compiler can count loads in flight across tiles
-  auto load_tile = [&](int tile, u32x4 (&r)[CPW]) {
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int row = s_rows[tile * kTE + u_entry[c]];
-      const uint64_t src = (row >= 0 && u_live[c])
-          ? u_base[c] + (uint64_t)((int64_t)row * u_stride[c] + u_off[c]) : zero_addr;
-      r[c] = ld_global_16_addr(src);
-    }
-  };
-  auto store_tile = [&](const u32x4 (&r)[CPW], uint8_t* raw) {
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-      if (u_live[c]) *reinterpret_cast<u32x4*>(raw + u_dst[c]) = r[c];
-  };
-
-#pragma unroll
-  for (int b = 0; b < kNPre; ++b)
-    if (b < ntiles) load_tile(b, stg[b]);
-  if (ntiles > 0) store_tile(stg[0], s_raw[0]);
+  // ---- pipeline prologue: raw(0) and V^T(0) in LDS; registers hold tiles 1 .. kNPre
+  store_tile(stg[0], s_raw[0]);
+  load_tile(kNPre, stg[0]);
+  __syncthreads();
+  build_vt(s_raw[0], s_vt[0]);
   __syncthreads();
 
+  // ---- tile i: QK^T + softmax (score waves) | stage raw(i+1) | PV(i) with V^T(i+1)
   const float sc_log2 = p.sm_scale_log2;
   for (int i0 = 0; i0 < ntiles; i0 += kNPre) {
 #pragma unroll
@@ -258,174 +295,143 @@ __global__ __launch_bounds__(128 * NHG) void sparse_attn_kernel(AttnParams p) {
       const int i = i0 + bb;
       if (i < ntiles) {
         const uint8_t* raw = s_raw[i & 1];
-        // tile i's registers are in LDS: reuse them for tile i + kNPre
-        if (i + kNPre < ntiles) load_tile(i + kNPre, stg[bb]);
-
-        // ---- V^T (fp16, channel-major, entries at vt_pos order) for the tile
+        const uint32_t tm = s_tmask[i];
+        uint32_t raised_mask = 0u;
 #pragma unroll
-        for (int r = 0; r < VT_PER_T; ++r) {
-          const int it = tid + NT * r;
-          if (it < VT_ITEMS) {
-            const int eq = it & 7;               // entries 4eq .. 4eq+3
-            const int co = it >> 3;              // channels 8co .. 8co+7
-            uint32_t hv[4][4];
+        for (int sb = 0; sb < SPW; ++sb) {
+          const int hb = wave + NW * sb;
+          if (hb < NHB) {
+            // ---- S^T[entries 16mb + 4g + k][head n] for this 16-head block
+            f32x4 sacc[2];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int e = 4 * eq + k;
-              const int slot = (co >> 2) ^ (e & 15);
-              const uint32_t w = *reinterpret_cast<const uint32_t*>(
-                  raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
-              const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);
-              fp4x8_to_f16_pairs(w, sc, hv[k]);
+            for (int mb = 0; mb < 2; ++mb) {
+              const int e = 16 * mb + n;
+              f32x4 a = {0.f, 0.f, 0.f, 0.f};
+              const u32x4 sc4 = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * e);
+#pragma unroll
+              for (int kk = 0; kk < 4; ++kk) {
+                const int chunk = 4 * kk + g;         // this lane's 32-channel block
+                const u32x4 w4 = *reinterpret_cast<const u32x4*>(
+                    raw + kRawLat + 256 * e + 16 * (chunk ^ (e & 15)));
+                const int ksc = (int)((sc4[kk] >> (8 * g)) & 255u);
+                const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};
+                a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[sb][kk], a, 4, 0, 0, ksc, 0, qsc[sb][kk]);
+                a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[sb][kk], a, 4, 0, 0, ksc, 0, qsc[sb][kk]);
+              }
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2) {
+                const int chunk = 4 * s2 + g;
+                const u32x4 rv = *reinterpret_cast<const u32x4*>(
+                    raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), as_bf16x8(qrope[sb][s2]), a, 0, 0, 0);
+              }
+              sacc[mb] = a;
             }
-            uint8_t* dst = s_vt + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
+            // ---- online softmax; masked slots get -inf (exp2 -> 0)
+            float x[8];
+            bool raise_lane = false;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
-              lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
-              lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
-              hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
-              hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
-              *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
-              *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
+            for (int mb = 0; mb < 2; ++mb) {
+              const uint32_t bits = tm >> (16 * mb + 4 * g);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float v = ((bits >> k) & 1u) ? sacc[mb][k] * sc_log2 : -INFINITY;
+                x[4 * mb + k] = v;
+                raise_lane |= v > m_run[sb] + 8.f;
+              }
             }
-          }
-        }
-
-        // ---- partial S^T over this wave's channel half: [mb][nb], lane (g, n)
-        f32x4 sacc[2][NB];
+            float alpha = 1.f;
+            if (__ballot(raise_lane)) {              // rare after the first tile
+              float tmax = x[0];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int e = 16 * mb + n;
-          f32x4 a[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) a[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const u32x4 sc4 = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * e);
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2) {
-            const int kk = 2 * half + k2;
-            const int chunk = 4 * kk + g;             // this lane's 32-channel block
-            const u32x4 w4 = *reinterpret_cast<const u32x4*>(
-                raw + kRawLat + 256 * e + 16 * (chunk ^ (e & 15)));
-            const int ksc = (int)((sc4[kk] >> (8 * g)) & 255u);
-            const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              a[nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  ka, qhi[nb][k2], a[nb], 4, 0, 0, ksc, 0, qsc[nb][k2]);
-              a[nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  ka, qlo[nb][k2], a[nb], 4, 0, 0, ksc, 0, qsc[nb][k2]);
+              for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
+              tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+              tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+              if (tmax > m_run[sb] + 8.f) {
+                alpha = __builtin_amdgcn_exp2f(m_run[sb] - tmax);
+                m_run[sb] = tmax;
+                l_run[sb] *= alpha;
+              }
+              if (g == 0) s_alpha[hb][n] = alpha;
+              raised_mask |= 1u << hb;
             }
-          }
-          {
-            const int chunk = 4 * half + g;
-            const u32x4 rv = *reinterpret_cast<const u32x4*>(
-                raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              a[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), as_bf16x8(qrope[nb]), a[nb], 0, 0, 0);
-          }
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = a[nb];
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) s_part[wave][NB * mb + nb][lane] = sacc[mb][nb];
-        // the next tile's raw bytes (staged one round ago) go to the other buffer
-        if (i + 1 < ntiles) store_tile(stg[(bb + 1) % kNPre], s_raw[(i + 1) & 1]);
-        __syncthreads();                         // partial S, V^T and raw(i+1) visible
-
-        // ---- full S^T = half 0 + half 1 (same order in both waves), online softmax
-        float x[NB][8];
-        float tmax[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) tmax[nb] = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const f32x4 o4 = s_part[wave ^ 1][NB * mb + nb][lane];
-            const f32x4 tot = half ? (o4 + sacc[mb][nb]) : (sacc[mb][nb] + o4);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const bool ok = s_rows[i * kTE + 16 * mb + 4 * g + k] >= 0;
-              const float v = ok ? tot[k] * sc_log2 : -INFINITY;
-              x[nb][4 * mb + k] = v;
-              tmax[nb] = fmaxf(tmax[nb], v);
-            }
-          }
-        f16x8 pb[NB];
-        bool any_valid = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          tmax[nb] = fmaxf(tmax[nb], __shfl_xor(tmax[nb], 16));
-          tmax[nb] = fmaxf(tmax[nb], __shfl_xor(tmax[nb], 32));
-          any_valid |= tmax[nb] != -INFINITY;
-        }
-        if (any_valid) {                         // uniform: the tile mask is shared
-          bool raise[NB], any_raise = false;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            raise[nb] = tmax[nb] > m_run[nb] + 8.f;
-            any_raise |= raise[nb];
-          }
-          if (__ballot(any_raise)) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const float al = raise[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - tmax[nb]) : 1.f;
-              m_run[nb] = raise[nb] ? tmax[nb] : m_run[nb];
-              l_run[nb] *= al;
-#pragma unroll
-              for (int c = 0; c < 16; ++c) acc[c][nb] *= al;
-            }
-          }
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
+            f16x8 pb;
             float ps = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(x[nb][k] - m_run[nb]);
-              pb[nb][k] = ph;
-              ps += (float)ph;
+              const float pv = __builtin_amdgcn_exp2f(x[k] - m_run[sb]);
+              ps += pv;
+              pb[k] = (_Float16)pv;
             }
-            l_run[nb] += ps;
-          }
-          // ---- O^T += V^T P^T over this wave's 256 channels
-          const uint8_t* vt = s_vt + (256 * half + n) * kVtStride + 16 * g;
-#pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              acc[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[nb], acc[c][nb], 0, 0, 0);
+            l_run[sb] += ps;
+            s_p[hb][lane] = __builtin_bit_cast(u32x4, pb);
           }
         }
-        __syncthreads();                         // V^T, s_part and raw(i) free again
+        if (raised_mask && lane == 0) atomicOr(&s_raised[i & 1], raised_mask);
+        // stage raw(i+1) (loaded kNPre-1 tiles ago) and reuse its registers for i+1+kNPre
+        store_tile(stg[(bb + 1) % kNPre], s_raw[(i + 1) & 1]);
+        load_tile(i + 1 + kNPre, stg[(bb + 1) % kNPre]);
+        __syncthreads();                         // P, rescale factors and raw(i+1) visible
+
+        // ---- value wave: rescale (rare), then O^T += V^T P^T; V^T(i+1) built alongside
+        const uint32_t raised = s_raised[i & 1];
+        if (raised) {
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            if (raised & (1u << hb)) {
+              const float al = s_alpha[hb][n];
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[c][hb] *= al;
+            }
+          }
+        }
+        f16x8 pbs[NHB];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) pbs[hb] = as_f16x8(s_p[hb][lane]);
+        build_vt(s_raw[(i + 1) & 1], s_vt[(i + 1) & 1]);
+        const uint8_t* vt = s_vt[i & 1] + (128 * wave + n) * kVtStride + 16 * g;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+            acc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[hb], acc[c][hb], 0, 0, 0);
+        }
+        __syncthreads();                         // V^T(i+1) complete; P, raw(i) free
+        // s_raised[i & 1] is next or-ed in tile i + 2, after a barrier tid 0 reaches later
+        if (raised && tid == 0) s_raised[i & 1] = 0u;
       }
     }
   }
 
-  // ---- epilogue: normalize, write (partial) output and log2-sum-exp
+  // ---- epilogue: score waves publish the softmax denominators, value waves normalize
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const float lse2 = (l_tot > 0.f) ? m_run[nb] + log2f(l_tot) : -INFINITY;
-    const int h = HG * hg + 16 * nb + n;
-    float* obase;
-    if (p.splits == 1) {
-      obase = p.o + ((int64_t)t * p.H + h) * kLat;
-      if (g == 0 && half == 0) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
-    } else {
-      const int64_t slot = ((int64_t)t * p.splits + sp) * p.H + h;
-      obase = p.o_part + slot * kLat;
-      if (g == 0 && half == 0) p.lse_part[slot] = lse2;
+  for (int sb = 0; sb < SPW; ++sb) {
+    const int hb = wave + NW * sb;
+    if (hb < NHB) {
+      float l_tot = l_run[sb] + __shfl_xor(l_run[sb], 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      const float lse2 = (l_tot > 0.f) ? m_run[sb] + log2f(l_tot) : -INFINITY;
+      if (g == 0) {
+        s_l[hb][n] = l_tot;
+        const int h = h0 + 16 * hb + n;
+        if (p.splits == 1) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
+        else p.lse_part[((int64_t)t * p.splits + sp) * p.H + h] = lse2;
+      }
     }
+  }
+  __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-      *reinterpret_cast<f32x4*>(obase + 256 * half + 16 * c + 4 * g) = acc[c][nb] * inv;
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float l_tot = s_l[hb][n];
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int h = h0 + 16 * hb + n;
+    float* obase = (p.splits == 1)
+        ? p.o + ((int64_t)t * p.H + h) * kLat
+        : p.o_part + (((int64_t)t * p.splits + sp) * p.H + h) * kLat;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<f32x4*>(obase + 128 * wave + 16 * c + 4 * g) = acc[c][hb] * inv;
   }
 }
 
@@ -460,10 +466,10 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(MergeParams p) {
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * p.splits);
   switch (p.H) {
-    case 16: hipLaunchKernelGGL((sparse_attn_kernel<1, 1>), dim3(blocks), dim3(128), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((sparse_attn_kernel<1, 2>), dim3(blocks), dim3(128), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((sparse_attn_kernel<2, 2>), dim3(blocks), dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((sparse_attn_kernel<4, 2>), dim3(blocks), dim3(512), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((sparse_attn_kernel<1>), dim3(blocks), dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((sparse_attn_kernel<2>), dim3(blocks), dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks), dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
