@@ -8,28 +8,31 @@
 // Every head of a row shares each entry (MLA-style latent): key = [latent ; rope] (576),
 // value = latent (512).
 //
-// One workgroup per (row, split of the K index slots) with four waves (one per SIMD).
-// Wave w is the "score wave" of heads 16w'.. (w' = w for H = 64; fewer heads per wave for
-// smaller H) and the "value wave" of latent channels 128w .. 128w+127 for every head.
+// One workgroup per (row, split of the K index slots, 64-head group) with eight waves: four
+// score waves and four value waves, one of each per SIMD, so that one wave's LDS and VALU
+// work hides behind the other's matrix work.  The query operands of a score wave and the
+// accumulators of a value wave occupy the same registers.
 //   gather  : the split's physical rows are resolved once into LDS.  Each 32-entry tile
 //             (8 KB codes, 4 KB rope, 0.5 KB scales) is fetched with coalesced 16-byte loads
 //             into registers two tiles ahead, then written to LDS with an XOR swizzle of
 //             the 16-byte slots so the operand reads below are bank-conflict free.
-//   QK^T    : S^T[32 entries x 16 heads] per score wave over all 576 channels.  The latent
-//             part runs on the MXFP4 matrix path (v_mfma_scale 16x16x128: A = the cached
-//             E2M1 codes with their own E8M0 block scales, dequantized inside the MFMA);
-//             the query enters as two fp8 (E4M3) parts with per-32-channel E8M0 scales,
-//             hi + lo, which reproduce the bf16 query exactly.  The rope part is bf16 MFMA.
+//   QK^T    : score wave hb computes S^T[32 entries x 16 heads 16hb..] over all 576
+//             channels.  The latent part runs on the MXFP4 matrix path (v_mfma_scale
+//             16x16x128: A = the cached E2M1 codes with their own E8M0 block scales,
+//             dequantized inside the MFMA); the query enters as two fp8 (E4M3) parts with
+//             per-32-channel E8M0 scales, hi + lo, which reproduce the bf16 query exactly.
+//             The rope part is bf16 MFMA.
 //   softmax : online, per head, log2 domain, fp32, in the score wave; the running maximum
-//             is raised only when a tile exceeds it by more than 2^8 (fp16 P <= 256).  The
-//             wave publishes P (fp16) and, when it raised a maximum, the rescale factors.
-//   PV      : O^T[128 channels x 64 heads] += V^T P^T per value wave on fp16 MFMA 16x16x32
-//             with fp32 accumulation; each V^T operand (one 16-byte LDS read) feeds the
-//             four 16-head blocks.  V^T is dequantized once per tile into LDS (fp16,
-//             channel-major, entries in the order the P^T operand has in registers), one
-//             tile ahead, alongside the PV of the current tile.  fp16 rather than bf16 for
-//             P: bf16 rounding of P alone would put the output's relative error near 1.7e-3.
-// Splits write normalized partial outputs plus log2-sum-exp; a merge kernel combines them.
+//             is raised only when a tile exceeds it by more than 2^12 (fp16 P <= 4096).
+//             The wave publishes P (fp16) and, when it raised a maximum, the rescale factors.
+//   PV      : value wave v accumulates O^T[128 channels 128v.. x all heads] += V^T P^T on
+//             fp16 MFMA 16x16x32 with fp32 accumulation; each V^T operand (one 16-byte LDS
+//             read) feeds every 16-head block.  V^T is dequantized once per tile into LDS
+//             (fp16, channel-major, entries in the order the P^T operand has in registers)
+//             by all eight waves, one tile ahead.  fp16 rather than bf16 for P: bf16
+//             rounding of P alone would put the output's relative error near 1.7e-3.
+// Shared buffers are double-buffered by tile parity, so each tile needs one barrier.  Splits
+// write normalized partial outputs plus log2-sum-exp; a merge kernel combines them.
 #include "csa2_internal.h"
 #include "csa2_device.h"
 
@@ -37,7 +40,9 @@ namespace csa2 {
 
 constexpr int kTE = 32;              // entries per tile
 constexpr int kMaxPerSplit = 2048;   // idx slots per split (LDS row table size)
-constexpr int kNPre = 2;             // tiles in flight in registers
+constexpr int kNPre = 2;             // tiles in flight in registers (= unroll, so that the
+                                     // tile parity, which picks every LDS buffer, is static)
+constexpr float kRaise = 12.f;       // log2 headroom before the running maximum is raised
 // raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16]
 constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 12800;
 constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rope, 1 scales
@@ -67,20 +72,20 @@ __device__ __forceinline__ int vt_pos(int e) {
 }
 
 template <int NHB>   // 16-head blocks per workgroup: 1, 2 or 4 (blockIdx.y picks 64-head groups)
-__global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
-  constexpr int NW = 4;
+__global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
+  constexpr int NW = 8;
   constexpr int NT = 64 * NW;
-  constexpr int SPW = (NHB + NW - 1) / NW;          // 16-head blocks scored per wave
-  constexpr int CPW = (kChunks + NW - 1) / NW;       // load units per wave
-  constexpr int VT_PER_T = (kTE / 4) * (kLat / 8) / NT;
-  constexpr float kMInit = -1.0e30f;                 // running max before any valid entry
+  constexpr int CPW = (kChunks + NW - 1) / NW;       // load units per wave and tile
+  constexpr int NACC = 8 * NHB;                      // f32x4 accumulators of a value wave
+  constexpr int NR = NACC > 19 ? NACC : 19;          // shared register slots (f32x4)
+  static_assert((kTE / 4) * (kLat / 8) == NT, "one V^T unit per thread and tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLat * kVtStride];
-  __shared__ __attribute__((aligned(16))) u32x4 s_p[NHB][64];      // P^T operands
-  __shared__ float s_alpha[NHB][16];                                // rescale factors
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[2][NHB][64];     // P^T operands
+  __shared__ float s_alpha[2][NHB][16];              // rescale factors of a raise
   __shared__ float s_l[NHB][16];
-  __shared__ uint32_t s_raised[2];                // per tile parity: blocks that raised
+  __shared__ uint32_t s_flag[3];                     // per tile mod 3: blocks that raised
   __shared__ int32_t s_rows[kMaxPerSplit];
   __shared__ uint32_t s_tmask[kMaxPerSplit / kTE];
 
@@ -90,8 +95,30 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
   const int nslots = max(min(k0 + p.per_split, p.K) - k0, 0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int h0 = 16 * NHB * blockIdx.y;            // first head of this workgroup
+  const int h0 = 16 * NHB * blockIdx.y;              // first head of this workgroup
   const int ntiles = (nslots + kTE - 1) / kTE;
+  // Roles: the parity of wave ^ (wave >> 2) splits each pair of waves that can share a
+  // SIMD (w, w + 4) and (2m, 2m + 1) into one score and one value wave.
+  const bool scorer_role = ((wave ^ (wave >> 2)) & 1) == 0;
+  const int rid = wave >> 1;                         // index within the role, 0..3
+  const bool scorer = scorer_role && rid < NHB;      // score wave of head block hb = rid
+  const int hb = min(rid, NHB - 1);
+
+  // ---- query loads first (independent of everything else); every wave issues them, so
+  //      that the compiler can count loads in flight
+  const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
+  u32x4 qraw[4][2][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
+      qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
+    }
+  }
+  const u32x4 qrope0 = ld_global_16(qp + kLat + 8 * g);
+  const u32x4 qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
 
   // ---- resolve the split's physical rows once (-1 = empty slot); one validity bit per
   //      entry of each tile
@@ -110,7 +137,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
       if (lane == 0) s_tmask[i >> 5] = (uint32_t)bal;
       if (lane == 32) s_tmask[i >> 5] = (uint32_t)(bal >> 32);
     }
-    if (tid < 2) s_raised[tid] = 0u;
+    if (tid < 3) s_flag[tid] = 0u;
   }
   __syncthreads();                                   // s_rows ready
 
@@ -118,7 +145,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
   //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
   //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
   //   j == 12    : scales of entry l (lanes < 32)
-  // Wave w owns units j = w + 4c.  Every wave issues CPW loads per tile without branches
+  // Wave w owns units j = w + 8c.  Every wave issues CPW loads per tile without branches
   // (dead units, empty slots and tiles past the end read the zero row), so the compiler
   // can count the loads in flight.
   const uint8_t* const lat_base = p.kv_lat;
@@ -156,34 +183,31 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
       }
     }
   };
-  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`
+  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`:
+  // thread (eq, co) converts entries 4eq..4eq+3 x channels 8co..8co+7
   auto build_vt = [&](const uint8_t* raw, uint8_t* vtb) {
+    const int eq = tid & 7;
+    const int co = tid >> 3;
+    uint32_t hv[4][4];
 #pragma unroll
-    for (int r = 0; r < VT_PER_T; ++r) {
-      const int it = tid + NT * r;
-      const int eq = it & 7;                       // entries 4eq .. 4eq+3
-      const int co = it >> 3;                      // channels 8co .. 8co+7
-      uint32_t hv[4][4];
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * eq + k;
+      const int slot = (co >> 2) ^ (e & 15);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(
+          raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
+      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);
+      fp4x8_to_f16_pairs(w, sc, hv[k]);
+    }
+    uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = 4 * eq + k;
-        const int slot = (co >> 2) ^ (e & 15);
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(
-            raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
-        const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);
-        fp4x8_to_f16_pairs(w, sc, hv[k]);
-      }
-      uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
-        lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
-        *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
-        *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
-      }
+    for (int k = 0; k < 4; ++k) {
+      u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
+      lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
+      *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
+      *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
     }
   };
 
@@ -191,32 +215,31 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
 #pragma unroll
   for (int b = 0; b < kNPre; ++b) load_tile(b, stg[b]);
 
-  // ---- query operands of this wave's score blocks, prepared while the first tiles fly.
-  // Latent part, per 128-channel chunk kk: the scaled MFMA pairs A lane group gA (one
-  // 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16), byte
-  // p%16 + 16(gA>>1).  So B lane (g, n) carries channels 32(4kk + g/2) + 16(g&1) + [0,16)
-  // in bytes 0..15 and the same run of block 4kk + g/2 + 2 in bytes 16..31; it supplies the
-  // E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2 max|q|) - 7,
-  // and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every bf16 value within
-  // 2^9 of the block maximum, and within 2^-16 of it below that.
-  i32x8 qhi[SPW][4], qlo[SPW][4];
-  int qsc[SPW][4];
-  u32x4 qrope[SPW][2];
-#pragma unroll
-  for (int sb = 0; sb < SPW; ++sb) {
-    const int hb = wave + NW * sb;                   // 16-head block scored by this wave
-    const int h = h0 + 16 * (hb < NHB ? hb : 0) + n;
-    const uint16_t* qp = p.q + ((int64_t)t * p.H + h) * kDq;
+  // ---- shared registers: score wave: R[2kk], R[2kk+1] = query hi part of chunk kk,
+  //      R[8+2kk], R[9+2kk] = lo part, R[16], R[17] = rope query, R[18] = scales;
+  //      value wave: R[c * NHB + b] = O^T block (channels 128v + 16c + 4g + i, head 16b + n)
+  f32x4 R[NR];
+  auto qpart = [&](int base) {
+    const u32x4 a = __builtin_bit_cast(u32x4, R[base]), b = __builtin_bit_cast(u32x4, R[base + 1]);
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  };
+  if (scorer_role) {
+    // Query operands, per 128-channel chunk kk: the scaled MFMA pairs A lane group gA (one
+    // 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16), byte
+    // p%16 + 16(gA>>1).  So B lane (g, n) carries channels 32(4kk + g/2) + 16(g&1) + [0,16)
+    // in bytes 0..15 and the same run of block 4kk + g/2 + 2 in bytes 16..31; it supplies the
+    // E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2 max|q|) - 7,
+    // and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every bf16 value within
+    // 2^9 of the block maximum, and within 2^-16 of it below that.
+    u32x4 scv = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
       float x[2][16];
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
-        const u32x4 v0 = ld_global_16(qp + c0 + 64 * run);
-        const u32x4 v1 = ld_global_16(qp + c0 + 64 * run + 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const u32x4 v0 = qraw[kk][run][0], v1 = qraw[kk][run][1];
           x[run][2 * e] = __uint_as_float(v0[e] << 16);
           x[run][2 * e + 1] = __uint_as_float(v0[e] & 0xffff0000u);
           x[run][8 + 2 * e] = __uint_as_float(v1[e] << 16);
@@ -238,8 +261,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
       // g = 1: run 0 of lane g = 3, g = 2: run 1 of lane g = 0)
       const int x0o = __shfl_xor(X[0], 32), x1o = __shfl_xor(X[1], 32);
       const int Xs = (g == 0) ? X[0] : (g == 3) ? X[1] : (g == 1) ? x0o : x1o;
-      qsc[sb][kk] = Xs + 127;
-      i32x8 hi, lo;
+      scv[kk] = (uint32_t)(Xs + 127);
+      u32x4 hi[2], lo[2];
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
         const float inv = __uint_as_float((uint32_t)(127 - X[run]) << 23);
@@ -256,182 +279,175 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnParams p) {
           r[3] = y[3] - __builtin_amdgcn_cvt_f32_fp8(hh, 3);
           int ll = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
           ll = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], ll, true);
-          hi[4 * run + d] = hh;
-          lo[4 * run + d] = ll;
+          hi[run][d] = (uint32_t)hh;
+          lo[run][d] = (uint32_t)ll;
         }
       }
-      qhi[sb][kk] = hi;
-      qlo[sb][kk] = lo;
+      R[2 * kk] = __builtin_bit_cast(f32x4, hi[0]);
+      R[2 * kk + 1] = __builtin_bit_cast(f32x4, hi[1]);
+      R[8 + 2 * kk] = __builtin_bit_cast(f32x4, lo[0]);
+      R[9 + 2 * kk] = __builtin_bit_cast(f32x4, lo[1]);
     }
-    qrope[sb][0] = ld_global_16(qp + kLat + 8 * g);
-    qrope[sb][1] = ld_global_16(qp + kLat + 32 + 8 * g);
+    R[16] = __builtin_bit_cast(f32x4, qrope0);
+    R[17] = __builtin_bit_cast(f32x4, qrope1);
+    R[18] = __builtin_bit_cast(f32x4, scv);
+#pragma unroll
+    for (int r = 19; r < NR; ++r) R[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) R[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // O^T accumulators of this value wave: channels 128 wave + 16 c + 4g + i, head 16 hb + n
-  f32x4 acc[8][NHB];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[SPW], l_run[SPW];
-#pragma unroll
-  for (int sb = 0; sb < SPW; ++sb) {
-    m_run[sb] = kMInit;
-    l_run[sb] = 0.f;
-  }
+  // score-wave state per head n; a finite initial maximum keeps fully masked tiles at
+  // 2^(-inf) = 0 instead of -inf - (-inf)
+  float m_run = -1.0e30f, l_run = 0.f;
 
   // ---- pipeline prologue: raw(0) and V^T(0) in LDS; registers hold tiles 1 .. kNPre
   store_tile(stg[0], s_raw[0]);
   load_tile(kNPre, stg[0]);
   __syncthreads();
   build_vt(s_raw[0], s_vt[0]);
-  __syncthreads();
 
-  // ---- tile i: QK^T + softmax (score waves) | stage raw(i+1) | PV(i) with V^T(i+1)
+  // ---- tile i: QK^T + softmax (score waves) | stage raw(i+1) | barrier |
+  //      PV(i) (value waves) | V^T(i+1) (all waves)
   const float sc_log2 = p.sm_scale_log2;
   for (int i0 = 0; i0 < ntiles; i0 += kNPre) {
 #pragma unroll
-    for (int bb = 0; bb < kNPre; ++bb) {
+    for (int bb = 0; bb < kNPre; ++bb) {             // bb = i & 1: static buffer parity
       const int i = i0 + bb;
       if (i < ntiles) {
-        const uint8_t* raw = s_raw[i & 1];
-        const uint32_t tm = s_tmask[i];
-        uint32_t raised_mask = 0u;
+        if (scorer) {
+          // ---- S^T[entries 16mb + 4g + k][head n]
+          const uint8_t* raw = s_raw[bb];
+          const u32x4 scv = __builtin_bit_cast(u32x4, R[18]);
+          f32x4 sacc[2];
 #pragma unroll
-        for (int sb = 0; sb < SPW; ++sb) {
-          const int hb = wave + NW * sb;
-          if (hb < NHB) {
-            // ---- S^T[entries 16mb + 4g + k][head n] for this 16-head block
-            f32x4 sacc[2];
+          for (int mb = 0; mb < 2; ++mb) {
+            const int e = 16 * mb + n;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+            const u32x4 sc4 = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * e);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-              const int e = 16 * mb + n;
-              f32x4 a = {0.f, 0.f, 0.f, 0.f};
-              const u32x4 sc4 = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * e);
-#pragma unroll
-              for (int kk = 0; kk < 4; ++kk) {
-                const int chunk = 4 * kk + g;         // this lane's 32-channel block
-                const u32x4 w4 = *reinterpret_cast<const u32x4*>(
-                    raw + kRawLat + 256 * e + 16 * (chunk ^ (e & 15)));
-                const int ksc = (int)((sc4[kk] >> (8 * g)) & 255u);
-                const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};
-                a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[sb][kk], a, 4, 0, 0, ksc, 0, qsc[sb][kk]);
-                a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[sb][kk], a, 4, 0, 0, ksc, 0, qsc[sb][kk]);
-              }
-#pragma unroll
-              for (int s2 = 0; s2 < 2; ++s2) {
-                const int chunk = 4 * s2 + g;
-                const u32x4 rv = *reinterpret_cast<const u32x4*>(
-                    raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), as_bf16x8(qrope[sb][s2]), a, 0, 0, 0);
-              }
-              sacc[mb] = a;
+            for (int kk = 0; kk < 4; ++kk) {
+              const int chunk = 4 * kk + g;           // this lane's 32-channel block
+              const u32x4 w4 = *reinterpret_cast<const u32x4*>(
+                  raw + kRawLat + 256 * e + 16 * (chunk ^ (e & 15)));
+              const int ksc = (int)((sc4[kk] >> (8 * g)) & 255u);
+              const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};
+              a0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qpart(2 * kk), a0, 4, 0, 0, ksc, 0, (int)scv[kk]);
+              a1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qpart(8 + 2 * kk), a1, 4, 0, 0, ksc, 0, (int)scv[kk]);
             }
-            // ---- online softmax; masked slots get -inf (exp2 -> 0)
-            float x[8];
-            bool raise_lane = false;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-              const uint32_t bits = tm >> (16 * mb + 4 * g);
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const float v = ((bits >> k) & 1u) ? sacc[mb][k] * sc_log2 : -INFINITY;
-                x[4 * mb + k] = v;
-                raise_lane |= v > m_run[sb] + 8.f;
-              }
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int chunk = 4 * s2 + g;
+              const u32x4 rv = *reinterpret_cast<const u32x4*>(
+                  raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
+              const bf16x8 qr = as_bf16x8(__builtin_bit_cast(u32x4, R[16 + s2]));
+              if (s2 == 0) a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, a0, 0, 0, 0);
+              else a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, a1, 0, 0, 0);
             }
+            sacc[mb] = a0 + a1;
+          }
+          // ---- online softmax; masked slots get -inf (exp2 -> 0)
+          const uint32_t tm = s_tmask[i];
+          float x[8];
+          bool raise_lane = false;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const uint32_t bits = tm >> (16 * mb + 4 * g);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float v = ((bits >> k) & 1u) ? sacc[mb][k] * sc_log2 : -INFINITY;
+              x[4 * mb + k] = v;
+              raise_lane |= v > m_run + kRaise;
+            }
+          }
+          if (__ballot(raise_lane)) {                // rare after the first tile
+            float tmax = x[0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             float alpha = 1.f;
-            if (__ballot(raise_lane)) {              // rare after the first tile
-              float tmax = x[0];
-#pragma unroll
-              for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
-              tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-              tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-              if (tmax > m_run[sb] + 8.f) {
-                alpha = __builtin_amdgcn_exp2f(m_run[sb] - tmax);
-                m_run[sb] = tmax;
-                l_run[sb] *= alpha;
-              }
-              if (g == 0) s_alpha[hb][n] = alpha;
-              raised_mask |= 1u << hb;
+            if (tmax > m_run + kRaise) {
+              alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+              m_run = tmax;
+              l_run *= alpha;
             }
-            f16x8 pb;
-            float ps = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const float pv = __builtin_amdgcn_exp2f(x[k] - m_run[sb]);
-              ps += pv;
-              pb[k] = (_Float16)pv;
-            }
-            l_run[sb] += ps;
-            s_p[hb][lane] = __builtin_bit_cast(u32x4, pb);
+            if (g == 0) s_alpha[bb][hb][n] = alpha;
+            if (lane == 0) atomicOr(&s_flag[i % 3], 1u << hb);
           }
+          f16x8 pb;
+          float ps = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float pv = __builtin_amdgcn_exp2f(x[k] - m_run);
+            ps += pv;
+            pb[k] = (_Float16)pv;
+          }
+          l_run += ps;
+          s_p[bb][hb][lane] = __builtin_bit_cast(u32x4, pb);
         }
-        if (raised_mask && lane == 0) atomicOr(&s_raised[i & 1], raised_mask);
         // stage raw(i+1) (loaded kNPre-1 tiles ago) and reuse its registers for i+1+kNPre
-        store_tile(stg[(bb + 1) % kNPre], s_raw[(i + 1) & 1]);
+        store_tile(stg[(bb + 1) % kNPre], s_raw[bb ^ 1]);
         load_tile(i + 1 + kNPre, stg[(bb + 1) % kNPre]);
-        __syncthreads();                         // P, rescale factors and raw(i+1) visible
+        __syncthreads();                 // P(i), rescale factors, raw(i+1), V^T(i) visible
 
-        // ---- value wave: rescale (rare), then O^T += V^T P^T; V^T(i+1) built alongside
-        const uint32_t raised = s_raised[i & 1];
-        if (raised) {
+        const uint32_t flag = s_flag[i % 3];
+        if (tid == 0) s_flag[(i + 2) % 3] = 0u;      // tile i-1's requests, all read by now
+        if (!scorer_role) {
+          // ---- value wave: rescale (rare), then O^T += V^T P^T
+          if (flag) {
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) {
-            if (raised & (1u << hb)) {
-              const float al = s_alpha[hb][n];
+            for (int b = 0; b < NHB; ++b) {
+              if ((flag >> b) & 1u) {
+                const float al = s_alpha[bb][b][n];
 #pragma unroll
-              for (int c = 0; c < 8; ++c) acc[c][hb] *= al;
+                for (int c = 0; c < 8; ++c) R[c * NHB + b] *= al;
+              }
             }
           }
+          f16x8 pbs[NHB];
+#pragma unroll
+          for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[bb][b][lane]);
+          const uint8_t* vt = s_vt[bb] + (128 * rid + n) * kVtStride + 16 * g;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
+#pragma unroll
+            for (int b = 0; b < NHB; ++b)
+              R[c * NHB + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], R[c * NHB + b], 0, 0, 0);
+          }
         }
-        f16x8 pbs[NHB];
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) pbs[hb] = as_f16x8(s_p[hb][lane]);
-        build_vt(s_raw[(i + 1) & 1], s_vt[(i + 1) & 1]);
-        const uint8_t* vt = s_vt[i & 1] + (128 * wave + n) * kVtStride + 16 * g;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-            acc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[hb], acc[c][hb], 0, 0, 0);
-        }
-        __syncthreads();                         // V^T(i+1) complete; P, raw(i) free
-        // s_raised[i & 1] is next or-ed in tile i + 2, after a barrier tid 0 reaches later
-        if (raised && tid == 0) s_raised[i & 1] = 0u;
+        build_vt(s_raw[bb ^ 1], s_vt[bb ^ 1]);
       }
     }
   }
 
   // ---- epilogue: score waves publish the softmax denominators, value waves normalize
-#pragma unroll
-  for (int sb = 0; sb < SPW; ++sb) {
-    const int hb = wave + NW * sb;
-    if (hb < NHB) {
-      float l_tot = l_run[sb] + __shfl_xor(l_run[sb], 16);
-      l_tot += __shfl_xor(l_tot, 32);
-      const float lse2 = (l_tot > 0.f) ? m_run[sb] + log2f(l_tot) : -INFINITY;
-      if (g == 0) {
-        s_l[hb][n] = l_tot;
-        const int h = h0 + 16 * hb + n;
-        if (p.splits == 1) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
-        else p.lse_part[((int64_t)t * p.splits + sp) * p.H + h] = lse2;
-      }
+  if (scorer) {
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (g == 0) {
+      s_l[hb][n] = l_tot;
+      const float lse2 = (l_tot > 0.f) ? m_run + log2f(l_tot) : -INFINITY;
+      const int h = h0 + 16 * hb + n;
+      if (p.splits == 1) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
+      else p.lse_part[((int64_t)t * p.splits + sp) * p.H + h] = lse2;
     }
   }
   __syncthreads();
+  if (!scorer_role) {
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const float l_tot = s_l[hb][n];
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int h = h0 + 16 * hb + n;
-    float* obase = (p.splits == 1)
-        ? p.o + ((int64_t)t * p.H + h) * kLat
-        : p.o_part + (((int64_t)t * p.splits + sp) * p.H + h) * kLat;
+    for (int b = 0; b < NHB; ++b) {
+      const float l_tot = s_l[b][n];
+      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const int h = h0 + 16 * b + n;
+      float* obase = (p.splits == 1)
+          ? p.o + ((int64_t)t * p.H + h) * kLat
+          : p.o_part + (((int64_t)t * p.splits + sp) * p.H + h) * kLat;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      *reinterpret_cast<f32x4*>(obase + 128 * wave + 16 * c + 4 * g) = acc[c][hb] * inv;
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<f32x4*>(obase + 128 * rid + 16 * c + 4 * g) = R[c * NHB + b] * inv;
+    }
   }
 }
 
@@ -466,10 +482,10 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(MergeParams p) {
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * p.splits);
   switch (p.H) {
-    case 16: hipLaunchKernelGGL((sparse_attn_kernel<1>), dim3(blocks), dim3(256), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((sparse_attn_kernel<2>), dim3(blocks), dim3(256), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks), dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((sparse_attn_kernel<1>), dim3(blocks), dim3(512), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((sparse_attn_kernel<2>), dim3(blocks), dim3(512), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks), dim3(512), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(512), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
