@@ -89,6 +89,8 @@ constexpr int kTopkThreads = 1024;
 // Split plan of the attention launch: `splits` workgroups per row, each covering
 // `per_split` (a multiple of 32, <= 2048) consecutive index slots.
 void attn_plan(int T, int H, int K, int* splits, int* per_split);
+// 64-head workgroups per (row, split) of the sparse attention kernel
+inline int attn_head_groups(int H) { return H > 64 ? H / 64 : 1; }
 
 // ---------------------------------------------------------------- launchers
 // Each launcher enqueues one kernel on `s` and returns hipGetLastError().

@@ -32,7 +32,9 @@
 //             by all eight waves, one tile ahead.  fp16 rather than bf16 for P: bf16
 //             rounding of P alone would put the output's relative error near 1.7e-3.
 // Shared buffers are double-buffered by tile parity, so each tile needs one barrier.  Splits
-// write normalized partial outputs plus log2-sum-exp; a merge kernel combines them.
+// write normalized partial outputs plus log2-sum-exp, and a merge kernel combines them.
+// Both kernels number their workgroups so that everything of a row runs on one XCD, whose
+// L2 then serves the row's shared query and its partial outputs.
 #include "csa2_internal.h"
 #include "csa2_device.h"
 
@@ -49,7 +51,7 @@ constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rop
 constexpr int kVtStride = 80;        // LDS bytes per V^T channel row (32 fp16 + 16 pad)
 
 void attn_plan(int T, int H, int K, int* splits, int* per_split) {
-  const int groups = H > 64 ? H / 64 : 1;                    // 64-head workgroups per split
+  const int groups = attn_head_groups(H);
   const int min_s = (K + kMaxPerSplit - 1) / kMaxPerSplit;
   const int max_s = max(1, (K + 2 * kTE - 1) / (2 * kTE));   // >= 2 tiles per split
   int s = (T > 0) ? (256 + T * groups - 1) / (T * groups) : 1;
@@ -71,6 +73,14 @@ __device__ __forceinline__ int vt_pos(int e) {
   return (e < 16) ? (8 * (e >> 2) + (e & 3)) : (8 * ((e - 16) >> 2) + 4 + (e & 3));
 }
 
+// Workgroup b of n runs on XCD b % 8; return the index of the b-th workgroup when XCD x
+// takes the x-th contiguous range of [0, n).
+__device__ __forceinline__ int xcd_linear(int b, int n) {
+  const int q8 = n >> 3, r8 = n & 7;
+  const int x = b & 7, slot = b >> 3;
+  return (x < r8) ? x * (q8 + 1) + slot : r8 * (q8 + 1) + (x - r8) * q8 + slot;
+}
+
 template <int NHB>   // 16-head blocks per workgroup: 1, 2 or 4 (blockIdx.y picks 64-head groups)
 __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
   constexpr int NW = 8;
@@ -89,8 +99,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
   __shared__ int32_t s_rows[kMaxPerSplit];
   __shared__ uint32_t s_tmask[kMaxPerSplit / kTE];
 
-  const int t = blockIdx.x / p.splits;
-  const int sp = blockIdx.x - t * p.splits;
+  // blockIdx.x -> (row, split): XCD x takes the x-th contiguous range of (row, split)
+  const int lin = xcd_linear((int)blockIdx.x, p.T * p.splits);
+  const int t = lin / p.splits;
+  const int sp = lin - t * p.splits;
   const int k0 = sp * p.per_split;
   const int nslots = max(min(k0 + p.per_split, p.K) - k0, 0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -104,21 +116,24 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
   const bool scorer = scorer_role && rid < NHB;      // score wave of head block hb = rid
   const int hb = min(rid, NHB - 1);
 
-  // ---- query loads first (independent of everything else); every wave issues them, so
-  //      that the compiler can count loads in flight
+  // ---- query loads of the score waves first (they precede every other load, so the
+  //      count of loads in flight stays exact on both sides of the branch)
   const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
   u32x4 qraw[4][2][2];
+  u32x4 qrope0, qrope1;
+  if (scorer_role) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
 #pragma unroll
-    for (int run = 0; run < 2; ++run) {
-      qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
-      qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
+      for (int run = 0; run < 2; ++run) {
+        qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
+        qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
+      }
     }
+    qrope0 = ld_global_16(qp + kLat + 8 * g);
+    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
   }
-  const u32x4 qrope0 = ld_global_16(qp + kLat + 8 * g);
-  const u32x4 qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
 
   // ---- resolve the split's physical rows once (-1 = empty slot); one validity bit per
   //      entry of each tile
@@ -435,48 +450,76 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
+  float inv[NHB];
+#pragma unroll
+  for (int b = 0; b < NHB; ++b) {
+    const float l_tot = s_l[b][n];
+    inv[b] = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  }
+  if (p.splits == 1) {
+    if (!scorer_role) {
+#pragma unroll
+      for (int b = 0; b < NHB; ++b) {
+        float* obase = p.o + ((int64_t)t * p.H + h0 + 16 * b + n) * kLat + 128 * rid + 4 * g;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          *reinterpret_cast<f32x4*>(obase + 16 * c) = R[c * NHB + b] * inv[b];
+      }
+    }
+    return;
+  }
   if (!scorer_role) {
 #pragma unroll
     for (int b = 0; b < NHB; ++b) {
-      const float l_tot = s_l[b][n];
-      const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      const int h = h0 + 16 * b + n;
-      float* obase = (p.splits == 1)
-          ? p.o + ((int64_t)t * p.H + h) * kLat
-          : p.o_part + (((int64_t)t * p.splits + sp) * p.H + h) * kLat;
+      float* obase = p.o_part + (((int64_t)t * p.splits + sp) * p.H + h0 + 16 * b + n) * kLat +
+                     128 * rid + 4 * g;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<f32x4*>(obase + 128 * rid + 16 * c + 4 * g) = R[c * NHB + b] * inv;
+        *reinterpret_cast<f32x4*>(obase + 16 * c) = R[c * NHB + b] * inv[b];
     }
   }
 }
 
-// o = sum_s 2^(lse2_s - lse2) o_s, lse2 = log2 sum_s 2^lse2_s; one block per (row, head).
-__global__ __launch_bounds__(128) void attn_merge_kernel(MergeParams p) {
-  const int th = blockIdx.x;
-  const int t = th / p.H, h = th - t * p.H;
+// o = sum_s 2^(lse2_s - lse2) o_s, lse = ln 2 * lse2 with lse2 = log2 sum_s 2^lse2_s.
+// Thread: 4 channels of one head; workgroup: 2 heads of one row.  All splits' loads are
+// issued before any is used (up to kMergeUnroll splits per round).
+constexpr int kMergeUnroll = 8;
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
+  const int hpb = 2;                                   // heads per workgroup
+  const int lin = xcd_linear((int)blockIdx.x, (int)gridDim.x);
+  const int per_row = p.H / hpb;
+  const int t = lin / per_row;
+  const int h = (lin - t * per_row) * hpb + (threadIdx.x >> 7);
+  const int c = 4 * (threadIdx.x & 127);
   const int S = p.splits;
+  const float* lp = p.lse_part + (int64_t)t * S * p.H + h;
+  const float* op = p.o_part + ((int64_t)t * S * p.H + h) * kLat + c;
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.lse_part[((int64_t)t * S + s) * p.H + h]);
-  float* o = p.o + ((int64_t)t * p.H + h) * kLat;
-  const int c = 4 * threadIdx.x;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * p.H]);
+  float* o = p.o + ((int64_t)t * p.H + h) * kLat + c;
   if (mx == -INFINITY) {
-    *reinterpret_cast<f32x4*>(o + c) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (threadIdx.x == 0) p.lse[(int64_t)t * p.H + h] = -INFINITY;
+    *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c == 0) p.lse[(int64_t)t * p.H + h] = -INFINITY;
     return;
   }
   float z = 0.f;
-  for (int s = 0; s < S; ++s)
-    z += __builtin_amdgcn_exp2f(p.lse_part[((int64_t)t * S + s) * p.H + h] - mx);
+  for (int s = 0; s < S; ++s) z += __builtin_amdgcn_exp2f(lp[(int64_t)s * p.H] - mx);
   const float lse2 = mx + __log2f(z);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const int64_t slot = ((int64_t)t * S + s) * p.H + h;
-    const float wgt = __builtin_amdgcn_exp2f(p.lse_part[slot] - lse2);
-    if (wgt > 0.f) acc += wgt * *reinterpret_cast<const f32x4*>(p.o_part + slot * kLat + c);
+  for (int s0 = 0; s0 < S; s0 += kMergeUnroll) {
+    f32x4 v[kMergeUnroll];
+    float wgt[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int s = min(s0 + u, S - 1);
+      v[u] = *reinterpret_cast<const f32x4*>(op + (int64_t)s * p.H * kLat);
+      wgt[u] = (s0 + u < S) ? __builtin_amdgcn_exp2f(lp[(int64_t)s * p.H] - lse2) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) acc += wgt[u] * v[u];
   }
-  *reinterpret_cast<f32x4*>(o + c) = acc;
-  if (threadIdx.x == 0) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
+  *reinterpret_cast<f32x4*>(o) = acc;
+  if (c == 0) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
 }
 
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
@@ -492,7 +535,7 @@ hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
 }
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)p.T * p.H)), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)p.T * p.H / 2)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
