@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -78,6 +79,48 @@ csa2_status timed(const char* name, hipStream_t s, F&& fn) {
     (void)hipEventRecord(e1, s);
     g_timing.pending.push_back({name, e0, e1});
   }
+  return CSA2_OK;
+}
+
+// ---------------------------------------------------------------- side stream
+// The SWA branch depends only on its own inputs, so it runs on a library-owned stream of
+// the current device (default priority), forked from and joined back into the caller's
+// stream with events.  Both are capturable, so a caller may record the calls in a graph.
+// One side stream and event pair per host thread and device.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false;
+};
+
+Side* side_for_current_device() {
+  thread_local std::map<int, Side> sides;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  Side& sd = sides[dev];
+  if (!sd.ok) {
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    sd.ok = true;
+  }
+  return &sd;
+}
+
+// Make `side` wait for everything issued to `s` so far.
+csa2_status fork_to(Side* sd, hipStream_t s) {
+  hipError_t e = hipEventRecord(sd->fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+  if (e != hipSuccess) return fail(CSA2_ERR_HIP, "side stream fork: %s", hipGetErrorString(e));
+  return CSA2_OK;
+}
+
+// Make `s` wait for everything issued to the side stream so far.
+csa2_status join_from(Side* sd, hipStream_t s) {
+  hipError_t e = hipEventRecord(sd->join, sd->s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
+  if (e != hipSuccess) return fail(CSA2_ERR_HIP, "side stream join: %s", hipGetErrorString(e));
   return CSA2_OK;
 }
 
@@ -265,7 +308,13 @@ csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
     st = timed("attn_merge", s, [&] { return launch_attn_merge(mp, s); });
     if (st) return st;
   }
-  if (a->q_swa) {
+  return CSA2_OK;
+}
+
+csa2_status run_swa(const csa2_attn_args* a, hipStream_t s) {
+  if (a->T == 0 || !a->q_swa) return CSA2_OK;
+  csa2_status st;
+  {
     SwaParams wp;
     wp.T = a->T;
     wp.H = a->H;
@@ -284,6 +333,29 @@ csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
     if (st) return st;
   }
   return CSA2_OK;
+}
+
+// The global branch on `s` and the SWA branches of `a[0..n)` on the side stream (on `s`
+// itself while kernel timing is on, or if no side stream could be made).
+template <class Global>
+csa2_status run_with_swa(const csa2_attn_args* a, int n, hipStream_t s, Global&& global) {
+  bool any_swa = false;
+  for (int i = 0; i < n; ++i) any_swa |= (a[i].q_swa != nullptr && a[i].T > 0);
+  // with per-kernel timing on, the branches run in sequence so that each kernel's
+  // events bracket that kernel alone
+  Side* sd = (any_swa && !g_timing.on) ? side_for_current_device() : nullptr;
+  csa2_status st;
+  if (sd) {
+    st = fork_to(sd, s);
+    if (st) return st;
+    for (int i = 0; i < n && !st; ++i) st = run_swa(&a[i], sd->s);
+    csa2_status st2 = global();
+    csa2_status st3 = join_from(sd, s);
+    return st ? st : (st2 ? st2 : st3);
+  }
+  st = global();
+  for (int i = 0; i < n && !st; ++i) st = run_swa(&a[i], s);
+  return st;
 }
 
 // ---------------------------------------------------------------- layer group
@@ -403,7 +475,8 @@ csa2_status csa2_sparse_attn_fp4(const csa2_attn_args* a, void* ws, size_t ws_by
   if (st) return st;
   st = check_ws("csa2_sparse_attn_fp4", ws, ws_bytes, a->T ? attn_ws_bytes(a->T, a->H, a->K) : 0);
   if (st) return st;
-  return run_attn(a, ws, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_with_swa(a, 1, s, [&] { return run_attn(a, ws, s); });
 }
 
 csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
@@ -418,19 +491,21 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
                 csa2_workspace_bytes(CSA2_OP_LAYER_GROUP, g));
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int i = 0; i < n_layers; ++i) {
-    if (L[i].mode != CSA2_REUSE) {
-      ia.q_idx = L[i].q_idx;
-      ia.w_idx = L[i].w_idx;
-      ia.k_idx = L[i].k_idx;
-      ia.idx_out = L[i].idx_out;
-      st = run_index(&ia, ws, s);
-      if (st) return st;
+  return run_with_swa(aa, n_layers, s, [&]() -> csa2_status {
+    for (int i = 0; i < n_layers; ++i) {
+      if (L[i].mode != CSA2_REUSE) {
+        ia.q_idx = L[i].q_idx;
+        ia.w_idx = L[i].w_idx;
+        ia.k_idx = L[i].k_idx;
+        ia.idx_out = L[i].idx_out;
+        csa2_status st2 = run_index(&ia, ws, s);
+        if (st2) return st2;
+      }
+      csa2_status st2 = run_attn(&aa[i], ws, s);
+      if (st2) return st2;
     }
-    st = run_attn(&aa[i], ws, s);
-    if (st) return st;
-  }
-  return CSA2_OK;
+    return CSA2_OK;
+  });
 }
 
 csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,

@@ -21,9 +21,13 @@
  *   the two branches are returned separately as (o, lse) pairs.
  *
  * Conventions (all entry points):
- *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
- *     No host synchronisation, no allocation: the caller owns all memory, including
- *     the workspace, whose size csa2_workspace_bytes() returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t of the current device;
+ *     NULL = the null stream).  No host synchronisation, no device allocation: the caller
+ *     owns all memory, including the workspace, whose size csa2_workspace_bytes()
+ *     returns.  The SWA branch runs on a library-owned stream of the current device
+ *     (one per host thread, created on first use), forked from `stream` and joined back
+ *     into it with events before the call returns; work queued on `stream` afterwards
+ *     sees every output.  Fork and join are capturable.
  *   - "device" pointers are device memory and must be 16-byte aligned.
  *   - bf16 tensors are raw 16-bit patterns; all layouts are dense row-major.
  *   - Paged caches: 64 entries per page; entry j of sequence b lives in physical row
@@ -207,7 +211,8 @@ int32_t csa2_abi_version(void);
 
 /* Kernel timing: while enabled, the library records a HIP event pair on the launch
  * stream around every kernel it launches and accumulates the elapsed time per kernel
- * name.  csa2_timing_read synchronizes on the recorded events, returns the number of
+ * name; the SWA branch then runs on the caller's stream after the global branch, so that
+ * every event pair brackets one kernel alone.  csa2_timing_read synchronizes on the recorded events, returns the number of
  * distinct kernels (at most `max`) with their names (NUL-terminated, 64 bytes each),
  * launch counts and total milliseconds, and resets the totals. */
 csa2_status csa2_timing_enable(int32_t on);
