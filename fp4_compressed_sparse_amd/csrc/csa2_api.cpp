@@ -193,8 +193,10 @@ csa2_status validate_index(const csa2_index_args* a) {
   return CSA2_OK;
 }
 
-csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {
-  if (a->T == 0) return CSA2_OK;
+// Indexer scoring, then Top-K; `between` runs after the scoring launch.
+template <class Between>
+csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, Between&& between) {
+  if (a->T == 0) return between();
   const int64_t E = (int64_t)a->max_pages * CSA2_PAGE;
   IdxScoreParams sp;
   sp.T = a->T;
@@ -211,6 +213,8 @@ csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {
   sp.keys = static_cast<uint32_t*>(ws);
   csa2_status st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
   if (st) return st;
+  st = between();
+  if (st) return st;
   TopkParams tp;
   tp.T = a->T;
   tp.K = a->K;
@@ -219,6 +223,10 @@ csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {
   tp.n_vis = a->n_vis;
   tp.idx_out = a->idx_out;
   return timed("topk", s, [&] { return launch_topk(tp, s); });
+}
+
+csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {
+  return run_index_split(a, ws, s, [] { return CSA2_OK; });
 }
 
 // ---------------------------------------------------------------- attention
@@ -491,21 +499,41 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
                 csa2_workspace_bytes(CSA2_OP_LAYER_GROUP, g));
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return run_with_swa(aa, n_layers, s, [&]() -> csa2_status {
-    for (int i = 0; i < n_layers; ++i) {
-      if (L[i].mode != CSA2_REUSE) {
-        ia.q_idx = L[i].q_idx;
-        ia.w_idx = L[i].w_idx;
-        ia.k_idx = L[i].k_idx;
-        ia.idx_out = L[i].idx_out;
-        csa2_status st2 = run_index(&ia, ws, s);
-        if (st2) return st2;
-      }
-      csa2_status st2 = run_attn(&aa[i], ws, s);
-      if (st2) return st2;
-    }
+  // Layer i's SWA branch goes to the side stream once layer i's indexer scoring is queued:
+  // both stream from HBM, so SWA overlaps Top-K, attention and the merge instead (forking
+  // before the scoring or after Top-K measured slower).
+  bool any_swa = false;
+  for (int i = 0; i < n_layers; ++i) any_swa |= (aa[i].q_swa != nullptr);
+  Side* sd = (any_swa && !g_timing.on) ? side_for_current_device() : nullptr;
+  csa2_status st_swa = CSA2_OK;
+  bool forked = false;
+  auto swa_now = [&](int i) -> csa2_status {
+    if (!sd) return CSA2_OK;
+    csa2_status f = fork_to(sd, s);
+    if (f) return f;
+    forked = true;
+    if (!st_swa) st_swa = run_swa(&aa[i], sd->s);
     return CSA2_OK;
-  });
+  };
+  for (int i = 0; i < n_layers && !st; ++i) {
+    if (L[i].mode != CSA2_REUSE) {
+      ia.q_idx = L[i].q_idx;
+      ia.w_idx = L[i].w_idx;
+      ia.k_idx = L[i].k_idx;
+      ia.idx_out = L[i].idx_out;
+      st = run_index_split(&ia, ws, s, [&] { return swa_now(i); });
+    } else {
+      st = swa_now(i);
+    }
+    if (!st) st = run_attn(&aa[i], ws, s);
+  }
+  if (forked) {
+    csa2_status sj = join_from(sd, s);
+    if (!st) st = sj;
+  }
+  if (!sd)
+    for (int i = 0; i < n_layers && !st; ++i) st = run_swa(&aa[i], s);
+  return st ? st : st_swa;
 }
 
 csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,

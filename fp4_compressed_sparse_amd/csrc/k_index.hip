@@ -41,10 +41,15 @@ __device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, i
 }
 
 // Score one page: MFMA A = q_idx (rows = heads, zero-padded to 16), B = keys (columns =
-// entries); the result lane (g, n) holds heads 4g..4g+3 of entry n.
+// entries); the result of group u in lane (g, n) holds heads 4g..4g+3 of entry 16u + n.
+// Each lane first sums its own four heads, then a reduce-scatter over the four lane groups
+// (v_permlane32_swap pairs groups g and g+2, v_permlane16_swap groups g and g+1) leaves
+// lane (g, n) with the whole sum of entry 16g + n, so the page's 64 keys go out in one
+// store.
 __device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa1,
                                                const float (&w)[4], const u32x4 (&kb)[8],
                                                int valid, int n, int g, uint32_t* keys) {
+  float su[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -54,10 +59,17 @@ __device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa
     s += w[1] * fmaxf(acc[1], 0.f);
     s += w[2] * fmaxf(acc[2], 0.f);
     s += w[3] * fmaxf(acc[3], 0.f);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    if (g == 0 && 16 * u + n < valid) keys[16 * u + n] = float_key(s);
+    su[u] = s;
   }
+  // lanes 0..31 (g = 0, 1) gather groups u = 0, 1 from g + 2; lanes 32..63 gather u = 2, 3
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(su[0]), __float_as_uint(su[2]), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(su[1]), __float_as_uint(su[3]), false, false);
+  const float ha = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float hb = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  // then each row g keeps group u = g from rows g and g ^ 1
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(ha), __float_as_uint(hb), false, false);
+  const float tot = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  if (16 * g + n < valid) keys[16 * g + n] = float_key(tot);
 }
 
 // One workgroup scores kIdxChunk consecutive entries of one row, each wave a run of whole
@@ -256,6 +268,23 @@ __device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_
   }
 }
 
+// Write the selected indices of one thread's keys (i0 + e) to their ordered positions.
+template <int KPT, class Ptr>
+__device__ __forceinline__ void topk_emit_regs(const uint32_t (&kv)[KPT], int i0, uint32_t tau,
+                                               uint32_t need_eq, uint32_t gtb, uint32_t eqb,
+                                               Ptr dst) {
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    if (kv[e] > tau) {
+      dst[gtb + min(eqb, need_eq)] = i0 + e;
+      ++gtb;
+    } else if (kv[e] == tau) {
+      if (eqb < need_eq) dst[gtb + eqb] = i0 + e;
+      ++eqb;
+    }
+  }
+}
+
 // Rows of at most 4096 * NR keys: thread t keeps keys [4NR t, 4NR (t+1)) in registers,
 // so the row is read from memory once and one block-wide scan orders the output.
 template <int NR>
@@ -290,23 +319,51 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) hist[0][4 * tid + e] = 0u;
-  __syncthreads();
 
-  uint32_t prefix = 0u, remaining = (uint32_t)K;
+  // Digit schedule.  Scores of one row mostly share the sign and the top exponent bits, so
+  // a first digit over bits 31..20 would pile them into a few bins (and the histogram
+  // atomics onto a few addresses).  When at least K keys share the top 4 bits of the row
+  // maximum, the K-th key is among them: take that nibble as a fixed prefix and digits
+  // over bits 27..16, 15..4, 3..0; otherwise bits 31..20, 19..8, 7..0.
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) kmax = max(kmax, kv[e]);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) s_wtot[wave] = kmax;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) kmax = max(kmax, s_wtot[w]);
+  uint32_t ctop = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) ctop += (kv[e] != 0u && (kv[e] >> 28) == (kmax >> 28));
+  uint32_t ctot;
+  (void)wave_prefix_small<7>(ctop, ctot);
+  __syncthreads();                                   // everyone has read the maxima
+  if (lane == 0) s_wtot[wave] = ctot;
+  __syncthreads();
+  ctop = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) ctop += s_wtot[w];
+  const bool narrow = ctop >= (uint32_t)K;
+  uint32_t prefix = narrow ? (kmax & 0xf0000000u) : 0u, remaining = (uint32_t)K;
+  __syncthreads();                                   // s_wtot is reused below
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
-    const uint32_t pmask = topk_prefix_mask(pass);
+    const int shift = narrow ? (pass == 0 ? 16 : (pass == 1 ? 4 : 0)) : (pass == 0 ? 20 : (pass == 1 ? 8 : 0));
+    const int width = narrow ? (pass == 2 ? 4 : 12) : (pass == 2 ? 8 : 12);
+    const uint32_t pmask = ~((2u << (shift + width - 1)) - 1u);   // bits above the digit
+    const uint32_t dmask = (1u << width) - 1u;
     uint32_t* h = hist[pass & 1];
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
-      if (kv[e] != 0u && (kv[e] & pmask) == prefix) atomicAdd(&h[topk_digit(kv[e], pass)], 1u);
+      if (kv[e] != 0u && (kv[e] & pmask) == prefix) atomicAdd(&h[(kv[e] >> shift) & dmask], 1u);
     // the other buffer is free: clear it for the next pass
 #pragma unroll
     for (int e = 0; e < 4; ++e) hist[(pass + 1) & 1][4 * tid + e] = 0u;
     __syncthreads();
     if (wave == 0) topk_find_digit_w0(h, remaining, &s_digit, &s_rem);
     __syncthreads();
-    prefix |= topk_place(s_digit, pass);
+    prefix |= s_digit << shift;
     remaining = s_rem;
   }
   const uint32_t tau = prefix, need_eq = remaining;
@@ -327,15 +384,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   for (int w = 0; w < wave; ++w) off += s_wtot[w];
   uint32_t gtb = (off & 0xffffu) + pg;
   uint32_t eqb = (off >> 16) + pe;
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    if (kv[e] > tau) {
-      out[gtb + min(eqb, need_eq)] = i0 + e;
-      ++gtb;
-    } else if (kv[e] == tau) {
-      if (eqb < need_eq) out[gtb + eqb] = i0 + e;
-      ++eqb;
-    }
+  // Stage the ordered output in the (now free) histogram space when it fits, so that the
+  // row goes out in coalesced stores; else write it in place.
+  if (K <= 2 * kHistBins) {
+    int32_t* s_out = reinterpret_cast<int32_t*>(&hist[0][0]);
+    topk_emit_regs<KPT>(kv, i0, tau, need_eq, gtb, eqb, s_out);
+    __syncthreads();
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = s_out[i];
+  } else {
+    topk_emit_regs<KPT>(kv, i0, tau, need_eq, gtb, eqb, out);
   }
 }
 
