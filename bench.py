@@ -11,7 +11,8 @@ One step = one Full-mode CSA2 layer through csa2_layer_group: indexer scoring, T
 FP4 gather attention (+ split merge) and the SWA branch (on the library's side stream,
 concurrent with the others), inputs resident in HBM.  The step clock runs without
 per-kernel events; a second pass of the same steps brackets every launch with HIP events
-on the stream it runs on.  Prints one JSON line (metric: decode query-tokens/s), with the
+on the stream it runs on, after a read sweep that evicts the last-level cache before each
+step.  Prints one JSON line (metric: decode query-tokens/s), with the
 dominant kernel's roofline (algorithmic bytes / its average duration) and the CPU oracle
 timed on a sample of the same workload.
 """
@@ -41,6 +42,12 @@ def parse_args():
                     help="1..5: which named workload (2 = the headline decode)")
     ap.add_argument("--cpu-rows", type=int, default=64,
                     help="query rows of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="MiB read before each step of the per-kernel timing pass, so that no "
+                         "kernel reads its inputs from the 256 MB last-level cache")
+    ap.add_argument("--kernel-pass-only", action="store_true",
+                    help="skip the whole-step clock; run only the per-kernel pass (warm-up "
+                         "steps included), so that a profiler's kernel averages match it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -212,28 +219,41 @@ def main():
     t_build = time.perf_counter() - t_build
     print(f"[bench] {w.name}: inputs built in {t_build:.1f} s", file=sys.stderr, flush=True)
 
+    scratch = (torch.ones(args.flush_mb << 18, dtype=torch.float32, device=dev)
+               if args.flush_mb > 0 else None)
+    if args.kernel_pass_only:
+        csa2.timing_enable(True)
     for _ in range(args.warmup):
+        if args.kernel_pass_only and scratch is not None:
+            scratch.sum()          # read-only sweep: no dirty lines left behind
         inp.step()
     torch.cuda.synchronize()
-    # whole-step clock: no per-kernel events inside the timed region
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        inp.step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr,
-          flush=True)
+    elapsed = float("nan")
+    if not args.kernel_pass_only:
+        # whole-step clock: no per-kernel events inside the timed region
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            inp.step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr,
+              flush=True)
     # per-kernel durations: a second pass of the same steps with HIP events around each
-    # launch, recorded on the stream that launch runs on
+    # launch, recorded on the stream that launch runs on; a scratch write before each step
+    # evicts the last-level cache
     csa2.timing_read()                       # drop anything recorded so far
     csa2.timing_enable(True)
     for _ in range(args.steps):
+        if scratch is not None:
+            scratch.sum()          # read-only sweep: no dirty lines left behind
         inp.step()
     torch.cuda.synchronize()
     csa2.timing_enable(False)
     kt = csa2.timing_read()
     ms_step = elapsed * 1e3 / args.steps
     qtok_s = w.T / (ms_step * 1e-3)
+    if args.kernel_pass_only:
+        ms_step = qtok_s = None
     algo = algorithmic_bytes(w)
     step_bytes = sum(algo.values())
     kernels = {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in kt.items()}
@@ -254,12 +274,12 @@ def main():
 
     result = {
         "metric": "decode query-tokens/s and achieved HBM GB/s (% peak) at 128K ctx, Top-K 2048",
-        "value": round(qtok_s, 1),
+        "value": round(qtok_s, 1) if qtok_s else None,
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms_step, 4) if ms_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -272,8 +292,9 @@ def main():
                    "layers": ["full", "reindex", "reuse"][:len(w.modes)] if len(w.modes) > 1
                    else ["full"], "parallelism": "single GPU"},
         "step_algo_bytes": step_bytes,
-        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1) if ms_step else None,
+        "step_hbm_frac": (round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                          if ms_step else None),
         "kernels": kernels,
         "roofline": roofline,
     }
