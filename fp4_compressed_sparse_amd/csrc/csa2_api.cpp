@@ -17,6 +17,10 @@
 
 using namespace csa2;
 
+namespace csa2 {
+thread_local hipEvent_t g_launch_events[2] = {nullptr, nullptr};
+}
+
 namespace {
 
 thread_local std::string g_err;
@@ -62,7 +66,8 @@ hipEvent_t timing_event() {
   return g_timing.pool[g_timing.used++];
 }
 
-// Launch `fn` (returning hipError_t) on `s`, bracketed by events when timing is on.
+// Launch `fn` (returning hipError_t, one kernel launch) on `s`; while timing is on, the
+// launch itself records a start and a stop event, so the pair brackets the kernel alone.
 template <class F>
 csa2_status timed(const char* name, hipStream_t s, F&& fn) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -70,13 +75,17 @@ csa2_status timed(const char* name, hipStream_t s, F&& fn) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     e0 = timing_event();
     e1 = timing_event();
-    if (e0) (void)hipEventRecord(e0, s);
+  }
+  (void)s;
+  if (e0 && e1) {
+    csa2::g_launch_events[0] = e0;
+    csa2::g_launch_events[1] = e1;
   }
   hipError_t err = fn();
+  csa2::g_launch_events[0] = csa2::g_launch_events[1] = nullptr;
   if (err != hipSuccess) return fail(CSA2_ERR_HIP, "%s launch: %s", name, hipGetErrorString(err));
   if (e0 && e1) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    (void)hipEventRecord(e1, s);
     g_timing.pending.push_back({name, e0, e1});
   }
   return CSA2_OK;

@@ -2,10 +2,18 @@
 // and small device helpers.  Not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace csa2 {
+
+// Start/stop events that the next kernel launch records itself (null = none): set by the
+// host-side timing wrapper around a launcher while kernel timing is on.
+extern thread_local hipEvent_t g_launch_events[2];
+#define CSA2_LAUNCH(kernel, grid, block, stream, ...)                                        \
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ::csa2::g_launch_events[0],        \
+                        ::csa2::g_launch_events[1], 0, __VA_ARGS__)
 
 constexpr int kLat = 512;        // latent channels (E2M1 codes, 2 per byte)
 constexpr int kLatBytes = 256;

@@ -525,17 +525,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * p.splits);
   switch (p.H) {
-    case 16: hipLaunchKernelGGL((sparse_attn_kernel<1>), dim3(blocks), dim3(512), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((sparse_attn_kernel<2>), dim3(blocks), dim3(512), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks), dim3(512), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(512), 0, s, p); break;
+    case 16: CSA2_LAUNCH((sparse_attn_kernel<1>), dim3(blocks), dim3(512), s, p); break;
+    case 32: CSA2_LAUNCH((sparse_attn_kernel<2>), dim3(blocks), dim3(512), s, p); break;
+    case 64: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks), dim3(512), s, p); break;
+    case 128: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(512), s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)p.T * p.H / 2)), dim3(256), 0, s, p);
+  CSA2_LAUNCH(attn_merge_kernel, dim3((unsigned)((int64_t)p.T * p.H / 2)), dim3(256), s, p);
   return hipGetLastError();
 }
 

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
 
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.T * p.chunks;
-  hipLaunchKernelGGL(idx_score_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   return hipGetLastError();
 }
 
@@ -465,11 +465,11 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   // key_stride bounds every row's n_vis; pick the register-resident variant that holds it
   const int64_t nr = (p.key_stride + 4 * kTopkThreads - 1) / (4 * kTopkThreads);
   const dim3 grid((unsigned)p.T), block(kTopkThreads);
-  if (nr <= 2) hipLaunchKernelGGL(topk_reg_kernel<2>, grid, block, 0, s, p);
-  else if (nr <= 4) hipLaunchKernelGGL(topk_reg_kernel<4>, grid, block, 0, s, p);
-  else if (nr <= 8) hipLaunchKernelGGL(topk_reg_kernel<8>, grid, block, 0, s, p);
-  else if (nr <= 16) hipLaunchKernelGGL(topk_reg_kernel<16>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, s, p);
+  if (nr <= 2) CSA2_LAUNCH(topk_reg_kernel<2>, grid, block, s, p);
+  else if (nr <= 4) CSA2_LAUNCH(topk_reg_kernel<4>, grid, block, s, p);
+  else if (nr <= 8) CSA2_LAUNCH(topk_reg_kernel<8>, grid, block, s, p);
+  else if (nr <= 16) CSA2_LAUNCH(topk_reg_kernel<16>, grid, block, s, p);
+  else CSA2_LAUNCH(topk_stream_kernel, grid, block, s, p);
   return hipGetLastError();
 }
 

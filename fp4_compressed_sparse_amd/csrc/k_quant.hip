@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
   const int64_t blocks = (p.rows + 3) / 4;
-  hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  CSA2_LAUNCH(mxfp4_quantize_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   return hipGetLastError();
 }
 

@@ -154,10 +154,10 @@ __global__ __launch_bounds__(256) void swa_kernel(SwaParams p) {
 hipError_t launch_swa(const SwaParams& p, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * p.H_kv);
   switch (p.H / p.H_kv) {
-    case 1: hipLaunchKernelGGL(swa_kernel<1>, dim3(blocks), dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(swa_kernel<2>, dim3(blocks), dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(swa_kernel<4>, dim3(blocks), dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(swa_kernel<8>, dim3(blocks), dim3(256), 0, s, p); break;
+    case 1: CSA2_LAUNCH(swa_kernel<1>, dim3(blocks), dim3(256), s, p); break;
+    case 2: CSA2_LAUNCH(swa_kernel<2>, dim3(blocks), dim3(256), s, p); break;
+    case 4: CSA2_LAUNCH(swa_kernel<4>, dim3(blocks), dim3(256), s, p); break;
+    case 8: CSA2_LAUNCH(swa_kernel<8>, dim3(blocks), dim3(256), s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -209,12 +209,12 @@ const char* csa2_last_error(void);
 const char* csa2_status_string(csa2_status s);
 int32_t csa2_abi_version(void);
 
-/* Kernel timing: while enabled, the library records a HIP event pair on the launch
- * stream around every kernel it launches and accumulates the elapsed time per kernel
+/* Kernel timing: while enabled, every kernel launch of the library records a start and a
+ * stop event itself (hipExtLaunchKernel), and the elapsed time accumulates per kernel
  * name; the SWA branch then runs on the caller's stream after the global branch, so that
- * every event pair brackets one kernel alone.  csa2_timing_read synchronizes on the recorded events, returns the number of
- * distinct kernels (at most `max`) with their names (NUL-terminated, 64 bytes each),
- * launch counts and total milliseconds, and resets the totals. */
+ * kernels do not overlap.  csa2_timing_read synchronizes on the recorded events, returns
+ * the number of distinct kernels (at most `max`) with their names (NUL-terminated, 64
+ * bytes each), launch counts and total milliseconds, and resets the totals. */
 csa2_status csa2_timing_enable(int32_t on);
 int32_t csa2_timing_read(char* names_64, int64_t* launches, double* total_ms, int32_t max);
 
