@@ -8,9 +8,9 @@
 // Every head of a row shares each entry (MLA-style latent): key = [latent ; rope] (576),
 // value = latent (512).
 //
-// One workgroup per (row, split of the K index slots, 64-head group) with eight waves: four
-// score waves and four value waves, one of each per SIMD, so that one wave's LDS and VALU
-// work hides behind the other's matrix work.  The query operands of a score wave and the
+// One workgroup per (row, split of the K index slots, 64-head group) with twelve waves: four
+// score waves and eight value waves, three waves per SIMD, so that one wave's LDS and VALU
+// work hides behind the others' matrix work.  The query operands of a score wave and the
 // accumulators of a value wave occupy the same registers.
 //   gather  : the split's physical rows are resolved once into LDS.  Each 32-entry tile
 //             (8 KB codes, 4 KB rope, 0.5 KB scales) is fetched with coalesced 16-byte loads
@@ -25,11 +25,11 @@
 //   softmax : online, per head, log2 domain, fp32, in the score wave; the running maximum
 //             is raised only when a tile exceeds it by more than 2^12 (fp16 P <= 4096).
 //             The wave publishes P (fp16) and, when it raised a maximum, the rescale factors.
-//   PV      : value wave v accumulates O^T[128 channels 128v.. x all heads] += V^T P^T on
+//   PV      : value wave v accumulates O^T[64 channels 64v.. x all heads] += V^T P^T on
 //             fp16 MFMA 16x16x32 with fp32 accumulation; each V^T operand (one 16-byte LDS
 //             read) feeds every 16-head block.  V^T is dequantized once per tile into LDS
 //             (fp16, channel-major, entries in the order the P^T operand has in registers)
-//             by all eight waves, one tile ahead.  fp16 rather than bf16 for P: bf16
+//             by the value waves, one tile ahead.  fp16 rather than bf16 for P: bf16
 //             rounding of P alone would put the output's relative error near 1.7e-3.
 // Shared buffers are double-buffered by tile parity, so each tile needs one barrier.  Splits
 // write normalized partial outputs plus log2-sum-exp, and a merge kernel combines them.
@@ -82,13 +82,12 @@ __device__ __forceinline__ int xcd_linear(int b, int n) {
 }
 
 template <int NHB>   // 16-head blocks per workgroup: 1, 2 or 4 (blockIdx.y picks 64-head groups)
-__global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
-  constexpr int NW = 8;
+__global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
+  constexpr int NW = 12;
   constexpr int NT = 64 * NW;
-  constexpr int CPW = (kChunks + NW - 1) / NW;       // load units per wave and tile
-  constexpr int NACC = 8 * NHB;                      // f32x4 accumulators of a value wave
-  constexpr int NR = NACC > 19 ? NACC : 19;          // shared register slots (f32x4)
-  static_assert((kTE / 4) * (kLat / 8) == NT, "one V^T unit per thread and tile");
+  constexpr int NV = 8;                              // value waves
+  constexpr int CPW = (kChunks + NV - 1) / NV;       // load units per value wave and tile
+  static_assert((kTE / 4) * (kLat / 8) == 64 * NV, "one V^T unit per value thread");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLat * kVtStride];
@@ -109,31 +108,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int h0 = 16 * NHB * blockIdx.y;              // first head of this workgroup
   const int ntiles = (nslots + kTE - 1) / kTE;
-  // Roles: the parity of wave ^ (wave >> 2) splits each pair of waves that can share a
-  // SIMD (w, w + 4) and (2m, 2m + 1) into one score and one value wave.
-  const bool scorer_role = ((wave ^ (wave >> 2)) & 1) == 0;
-  const int rid = wave >> 1;                         // index within the role, 0..3
-  const bool scorer = scorer_role && rid < NHB;      // score wave of head block hb = rid
-  const int hb = min(rid, NHB - 1);
-
-  // ---- query loads of the score waves first (they precede every other load, so the
-  //      count of loads in flight stays exact on both sides of the branch)
-  const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
-  u32x4 qraw[4][2][2];
-  u32x4 qrope0, qrope1;
-  if (scorer_role) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
-#pragma unroll
-      for (int run = 0; run < 2; ++run) {
-        qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
-        qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
-      }
-    }
-    qrope0 = ld_global_16(qp + kLat + 8 * g);
-    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
-  }
+  // Roles: waves 0..3 score (one per SIMD, as waves go to the SIMDs in turn), waves 4..11
+  // are value waves (two per SIMD).  Each role runs its own loop; both loops pass the same
+  // barriers in the same order.
+  const bool scorer_role = wave < 4;
 
   // ---- resolve the split's physical rows once (-1 = empty slot); one validity bit per
   //      entry of each tile
@@ -156,105 +134,31 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
   }
   __syncthreads();                                   // s_rows ready
 
-  // ---- gather: load unit j of a tile = 1 KB, lane l moves 16 bytes
-  //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
-  //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
-  //   j == 12    : scales of entry l (lanes < 32)
-  // Wave w owns units j = w + 8c.  Every wave issues CPW loads per tile without branches
-  // (dead units, empty slots and tiles past the end read the zero row), so the compiler
-  // can count the loads in flight.
-  const uint8_t* const lat_base = p.kv_lat;
-  const uint8_t* const rope_base = reinterpret_cast<const uint8_t*>(p.kv_rope);
-  const uint8_t* const scl_base = p.kv_scl;
-  auto unit_entry = [&](int j) {
-    return j < 8 ? 4 * j + (lane >> 4) : (j < 12 ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
-  };
-  auto load_tile = [&](int tile, u32x4 (&r)[CPW]) {
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int j = wave + NW * c;
-      const int row = (tile < ntiles && j < kChunks) ? s_rows[tile * kTE + unit_entry(j)] : -1;
-      const uint8_t* src;
-      if (j < 8) src = lat_base + (int64_t)row * kLatBytes + 16 * (lane & 15);
-      else if (j < 12) src = rope_base + (int64_t)row * (2 * kRope) + 16 * (lane & 7);
-      else src = scl_base + (int64_t)row * kScl;
-      const bool live = row >= 0 && (j < 12 || lane < 32);
-      r[c] = ld_global_16_addr(live ? reinterpret_cast<uint64_t>(src)
-                                    : reinterpret_cast<uint64_t>(g_zero_row));
-    }
-  };
-  auto store_tile = [&](const u32x4 (&r)[CPW], uint8_t* raw) {
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int j = wave + NW * c;
-      if (j < 8) {
-        const int e = 4 * j + (lane >> 4);
-        *reinterpret_cast<u32x4*>(raw + kRawLat + 256 * e + 16 * ((lane & 15) ^ (e & 15))) = r[c];
-      } else if (j < 12) {
-        const int e = 8 * (j - 8) + (lane >> 3);
-        *reinterpret_cast<u32x4*>(raw + kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7))) = r[c];
-      } else if (j == 12 && lane < 32) {
-        *reinterpret_cast<u32x4*>(raw + kRawScl + 16 * lane) = r[c];
-      }
-    }
-  };
-  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`:
-  // thread (eq, co) converts entries 4eq..4eq+3 x channels 8co..8co+7
-  auto build_vt = [&](const uint8_t* raw, uint8_t* vtb) {
-    const int eq = tid & 7;
-    const int co = tid >> 3;
-    uint32_t hv[4][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = 4 * eq + k;
-      const int slot = (co >> 2) ^ (e & 15);
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(
-          raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
-      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);
-      fp4x8_to_f16_pairs(w, sc, hv[k]);
-    }
-    uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
-      lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
-      *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
-      *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
-    }
-  };
-
-  u32x4 stg[kNPre][CPW];
-#pragma unroll
-  for (int b = 0; b < kNPre; ++b) load_tile(b, stg[b]);
-
-  // ---- shared registers: score wave: R[2kk], R[2kk+1] = query hi part of chunk kk,
-  //      R[8+2kk], R[9+2kk] = lo part, R[16], R[17] = rope query, R[18] = scales;
-  //      value wave: R[c * NHB + b] = O^T block (channels 128v + 16c + 4g + i, head 16b + n)
-  f32x4 R[NR];
-  auto qpart = [&](int base) {
-    const u32x4 a = __builtin_bit_cast(u32x4, R[base]), b = __builtin_bit_cast(u32x4, R[base + 1]);
-    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-  };
+  const float sc_log2 = p.sm_scale_log2;
   if (scorer_role) {
+    // ======================================================== score waves
+    const int hb = min(wave, NHB - 1);
+    const bool active = wave < NHB;                  // score wave of heads 16hb..16hb+15
     // Query operands, per 128-channel chunk kk: the scaled MFMA pairs A lane group gA (one
     // 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16), byte
     // p%16 + 16(gA>>1).  So B lane (g, n) carries channels 32(4kk + g/2) + 16(g&1) + [0,16)
-    // in bytes 0..15 and the same run of block 4kk + g/2 + 2 in bytes 16..31; it supplies the
-    // E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2 max|q|) - 7,
-    // and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every bf16 value within
-    // 2^9 of the block maximum, and within 2^-16 of it below that.
-    u32x4 scv = {0u, 0u, 0u, 0u};
+    // in bytes 0..15 and the same run of block 4kk + g/2 + 2 in bytes 16..31; it supplies
+    // the E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2
+    // max|q|) - 7, and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every
+    // bf16 value within 2^9 of the block maximum, and within 2^-16 of it below that.
+    const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
+    i32x8 qhi[4], qlo[4];
+    int qscp = 0;                                    // byte kk: E8M0 scale of block 4kk + g
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
       float x[2][16];
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
+        const u32x4 v0 = ld_global_16(qp + c0 + 64 * run);
+        const u32x4 v1 = ld_global_16(qp + c0 + 64 * run + 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const u32x4 v0 = qraw[kk][run][0], v1 = qraw[kk][run][1];
           x[run][2 * e] = __uint_as_float(v0[e] << 16);
           x[run][2 * e + 1] = __uint_as_float(v0[e] & 0xffff0000u);
           x[run][8 + 2 * e] = __uint_as_float(v1[e] << 16);
@@ -276,8 +180,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
       // g = 1: run 0 of lane g = 3, g = 2: run 1 of lane g = 0)
       const int x0o = __shfl_xor(X[0], 32), x1o = __shfl_xor(X[1], 32);
       const int Xs = (g == 0) ? X[0] : (g == 3) ? X[1] : (g == 1) ? x0o : x1o;
-      scv[kk] = (uint32_t)(Xs + 127);
-      u32x4 hi[2], lo[2];
+      qscp |= (Xs + 127) << (8 * kk);
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
         const float inv = __uint_as_float((uint32_t)(127 - X[run]) << 23);
@@ -294,189 +197,274 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttnParams p) {
           r[3] = y[3] - __builtin_amdgcn_cvt_f32_fp8(hh, 3);
           int ll = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
           ll = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], ll, true);
-          hi[run][d] = (uint32_t)hh;
-          lo[run][d] = (uint32_t)ll;
+          qhi[kk][4 * run + d] = hh;
+          qlo[kk][4 * run + d] = ll;
         }
       }
-      R[2 * kk] = __builtin_bit_cast(f32x4, hi[0]);
-      R[2 * kk + 1] = __builtin_bit_cast(f32x4, hi[1]);
-      R[8 + 2 * kk] = __builtin_bit_cast(f32x4, lo[0]);
-      R[9 + 2 * kk] = __builtin_bit_cast(f32x4, lo[1]);
     }
-    R[16] = __builtin_bit_cast(f32x4, qrope0);
-    R[17] = __builtin_bit_cast(f32x4, qrope1);
-    R[18] = __builtin_bit_cast(f32x4, scv);
-#pragma unroll
-    for (int r = 19; r < NR; ++r) R[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) R[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // score-wave state per head n; a finite initial maximum keeps fully masked tiles at
-  // 2^(-inf) = 0 instead of -inf - (-inf)
-  float m_run = -1.0e30f, l_run = 0.f;
+    const u32x4 qrope0 = ld_global_16(qp + kLat + 8 * g);
+    const u32x4 qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
+    // running state per head n; a finite initial maximum keeps fully masked tiles at
+    // 2^(-inf) = 0 instead of -inf - (-inf)
+    float m_run = -1.0e30f, l_run = 0.f;
+    __syncthreads();                                 // prologue: raw(0) staged
 
+    for (int i0 = 0; i0 < ntiles; i0 += kNPre) {
+#pragma unroll
+      for (int bb = 0; bb < kNPre; ++bb) {           // bb = i & 1: static buffer parity
+        const int i = i0 + bb;
+        if (i < ntiles) {
+          if (active) {
+            // ---- S^T[entries 16mb + 4g + k][head n]: four independent chains
+            const uint8_t* raw = s_raw[bb];
+            f32x4 ah[2], al[2];
+            int ksc[2];                                // blocks g, 4+g, 8+g, 12+g of entry e
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+              ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+              al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+              ksc[mb] = *reinterpret_cast<const int*>(raw + kRawScl + 16 * (16 * mb + n) + 4 * g);
+            }
+            // op_sel = kk picks byte kk of both scale dwords (scale of block 4kk + g)
+#define CSA2_QK_CHUNK(kk)                                                                     \
+  _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                        \
+    const int e = 16 * mb + n;                                                              \
+    const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
+        raw + kRawLat + 256 * e + 16 * ((4 * (kk) + g) ^ (e & 15)));                        \
+    const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};          \
+    ah[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[kk], ah[mb], 4, 0, kk, \
+                                                               ksc[mb], kk, qscp);          \
+    al[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[kk], al[mb], 4, 0, kk, \
+                                                               ksc[mb], kk, qscp);          \
+  }
+            CSA2_QK_CHUNK(0)
+            CSA2_QK_CHUNK(1)
+            CSA2_QK_CHUNK(2)
+            CSA2_QK_CHUNK(3)
+#undef CSA2_QK_CHUNK
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int chunk = 4 * s2 + g;
+              const bf16x8 qr = as_bf16x8(s2 == 0 ? qrope0 : qrope1);
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb) {
+                const int e = 16 * mb + n;
+                const u32x4 rv = *reinterpret_cast<const u32x4*>(
+                    raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
+                if (s2 == 0) ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, ah[mb], 0, 0, 0);
+                else al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, al[mb], 0, 0, 0);
+              }
+            }
+            // ---- online softmax; masked slots get -inf (exp2 -> 0)
+            const uint32_t tm = s_tmask[i];
+            float x[8];
+            bool raise_lane = false;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+              const uint32_t bits = tm >> (16 * mb + 4 * g);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float v = ((bits >> k) & 1u) ? (ah[mb][k] + al[mb][k]) * sc_log2 : -INFINITY;
+                x[4 * mb + k] = v;
+                raise_lane |= v > m_run + kRaise;
+              }
+            }
+            if (__ballot(raise_lane)) {              // rare after the first tile
+              float tmax = x[0];
+#pragma unroll
+              for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
+              tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+              tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+              float alpha = 1.f;
+              if (tmax > m_run + kRaise) {
+                alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+                m_run = tmax;
+                l_run *= alpha;
+              }
+              if (g == 0) s_alpha[bb][hb][n] = alpha;
+              if (lane == 0) atomicOr(&s_flag[i % 3], 1u << hb);
+            }
+            f16x8 pb;
+            float ps = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float pv = __builtin_amdgcn_exp2f(x[k] - m_run);
+              ps += pv;
+              pb[k] = (_Float16)pv;
+            }
+            l_run += ps;
+            s_p[bb][hb][lane] = __builtin_bit_cast(u32x4, pb);
+          }
+          __syncthreads();               // P(i), rescale factors, raw(i+1), V^T(i) visible
+        }
+      }
+    }
+    // ---- epilogue: publish the softmax denominators
+    if (active) {
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      if (g == 0) {
+        s_l[hb][n] = l_tot;
+        const float lse2 = (l_tot > 0.f) ? m_run + log2f(l_tot) : -INFINITY;
+        const int h = h0 + 16 * hb + n;
+        if (p.splits == 1) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
+        else p.lse_part[((int64_t)t * p.splits + sp) * p.H + h] = lse2;
+      }
+    }
+    __syncthreads();
+    return;
+  }
+
+  // ========================================================== value waves
+  const int rid = wave - 4;                          // 0..7: channels 64rid .. 64rid+63
+  // ---- gather: load unit j of a tile = 1 KB, lane l moves 16 bytes
+  //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
+  //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
+  //   j == 12    : scales of entry l (lanes < 32)
+  // Value wave v owns units j = v + 8c.  Every value wave issues CPW loads per tile without
+  // branches (dead units, empty slots and tiles past the end read the zero row), so the
+  // compiler can count the loads in flight.
+  const uint8_t* const lat_base = p.kv_lat;
+  const uint8_t* const rope_base = reinterpret_cast<const uint8_t*>(p.kv_rope);
+  const uint8_t* const scl_base = p.kv_scl;
+  auto unit_entry = [&](int j) {
+    return j < 8 ? 4 * j + (lane >> 4) : (j < 12 ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
+  };
+  auto load_tile = [&](int tile, u32x4 (&r)[CPW]) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int j = rid + NV * c;
+      const int row = (tile < ntiles && j < kChunks) ? s_rows[tile * kTE + unit_entry(j)] : -1;
+      const uint8_t* src;
+      if (j < 8) src = lat_base + (int64_t)row * kLatBytes + 16 * (lane & 15);
+      else if (j < 12) src = rope_base + (int64_t)row * (2 * kRope) + 16 * (lane & 7);
+      else src = scl_base + (int64_t)row * kScl;
+      const bool live = row >= 0 && (j < 12 || lane < 32);
+      r[c] = ld_global_16_addr(live ? reinterpret_cast<uint64_t>(src)
+                                    : reinterpret_cast<uint64_t>(g_zero_row));
+    }
+  };
+  auto store_tile = [&](const u32x4 (&r)[CPW], uint8_t* raw) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int j = rid + NV * c;
+      if (j < 8) {
+        const int e = 4 * j + (lane >> 4);
+        *reinterpret_cast<u32x4*>(raw + kRawLat + 256 * e + 16 * ((lane & 15) ^ (e & 15))) = r[c];
+      } else if (j < 12) {
+        const int e = 8 * (j - 8) + (lane >> 3);
+        *reinterpret_cast<u32x4*>(raw + kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7))) = r[c];
+      } else if (j == 12 && lane < 32) {
+        // entry `lane`'s 16 block scales, stored transposed: dword g holds blocks g, 4+g,
+        // 8+g, 12+g (bytes 0..3), so lane group g of the score MFMA reads one dword and
+        // picks chunk kk's byte with op_sel
+        const u32x4 v = r[c];
+        u32x4 tr;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const uint32_t sel = (uint32_t)gg | ((uint32_t)(4 + gg) << 8);
+          const uint32_t t01 = __builtin_amdgcn_perm(v[1], v[0], sel);   // blocks gg, 4+gg
+          const uint32_t t23 = __builtin_amdgcn_perm(v[3], v[2], sel);   // 8+gg, 12+gg
+          tr[gg] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+        }
+        *reinterpret_cast<u32x4*>(raw + kRawScl + 16 * lane) = tr;
+      }
+    }
+  };
+  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`: thread
+  // (eq, co) = (lane & 7, 8rid + lane / 8) converts entries 4eq..4eq+3 x channels
+  // 8co..8co+7
+  auto build_vt = [&](const uint8_t* raw, uint8_t* vtb) {
+    const int u = 64 * rid + lane;
+    const int eq = u & 7;
+    const int co = u >> 3;
+    uint32_t hv[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * eq + k;
+      const int slot = (co >> 2) ^ (e & 15);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(
+          raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
+      const int blk = co >> 2;                       // transposed scale layout
+      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + 4 * (blk & 3) + (blk >> 2)]);
+      fp4x8_to_f16_pairs(w, sc, hv[k]);
+    }
+    uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
+      lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
+      *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
+      *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
+    }
+  };
+
+  u32x4 stg[kNPre][CPW];
+#pragma unroll
+  for (int b = 0; b < kNPre; ++b) load_tile(b, stg[b]);
+  // O^T accumulators: channels 64rid + 16c + 4g + i, head h0 + 16b + n
+  f32x4 acc[4][NHB];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int b = 0; b < NHB; ++b) acc[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   // ---- pipeline prologue: raw(0) and V^T(0) in LDS; registers hold tiles 1 .. kNPre
   store_tile(stg[0], s_raw[0]);
   load_tile(kNPre, stg[0]);
-  __syncthreads();
-  build_vt(s_raw[0], s_vt[0]);
+  __syncthreads();                                   // prologue: raw(0) staged
+  build_vt(s_raw[0], s_vt[0]);                       // read by PV(0) after the first loop barrier
 
-  // ---- tile i: QK^T + softmax (score waves) | stage raw(i+1) | barrier |
-  //      PV(i) (value waves) | V^T(i+1) (all waves)
-  const float sc_log2 = p.sm_scale_log2;
   for (int i0 = 0; i0 < ntiles; i0 += kNPre) {
 #pragma unroll
     for (int bb = 0; bb < kNPre; ++bb) {             // bb = i & 1: static buffer parity
       const int i = i0 + bb;
       if (i < ntiles) {
-        if (scorer) {
-          // ---- S^T[entries 16mb + 4g + k][head n]
-          const uint8_t* raw = s_raw[bb];
-          const u32x4 scv = __builtin_bit_cast(u32x4, R[18]);
-          f32x4 sacc[2];
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const int e = 16 * mb + n;
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-            const u32x4 sc4 = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * e);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              const int chunk = 4 * kk + g;           // this lane's 32-channel block
-              const u32x4 w4 = *reinterpret_cast<const u32x4*>(
-                  raw + kRawLat + 256 * e + 16 * (chunk ^ (e & 15)));
-              const int ksc = (int)((sc4[kk] >> (8 * g)) & 255u);
-              const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};
-              a0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qpart(2 * kk), a0, 4, 0, 0, ksc, 0, (int)scv[kk]);
-              a1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qpart(8 + 2 * kk), a1, 4, 0, 0, ksc, 0, (int)scv[kk]);
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              const int chunk = 4 * s2 + g;
-              const u32x4 rv = *reinterpret_cast<const u32x4*>(
-                  raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
-              const bf16x8 qr = as_bf16x8(__builtin_bit_cast(u32x4, R[16 + s2]));
-              if (s2 == 0) a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, a0, 0, 0, 0);
-              else a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, a1, 0, 0, 0);
-            }
-            sacc[mb] = a0 + a1;
-          }
-          // ---- online softmax; masked slots get -inf (exp2 -> 0)
-          const uint32_t tm = s_tmask[i];
-          float x[8];
-          bool raise_lane = false;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const uint32_t bits = tm >> (16 * mb + 4 * g);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float v = ((bits >> k) & 1u) ? sacc[mb][k] * sc_log2 : -INFINITY;
-              x[4 * mb + k] = v;
-              raise_lane |= v > m_run + kRaise;
-            }
-          }
-          if (__ballot(raise_lane)) {                // rare after the first tile
-            float tmax = x[0];
-#pragma unroll
-            for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            float alpha = 1.f;
-            if (tmax > m_run + kRaise) {
-              alpha = __builtin_amdgcn_exp2f(m_run - tmax);
-              m_run = tmax;
-              l_run *= alpha;
-            }
-            if (g == 0) s_alpha[bb][hb][n] = alpha;
-            if (lane == 0) atomicOr(&s_flag[i % 3], 1u << hb);
-          }
-          f16x8 pb;
-          float ps = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float pv = __builtin_amdgcn_exp2f(x[k] - m_run);
-            ps += pv;
-            pb[k] = (_Float16)pv;
-          }
-          l_run += ps;
-          s_p[bb][hb][lane] = __builtin_bit_cast(u32x4, pb);
-        }
         // stage raw(i+1) (loaded kNPre-1 tiles ago) and reuse its registers for i+1+kNPre
         store_tile(stg[(bb + 1) % kNPre], s_raw[bb ^ 1]);
         load_tile(i + 1 + kNPre, stg[(bb + 1) % kNPre]);
         __syncthreads();                 // P(i), rescale factors, raw(i+1), V^T(i) visible
-
+        // ---- rescale (rare), then O^T += V^T P^T, V^T(i+1) alongside
         const uint32_t flag = s_flag[i % 3];
-        if (tid == 0) s_flag[(i + 2) % 3] = 0u;      // tile i-1's requests, all read by now
-        if (!scorer_role) {
-          // ---- value wave: rescale (rare), then O^T += V^T P^T
-          if (flag) {
+        if (tid == 256) s_flag[(i + 2) % 3] = 0u;    // tile i-1's requests, all read by now
+        if (flag) {
 #pragma unroll
-            for (int b = 0; b < NHB; ++b) {
-              if ((flag >> b) & 1u) {
-                const float al = s_alpha[bb][b][n];
+          for (int b = 0; b < NHB; ++b) {
+            if ((flag >> b) & 1u) {
+              const float al = s_alpha[bb][b][n];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) R[c * NHB + b] *= al;
-              }
+              for (int c = 0; c < 4; ++c) acc[c][b] *= al;
             }
           }
-          f16x8 pbs[NHB];
+        }
+        f16x8 pbs[NHB];
 #pragma unroll
-          for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[bb][b][lane]);
-          const uint8_t* vt = s_vt[bb] + (128 * rid + n) * kVtStride + 16 * g;
+        for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[bb][b][lane]);
+        const uint8_t* vt = s_vt[bb] + (64 * rid + n) * kVtStride + 16 * g;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
+        for (int c = 0; c < 4; ++c) {
+          const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
 #pragma unroll
-            for (int b = 0; b < NHB; ++b)
-              R[c * NHB + b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], R[c * NHB + b], 0, 0, 0);
-          }
+          for (int b = 0; b < NHB; ++b)
+            acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], acc[c][b], 0, 0, 0);
         }
         build_vt(s_raw[bb ^ 1], s_vt[bb ^ 1]);
       }
     }
   }
-
-  // ---- epilogue: score waves publish the softmax denominators, value waves normalize
-  if (scorer) {
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (g == 0) {
-      s_l[hb][n] = l_tot;
-      const float lse2 = (l_tot > 0.f) ? m_run + log2f(l_tot) : -INFINITY;
-      const int h = h0 + 16 * hb + n;
-      if (p.splits == 1) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
-      else p.lse_part[((int64_t)t * p.splits + sp) * p.H + h] = lse2;
-    }
-  }
-  __syncthreads();
-  float inv[NHB];
+  __syncthreads();                                   // denominators published
+  // ---- epilogue: normalize and write
 #pragma unroll
   for (int b = 0; b < NHB; ++b) {
     const float l_tot = s_l[b][n];
-    inv[b] = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  }
-  if (p.splits == 1) {
-    if (!scorer_role) {
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int64_t row = (p.splits == 1) ? ((int64_t)t * p.H + h0 + 16 * b + n)
+                                        : (((int64_t)t * p.splits + sp) * p.H + h0 + 16 * b + n);
+    float* obase = ((p.splits == 1) ? p.o : p.o_part) + row * kLat + 64 * rid + 4 * g;
 #pragma unroll
-      for (int b = 0; b < NHB; ++b) {
-        float* obase = p.o + ((int64_t)t * p.H + h0 + 16 * b + n) * kLat + 128 * rid + 4 * g;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          *reinterpret_cast<f32x4*>(obase + 16 * c) = R[c * NHB + b] * inv[b];
-      }
-    }
-    return;
-  }
-  if (!scorer_role) {
-#pragma unroll
-    for (int b = 0; b < NHB; ++b) {
-      float* obase = p.o_part + (((int64_t)t * p.splits + sp) * p.H + h0 + 16 * b + n) * kLat +
-                     128 * rid + 4 * g;
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<f32x4*>(obase + 16 * c) = R[c * NHB + b] * inv[b];
-    }
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<f32x4*>(obase + 16 * c) = acc[c][b] * inv;
   }
 }
 
@@ -525,10 +513,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * p.splits);
   switch (p.H) {
-    case 16: CSA2_LAUNCH((sparse_attn_kernel<1>), dim3(blocks), dim3(512), s, p); break;
-    case 32: CSA2_LAUNCH((sparse_attn_kernel<2>), dim3(blocks), dim3(512), s, p); break;
-    case 64: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks), dim3(512), s, p); break;
-    case 128: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(512), s, p); break;
+    case 16: CSA2_LAUNCH((sparse_attn_kernel<1>), dim3(blocks), dim3(768), s, p); break;
+    case 32: CSA2_LAUNCH((sparse_attn_kernel<2>), dim3(blocks), dim3(768), s, p); break;
+    case 64: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks), dim3(768), s, p); break;
+    case 128: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(768), s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
