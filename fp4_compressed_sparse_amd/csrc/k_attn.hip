@@ -113,6 +113,25 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   // barriers in the same order.
   const bool scorer_role = wave < 4;
 
+  // ---- the score waves' query loads go out first, so that their latency overlaps the
+  //      row resolution below
+  const int hb = min(wave, NHB - 1);
+  const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
+  u32x4 qraw[4][2][2], qrope0, qrope1;
+  if (scorer_role) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
+        qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
+      }
+    }
+    qrope0 = ld_global_16(qp + kLat + 8 * g);
+    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
+  }
+
   // ---- resolve the split's physical rows once (-1 = empty slot); one validity bit per
   //      entry of each tile
   {
@@ -137,7 +156,6 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   const float sc_log2 = p.sm_scale_log2;
   if (scorer_role) {
     // ======================================================== score waves
-    const int hb = min(wave, NHB - 1);
     const bool active = wave < NHB;                  // score wave of heads 16hb..16hb+15
     // Query operands, per 128-channel chunk kk: the scaled MFMA pairs A lane group gA (one
     // 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16), byte
@@ -146,17 +164,14 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     // the E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2
     // max|q|) - 7, and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every
     // bf16 value within 2^9 of the block maximum, and within 2^-16 of it below that.
-    const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
     i32x8 qhi[4], qlo[4];
     int qscp = 0;                                    // byte kk: E8M0 scale of block 4kk + g
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
       float x[2][16];
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
-        const u32x4 v0 = ld_global_16(qp + c0 + 64 * run);
-        const u32x4 v1 = ld_global_16(qp + c0 + 64 * run + 8);
+        const u32x4 v0 = qraw[kk][run][0], v1 = qraw[kk][run][1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[run][2 * e] = __uint_as_float(v0[e] << 16);
@@ -202,8 +217,6 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
         }
       }
     }
-    const u32x4 qrope0 = ld_global_16(qp + kLat + 8 * g);
-    const u32x4 qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
     // running state per head n; a finite initial maximum keeps fully masked tiles at
     // 2^(-inf) = 0 instead of -inf - (-inf)
     float m_run = -1.0e30f, l_run = 0.f;
