@@ -43,7 +43,8 @@ namespace csa2 {
 constexpr int kTE = 32;              // entries per tile
 constexpr int kMaxPerSplit = 2048;   // idx slots per split (LDS row table size)
 constexpr int kNPre = 2;             // tiles in flight in registers (= unroll, so that the
-                                     // tile parity, which picks every LDS buffer, is static)
+                                     // staging slot and the tile parity, which picks every
+                                     // LDS buffer, are static)
 constexpr float kRaise = 12.f;       // log2 headroom before the running maximum is raised
 // raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16]
 constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 12800;
@@ -67,6 +68,12 @@ void attn_plan(int T, int H, int K, int* splits, int* per_split) {
 // An all-zero row stands in for empty index slots (so staged tiles never hold garbage).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[256];
 
+// LDS swizzles of a staged tile.  Codes: entry e's 16-byte slot c sits at slot
+// c ^ (e & 15) ^ (e >> 4); scales: entry e's (transposed) dword d sits at d ^ 2 (e >> 4).
+// Readers that take entries e and e + 16 in one access then hit different banks.
+__device__ __forceinline__ int lat_slot(int c, int e) { return c ^ (e & 15) ^ (e >> 4); }
+__device__ __forceinline__ int scl_dword(int d, int e) { return d ^ ((e >> 4) << 1); }
+
 // Position of entry e of a tile in a V^T row: the P^T operand of lane group g carries
 // entries 4g..4g+3 then 16+4g..16+4g+3, so contraction slots 8g..8g+7 map to those.
 __device__ __forceinline__ int vt_pos(int e) {
@@ -89,7 +96,8 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   constexpr int CPW = (kChunks + NV - 1) / NV;       // load units per value wave and tile
   static_assert((kTE / 4) * (kLat / 8) == 64 * NV, "one V^T unit per value thread");
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBytes];
+  // raw tiles, each followed by 1 KB that dead staging lanes write to
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBytes + 1024];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLat * kVtStride];
   __shared__ __attribute__((aligned(16))) u32x4 s_p[2][NHB][64];     // P^T operands
   __shared__ float s_alpha[2][NHB][16];              // rescale factors of a raise
@@ -108,6 +116,10 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int h0 = 16 * NHB * blockIdx.y;              // first head of this workgroup
   const int ntiles = (nslots + kTE - 1) / kTE;
+  // the loops run whole groups of kNPre tiles (static buffer parity and staging slot, and
+  // no path on which a tile of a group is skipped, so the compiler counts loads in flight
+  // exactly); a padding tile has no valid entry
+  const int ntiles2 = (ntiles + kNPre - 1) / kNPre * kNPre;
   // Roles: waves 0..3 score (one per SIMD, as waves go to the SIMDs in turn), waves 4..11
   // are value waves (two per SIMD).  Each role runs its own loop; both loops pass the same
   // barriers in the same order.
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     const int b = p.seq_id[t];
     const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
     const int32_t* idx = p.idx + (int64_t)t * p.K + k0;
-    for (int i = tid; i < ntiles * kTE; i += NT) {
+    for (int i = tid; i < ntiles2 * kTE; i += NT) {
       int32_t row = -1;
       if (i < nslots) {
         const int j = idx[i];
@@ -152,6 +164,36 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     if (tid < 3) s_flag[tid] = 0u;
   }
   __syncthreads();                                   // s_rows ready
+
+  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`, built
+  // by the value waves, one tile ahead: unit u = 64 (wave - 4) + lane = (eq, co) converts
+  // entries 4eq..4eq+3 x channels 8co..8co+7
+  auto build_vt_unit = [&](const uint8_t* raw, uint8_t* vtb, int u) {
+    const int eq = u & 7;
+    const int co = u >> 3;
+    uint32_t hv[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * eq + k;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(
+          raw + kRawLat + 256 * e + 16 * lat_slot(co >> 2, e) + 4 * (co & 3));
+      const int blk = co >> 2;                       // transposed, swizzled scale layout
+      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + 4 * scl_dword(blk & 3, e) + (blk >> 2)]);
+      fp4x8_to_f16_pairs(w, sc, hv[k]);
+    }
+    uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
+      lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
+      *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
+      *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
+    }
+  };
+
 
   const float sc_log2 = p.sm_scale_log2;
   if (scorer_role) {
@@ -222,28 +264,29 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     float m_run = -1.0e30f, l_run = 0.f;
     __syncthreads();                                 // prologue: raw(0) staged
 
-    for (int i0 = 0; i0 < ntiles; i0 += kNPre) {
+    for (int i0 = 0; i0 < ntiles2; i0 += kNPre) {
 #pragma unroll
-      for (int bb = 0; bb < kNPre; ++bb) {           // bb = i & 1: static buffer parity
+      for (int bb = 0; bb < kNPre; ++bb) {           // bb & 1 = i & 1: static buffer parity
         const int i = i0 + bb;
-        if (i < ntiles) {
+        {
           if (active) {
             // ---- S^T[entries 16mb + 4g + k][head n]: four independent chains
-            const uint8_t* raw = s_raw[bb];
+            const uint8_t* raw = s_raw[bb & 1];
             f32x4 ah[2], al[2];
             int ksc[2];                                // blocks g, 4+g, 8+g, 12+g of entry e
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
               ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
               al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-              ksc[mb] = *reinterpret_cast<const int*>(raw + kRawScl + 16 * (16 * mb + n) + 4 * g);
+              ksc[mb] = *reinterpret_cast<const int*>(raw + kRawScl + 16 * (16 * mb + n) +
+                                                      4 * scl_dword(g, 16 * mb + n));
             }
             // op_sel = kk picks byte kk of both scale dwords (scale of block 4kk + g)
 #define CSA2_QK_CHUNK(kk)                                                                     \
   _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                        \
     const int e = 16 * mb + n;                                                              \
     const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
-        raw + kRawLat + 256 * e + 16 * ((4 * (kk) + g) ^ (e & 15)));                        \
+        raw + kRawLat + 256 * e + 16 * lat_slot(4 * (kk) + g, e));                          \
     const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};          \
     ah[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[kk], ah[mb], 4, 0, kk, \
                                                                ksc[mb], kk, qscp);          \
@@ -294,7 +337,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
                 m_run = tmax;
                 l_run *= alpha;
               }
-              if (g == 0) s_alpha[bb][hb][n] = alpha;
+              if (g == 0) s_alpha[bb & 1][hb][n] = alpha;
               if (lane == 0) atomicOr(&s_flag[i % 3], 1u << hb);
             }
             f16x8 pb;
@@ -306,8 +349,9 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
               pb[k] = (_Float16)pv;
             }
             l_run += ps;
-            s_p[bb][hb][lane] = __builtin_bit_cast(u32x4, pb);
+            s_p[bb & 1][hb][lane] = __builtin_bit_cast(u32x4, pb);
           }
+
           __syncthreads();               // P(i), rescale factors, raw(i+1), V^T(i) visible
         }
       }
@@ -334,90 +378,70 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
   //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
   //   j == 12    : scales of entry l (lanes < 32)
-  // Value wave v owns units j = v + 8c.  Every value wave issues CPW loads per tile without
-  // branches (dead units, empty slots and tiles past the end read the zero row), so the
-  // compiler can count the loads in flight.
-  const uint8_t* const lat_base = p.kv_lat;
-  const uint8_t* const rope_base = reinterpret_cast<const uint8_t*>(p.kv_rope);
-  const uint8_t* const scl_base = p.kv_scl;
-  auto unit_entry = [&](int j) {
-    return j < 8 ? 4 * j + (lane >> 4) : (j < 12 ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
+  // Value wave v owns units j = v + 8c.  Everything about a unit that does not depend on
+  // the tile is worked out once, so that staging is straight-line code: every lane issues
+  // one 16-byte load and one 16-byte LDS store per unit and tile (dead lanes load the zero
+  // row and store to a scratch area of LDS), and the compiler counts the loads in flight
+  // exactly.  Row indices are read from LDS one tile ahead of their loads.
+  const uint8_t* u_base[CPW];
+  int u_stride[CPW], u_goff[CPW], u_lds[CPW], u_entry[CPW];
+  bool u_live[CPW], u_scl[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int j = rid + NV * c;
+    const bool codes = j < 8, rope = !codes && j < 12, scl = j == 12;
+    const int e = codes ? 4 * j + (lane >> 4) : (rope ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
+    u_entry[c] = e;
+    u_scl[c] = scl;
+    u_live[c] = codes || rope || (scl && lane < 32);
+    u_base[c] = codes ? p.kv_lat : (rope ? reinterpret_cast<const uint8_t*>(p.kv_rope) : p.kv_scl);
+    u_stride[c] = codes ? kLatBytes : (rope ? 2 * kRope : kScl);
+    u_goff[c] = codes ? 16 * (lane & 15) : (rope ? 16 * (lane & 7) : 0);
+    u_lds[c] = !u_live[c] ? kRawBytes + 16 * lane      // dead: the scratch area below
+             : codes ? kRawLat + 256 * e + 16 * lat_slot(lane & 15, e)
+             : rope ? kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7))
+                    : kRawScl + 16 * lane;
+  }
+  auto rows_of = [&](int tile, int (&rr)[CPW]) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      rr[c] = (tile < ntiles && u_live[c]) ? s_rows[tile * kTE + u_entry[c]] : -1;
   };
-  auto load_tile = [&](int tile, u32x4 (&r)[CPW]) {
+  auto load_tile = [&](const int (&rr)[CPW], u32x4 (&r)[CPW]) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int j = rid + NV * c;
-      const int row = (tile < ntiles && j < kChunks) ? s_rows[tile * kTE + unit_entry(j)] : -1;
-      const uint8_t* src;
-      if (j < 8) src = lat_base + (int64_t)row * kLatBytes + 16 * (lane & 15);
-      else if (j < 12) src = rope_base + (int64_t)row * (2 * kRope) + 16 * (lane & 7);
-      else src = scl_base + (int64_t)row * kScl;
-      const bool live = row >= 0 && (j < 12 || lane < 32);
-      r[c] = ld_global_16_addr(live ? reinterpret_cast<uint64_t>(src)
-                                    : reinterpret_cast<uint64_t>(g_zero_row));
+      const uint8_t* src = u_base[c] + (int64_t)rr[c] * u_stride[c] + u_goff[c];
+      r[c] = ld_global_16_addr(rr[c] >= 0 ? reinterpret_cast<uint64_t>(src)
+                                          : reinterpret_cast<uint64_t>(g_zero_row));
     }
   };
   auto store_tile = [&](const u32x4 (&r)[CPW], uint8_t* raw) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int j = rid + NV * c;
-      if (j < 8) {
-        const int e = 4 * j + (lane >> 4);
-        *reinterpret_cast<u32x4*>(raw + kRawLat + 256 * e + 16 * ((lane & 15) ^ (e & 15))) = r[c];
-      } else if (j < 12) {
-        const int e = 8 * (j - 8) + (lane >> 3);
-        *reinterpret_cast<u32x4*>(raw + kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7))) = r[c];
-      } else if (j == 12 && lane < 32) {
-        // entry `lane`'s 16 block scales, stored transposed: dword g holds blocks g, 4+g,
-        // 8+g, 12+g (bytes 0..3), so lane group g of the score MFMA reads one dword and
-        // picks chunk kk's byte with op_sel
-        const u32x4 v = r[c];
-        u32x4 tr;
+      // entry `lane`'s 16 block scales are stored transposed: dword d holds blocks d, 4+d,
+      // 8+d, 12+d, at position scl_dword(d, e), so lane group g of the score MFMA reads one
+      // dword and picks chunk kk's byte with op_sel
+      const u32x4 v = r[c];
+      u32x4 sw;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const uint32_t sel = (uint32_t)gg | ((uint32_t)(4 + gg) << 8);
-          const uint32_t t01 = __builtin_amdgcn_perm(v[1], v[0], sel);   // blocks gg, 4+gg
-          const uint32_t t23 = __builtin_amdgcn_perm(v[3], v[2], sel);   // 8+gg, 12+gg
-          tr[gg] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-        }
-        *reinterpret_cast<u32x4*>(raw + kRawScl + 16 * lane) = tr;
+      for (int d = 0; d < 4; ++d) {
+        const int dd = scl_dword(d, lane & 31);        // position of dword d
+        const uint32_t sel = (uint32_t)d | ((uint32_t)(4 + d) << 8);
+        const uint32_t t01 = __builtin_amdgcn_perm(v[1], v[0], sel);   // blocks d, 4+d
+        const uint32_t t23 = __builtin_amdgcn_perm(v[3], v[2], sel);   // 8+d, 12+d
+        const uint32_t tr = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+        sw[dd] = tr;
       }
+      *reinterpret_cast<u32x4*>(raw + u_lds[c]) = u_scl[c] ? sw : v;
     }
   };
-  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`: thread
-  // (eq, co) = (lane & 7, 8rid + lane / 8) converts entries 4eq..4eq+3 x channels
-  // 8co..8co+7
-  auto build_vt = [&](const uint8_t* raw, uint8_t* vtb) {
-    const int u = 64 * rid + lane;
-    const int eq = u & 7;
-    const int co = u >> 3;
-    uint32_t hv[4][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = 4 * eq + k;
-      const int slot = (co >> 2) ^ (e & 15);
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(
-          raw + kRawLat + 256 * e + 16 * slot + 4 * (co & 3));
-      const int blk = co >> 2;                       // transposed scale layout
-      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + 4 * (blk & 3) + (blk >> 2)]);
-      fp4x8_to_f16_pairs(w, sc, hv[k]);
-    }
-    uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
-      lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
-      *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
-      *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
-    }
-  };
-
   u32x4 stg[kNPre][CPW];
+  int rr[CPW];
 #pragma unroll
-  for (int b = 0; b < kNPre; ++b) load_tile(b, stg[b]);
+  for (int b = 0; b < kNPre; ++b) {
+    rows_of(b, rr);
+    load_tile(rr, stg[b]);
+  }
   // O^T accumulators: channels 64rid + 16c + 4g + i, head h0 + 16b + n
   f32x4 acc[4][NHB];
 #pragma unroll
@@ -426,18 +450,21 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     for (int b = 0; b < NHB; ++b) acc[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   // ---- pipeline prologue: raw(0) and V^T(0) in LDS; registers hold tiles 1 .. kNPre
   store_tile(stg[0], s_raw[0]);
-  load_tile(kNPre, stg[0]);
+  rows_of(kNPre, rr);
+  load_tile(rr, stg[0]);
+  rows_of(kNPre + 1, rr);                            // rows of the first loop load
   __syncthreads();                                   // prologue: raw(0) staged
-  build_vt(s_raw[0], s_vt[0]);                       // read by PV(0) after the first loop barrier
+  build_vt_unit(s_raw[0], s_vt[0], 64 * rid + lane); // read by PV(0) after the first barrier
 
-  for (int i0 = 0; i0 < ntiles; i0 += kNPre) {
+  for (int i0 = 0; i0 < ntiles2; i0 += kNPre) {
 #pragma unroll
-    for (int bb = 0; bb < kNPre; ++bb) {             // bb = i & 1: static buffer parity
+    for (int bb = 0; bb < kNPre; ++bb) {             // bb & 1 = i & 1: static buffer parity
       const int i = i0 + bb;
-      if (i < ntiles) {
+      {
         // stage raw(i+1) (loaded kNPre-1 tiles ago) and reuse its registers for i+1+kNPre
-        store_tile(stg[(bb + 1) % kNPre], s_raw[bb ^ 1]);
-        load_tile(i + 1 + kNPre, stg[(bb + 1) % kNPre]);
+        store_tile(stg[(bb + 1) % kNPre], s_raw[(bb & 1) ^ 1]);
+        load_tile(rr, stg[(bb + 1) % kNPre]);
+        rows_of(i + 2 + kNPre, rr);                  // for the next tile's loads
         __syncthreads();                 // P(i), rescale factors, raw(i+1), V^T(i) visible
         // ---- rescale (rare), then O^T += V^T P^T, V^T(i+1) alongside
         const uint32_t flag = s_flag[i % 3];
@@ -446,7 +473,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
 #pragma unroll
           for (int b = 0; b < NHB; ++b) {
             if ((flag >> b) & 1u) {
-              const float al = s_alpha[bb][b][n];
+              const float al = s_alpha[bb & 1][b][n];
 #pragma unroll
               for (int c = 0; c < 4; ++c) acc[c][b] *= al;
             }
@@ -454,8 +481,8 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
         }
         f16x8 pbs[NHB];
 #pragma unroll
-        for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[bb][b][lane]);
-        const uint8_t* vt = s_vt[bb] + (64 * rid + n) * kVtStride + 16 * g;
+        for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[bb & 1][b][lane]);
+        const uint8_t* vt = s_vt[bb & 1] + (64 * rid + n) * kVtStride + 16 * g;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
@@ -463,7 +490,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
           for (int b = 0; b < NHB; ++b)
             acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], acc[c][b], 0, 0, 0);
         }
-        build_vt(s_raw[bb ^ 1], s_vt[bb ^ 1]);
+        build_vt_unit(s_raw[(bb & 1) ^ 1], s_vt[(bb & 1) ^ 1], 64 * rid + lane);
       }
     }
   }
