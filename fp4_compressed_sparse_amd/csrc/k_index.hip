@@ -268,23 +268,6 @@ __device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_
   }
 }
 
-// Write the selected indices of one thread's keys (i0 + e) to their ordered positions.
-template <int KPT, class Ptr>
-__device__ __forceinline__ void topk_emit_regs(const uint32_t (&kv)[KPT], int i0, uint32_t tau,
-                                               uint32_t need_eq, uint32_t gtb, uint32_t eqb,
-                                               Ptr dst) {
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    if (kv[e] > tau) {
-      dst[gtb + min(eqb, need_eq)] = i0 + e;
-      ++gtb;
-    } else if (kv[e] == tau) {
-      if (eqb < need_eq) dst[gtb + eqb] = i0 + e;
-      ++eqb;
-    }
-  }
-}
-
 // Rows of at most 4096 * NR keys: thread t keeps keys [4NR t, 4NR (t+1)) in registers,
 // so the row is read from memory once and one block-wide scan orders the output.
 template <int NR>
@@ -368,13 +351,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   }
   const uint32_t tau = prefix, need_eq = remaining;
 
-  // ---- ordered compaction: position = (#greater before) + min(#equal before, need_eq)
-  uint32_t cg = 0u, ce = 0u;
+  // ---- ordered compaction: position = (#greater before) + min(#equal before, need_eq).
+  // Each thread marks its keys above and at tau in bit masks, so the emission walks only
+  // the selected keys (about K / n of them).
+  uint64_t gtm = 0u, eqm = 0u;
 #pragma unroll
   for (int e = 0; e < KPT; ++e) {
-    cg += (kv[e] > tau);
-    ce += (kv[e] == tau);
+    gtm |= (uint64_t)(kv[e] > tau) << e;
+    eqm |= (uint64_t)(kv[e] == tau) << e;
   }
+  const uint32_t cg = (uint32_t)__popcll(gtm), ce = (uint32_t)__popcll(eqm);
   uint32_t wg, we;
   const uint32_t pg = wave_prefix_small<7>(cg, wg);
   const uint32_t pe = wave_prefix_small<7>(ce, we);
@@ -382,17 +368,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   __syncthreads();
   uint32_t off = 0u;
   for (int w = 0; w < wave; ++w) off += s_wtot[w];
-  uint32_t gtb = (off & 0xffffu) + pg;
-  uint32_t eqb = (off >> 16) + pe;
+  const uint32_t gtb = (off & 0xffffu) + pg;         // keys above tau before this thread
+  const uint32_t eqb = (off >> 16) + pe;             // keys at tau before this thread
+  // the first need_eq keys at tau (in index order) are selected
+  uint32_t r = (need_eq > eqb) ? min(need_eq - eqb, ce) : 0u;
+  uint64_t sel = gtm;
+  while (r--) {
+    const uint64_t low = eqm & (0ull - eqm);
+    sel |= low;
+    eqm ^= low;
+  }
+  uint32_t pos = gtb + min(eqb, need_eq);
   // Stage the ordered output in the (now free) histogram space when it fits, so that the
   // row goes out in coalesced stores; else write it in place.
   if (K <= 2 * kHistBins) {
     int32_t* s_out = reinterpret_cast<int32_t*>(&hist[0][0]);
-    topk_emit_regs<KPT>(kv, i0, tau, need_eq, gtb, eqb, s_out);
+    while (sel) {
+      s_out[pos++] = i0 + (int)__builtin_ctzll(sel);
+      sel &= sel - 1;
+    }
     __syncthreads();
     for (int i = tid; i < K; i += kTopkThreads) out[i] = s_out[i];
   } else {
-    topk_emit_regs<KPT>(kv, i0, tau, need_eq, gtb, eqb, out);
+    while (sel) {
+      out[pos++] = i0 + (int)__builtin_ctzll(sel);
+      sel &= sel - 1;
+    }
   }
 }
 
