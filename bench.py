@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--kernel-pass-only", action="store_true",
                     help="skip the whole-step clock; run only the per-kernel pass (warm-up "
                          "steps included), so that a profiler's kernel averages match it")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra lines for the 1M-context decode and the chunked "
+                         "prefill workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -130,6 +133,65 @@ def algorithmic_bytes(w):
     win = w.swa_len().astype(np.int64)
     swa = n_layers * (int(win.sum()) * w.H_kv * 128 * 2 * 2 + w.T * w.H * (128 * 2 + 128 * 4 + 4))
     return {"idx_score": idx_score, "topk": topk, "sparse_attn": attn, "swa": swa}
+
+
+def algorithmic_flops(w):
+    """Matrix-math work per step: indexer 2 H_I 64 n_vis, attention 2 H sel (576 + 512),
+    SWA 2 H len 128 x 2 per row (the fp8 hi/lo query split is not counted)."""
+    import numpy as np
+    nv = w.n_vis().astype(np.int64)
+    sel = np.minimum(nv, w.K)
+    win = w.swa_len().astype(np.int64)
+    n_idx_layers = sum(1 for m in w.modes if m in (0, 1))
+    n_layers = len(w.modes)
+    return (n_idx_layers * 2 * w.H_I * 64 * int(nv.sum()) +
+            n_layers * 2 * w.H * 1088 * int(sel.sum()) +
+            n_layers * 2 * w.H * 256 * int(win.sum()))
+
+
+def measure_extra(workload, dev, steps, warmup, flush_mb):
+    """Whole-step time and per-kernel times of another named workload (smaller bench)."""
+    import torch
+    import synth
+    from fp4_compressed_sparse_amd import csa2
+    w = synth.workload(workload)
+    inp = Inputs(w, dev)
+    for _ in range(warmup):
+        inp.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        inp.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    scratch = (torch.ones(flush_mb << 18, dtype=torch.float32, device=dev)
+               if flush_mb > 0 else None)
+    csa2.timing_read()
+    csa2.timing_enable(True)
+    for _ in range(steps):
+        if scratch is not None:
+            scratch.sum()
+        inp.step()
+    torch.cuda.synchronize()
+    csa2.timing_enable(False)
+    kt = csa2.timing_read()
+    algo = algorithmic_bytes(w)
+    flops = algorithmic_flops(w)
+    step_bytes = sum(algo.values())
+    out = {"workload": w.name, "query_rows": w.T, "entries_per_seq": w.E, "top_k": w.K,
+           "steps": steps, "ms_per_step": round(ms, 4),
+           "query_tokens_per_s": round(w.T / (ms * 1e-3), 1),
+           "step_algo_bytes": step_bytes,
+           "step_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+           "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "step_algo_flops": flops,
+           "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "step_mfma_frac_bf16": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "kernels": {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)}
+                       for k, (n, t) in kt.items()}}
+    del inp
+    torch.cuda.empty_cache()
+    return out
 
 
 def kernel_source_sha(name):
@@ -298,6 +360,11 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if not args.no_extra and not args.kernel_pass_only:
+        result["extra"] = []
+        for wl, steps in ((4, 20), (5, 3)):
+            print(f"[bench] extra workload {wl}", file=sys.stderr, flush=True)
+            result["extra"].append(measure_extra(wl, dev, steps, 2, args.flush_mb))
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, w.T))

@@ -509,21 +509,25 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
 }
 
 // o = sum_s 2^(lse2_s - lse2) o_s, lse = ln 2 * lse2 with lse2 = log2 sum_s 2^lse2_s.
-// Thread: 4 channels of one head; workgroup: 2 heads of one row.  All splits' loads are
-// issued before any is used (up to kMergeUnroll splits per round).
-constexpr int kMergeUnroll = 8;
+// Workgroup: 2 heads of one row; the splits' log2-sum-exps go through LDS first, then each
+// thread (4 channels of one head) issues kMergeUnroll partial loads at a time.
+constexpr int kMergeUnroll = 16;
+constexpr int kMergeMaxSplits = 512;
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
+  __shared__ float s_lse[2][kMergeMaxSplits];
   const int hpb = 2;                                   // heads per workgroup
   const int lin = xcd_linear((int)blockIdx.x, (int)gridDim.x);
   const int per_row = p.H / hpb;
   const int t = lin / per_row;
-  const int h = (lin - t * per_row) * hpb + (threadIdx.x >> 7);
+  const int hh = threadIdx.x >> 7;
+  const int h = (lin - t * per_row) * hpb + hh;
   const int c = 4 * (threadIdx.x & 127);
   const int S = p.splits;
-  const float* lp = p.lse_part + (int64_t)t * S * p.H + h;
-  const float* op = p.o_part + ((int64_t)t * S * p.H + h) * kLat + c;
+  const float* lp = p.lse_part + (int64_t)t * S * p.H + (lin - t * per_row) * hpb;
+  for (int i = threadIdx.x; i < hpb * S; i += 256) s_lse[i % hpb][i / hpb] = lp[(int64_t)(i / hpb) * p.H + (i % hpb)];
+  __syncthreads();
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[(int64_t)s * p.H]);
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, s_lse[hh][s]);
   float* o = p.o + ((int64_t)t * p.H + h) * kLat + c;
   if (mx == -INFINITY) {
     *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -531,20 +535,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
     return;
   }
   float z = 0.f;
-  for (int s = 0; s < S; ++s) z += __builtin_amdgcn_exp2f(lp[(int64_t)s * p.H] - mx);
+  for (int s = 0; s < S; ++s) z += __builtin_amdgcn_exp2f(s_lse[hh][s] - mx);
   const float lse2 = mx + __log2f(z);
+  const float* op = p.o_part + ((int64_t)t * S * p.H + h) * kLat + c;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += kMergeUnroll) {
     f32x4 v[kMergeUnroll];
-    float wgt[kMergeUnroll];
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int s = min(s0 + u, S - 1);
       v[u] = *reinterpret_cast<const f32x4*>(op + (int64_t)s * p.H * kLat);
-      wgt[u] = (s0 + u < S) ? __builtin_amdgcn_exp2f(lp[(int64_t)s * p.H] - lse2) : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) acc += wgt[u] * v[u];
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float wgt = (s0 + u < S) ? __builtin_amdgcn_exp2f(s_lse[hh][min(s0 + u, S - 1)] - lse2) : 0.f;
+      acc += wgt * v[u];
+    }
   }
   *reinterpret_cast<f32x4*>(o) = acc;
   if (c == 0) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
