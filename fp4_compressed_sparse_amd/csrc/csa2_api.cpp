@@ -158,8 +158,16 @@ csa2_status check_paging(const char* fn, int32_t B, int32_t max_pages, int32_t n
   return CSA2_OK;
 }
 
+// Keys [T, E]; for the chunked Top-K also row histograms [T, kCkHistWords], per-chunk
+// counts [T, chunks, 2] and per-row digits [T, 8].
 size_t index_ws_bytes(int32_t T, int32_t max_pages) {
-  return round_up((size_t)T * (size_t)max_pages * CSA2_PAGE * sizeof(uint32_t));
+  const int64_t E = (int64_t)max_pages * CSA2_PAGE;
+  size_t b = round_up((size_t)T * (size_t)E * sizeof(uint32_t));
+  if (topk_chunked(T, E))
+    b += round_up((size_t)T * kCkHistWords * sizeof(uint32_t)) +
+         round_up((size_t)T * topk_chunks(E) * 2 * sizeof(uint32_t)) +
+         round_up((size_t)T * 8 * sizeof(uint32_t));
+  return b;
 }
 
 size_t attn_ws_bytes(int32_t T, int32_t H, int32_t K) {
@@ -220,6 +228,12 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   sp.seq_id = a->seq_id;
   sp.n_vis = a->n_vis;
   sp.keys = static_cast<uint32_t*>(ws);
+  // the chunked Top-K keeps row histograms right after the keys; scoring zeroes them
+  const bool chunked = topk_chunked(a->T, E);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) +
+                                             round_up((size_t)a->T * (size_t)E * sizeof(uint32_t)));
+  sp.clear = chunked ? ck : nullptr;
+  sp.clear_words = chunked ? a->T * kCkHistWords : 0;
   csa2_status st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
   if (st) return st;
   st = between();
@@ -231,7 +245,21 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   tp.keys = sp.keys;
   tp.n_vis = a->n_vis;
   tp.idx_out = a->idx_out;
-  return timed("topk", s, [&] { return launch_topk(tp, s); });
+  tp.ck_hist = tp.ck_counts = tp.ck_sel = nullptr;
+  if (!chunked) return timed("topk", s, [&] { return launch_topk(tp, s); });
+  tp.ck_hist = ck;
+  char* w = reinterpret_cast<char*>(ck);
+  w += round_up((size_t)a->T * kCkHistWords * sizeof(uint32_t));
+  tp.ck_counts = reinterpret_cast<uint32_t*>(w);
+  w += round_up((size_t)a->T * topk_chunks(E) * 2 * sizeof(uint32_t));
+  tp.ck_sel = reinterpret_cast<uint32_t*>(w);
+  static const char* const names[6] = {"", "topk_ck_hist0", "topk_ck_hist1",
+                                       "topk_ck_hist2", "topk_ck_count", "topk_ck_emit"};
+  for (int pass = 1; pass < 6; ++pass) {
+    st = timed(names[pass], s, [&] { return launch_topk_chunked(tp, pass, s); });
+    if (st) return st;
+  }
+  return CSA2_OK;
 }
 
 csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {

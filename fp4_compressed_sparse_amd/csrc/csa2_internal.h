@@ -35,6 +35,8 @@ struct IdxScoreParams {
   const int32_t* seq_id;
   const int32_t* n_vis;
   uint32_t* keys;                      // [T, key_stride] order-preserving keys
+  uint32_t* clear;                     // optional: words zeroed by the first blocks
+  int clear_words;
 };
 
 struct TopkParams {
@@ -43,7 +45,22 @@ struct TopkParams {
   const uint32_t* keys;
   const int32_t* n_vis;
   int32_t* idx_out;                    // [T, K]
+  // chunked path (few long rows): workspace for per-row histograms, per-chunk counts and
+  // the digits found so far; null otherwise
+  uint32_t* ck_hist;                   // [T, kCkHistWords]
+  uint32_t* ck_counts;                 // [T, n_chunks, 2]
+  uint32_t* ck_sel;                    // [T, 8]
 };
+
+// Top-K over few long rows runs chunked: rows longer than 65536 keys with at most
+// kCkMaxRows rows are split into 4096-key chunks, one workgroup each.
+constexpr int kCkKeys = 4096;
+constexpr int kCkHistWords = 4096 + 4096 + 256;
+constexpr int kCkMaxRows = 64;
+inline bool topk_chunked(int T, int64_t key_stride) {
+  return key_stride > 65536 && T <= kCkMaxRows;
+}
+inline int64_t topk_chunks(int64_t key_stride) { return (key_stride + kCkKeys - 1) / kCkKeys; }
 
 struct AttnParams {
   int T, H, K, max_pages, splits, per_split;   // per_split: idx slots per split
@@ -104,6 +121,7 @@ inline int attn_head_groups(int H) { return H > 64 ? H / 64 : 1; }
 // Each launcher enqueues one kernel on `s` and returns hipGetLastError().
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_topk_chunked(const TopkParams& p, int pass, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_swa(const SwaParams& p, hipStream_t s);

@@ -77,6 +77,9 @@ __device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa
 // lane, broadcast by shuffle) and keeps the next page's 8 KB of keys in flight while it
 // scores the current one.
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
+  // zero a workspace area for the Top-K that follows
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
+    p.clear[i] = 0u;
   const int t = blockIdx.x / p.chunks;
   const int c = blockIdx.x - t * p.chunks;
   const int nv = p.n_vis[t];
@@ -456,9 +459,224 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
   }
 }
 
+// ---------------------------------------------------------------- chunked Top-K
+// Few long rows: every pass runs on 4096-key chunks, one workgroup of 256 threads each
+// (16 keys per thread), so a row's work spreads over many CUs.  Passes (one launch each),
+// after the scoring launch has zeroed the row histograms: histogram of bits 31..20 (chunk histograms in LDS, non-zero bins
+// added to the row's histogram in memory); bits 19..8 of the keys under the chosen top
+// digit; bits 7..0 under the chosen 24-bit prefix; per-chunk counts above and at tau;
+// ordered emission, each chunk at the offset its predecessors' counts give.  Every pass
+// re-reads its chunk (4 B per key, L2-resident at these sizes).
+constexpr int kCkThreads = 256;
+constexpr int kCkPerThread = kCkKeys / kCkThreads;   // 16
+
+__device__ __forceinline__ void ck_load(const TopkParams& p, int t, int ch, int n,
+                                        uint32_t (&kv)[kCkPerThread]) {
+  const int i0 = ch * kCkKeys + kCkPerThread * (int)threadIdx.x;
+  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
+  if (i0 + kCkPerThread <= n) {
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(keys + i0);
+#pragma unroll
+    for (int r = 0; r < kCkPerThread / 4; ++r) {
+      const u32x4 v = k4[r];
+      kv[4 * r] = v[0]; kv[4 * r + 1] = v[1]; kv[4 * r + 2] = v[2]; kv[4 * r + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kCkPerThread; ++e) kv[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
+  }
+}
+
+// Digit holding the remaining-th key of a row histogram in memory (bins beyond `nbins`
+// read as zero); all threads get the digit and the rank left inside it.
+__device__ __forceinline__ void ck_find(const uint32_t* ghist, int nbins, uint32_t remaining,
+                                        uint32_t* s_hist, uint32_t* s_digit, uint32_t* s_rem,
+                                        uint32_t& digit, uint32_t& rem) {
+  for (int i = threadIdx.x; i < kHistBins; i += kCkThreads) s_hist[i] = (i < nbins) ? ghist[i] : 0u;
+  __syncthreads();
+  if (threadIdx.x < 64) topk_find_digit_w0(s_hist, remaining, s_digit, s_rem);
+  __syncthreads();
+  digit = *s_digit;
+  rem = *s_rem;
+  __syncthreads();                                   // s_hist is reused by the caller
+}
+
+// PASS 0, 1, 2: histogram of bits 31..20, 19..8, 7..0 among the keys under the prefix
+template <int PASS>
+__global__ __launch_bounds__(kCkThreads) void topk_ck_pass_kernel(TopkParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_digit, s_rem;
+  const int nch = (int)((p.key_stride + kCkKeys - 1) / kCkKeys);
+  const int t = blockIdx.x / nch, ch = blockIdx.x - t * nch;
+  const int n = p.n_vis[t];
+  if (n <= p.K || ch * kCkKeys >= n) return;         // uniform per workgroup
+  uint32_t* hrow = p.ck_hist + (int64_t)t * kCkHistWords;
+  uint32_t* sel = p.ck_sel + (int64_t)t * 8;
+  uint32_t kv[kCkPerThread];
+  ck_load(p, t, ch, n, kv);                          // in flight while the digit is found
+  uint32_t prefix = 0u, pmask = 0u;
+  if (PASS == 1) {                                   // top digit from the row histogram
+    uint32_t d0, r0;
+    ck_find(hrow, 4096, (uint32_t)p.K, s_hist, &s_digit, &s_rem, d0, r0);
+    prefix = d0 << 20;
+    pmask = 0xfff00000u;
+    if (ch == 0 && threadIdx.x == 0) { sel[0] = d0; sel[1] = r0; }
+  } else if (PASS == 2) {                            // top digit as the last launch found it
+    uint32_t d1, r1;
+    ck_find(hrow + 4096, 4096, sel[1], s_hist, &s_digit, &s_rem, d1, r1);
+    prefix = (sel[0] << 20) | (d1 << 8);
+    pmask = 0xffffff00u;
+    if (ch == 0 && threadIdx.x == 0) { sel[2] = d1; sel[3] = r1; }
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += kCkThreads) s_hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kCkPerThread; ++e) {
+    if (kv[e] != 0u && (kv[e] & pmask) == prefix) {
+      const uint32_t d = PASS == 0 ? (kv[e] >> 20) : (PASS == 1 ? ((kv[e] >> 8) & 0xfffu) : (kv[e] & 0xffu));
+      atomicAdd(&s_hist[d], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* g = hrow + (PASS == 0 ? 0 : (PASS == 1 ? 4096 : 8192));
+  const int nbins = PASS == 2 ? 256 : 4096;
+  for (int i = threadIdx.x; i < nbins; i += kCkThreads) {
+    const uint32_t c = s_hist[i];
+    if (c) atomicAdd(&g[i], c);
+  }
+}
+
+// counts above and at tau per chunk; tau and need_eq per row
+__global__ __launch_bounds__(kCkThreads) void topk_ck_count_kernel(TopkParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_digit, s_rem;
+  __shared__ uint32_t s_w[kCkThreads / 64];
+  const int nch = (int)((p.key_stride + kCkKeys - 1) / kCkKeys);
+  const int t = blockIdx.x / nch, ch = blockIdx.x - t * nch;
+  const int n = p.n_vis[t];
+  if (n <= p.K) return;
+  uint32_t* sel = p.ck_sel + (int64_t)t * 8;
+  uint32_t kv[kCkPerThread];
+  ck_load(p, t, ch, n, kv);
+  uint32_t d2, r2;
+  ck_find(p.ck_hist + (int64_t)t * kCkHistWords + 8192, 256, sel[3], s_hist, &s_digit, &s_rem, d2, r2);
+  const uint32_t tau = (sel[0] << 20) | (sel[2] << 8) | d2;
+  if (ch == 0 && threadIdx.x == 0) { sel[4] = tau; sel[5] = r2; }
+  uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+  for (int e = 0; e < kCkPerThread; ++e) {
+    cg += kv[e] > tau;
+    ce += kv[e] == tau;
+  }
+  const uint32_t packed = wave_sum_u32(cg | (ce << 16));
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = packed;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int w = 0; w < kCkThreads / 64; ++w) tot += s_w[w];
+    uint32_t* c = p.ck_counts + ((int64_t)t * nch + ch) * 2;
+    c[0] = tot & 0xffffu;
+    c[1] = tot >> 16;
+  }
+}
+
+// ordered emission: chunk ch writes its selected indices after those of chunks < ch
+__global__ __launch_bounds__(kCkThreads) void topk_ck_emit_kernel(TopkParams p) {
+  __shared__ int32_t s_out[kCkKeys];
+  __shared__ uint32_t s_w[kCkThreads / 64];
+  __shared__ uint32_t s_base[2];
+  const int nch = (int)((p.key_stride + kCkKeys - 1) / kCkKeys);
+  const int t = blockIdx.x / nch, ch = blockIdx.x - t * nch;
+  const int n = p.n_vis[t];
+  const int K = p.K;
+  int32_t* out = p.idx_out + (int64_t)t * K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n <= K) {                                      // every visible entry is selected
+    for (int i = ch * kCkKeys + tid; i < min((ch + 1) * kCkKeys, K); i += kCkThreads)
+      out[i] = (i < n) ? i : -1;
+    return;
+  }
+  const uint32_t* sel = p.ck_sel + (int64_t)t * 8;
+  const uint32_t tau = sel[4], need_eq = sel[5];
+  // keys above / at tau in the chunks before this one
+  if (wave == 0) {
+    uint32_t gt = 0u, eq = 0u;
+    for (int c = lane; c < ch; c += 64) {
+      gt += p.ck_counts[((int64_t)t * nch + c) * 2];
+      eq += p.ck_counts[((int64_t)t * nch + c) * 2 + 1];
+    }
+    gt = wave_sum_u32(gt);
+    eq = wave_sum_u32(eq);
+    if (lane == 0) { s_base[0] = gt; s_base[1] = eq; }
+  }
+  uint32_t kv[kCkPerThread];
+  ck_load(p, t, ch, n, kv);
+  uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+  for (int e = 0; e < kCkPerThread; ++e) {
+    gtm |= (uint32_t)(kv[e] > tau) << e;
+    eqm |= (uint32_t)(kv[e] == tau) << e;
+  }
+  const uint32_t cg = (uint32_t)__popc(gtm), ce = (uint32_t)__popc(eqm);
+  uint32_t wg, we;
+  const uint32_t pg = wave_prefix_small<5>(cg, wg);
+  const uint32_t pe = wave_prefix_small<5>(ce, we);
+  if (lane == 0) s_w[wave] = wg | (we << 16);
+  __syncthreads();
+  uint32_t off = 0u;
+  for (int w = 0; w < wave; ++w) off += s_w[w];
+  uint32_t chunk_sel = 0u;                           // selected in this chunk
+  const uint32_t gt0 = s_base[0], eq0 = s_base[1];
+  {
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int w = 0; w < kCkThreads / 64; ++w) tot += s_w[w];
+    const uint32_t tg = tot & 0xffffu, te = tot >> 16;
+    const uint32_t eq_sel = (need_eq > eq0) ? min(need_eq - eq0, te) : 0u;
+    chunk_sel = tg + eq_sel;
+  }
+  const uint32_t gtb = (off & 0xffffu) + pg;         // within the chunk
+  const uint32_t eqb = eq0 + (off >> 16) + pe;       // global rank of this thread's first tie
+  uint32_t r = (need_eq > eqb) ? min(need_eq - eqb, ce) : 0u;
+  uint32_t selm = gtm;
+  while (r--) {
+    const uint32_t low = eqm & (0u - eqm);
+    selm |= low;
+    eqm ^= low;
+  }
+  const uint32_t eq_before = (need_eq > eq0) ? min(eqb - eq0, need_eq - eq0) : 0u;
+  uint32_t pos = gtb + eq_before;                    // position within the chunk's output
+  const int i0 = ch * kCkKeys + kCkPerThread * tid;
+  while (selm) {
+    s_out[pos++] = i0 + (int)__builtin_ctz(selm);
+    selm &= selm - 1;
+  }
+  __syncthreads();
+  const uint32_t base = gt0 + min(eq0, need_eq);     // selected before this chunk
+  for (uint32_t i = tid; i < chunk_sel && base + i < (uint32_t)K; i += kCkThreads)
+    out[base + i] = s_out[i];
+}
+
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.T * p.chunks;
   CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  return hipGetLastError();
+}
+
+// One pass of the chunked Top-K (1..3: digit passes, 4: counts, 5: emit); the row
+// histograms must be zero before pass 1.
+hipError_t launch_topk_chunked(const TopkParams& p, int pass, hipStream_t s) {
+  const unsigned blocks = (unsigned)((int64_t)p.T * topk_chunks(p.key_stride));
+  const dim3 block(kCkThreads);
+  switch (pass) {
+    case 1: CSA2_LAUNCH(topk_ck_pass_kernel<0>, dim3(blocks), block, s, p); break;
+    case 2: CSA2_LAUNCH(topk_ck_pass_kernel<1>, dim3(blocks), block, s, p); break;
+    case 3: CSA2_LAUNCH(topk_ck_pass_kernel<2>, dim3(blocks), block, s, p); break;
+    case 4: CSA2_LAUNCH(topk_ck_count_kernel, dim3(blocks), block, s, p); break;
+    case 5: CSA2_LAUNCH(topk_ck_emit_kernel, dim3(blocks), block, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -470,7 +688,8 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   else if (nr <= 4) CSA2_LAUNCH(topk_reg_kernel<4>, grid, block, s, p);
   else if (nr <= 8) CSA2_LAUNCH(topk_reg_kernel<8>, grid, block, s, p);
   else if (nr <= 16) CSA2_LAUNCH(topk_reg_kernel<16>, grid, block, s, p);
-  else CSA2_LAUNCH(topk_stream_kernel, grid, block, s, p);
+  else if (!topk_chunked(p.T, p.key_stride)) CSA2_LAUNCH(topk_stream_kernel, grid, block, s, p);
+  else return hipErrorInvalidValue;                  // chunked rows go through launch_topk_chunked
   return hipGetLastError();
 }
 

@@ -163,6 +163,42 @@ def test_topk_all_equal_scores(csa2, dev):
     np.testing.assert_array_equal(idx[1], np.arange(K))
 
 
+# Rows longer than 65536 keys, few of them: the chunked Top-K (4096-key chunks, one
+# workgroup each), with a ragged last chunk, chunks past a short row's end and a row that
+# selects everything.
+CHUNKED = {
+    "chunked_t3_70016_k2048": W(B=3, T=3, E=70016, H=16, H_I=4, K=2048, H_kv=16,
+                                n_vis_rows=[70016, 66001, 1500], seq_id_rows=[0, 1, 2]),
+    "chunked_t2_70016_k6000": W(B=2, T=2, E=70016, H=16, H_I=3, K=6000, H_kv=16,
+                                n_vis_rows=[69999, 40000], seq_id_rows=[1, 0], hot="runs",
+                                n_hot=600, hot_runs=6),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNKED))
+def test_topk_chunked_parity(csa2, dev, name):
+    _index_parity(csa2, dev, CHUNKED[name], name)
+
+
+def test_topk_chunked_all_equal_scores(csa2, dev):
+    """Equal scores over many chunks: the lowest K indices win, in order, also when the
+    selection spans several chunks."""
+    _say("topk_chunked_all_equal_scores")
+    E, K = 70016, 9000
+    key = torch.from_numpy(synth.normal_bf16(9, 1, 0, 64).view(np.int16)).to(dev)
+    k_idx = key.view(1, 1, 64).expand(E // 64, 64, 64).contiguous().view(torch.bfloat16)
+    q = torch.from_numpy(synth.normal_bf16(9, 2, 0, 3 * 64).view(np.int16)).to(dev).view(
+        torch.bfloat16).view(3, 1, 64)
+    wv = torch.ones((3, 1), dtype=torch.float32, device=dev)
+    pt = torch.arange(E // 64, dtype=torch.int32, device=dev).view(1, -1)
+    sid = torch.zeros(3, dtype=torch.int32, device=dev)
+    nv = torch.tensor([E, 1000, K + 3], dtype=torch.int32, device=dev)
+    idx = csa2.index_topk(q, wv, k_idx, pt, sid, nv, K).cpu().numpy()
+    np.testing.assert_array_equal(idx[0], np.arange(K))
+    np.testing.assert_array_equal(idx[1], np.r_[np.arange(1000), -np.ones(K - 1000, np.int32)])
+    np.testing.assert_array_equal(idx[2], np.arange(K))
+
+
 def test_empty_rows_and_windows(csa2, dev):
     _say("empty_rows_and_windows")
     w = W(B=2, T=3, E=512, K=64, H=16, H_I=2, H_kv=16, seq_id_rows=[0, 1, 0],
