@@ -13,9 +13,11 @@
 // work hides behind the others' matrix work.  The query operands of a score wave and the
 // accumulators of a value wave occupy the same registers.
 //   gather  : the split's physical rows are resolved once into LDS.  Each 32-entry tile
-//             (8 KB codes, 4 KB rope, 0.5 KB scales) is fetched with coalesced 16-byte loads
-//             into registers two tiles ahead, then written to LDS with an XOR swizzle of
-//             the 16-byte slots so the operand reads below are bank-conflict free.
+//             (8 KB codes, 4 KB rope, 0.5 KB scales) goes straight from memory into a ring
+//             of four LDS tiles by LDS DMA (16 bytes per lane, three tiles ahead), the lanes
+//             fetching in an XOR-swizzled order of 16-byte slots so that the operand reads
+//             below are bank-conflict free; no registers or LDS store instructions are spent
+//             on staging.
 //   QK^T    : score wave hb computes S^T[32 entries x 16 heads 16hb..] over all 576
 //             channels.  The latent part runs on the MXFP4 matrix path (v_mfma_scale
 //             16x16x128: A = the cached E2M1 codes with their own E8M0 block scales,
@@ -42,13 +44,14 @@ namespace csa2 {
 
 constexpr int kTE = 32;              // entries per tile
 constexpr int kMaxPerSplit = 2048;   // idx slots per split (LDS row table size)
-constexpr int kNPre = 2;             // tiles in flight in registers (= unroll, so that the
-                                     // staging slot and the tile parity, which picks every
-                                     // LDS buffer, are static)
+constexpr int kNPre = 2;             // loop unroll: the tile parity picks the P and V^T
+                                     // buffers statically
+constexpr int kRing = 4;             // raw tiles in LDS: one read, one ready, two in flight
 constexpr float kRaise = 12.f;       // log2 headroom before the running maximum is raised
 // raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16]
 constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 12800;
 constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rope, 1 scales
+constexpr int kRawSlot = kRawBytes + 1024;   // a raw tile and the 1 KB its dead loads fill
 constexpr int kVtStride = 80;        // LDS bytes per V^T channel row (32 fp16 + 16 pad)
 
 void attn_plan(int T, int H, int K, int* splits, int* per_split) {
@@ -68,11 +71,18 @@ void attn_plan(int T, int H, int K, int* splits, int* per_split) {
 // An all-zero row stands in for empty index slots (so staged tiles never hold garbage).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[256];
 
-// LDS swizzles of a staged tile.  Codes: entry e's 16-byte slot c sits at slot
-// c ^ (e & 15) ^ (e >> 4); scales: entry e's (transposed) dword d sits at d ^ 2 (e >> 4).
-// Readers that take entries e and e + 16 in one access then hit different banks.
+// LDS swizzle of a staged tile's codes: entry e's 16-byte slot c sits at slot
+// c ^ (e & 15) ^ (e >> 4), so readers that take entries e and e + 16 in one access hit
+// different banks.  (The map is its own inverse.)
 __device__ __forceinline__ int lat_slot(int c, int e) { return c ^ (e & 15) ^ (e >> 4); }
-__device__ __forceinline__ int scl_dword(int d, int e) { return d ^ ((e >> 4) << 1); }
+
+// Barrier for the tile loop: this wave's LDS accesses are complete, no wait on vector
+// memory (the raw tiles arrive by LDS DMA, whose completion the loading waves await
+// explicitly).  The memory clobber keeps the compiler from moving LDS accesses across it;
+// `raw` is passed so that the DMA-filled buffer counts as written by it.
+__device__ __forceinline__ void tile_barrier(const void* raw) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : "v"(raw) : "memory");
+}
 
 // Position of entry e of a tile in a V^T row: the P^T operand of lane group g carries
 // entries 4g..4g+3 then 16+4g..16+4g+3, so contraction slots 8g..8g+7 map to those.
@@ -96,8 +106,8 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   constexpr int CPW = (kChunks + NV - 1) / NV;       // load units per value wave and tile
   static_assert((kTE / 4) * (kLat / 8) == 64 * NV, "one V^T unit per value thread");
 
-  // raw tiles, each followed by 1 KB that dead staging lanes write to
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBytes + 1024];
+  // ring of raw tiles, each followed by 1 KB that dead loads write to
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRing][kRawSlot];
   __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLat * kVtStride];
   __shared__ __attribute__((aligned(16))) u32x4 s_p[2][NHB][64];     // P^T operands
   __shared__ float s_alpha[2][NHB][16];              // rescale factors of a raise
@@ -177,8 +187,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
       const int e = 4 * eq + k;
       const uint32_t w = *reinterpret_cast<const uint32_t*>(
           raw + kRawLat + 256 * e + 16 * lat_slot(co >> 2, e) + 4 * (co & 3));
-      const int blk = co >> 2;                       // transposed, swizzled scale layout
-      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + 4 * scl_dword(blk & 3, e) + (blk >> 2)]);
+      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);   // block co / 4
       fp4x8_to_f16_pairs(w, sc, hv[k]);
     }
     uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     // running state per head n; a finite initial maximum keeps fully masked tiles at
     // 2^(-inf) = 0 instead of -inf - (-inf)
     float m_run = -1.0e30f, l_run = 0.f;
-    __syncthreads();                                 // prologue: raw(0) staged
+    tile_barrier(s_raw);                             // prologue: raw(0) staged
 
     for (int i0 = 0; i0 < ntiles2; i0 += kNPre) {
 #pragma unroll
@@ -271,27 +280,28 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
         {
           if (active) {
             // ---- S^T[entries 16mb + 4g + k][head n]: four independent chains
-            const uint8_t* raw = s_raw[bb & 1];
+            const uint8_t* raw = s_raw[i & (kRing - 1)];
             f32x4 ah[2], al[2];
-            int ksc[2];                                // blocks g, 4+g, 8+g, 12+g of entry e
+            u32x4 ksc[2];                              // the 16 block scales of entry e
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
               ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
               al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-              ksc[mb] = *reinterpret_cast<const int*>(raw + kRawScl + 16 * (16 * mb + n) +
-                                                      4 * scl_dword(g, 16 * mb + n));
+              ksc[mb] = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * (16 * mb + n));
             }
-            // op_sel = kk picks byte kk of both scale dwords (scale of block 4kk + g)
+            // A scale: block 4kk + g = byte g of dword kk, shifted down (op_sel 0); B scale:
+            // op_sel = kk picks byte kk of qscp
 #define CSA2_QK_CHUNK(kk)                                                                     \
   _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                        \
     const int e = 16 * mb + n;                                                              \
     const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
         raw + kRawLat + 256 * e + 16 * lat_slot(4 * (kk) + g, e));                          \
     const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};          \
-    ah[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[kk], ah[mb], 4, 0, kk, \
-                                                               ksc[mb], kk, qscp);          \
-    al[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[kk], al[mb], 4, 0, kk, \
-                                                               ksc[mb], kk, qscp);          \
+    const int asc = (int)(ksc[mb][kk] >> (8 * g));                                          \
+    ah[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[kk], ah[mb], 4, 0, 0,  \
+                                                               asc, kk, qscp);              \
+    al[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[kk], al[mb], 4, 0, 0,  \
+                                                               asc, kk, qscp);              \
   }
             CSA2_QK_CHUNK(0)
             CSA2_QK_CHUNK(1)
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
             s_p[bb & 1][hb][lane] = __builtin_bit_cast(u32x4, pb);
           }
 
-          __syncthreads();               // P(i), rescale factors, raw(i+1), V^T(i) visible
+          tile_barrier(s_raw);           // P(i), rescale factors, raw(i+1), V^T(i) visible
         }
       }
     }
@@ -374,126 +384,106 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
 
   // ========================================================== value waves
   const int rid = wave - 4;                          // 0..7: channels 64rid .. 64rid+63
-  // ---- gather: load unit j of a tile = 1 KB, lane l moves 16 bytes
-  //   j < 8      : codes of entries 4j + l/16, slot l%16 (16 B)
-  //   8 <= j < 12: rope of entries 8(j-8) + l/8, slot l%8
-  //   j == 12    : scales of entry l (lanes < 32)
-  // Value wave v owns units j = v + 8c.  Everything about a unit that does not depend on
-  // the tile is worked out once, so that staging is straight-line code: every lane issues
-  // one 16-byte load and one 16-byte LDS store per unit and tile (dead lanes load the zero
-  // row and store to a scratch area of LDS), and the compiler counts the loads in flight
-  // exactly.  Row indices are read from LDS one tile ahead of their loads.
+  // ---- gather by LDS DMA: load unit j of a tile = 1 KB, one 16-byte global load per lane
+  // whose data the hardware writes to LDS at (unit base + 16 lane), so the swizzle is applied
+  // by choosing what each lane fetches:
+  //   j < 8      : codes of entries 4j + l/16; LDS slot l%16 holds chunk lat_slot(l%16, e)
+  //   8 <= j < 12: rope of entries 8(j-8) + l/8; slot l%8 holds chunk (l%8) ^ (e%8)
+  //   j == 12    : the 16 scale bytes of entry l (lanes >= 32 fill the tile's tail)
+  // Value wave v owns units j = v + 8c; the units past 12 load the zero row into the tail,
+  // so that every value wave issues the same number of loads per tile and can wait for a
+  // tile with one counter value.  Row indices are read from LDS one tile ahead.
   const uint8_t* u_base[CPW];
-  int u_stride[CPW], u_goff[CPW], u_lds[CPW], u_entry[CPW];
-  bool u_live[CPW], u_scl[CPW];
+  int u_stride[CPW], u_goff[CPW], u_dst[CPW], u_entry[CPW];
+  bool u_live[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int j = rid + NV * c;
     const bool codes = j < 8, rope = !codes && j < 12, scl = j == 12;
     const int e = codes ? 4 * j + (lane >> 4) : (rope ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
     u_entry[c] = e;
-    u_scl[c] = scl;
     u_live[c] = codes || rope || (scl && lane < 32);
     u_base[c] = codes ? p.kv_lat : (rope ? reinterpret_cast<const uint8_t*>(p.kv_rope) : p.kv_scl);
     u_stride[c] = codes ? kLatBytes : (rope ? 2 * kRope : kScl);
-    u_goff[c] = codes ? 16 * (lane & 15) : (rope ? 16 * (lane & 7) : 0);
-    u_lds[c] = !u_live[c] ? kRawBytes + 16 * lane      // dead: the scratch area below
-             : codes ? kRawLat + 256 * e + 16 * lat_slot(lane & 15, e)
-             : rope ? kRawRope + 128 * e + 16 * ((lane & 7) ^ (e & 7))
-                    : kRawScl + 16 * lane;
+    u_goff[c] = codes ? 16 * lat_slot(lane & 15, e) : (rope ? 16 * ((lane & 7) ^ (e & 7)) : 0);
+    u_dst[c] = __builtin_amdgcn_readfirstlane(codes ? kRawLat + 1024 * j
+                                              : rope ? kRawRope + 1024 * (j - 8)
+                                              : scl ? kRawScl : kRawBytes);
   }
   auto rows_of = [&](int tile, int (&rr)[CPW]) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
       rr[c] = (tile < ntiles && u_live[c]) ? s_rows[tile * kTE + u_entry[c]] : -1;
   };
-  auto load_tile = [&](const int (&rr)[CPW], u32x4 (&r)[CPW]) {
+  auto dma_tile = [&](const int (&rr)[CPW], int slot) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const uint8_t* src = u_base[c] + (int64_t)rr[c] * u_stride[c] + u_goff[c];
-      r[c] = ld_global_16_addr(rr[c] >= 0 ? reinterpret_cast<uint64_t>(src)
-                                          : reinterpret_cast<uint64_t>(g_zero_row));
+      const uint8_t* src = rr[c] >= 0 ? u_base[c] + (int64_t)rr[c] * u_stride[c] + u_goff[c]
+                                      : g_zero_row;
+      __builtin_amdgcn_global_load_lds(src, &s_raw[slot][0] + u_dst[c], 16, 0, 0);
     }
   };
-  auto store_tile = [&](const u32x4 (&r)[CPW], uint8_t* raw) {
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      // entry `lane`'s 16 block scales are stored transposed: dword d holds blocks d, 4+d,
-      // 8+d, 12+d, at position scl_dword(d, e), so lane group g of the score MFMA reads one
-      // dword and picks chunk kk's byte with op_sel
-      const u32x4 v = r[c];
-      u32x4 sw;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int dd = scl_dword(d, lane & 31);        // position of dword d
-        const uint32_t sel = (uint32_t)d | ((uint32_t)(4 + d) << 8);
-        const uint32_t t01 = __builtin_amdgcn_perm(v[1], v[0], sel);   // blocks d, 4+d
-        const uint32_t t23 = __builtin_amdgcn_perm(v[3], v[2], sel);   // 8+d, 12+d
-        const uint32_t tr = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-        sw[dd] = tr;
-      }
-      *reinterpret_cast<u32x4*>(raw + u_lds[c]) = u_scl[c] ? sw : v;
-    }
-  };
-  u32x4 stg[kNPre][CPW];
+  // loads issued after those of the tile awaited: two tiles of CPW loads
+  auto wait_ready = [] { __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * CPW)); };
   int rr[CPW];
 #pragma unroll
-  for (int b = 0; b < kNPre; ++b) {
+  for (int b = 0; b < kRing - 1; ++b) {
     rows_of(b, rr);
-    load_tile(rr, stg[b]);
+    dma_tile(rr, b);
   }
+  rows_of(kRing - 1, rr);                            // rows of the first loop load
   // O^T accumulators: channels 64rid + 16c + 4g + i, head h0 + 16b + n
   f32x4 acc[4][NHB];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int b = 0; b < NHB; ++b) acc[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // ---- pipeline prologue: raw(0) and V^T(0) in LDS; registers hold tiles 1 .. kNPre
-  store_tile(stg[0], s_raw[0]);
-  rows_of(kNPre, rr);
-  load_tile(rr, stg[0]);
-  rows_of(kNPre + 1, rr);                            // rows of the first loop load
-  __syncthreads();                                   // prologue: raw(0) staged
-  build_vt_unit(s_raw[0], s_vt[0], 64 * rid + lane); // read by PV(0) after the first barrier
+  wait_ready();                                      // raw(0) in LDS
+  tile_barrier(s_raw);                               // prologue: raw(0) staged
 
+  // rescale (rare), then O^T += V^T P^T for tile `pt` (parity `par`)
+  auto pv_tile = [&](int pt, int par) {
+    const uint32_t flag = s_flag[pt % 3];
+    if (flag) {
+#pragma unroll
+      for (int b = 0; b < NHB; ++b) {
+        if ((flag >> b) & 1u) {
+          const float al = s_alpha[par][b][n];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c][b] *= al;
+        }
+      }
+    }
+    f16x8 pbs[NHB];
+#pragma unroll
+    for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[par][b][lane]);
+    const uint8_t* vt = s_vt[par] + (64 * rid + n) * kVtStride + 16 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
+#pragma unroll
+      for (int b = 0; b < NHB; ++b)
+        acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], acc[c][b], 0, 0, 0);
+    }
+  };
+
+  // Between barriers i-1 and i: PV(i-1), V^T(i) from raw(i), the loads of raw(i+3) into the
+  // slot raw(i-1) left, and the wait for raw(i+1).
   for (int i0 = 0; i0 < ntiles2; i0 += kNPre) {
 #pragma unroll
     for (int bb = 0; bb < kNPre; ++bb) {             // bb & 1 = i & 1: static buffer parity
       const int i = i0 + bb;
-      {
-        // stage raw(i+1) (loaded kNPre-1 tiles ago) and reuse its registers for i+1+kNPre
-        store_tile(stg[(bb + 1) % kNPre], s_raw[(bb & 1) ^ 1]);
-        load_tile(rr, stg[(bb + 1) % kNPre]);
-        rows_of(i + 2 + kNPre, rr);                  // for the next tile's loads
-        __syncthreads();                 // P(i), rescale factors, raw(i+1), V^T(i) visible
-        // ---- rescale (rare), then O^T += V^T P^T, V^T(i+1) alongside
-        const uint32_t flag = s_flag[i % 3];
-        if (tid == 256) s_flag[(i + 2) % 3] = 0u;    // tile i-1's requests, all read by now
-        if (flag) {
-#pragma unroll
-          for (int b = 0; b < NHB; ++b) {
-            if ((flag >> b) & 1u) {
-              const float al = s_alpha[bb & 1][b][n];
-#pragma unroll
-              for (int c = 0; c < 4; ++c) acc[c][b] *= al;
-            }
-          }
-        }
-        f16x8 pbs[NHB];
-#pragma unroll
-        for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[bb & 1][b][lane]);
-        const uint8_t* vt = s_vt[bb & 1] + (64 * rid + n) * kVtStride + 16 * g;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
-#pragma unroll
-          for (int b = 0; b < NHB; ++b)
-            acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], acc[c][b], 0, 0, 0);
-        }
-        build_vt_unit(s_raw[(bb & 1) ^ 1], s_vt[(bb & 1) ^ 1], 64 * rid + lane);
-      }
+      if (tid == 256) s_flag[(i + 1) % 3] = 0u;      // tile i-2's requests, all read by now
+      if (i > 0) pv_tile(i - 1, bb ^ 1);
+      build_vt_unit(s_raw[i & (kRing - 1)], s_vt[bb], 64 * rid + lane);
+      dma_tile(rr, (i + kRing - 1) & (kRing - 1));
+      rows_of(i + kRing, rr);                        // for the next tile's loads
+      wait_ready();                                  // raw(i+1) in LDS
+      tile_barrier(s_raw);               // P(i), rescale factors, raw(i+1), V^T(i) visible
     }
   }
+  pv_tile(ntiles2 - 1, (ntiles2 - 1) & 1);
+  wait_vmem_all();                                   // no LDS DMA may outlive the workgroup
   __syncthreads();                                   // denominators published
   // ---- epilogue: normalize and write
 #pragma unroll
