@@ -145,7 +145,7 @@ def index_topk(q_idx, w_idx, k_idx, page_table, seq_id, n_vis, K, idx_out=None, 
     need = lib.csa2_workspace_bytes(OP_INDEX_TOPK, ctypes.byref(a))
     ws = workspace if workspace is not None else _ws(need, q_idx.device)
     _check(lib.csa2_index_topk(ctypes.byref(a), _p(ws), need if workspace is None else
-                               ws.numel(), _stream(stream)))
+                               ws.numel() * ws.element_size(), _stream(stream)))
     return idx_out
 
 
@@ -216,7 +216,7 @@ def layer_group(descs, g: GroupArgs, stream=None, workspace=None, device=None):
     need = lib.csa2_workspace_bytes(OP_LAYER_GROUP, ctypes.byref(g))
     ws = workspace if workspace is not None else _ws(need, device or torch.device("cuda"))
     _check(lib.csa2_layer_group(arr, n, ctypes.byref(g), _p(ws),
-                                need if workspace is None else ws.numel(), _stream(stream)))
+                                need if workspace is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mxfp4_quantize(x, lat, scl, dst_row=None, stream=None):

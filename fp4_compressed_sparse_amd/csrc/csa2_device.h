@@ -81,6 +81,11 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// max(a - b, 0) for unsigned values, written without a comparison-guarded subtraction:
+// this compiler has been seen to hoist the subtraction of `a > b ? f(a - b) : 0` with a
+// no-wrap flag and then treat b <= a as known elsewhere (dropping a later min(b, a)).
+__device__ __forceinline__ uint32_t sub_sat_u32(uint32_t a, uint32_t b) { return a - min(a, b); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

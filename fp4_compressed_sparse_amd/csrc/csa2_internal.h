@@ -109,6 +109,7 @@ struct QuantParams {
 
 // ---------------------------------------------------------------- launch geometry
 constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
+constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-tiled
 constexpr int kTopkThreads = 1024;
 
 // Split plan of the attention launch: `splits` workgroups per row, each covering

@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   const uint32_t gtb = (off & 0xffffu) + pg;         // keys above tau before this thread
   const uint32_t eqb = (off >> 16) + pe;             // keys at tau before this thread
   // the first need_eq keys at tau (in index order) are selected
-  uint32_t r = (need_eq > eqb) ? min(need_eq - eqb, ce) : 0u;
+  uint32_t r = min(sub_sat_u32(need_eq, eqb), ce);
   uint64_t sel = gtm;
   while (r--) {
     const uint64_t low = eqm & (0ull - eqm);
@@ -633,19 +633,19 @@ __global__ __launch_bounds__(kCkThreads) void topk_ck_emit_kernel(TopkParams p) 
 #pragma unroll
     for (int w = 0; w < kCkThreads / 64; ++w) tot += s_w[w];
     const uint32_t tg = tot & 0xffffu, te = tot >> 16;
-    const uint32_t eq_sel = (need_eq > eq0) ? min(need_eq - eq0, te) : 0u;
+    const uint32_t eq_sel = min(sub_sat_u32(need_eq, eq0), te);
     chunk_sel = tg + eq_sel;
   }
   const uint32_t gtb = (off & 0xffffu) + pg;         // within the chunk
   const uint32_t eqb = eq0 + (off >> 16) + pe;       // global rank of this thread's first tie
-  uint32_t r = (need_eq > eqb) ? min(need_eq - eqb, ce) : 0u;
+  uint32_t r = min(sub_sat_u32(need_eq, eqb), ce);
   uint32_t selm = gtm;
   while (r--) {
     const uint32_t low = eqm & (0u - eqm);
     selm |= low;
     eqm ^= low;
   }
-  const uint32_t eq_before = (need_eq > eq0) ? min(eqb - eq0, need_eq - eq0) : 0u;
+  const uint32_t eq_before = min(eqb, need_eq) - min(eq0, need_eq);
   uint32_t pos = gtb + eq_before;                    // position within the chunk's output
   const int i0 = ch * kCkKeys + kCkPerThread * tid;
   while (selm) {
@@ -658,7 +658,168 @@ __global__ __launch_bounds__(kCkThreads) void topk_ck_emit_kernel(TopkParams p) 
     out[base + i] = s_out[i];
 }
 
+// ---------------------------------------------------------------- scoring, many rows
+// Many query rows over few sequences (prefill): a workgroup scores a tile of rows against a
+// 2048-entry range, so each key page is read once per row tile instead of once per row.
+// The (row, head) pairs form the MFMA's M dimension (heads padded to HP = 4, 8 or 16; 128
+// pairs per wave in 8 blocks of 16), entries its N dimension and the 64 key channels its
+// K dimension (two 32-channel steps); the head sum w . ReLU(.) runs on the accumulators.
+// Key pages come into a ring of three LDS pages by LDS DMA, chunk c (16 bytes) of key k at
+// slot c ^ ((k >> 1) & 7), so that the 16 lanes of an operand read hit distinct banks.  A
+// wave's scores of a page pass through LDS to leave as 256-byte row segments.  Rows of a
+// tile that belong to different sequences are scored in one pass per sequence.
+constexpr int kGemmChunk = 2048;     // entries per workgroup
+constexpr int kGemmRing = 3;         // LDS key pages
+constexpr int kGemmPageBytes = kPage * kDidx * 2;
+__device__ __attribute__((aligned(16))) uint16_t g_zero_key[8];
+
+// Barrier with this wave's LDS accesses complete and no wait on vector memory (the key
+// pages arrive by LDS DMA, awaited explicitly); `lds` counts as written by it.
+__device__ __forceinline__ void dma_barrier(const void* lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : "v"(lds) : "memory");
+}
+
+template <int HP>
+__global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
+  constexpr int RB = 16 / HP;            // rows per 16-pair MFMA block
+  constexpr int NRB = 8;                 // blocks per wave
+  constexpr int RW = RB * NRB;           // rows per wave
+  constexpr int RT = 4 * RW;             // rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t s_page[kGemmRing][kGemmPageBytes];
+  __shared__ __attribute__((aligned(16))) float s_out[4][RW][kPage];
+  __shared__ int s_seq[RT], s_nv[RT];
+
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
+    p.clear[i] = 0u;
+  const int nrt = (p.T + RT - 1) / RT;
+  const int rt = (int)blockIdx.x % nrt, ch = (int)blockIdx.x / nrt;   // an XCD's blocks share ch
+  const int t0 = rt * RT, c0 = ch * kGemmChunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  for (int i = tid; i < RT; i += 256) {
+    const int t = t0 + i;
+    s_seq[i] = t < p.T ? p.seq_id[t] : -1;
+    s_nv[i] = t < p.T ? p.n_vis[t] : 0;
+  }
+  __syncthreads();
+
+  int prev = -1;
+  for (;;) {
+    // next sequence of the tile (in increasing id) and the entries its rows see
+    int cur = INT32_MAX, nvmax = 0;
+    for (int i = 0; i < RT; ++i) {
+      const int sq = s_seq[i];
+      if (sq > prev && sq < cur) cur = sq;
+    }
+    if (cur == INT32_MAX) break;
+    for (int i = 0; i < RT; ++i)
+      if (s_seq[i] == cur) nvmax = max(nvmax, s_nv[i]);
+    prev = cur;
+    const int np = max(0, min((min(nvmax, c0 + kGemmChunk) - c0 + kPage - 1) / kPage, kGemmChunk / kPage));
+    if (np == 0) continue;
+
+    // operands of this wave's rows (zero for rows of other sequences and padded heads)
+    const int rw0 = wave * RW;                       // first tile row of the wave
+    u32x4 qa[NRB][2];
+    float wv[NRB][4];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int ra = rw0 + RB * rb + n / HP, ha = n % HP;
+      const bool va = s_seq[ra] == cur && ha < p.H_I;
+      const uint16_t* qp = p.q_idx + ((int64_t)(t0 + ra) * p.H_I + ha) * kDidx + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        qa[rb][ks] = va ? ld_global_16(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rw0 + RB * rb + (4 * g + i) / HP, h = (4 * g + i) % HP;
+        wv[rb][i] = (s_seq[r] == cur && h < p.H_I) ? p.w_idx[(int64_t)(t0 + r) * p.H_I + h] : 0.f;
+      }
+    }
+    const int32_t* pt = p.page_table + (int64_t)cur * p.max_pages + c0 / kPage;
+    // DMA of page pp: wave w moves keys 16w .. 16w+15 (two 1 KB units)
+    auto dma_page = [&](int pp) {
+      const int64_t prow = (int64_t)pt[pp] * kPage;
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int k = 16 * wave + 8 * d + (lane >> 3);
+        const int c = (lane & 7) ^ ((k >> 1) & 7);
+        const uint16_t* src = p.k_idx + (prow + k) * kDidx + 8 * c;
+        __builtin_amdgcn_global_load_lds(src, &s_page[pp % kGemmRing][0] +
+                                         __builtin_amdgcn_readfirstlane(1024 * (2 * wave + d)),
+                                         16, 0, 0);
+      }
+    };
+    dma_page(0);
+    if (np > 1) {
+      dma_page(1);
+      __builtin_amdgcn_s_waitcnt(0x0f72);            // page 0 in LDS
+    } else {
+      wait_vmem_all();
+    }
+    dma_barrier(s_page);
+
+    for (int pp = 0; pp < np; ++pp) {
+      const uint8_t* kp = s_page[pp % kGemmRing];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int k = 16 * kb + n;
+        u32x4 kv[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          kv[ks] = *reinterpret_cast<const u32x4*>(kp + 128 * k + 16 * ((4 * ks + g) ^ ((k >> 1) & 7)));
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][0]), as_bf16x8(kv[0]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][1]), as_bf16x8(kv[1]), acc, 0, 0, 0);
+          float sc = wv[rb][0] * fmaxf(acc[0], 0.f);
+          sc += wv[rb][1] * fmaxf(acc[1], 0.f);
+          sc += wv[rb][2] * fmaxf(acc[2], 0.f);
+          sc += wv[rb][3] * fmaxf(acc[3], 0.f);
+          if (HP >= 8) sc += __shfl_xor(sc, 16);
+          if (HP >= 16) sc += __shfl_xor(sc, 32);
+          // lanes holding the same row write the same value
+          const int rl = RB * rb + (HP == 4 ? g : (HP == 8 ? (g >> 1) : 0));
+          s_out[wave][rl][k] = sc;
+        }
+      }
+      // this wave's rows of the page, 256 bytes per row
+      const int e0 = c0 + kPage * pp + 4 * n;
+#pragma unroll
+      for (int r4 = 0; r4 < RW / 4; ++r4) {
+        const int rl = 4 * r4 + g;
+        const int r = rw0 + rl;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&s_out[wave][rl][4 * n]);
+        if (s_seq[r] == cur && e0 < s_nv[r]) {
+          u32x4 kk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[e] = float_key(v[e]);
+          *reinterpret_cast<u32x4*>(p.keys + (int64_t)(t0 + r) * p.key_stride + e0) = kk;
+        }
+      }
+      if (pp + 2 < np) {
+        dma_page(pp + 2);
+        __builtin_amdgcn_s_waitcnt(0x0f72);          // page pp+1 in LDS
+      } else {
+        wait_vmem_all();
+      }
+      dma_barrier(s_page);
+    }
+  }
+}
+
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
+  if (p.T >= kIdxGemmMinRows) {
+    const int64_t nch = (p.key_stride + kGemmChunk - 1) / kGemmChunk;
+    const int hp = p.H_I <= 4 ? 4 : (p.H_I <= 8 ? 8 : 16);
+    const int rt = 4 * 8 * (16 / hp);                 // rows per workgroup
+    const unsigned blocks = (unsigned)(((int64_t)p.T + rt - 1) / rt * nch);
+    if (hp == 4) CSA2_LAUNCH(idx_gemm_kernel<4>, dim3(blocks), dim3(256), s, p);
+    else if (hp == 8) CSA2_LAUNCH(idx_gemm_kernel<8>, dim3(blocks), dim3(256), s, p);
+    else CSA2_LAUNCH(idx_gemm_kernel<16>, dim3(blocks), dim3(256), s, p);
+    return hipGetLastError();
+  }
   const int64_t blocks = (int64_t)p.T * p.chunks;
   CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   return hipGetLastError();

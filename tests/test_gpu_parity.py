@@ -180,6 +180,42 @@ def test_topk_chunked_parity(csa2, dev, name):
     _index_parity(csa2, dev, CHUNKED[name], name)
 
 
+# From 256 rows on, scoring runs row-tiled (a tile of rows against each key page): tiles
+# that mix sequences, rows past the end of the last tile, ragged and empty visibility, and
+# indexer head counts padded to 4, 8 and 16.
+def _gemm_rows(T, seqs, seed):
+    rng = np.random.default_rng(seed)
+    sid = np.repeat(np.arange(len(seqs)), seqs)[:T]
+    sid = np.r_[sid, np.zeros(T - len(sid), np.int64)]
+    sid[rng.choice(T, 7, replace=False)] = len(seqs) - 1       # strays inside other runs
+    return sid.astype(np.int32)
+
+
+def _gemm_nvis(T, E, seed):
+    rng = np.random.default_rng(seed)
+    nv = rng.integers(1, E + 1, T)
+    nv[:5] = [0, 1, 63, 64, E]
+    return nv.astype(np.int32)
+
+
+GEMM = {
+    "rowtiled_t300_b3_hi8": W(B=3, T=300, E=4160, H=16, H_I=8, K=256, H_kv=16,
+                              seq_id_rows=_gemm_rows(300, [120, 60, 120], 5),
+                              n_vis_rows=_gemm_nvis(300, 4160, 6)),
+    "rowtiled_t260_b2_hi3": W(B=2, T=260, E=2112, H=16, H_I=3, K=100, H_kv=16,
+                              seq_id_rows=_gemm_rows(260, [200, 60], 7),
+                              n_vis_rows=_gemm_nvis(260, 2112, 8)),
+    "rowtiled_t257_b1_hi16": W(B=1, T=257, E=2048, H=16, H_I=16, K=512, H_kv=16, hot="runs",
+                               n_hot=64, hot_runs=4, seq_id_rows=np.zeros(257, np.int32),
+                               n_vis_rows=_gemm_nvis(257, 2048, 9)),
+}
+
+
+@pytest.mark.parametrize("name", list(GEMM))
+def test_index_topk_rowtiled_parity(csa2, dev, name):
+    _index_parity(csa2, dev, GEMM[name], name)
+
+
 def test_topk_chunked_all_equal_scores(csa2, dev):
     """Equal scores over many chunks: the lowest K indices win, in order, also when the
     selection spans several chunks."""
