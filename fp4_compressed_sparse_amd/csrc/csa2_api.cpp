@@ -167,6 +167,7 @@ size_t index_ws_bytes(int32_t T, int32_t max_pages) {
     b += round_up((size_t)T * kCkHistWords * sizeof(uint32_t)) +
          round_up((size_t)T * topk_chunks(E) * 2 * sizeof(uint32_t)) +
          round_up((size_t)T * 8 * sizeof(uint32_t));
+  if (T >= kIdxGemmMinRows) b += round_up(1024);   // the row-tiled scoring's store sink
   return b;
 }
 
@@ -234,6 +235,7 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
                                              round_up((size_t)a->T * (size_t)E * sizeof(uint32_t)));
   sp.clear = chunked ? ck : nullptr;
   sp.clear_words = chunked ? a->T * kCkHistWords : 0;
+  sp.trash = (a->T >= kIdxGemmMinRows) ? ck : nullptr;   // chunked and row-tiled never meet
   csa2_status st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
   if (st) return st;
   st = between();

@@ -37,6 +37,7 @@ struct IdxScoreParams {
   uint32_t* keys;                      // [T, key_stride] order-preserving keys
   uint32_t* clear;                     // optional: words zeroed by the first blocks
   int clear_words;
+  uint32_t* trash;                     // row-tiled scoring: 1 KB that masked stores hit
 };
 
 struct TopkParams {
@@ -110,6 +111,7 @@ struct QuantParams {
 // ---------------------------------------------------------------- launch geometry
 constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
 constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-tiled
+static_assert(kCkMaxRows < kIdxGemmMinRows, "row-tiled scoring reuses the chunked Top-K area");
 constexpr int kTopkThreads = 1024;
 
 // Split plan of the attention launch: `splits` workgroups per row, each covering

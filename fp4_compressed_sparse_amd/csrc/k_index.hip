@@ -663,20 +663,29 @@ __global__ __launch_bounds__(kCkThreads) void topk_ck_emit_kernel(TopkParams p) 
 // 2048-entry range, so each key page is read once per row tile instead of once per row.
 // The (row, head) pairs form the MFMA's M dimension (heads padded to HP = 4, 8 or 16; 128
 // pairs per wave in 8 blocks of 16), entries its N dimension and the 64 key channels its
-// K dimension (two 32-channel steps); the head sum w . ReLU(.) runs on the accumulators.
-// Key pages come into a ring of three LDS pages by LDS DMA, chunk c (16 bytes) of key k at
-// slot c ^ ((k >> 1) & 7), so that the 16 lanes of an operand read hit distinct banks.  A
-// wave's scores of a page pass through LDS to leave as 256-byte row segments.  Rows of a
-// tile that belong to different sequences are scored in one pass per sequence.
+// K dimension (two 32-channel steps, the eight blocks' chains interleaved); the head sum
+// w . ReLU(.) runs on the accumulators.  Key pages arrive by LDS DMA into a ring of four,
+// three pages ahead, chunk c (16 bytes) of key k at slot c ^ ((k >> 1) & 7), so that the 16
+// lanes of an operand read hit distinct banks.  A wave's scores of a page pass through LDS
+// and leave a page later as 256-byte row segments.  Every wave issues two DMA loads per page
+// (pages past the end reload the last one), so one counter value names the page to wait
+// for.  Rows of a tile that belong to different sequences are scored in one pass per
+// sequence.
 constexpr int kGemmChunk = 2048;     // entries per workgroup
-constexpr int kGemmRing = 3;         // LDS key pages
+constexpr int kGemmRing = 4;
 constexpr int kGemmPageBytes = kPage * kDidx * 2;
-__device__ __attribute__((aligned(16))) uint16_t g_zero_key[8];
 
 // Barrier with this wave's LDS accesses complete and no wait on vector memory (the key
 // pages arrive by LDS DMA, awaited explicitly); `lds` counts as written by it.
 __device__ __forceinline__ void dma_barrier(const void* lds) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : "v"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N < 64 (other counters unrestricted)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
 template <int HP>
@@ -685,8 +694,14 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
   constexpr int NRB = 8;                 // blocks per wave
   constexpr int RW = RB * NRB;           // rows per wave
   constexpr int RT = 4 * RW;             // rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t s_page[kGemmRing][kGemmPageBytes];
-  __shared__ __attribute__((aligned(16))) float s_out[4][RW][kPage];
+  constexpr int S = RW / 4;              // stores per wave and page
+  // the ring's pages are separate arrays, indexed statically, so that the compiler can tell
+  // a page being read from the pages whose DMA is still in flight
+  __shared__ __attribute__((aligned(16))) uint8_t s_pg0[kGemmPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_pg1[kGemmPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_pg2[kGemmPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_pg3[kGemmPageBytes];
+  __shared__ __attribute__((aligned(16))) float s_out[2][4][RW][kPage];
   __shared__ int s_seq[RT], s_nv[RT];
 
   for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
@@ -703,9 +718,11 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
   }
   __syncthreads();
 
+  const int rw0 = wave * RW;                         // first tile row of the wave
   int prev = -1;
   for (;;) {
-    // next sequence of the tile (in increasing id) and the entries its rows see
+    // next sequence of the tile (in increasing id, the same in every lane) and the entries
+    // its rows see
     int cur = INT32_MAX, nvmax = 0;
     for (int i = 0; i < RT; ++i) {
       const int sq = s_seq[i];
@@ -714,12 +731,13 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
     if (cur == INT32_MAX) break;
     for (int i = 0; i < RT; ++i)
       if (s_seq[i] == cur) nvmax = max(nvmax, s_nv[i]);
+    cur = __builtin_amdgcn_readfirstlane(cur);
     prev = cur;
-    const int np = max(0, min((min(nvmax, c0 + kGemmChunk) - c0 + kPage - 1) / kPage, kGemmChunk / kPage));
+    const int np = __builtin_amdgcn_readfirstlane(
+        min((max(min(nvmax, c0 + kGemmChunk) - c0, 0) + kPage - 1) / kPage, kGemmChunk / kPage));
     if (np == 0) continue;
 
     // operands of this wave's rows (zero for rows of other sequences and padded heads)
-    const int rw0 = wave * RW;                       // first tile row of the wave
     u32x4 qa[NRB][2];
     float wv[NRB][4];
 #pragma unroll
@@ -736,76 +754,100 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
         wv[rb][i] = (s_seq[r] == cur && h < p.H_I) ? p.w_idx[(int64_t)(t0 + r) * p.H_I + h] : 0.f;
       }
     }
-    const int32_t* pt = p.page_table + (int64_t)cur * p.max_pages + c0 / kPage;
-    // DMA of page pp: wave w moves keys 16w .. 16w+15 (two 1 KB units)
-    auto dma_page = [&](int pp) {
-      const int64_t prow = (int64_t)pt[pp] * kPage;
+    // store targets of this wave's rows (a row is written only where its sequence is
+    // scored and its entries are visible; other lanes store to the sink)
+    uint32_t* const sink = p.trash + 4 * lane;
+    // physical pages of the range, one per lane (read once: a load in the page loop would
+    // count among the operations the loop waits for)
+    const int my_page = lane < np ? p.page_table[(int64_t)cur * p.max_pages + c0 / kPage + lane] : 0;
+    // DMA of page pp (clamped to the last page) into ring slot `dst`: wave w moves keys
+    // 16w .. 16w+15 (two 1 KB units)
+    auto dma_page = [&](int pp, uint8_t* dst) {
+      const int64_t prow = (int64_t)__shfl(my_page, min(pp, np - 1)) * kPage;
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const int k = 16 * wave + 8 * d + (lane >> 3);
         const int c = (lane & 7) ^ ((k >> 1) & 7);
-        const uint16_t* src = p.k_idx + (prow + k) * kDidx + 8 * c;
-        __builtin_amdgcn_global_load_lds(src, &s_page[pp % kGemmRing][0] +
-                                         __builtin_amdgcn_readfirstlane(1024 * (2 * wave + d)),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(p.k_idx + (prow + k) * kDidx + 8 * c,
+                                         dst + 1024 * (2 * wave + d), 16, 0, 0);
       }
     };
-    dma_page(0);
-    if (np > 1) {
-      dma_page(1);
-      __builtin_amdgcn_s_waitcnt(0x0f72);            // page 0 in LDS
-    } else {
-      wait_vmem_all();
-    }
-    dma_barrier(s_page);
-
-    for (int pp = 0; pp < np; ++pp) {
-      const uint8_t* kp = s_page[pp % kGemmRing];
+    // this wave's rows of page pp's scores (LDS buffer pp & 1), 256 bytes per row; masked
+    // lanes store to the sink
+    auto store_page = [&](int pp) {
+      const int e0 = c0 + kPage * pp + 4 * n;
+#pragma unroll
+      for (int r4 = 0; r4 < S; ++r4) {
+        const int rl = 4 * r4 + g;
+        const int r = rw0 + rl;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&s_out[pp & 1][wave][rl][4 * n]);
+        u32x4 kk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[e] = float_key(v[e]);
+        const bool ok = s_seq[r] == cur && e0 < s_nv[r];
+        uint32_t* dst = ok ? p.keys + (int64_t)(t0 + r) * p.key_stride + e0 : sink;
+        *reinterpret_cast<u32x4*>(dst) = kk;
+      }
+    };
+    // One page: the stores of page pp-1, page pp's operands from slot `kp`, the DMA of page
+    // pp+3 into slot `nx`, the MFMAs, and the wait for page pp+1.  The wait counts only the
+    // loads issued after page pp+1's (those of pages pp+2 and pp+3): loads complete in
+    // order, while stores may complete before earlier loads.
+    auto page_step = [&](int pp, const uint8_t* kp, uint8_t* nx) {
+      dma_barrier(s_pg0);                              // page pp in LDS, page pp-1 consumed
+      if (pp > 0) store_page(pp - 1);
+      u32x4 kv[4][2];                                  // all operands read before the DMA
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int k = 16 * kb + n;
-        u32x4 kv[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          kv[ks] = *reinterpret_cast<const u32x4*>(kp + 128 * k + 16 * ((4 * ks + g) ^ ((k >> 1) & 7)));
+          kv[kb][ks] = *reinterpret_cast<const u32x4*>(kp + 128 * k + 16 * ((4 * ks + g) ^ ((k >> 1) & 7)));
+      }
+      dma_page(pp + 3, nx);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int k = 16 * kb + n;
+        f32x4 acc[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][0]), as_bf16x8(kv[kb][0]),
+                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][1]), as_bf16x8(kv[kb][1]),
+                                                            acc[rb], 0, 0, 0);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][0]), as_bf16x8(kv[0]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][1]), as_bf16x8(kv[1]), acc, 0, 0, 0);
-          float sc = wv[rb][0] * fmaxf(acc[0], 0.f);
-          sc += wv[rb][1] * fmaxf(acc[1], 0.f);
-          sc += wv[rb][2] * fmaxf(acc[2], 0.f);
-          sc += wv[rb][3] * fmaxf(acc[3], 0.f);
+          float sc = wv[rb][0] * fmaxf(acc[rb][0], 0.f);
+          sc += wv[rb][1] * fmaxf(acc[rb][1], 0.f);
+          sc += wv[rb][2] * fmaxf(acc[rb][2], 0.f);
+          sc += wv[rb][3] * fmaxf(acc[rb][3], 0.f);
           if (HP >= 8) sc += __shfl_xor(sc, 16);
           if (HP >= 16) sc += __shfl_xor(sc, 32);
           // lanes holding the same row write the same value
           const int rl = RB * rb + (HP == 4 ? g : (HP == 8 ? (g >> 1) : 0));
-          s_out[wave][rl][k] = sc;
+          s_out[pp & 1][wave][rl][k] = sc;
         }
       }
-      // this wave's rows of the page, 256 bytes per row
-      const int e0 = c0 + kPage * pp + 4 * n;
-#pragma unroll
-      for (int r4 = 0; r4 < RW / 4; ++r4) {
-        const int rl = 4 * r4 + g;
-        const int r = rw0 + rl;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&s_out[wave][rl][4 * n]);
-        if (s_seq[r] == cur && e0 < s_nv[r]) {
-          u32x4 kk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kk[e] = float_key(v[e]);
-          *reinterpret_cast<u32x4*>(p.keys + (int64_t)(t0 + r) * p.key_stride + e0) = kk;
-        }
-      }
-      if (pp + 2 < np) {
-        dma_page(pp + 2);
-        __builtin_amdgcn_s_waitcnt(0x0f72);          // page pp+1 in LDS
-      } else {
-        wait_vmem_all();
-      }
-      dma_barrier(s_page);
+      wait_vmem<4>();                                  // page pp+1 in LDS
+    };
+    dma_page(0, s_pg0);
+    dma_page(1, s_pg1);
+    dma_page(2, s_pg2);
+    wait_vmem<4>();                                    // page 0
+    for (int pp = 0; pp < np; pp += kGemmRing) {
+      page_step(pp, s_pg0, s_pg3);
+      if (pp + 1 >= np) break;
+      page_step(pp + 1, s_pg1, s_pg0);
+      if (pp + 2 >= np) break;
+      page_step(pp + 2, s_pg2, s_pg1);
+      if (pp + 3 >= np) break;
+      page_step(pp + 3, s_pg3, s_pg2);
     }
+    store_page(np - 1);
+    wait_vmem<0>();
+    dma_barrier(s_pg0);                                // ring free for the next pass
   }
 }
 
