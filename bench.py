@@ -118,20 +118,34 @@ class Inputs:
 
 # ------------------------------------------------------------------ algorithmic bytes
 def algorithmic_bytes(w):
-    """Bytes each kernel class must move per step (what the method itself reads/writes,
-    not what an implementation re-reads): per row, the indexer-key scan n_vis x 128 B, the
-    gather of the selected entries K x 400 B, the SWA window n_win x H_kv x 128 x 2 x 2 B,
-    plus queries and fp32 outputs.  Returned per kernel name of the library."""
+    """Bytes each kernel class must move per step (what the method itself reads/writes once,
+    not what an implementation re-reads), returned per kernel name of the library:
+    per sequence, its indexer keys up to the largest visibility of its rows (128 B each),
+    its distinct selected entries (at most min(E, the rows' selections), 400 B each) and the
+    union of its rows' SWA windows (H_kv x 128 x 2 x 2 B per token); per row, queries, the
+    Top-K output and fp32 outputs.  With one row per sequence (decode) this is the per-row
+    scan n_vis x 128 B, gather K x 400 B and window n_win x H_kv x 512 B."""
     import numpy as np
     nv = w.n_vis().astype(np.int64)
     sel = np.minimum(nv, w.K)
+    sid = w.seq_id().astype(np.int64)
+    start = w.swa_start().astype(np.int64)
+    win = w.swa_len().astype(np.int64)
+    keys = gathered = window = 0
+    for b in np.unique(sid):
+        r = sid == b
+        keys += int(nv[r].max())
+        gathered += min(int(w.E), int(sel[r].sum()))
+        tok = np.zeros(int((start[r] + win[r]).max()) if r.any() else 0, bool)
+        for s0, l in zip(start[r], win[r]):
+            tok[s0:s0 + l] = True
+        window += int(tok.sum())
     n_idx_layers = sum(1 for m in w.modes if m in (0, 1))
     n_layers = len(w.modes)
-    idx_score = n_idx_layers * (int(nv.sum()) * 128 + w.T * w.H_I * (64 * 2 + 4))
+    idx_score = n_idx_layers * (keys * 128 + w.T * w.H_I * (64 * 2 + 4))
     topk = n_idx_layers * w.T * w.K * 4
-    attn = n_layers * (int(sel.sum()) * 400 + w.T * w.H * (576 * 2 + 512 * 4 + 4))
-    win = w.swa_len().astype(np.int64)
-    swa = n_layers * (int(win.sum()) * w.H_kv * 128 * 2 * 2 + w.T * w.H * (128 * 2 + 128 * 4 + 4))
+    attn = n_layers * (gathered * 400 + w.T * w.H * (576 * 2 + 512 * 4 + 4))
+    swa = n_layers * (window * w.H_kv * 128 * 2 * 2 + w.T * w.H * (128 * 2 + 128 * 4 + 4))
     return {"idx_score": idx_score, "topk": topk, "sparse_attn": attn, "swa": swa}
 
 
