@@ -112,6 +112,7 @@ struct QuantParams {
 constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
 constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-tiled
 static_assert(kCkMaxRows < kIdxGemmMinRows, "row-tiled scoring reuses the chunked Top-K area");
+constexpr int kSwaTileMinRows = 256;   // from this many rows, SWA runs row-tiled on MFMA
 constexpr int kTopkThreads = 1024;
 
 // Split plan of the attention launch: `splits` workgroups per row, each covering

@@ -216,6 +216,28 @@ def test_index_topk_rowtiled_parity(csa2, dev, name):
     _index_parity(csa2, dev, GEMM[name], name)
 
 
+def _swa_windows(T, L, seed):
+    rng = np.random.default_rng(seed)
+    ln = rng.choice([0, 1, 17, 64, 128, 200], T)
+    st = np.array([rng.integers(0, L - l + 1) for l in ln])
+    st[:T // 2] = np.minimum(np.arange(T // 2), L - ln[:T // 2])   # a sliding run, as in prefill
+    return st.astype(np.int32), ln.astype(np.int32)
+
+
+_SW = _swa_windows(300, 400, 13)
+
+
+def test_layer_group_rowtiled_swa_and_scoring(csa2, dev):
+    """From 256 rows on, SWA also runs row-tiled on MFMA: tiles that mix sequences, GQA (4
+    query heads per KV head), empty, one-token and long windows, a partial last tile."""
+    w = W(name="rowtiled_t300_b3_gqa4", B=3, T=300, E=1024, H=16, H_I=4, K=64, H_kv=4,
+          L_swa=400, seq_id_rows=_gemm_rows(300, [120, 60, 120], 11),
+          n_vis_rows=_gemm_nvis(300, 1024, 12), swa_start_rows=_SW[0], swa_len_rows=_SW[1])
+    d, res, _ = _group_case(csa2, dev, w, np.arange(300), w.name)
+    empty = w.swa_len() == 0
+    assert np.all(res[0]["o_swa"][empty] == 0) and np.all(np.isneginf(res[0]["lse_swa"][empty]))
+
+
 def test_topk_chunked_all_equal_scores(csa2, dev):
     """Equal scores over many chunks: the lowest K indices win, in order, also when the
     selection spans several chunks."""
