@@ -163,13 +163,14 @@ __device__ __forceinline__ void topk_find_digit(TopkShared& sh, uint32_t remaini
   __syncthreads();
 }
 
-// Ordered compaction of one 4096-key tile: thread t holds keys 4t..4t+3 of the tile
-// (valid[e] marks keys below n).  Output position of a selected key i:
-// (#keys > tau before i) + min(#keys == tau before i, need_eq).
+// Ordered compaction of one tile of 4 x kTopkThreads keys: thread t holds the tile's keys
+// 4t..4t+3 (valid[e] marks real keys), whose indices are idx[e].  Output position of a
+// selected key i: (#keys > tau before i) + min(#keys == tau before i, need_eq).
 __device__ __forceinline__ void topk_emit_tile(TopkShared& sh, const uint32_t kv[4],
-                                               const bool valid[4], int i0, uint32_t tau,
-                                               uint32_t need_eq, uint32_t& gt_base,
-                                               uint32_t& eq_base, int32_t* out) {
+                                               const bool valid[4], const int idx[4],
+                                               uint32_t tau, uint32_t need_eq,
+                                               uint32_t& gt_base, uint32_t& eq_base,
+                                               int32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t cg = 0u, ce = 0u;
 #pragma unroll
@@ -200,10 +201,10 @@ __device__ __forceinline__ void topk_emit_tile(TopkShared& sh, const uint32_t kv
   for (int e = 0; e < 4; ++e) {
     if (!valid[e]) continue;
     if (kv[e] > tau) {
-      out[gtb + min(eqb, need_eq)] = i0 + e;
+      out[gtb + min(eqb, need_eq)] = idx[e];
       ++gtb;
     } else if (kv[e] == tau) {
-      if (eqb < need_eq) out[gtb + eqb] = i0 + e;
+      if (eqb < need_eq) out[gtb + eqb] = idx[e];
       ++eqb;
     }
   }
@@ -400,50 +401,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   }
 }
 
-// Rows of any length: every digit pass and the compaction stream the row's keys.
+// Rows of any length, streamed from memory.  The first pass histograms the top digit (bits
+// 31..20).  When the keys at or above the chosen digit fit in LDS (kTopkListCap), a second
+// stream copies them, with their indices and in index order, into an LDS list; the last two
+// digits are then found on the list and the emission walks the list: two streams of the row
+// in all.  Otherwise the remaining digit passes and the emission each stream the row.
+constexpr int kTopkListCap = 8192;
+
 __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p) {
   __shared__ TopkShared sh;
+  __shared__ uint32_t s_lkey[kTopkListCap];
+  __shared__ int32_t s_lidx[kTopkListCap];
   const int t = blockIdx.x;
   const int n = p.n_vis[t];
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (n <= K) {
     for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
     return;
   }
   const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
   const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
-  uint32_t prefix = 0u, remaining = (uint32_t)K;
-  for (int pass = 0; pass < 3; ++pass) {
-    const uint32_t pmask = topk_prefix_mask(pass);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
-    __syncthreads();
-    for (int i0 = 4 * tid; i0 < n; i0 += 4 * kTopkThreads) {
-      uint32_t kv[4];
-      if (i0 + 3 < n) {
-        const u32x4 v = k4[i0 >> 2];
-        kv[0] = v[0]; kv[1] = v[1]; kv[2] = v[2]; kv[3] = v[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kv[e] = (i0 + e < n) ? keys[i0 + e] : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i0 + e < n && (kv[e] & pmask) == prefix)
-          atomicAdd(&sh.hist[topk_digit(kv[e], pass)], 1u);
-    }
-    __syncthreads();
-    topk_find_digit(sh, remaining);
-    prefix |= topk_place(sh.digit, pass);
-    remaining = sh.remaining;
-  }
-  uint32_t gt_base = 0u, eq_base = 0u;
-  for (int base = 0; base < n; base += 4 * kTopkThreads) {
-    const int i0 = base + 4 * tid;
-    uint32_t kv[4];
-    bool valid[4];
+  auto load4 = [&](int i0, uint32_t (&kv)[4], bool (&valid)[4]) {
     if (i0 + 3 < n) {
       const u32x4 v = k4[i0 >> 2];
 #pragma unroll
@@ -455,7 +435,113 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
         kv[e] = valid[e] ? keys[i0 + e] : 0u;
       }
     }
-    topk_emit_tile(sh, kv, valid, i0, prefix, remaining, gt_base, eq_base, out);
+  };
+  uint32_t prefix = 0u, remaining = (uint32_t)K;
+  int pass = 0;
+  for (; pass < 3; ++pass) {
+    const uint32_t pmask = topk_prefix_mask(pass);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
+    __syncthreads();
+    for (int i0 = 4 * tid; i0 < n; i0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+      bool valid[4];
+      load4(i0, kv, valid);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid[e] && (kv[e] & pmask) == prefix)
+          atomicAdd(&sh.hist[topk_digit(kv[e], pass)], 1u);
+    }
+    __syncthreads();
+    topk_find_digit(sh, remaining);
+    prefix |= topk_place(sh.digit, pass);
+    remaining = sh.remaining;
+    if (pass == 0) {
+      // keys at or above the top digit: K - rank of the K-th key in its bin, plus the bin
+      const bool fits = (uint32_t)K - remaining + sh.hist[sh.digit] <= (uint32_t)kTopkListCap;
+      __syncthreads();                               // read by all before the next pass clears
+      if (fits) break;
+    }
+  }
+  if (pass == 0) {
+    // ---- second stream: keys with top digit >= d0 into the LDS list, in index order
+    const uint32_t d0 = prefix >> 20;
+    uint32_t base = 0u;
+    for (int tile = 0; tile < n; tile += 4 * kTopkThreads) {
+      const int i0 = tile + 4 * tid;
+      uint32_t kv[4];
+      bool valid[4];
+      load4(i0, kv, valid);
+      uint32_t f = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f |= (uint32_t)(valid[e] && (kv[e] >> 20) >= d0) << e;
+      uint32_t wtot;
+      const uint32_t pre = wave_prefix_small<3>((uint32_t)__popc(f), wtot);
+      if (lane == 0) sh.wave_tot[wave] = wtot;
+      __syncthreads();
+      uint32_t off = 0u, tot = 0u;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) {
+        const uint32_t x = sh.wave_tot[w];
+        off += (w < wave) ? x : 0u;
+        tot += x;
+      }
+      uint32_t pos = base + off + pre;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((f >> e) & 1u) {
+          s_lkey[pos] = kv[e];
+          s_lidx[pos] = i0 + e;
+          ++pos;
+        }
+      }
+      base += tot;
+      __syncthreads();                               // wave_tot is reused by the next tile
+    }
+    const int L = (int)base;                         // = K - rank + hist[d0] <= cap
+    // ---- the last two digits among the list's keys in bin d0
+#pragma unroll
+    for (int sub = 1; sub < 3; ++sub) {
+      const uint32_t pmask = topk_prefix_mask(sub);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
+      __syncthreads();
+      for (int i = tid; i < L; i += kTopkThreads) {
+        const uint32_t k = s_lkey[i];
+        if ((k & pmask) == prefix) atomicAdd(&sh.hist[topk_digit(k, sub)], 1u);
+      }
+      __syncthreads();
+      topk_find_digit(sh, remaining);
+      prefix |= topk_place(sh.digit, sub);
+      remaining = sh.remaining;
+    }
+    // ---- emission from the list (it holds every key >= tau, in index order)
+    uint32_t gt_base = 0u, eq_base = 0u;
+    for (int b0 = 0; b0 < L; b0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+      bool valid[4];
+      int idx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = b0 + 4 * tid + e;
+        valid[e] = i < L;
+        kv[e] = valid[e] ? s_lkey[i] : 0u;
+        idx[e] = valid[e] ? s_lidx[i] : 0;
+      }
+      topk_emit_tile(sh, kv, valid, idx, prefix, remaining, gt_base, eq_base, out);
+    }
+    return;
+  }
+  uint32_t gt_base = 0u, eq_base = 0u;
+  for (int base = 0; base < n; base += 4 * kTopkThreads) {
+    const int i0 = base + 4 * tid;
+    uint32_t kv[4];
+    bool valid[4];
+    int idx[4];
+    load4(i0, kv, valid);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) idx[e] = i0 + e;
+    topk_emit_tile(sh, kv, valid, idx, prefix, remaining, gt_base, eq_base, out);
   }
 }
 

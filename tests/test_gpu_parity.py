@@ -238,6 +238,38 @@ def test_layer_group_rowtiled_swa_and_scoring(csa2, dev):
     assert np.all(res[0]["o_swa"][empty] == 0) and np.all(np.isneginf(res[0]["lse_swa"][empty]))
 
 
+# Many rows longer than 65536 keys: the streamed Top-K.  Distinct scores take the path that
+# gathers the keys at or above the top digit into LDS; all-equal scores overflow that list
+# and take the streamed digit passes.
+STREAMED = {
+    "streamed_t66_65600_k512": W(B=2, T=66, E=65600, H=16, H_I=4, K=512, H_kv=16,
+                                 n_vis_rows=np.r_[[65600, 65537, 300, 40000],
+                                                  np.full(62, 65600)].astype(np.int32),
+                                 seq_id_rows=(np.arange(66) % 2).astype(np.int32)),
+}
+
+
+@pytest.mark.parametrize("name", list(STREAMED))
+def test_topk_streamed_parity(csa2, dev, name):
+    _index_parity(csa2, dev, STREAMED[name], name)
+
+
+def test_topk_streamed_all_equal_scores(csa2, dev):
+    _say("topk_streamed_all_equal_scores")
+    E, K, T = 65600, 300, 66
+    key = torch.from_numpy(synth.normal_bf16(9, 1, 0, 64).view(np.int16)).to(dev)
+    k_idx = key.view(1, 1, 64).expand(E // 64, 64, 64).contiguous().view(torch.bfloat16)
+    q = torch.from_numpy(synth.normal_bf16(9, 2, 0, T * 64).view(np.int16)).to(dev).view(
+        torch.bfloat16).view(T, 1, 64)
+    wv = torch.ones((T, 1), dtype=torch.float32, device=dev)
+    pt = torch.arange(E // 64, dtype=torch.int32, device=dev).view(1, -1)
+    sid = torch.zeros(T, dtype=torch.int32, device=dev)
+    nv = torch.full((T,), E, dtype=torch.int32, device=dev)
+    idx = csa2.index_topk(q, wv, k_idx, pt, sid, nv, K).cpu().numpy()
+    for r in range(T):
+        np.testing.assert_array_equal(idx[r], np.arange(K))
+
+
 def test_topk_chunked_all_equal_scores(csa2, dev):
     """Equal scores over many chunks: the lowest K indices win, in order, also when the
     selection spans several chunks."""
