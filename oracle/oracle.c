@@ -250,6 +250,70 @@ void csa2o_index_topk(int T, int H_I, int K, int max_pages, const uint16_t* q_id
   }
 }
 
+/* Candidate pool of the hierarchical sparse indexer ([summary] Architecture
+ * Components, item 3: the first Full layer builds a pool of up to 2,048 blocks of 8
+ * positions that bounds the search of the later Reindex layers).  Reading: a block is
+ * an aligned run of 8 compressed-entry positions, block b = {8b, ..., 8b + 7}; every
+ * entry the Full layer selected contributes its block, and the pool is the union of
+ * those blocks cut to the visible entries, in ascending order.  sel holds the Full
+ * layer's K_sel selected entries of the row (-1 = unused slot).  pool must hold
+ * 8 * K_sel positions; returns the pool size. */
+int64_t csa2o_pool_positions(const int32_t* sel, int K_sel, int64_t n_vis, int32_t* pool) {
+  const int64_t nb = (n_vis + 7) / 8;
+  unsigned char* in = (unsigned char*)calloc((size_t)(nb > 0 ? nb : 1), 1);
+  for (int i = 0; i < K_sel; ++i)
+    if (sel[i] >= 0 && sel[i] < n_vis) in[sel[i] / 8] = 1;
+  int64_t m = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    if (!in[b]) continue;
+    for (int64_t j = 8 * b; j < 8 * b + 8 && j < n_vis; ++j) pool[m++] = (int32_t)j;
+  }
+  free(in);
+  return m;
+}
+
+/* Reindex layer searching the pool: the layer's own indexer scores every pool
+ * position (the same score as csa2o_index_topk), and the Top-K runs over the pool
+ * alone: order the (score, position) pairs by descending score and ascending
+ * position, keep the first min(K, pool size), emit ascending, pad with -1.
+ * sel: [T, K_sel] selected entries of the Full layer that builds the pool.
+ * scores_out (optional): [n_rows, max_pages * 64], pool positions written, the
+ * rest left untouched. */
+void csa2o_index_topk_pool(int T, int H_I, int K, int max_pages, const uint16_t* q_idx,
+                           const float* w_idx, const uint16_t* k_idx,
+                           const int32_t* page_table, const int32_t* seq_id,
+                           const int32_t* n_vis, const int32_t* sel, int K_sel,
+                           const int32_t* rows, int n_rows, int32_t* idx_out,
+                           double* scores_out) {
+  (void)T;
+  const int64_t E = (int64_t)max_pages * PAGE;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < n_rows; ++r) {
+    int t = rows[r];
+    int64_t nv = n_vis[t];
+    int32_t* pool = (int32_t*)malloc(sizeof(int32_t) * (size_t)(8 * K_sel > 0 ? 8 * K_sel : 1));
+    int64_t m = csa2o_pool_positions(sel + (int64_t)t * K_sel, K_sel, nv, pool);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(nv > 0 ? nv : 1));
+    index_scores_row(q_idx + (int64_t)t * H_I * DIDX, w_idx + (int64_t)t * H_I, H_I, k_idx,
+                     page_table, max_pages, seq_id[t], nv, s);
+    scored* v = (scored*)malloc(sizeof(scored) * (size_t)(m > 0 ? m : 1));
+    for (int64_t i = 0; i < m; ++i) {
+      v[i].s = s[pool[i]];
+      v[i].j = pool[i];
+      if (scores_out) scores_out[(int64_t)r * E + pool[i]] = s[pool[i]];
+    }
+    qsort(v, (size_t)m, sizeof(scored), cmp_scored);
+    int32_t* out = idx_out + (int64_t)r * K;
+    int64_t keep = m < K ? m : K;
+    for (int64_t i = 0; i < keep; ++i) out[i] = (int32_t)v[i].j;
+    qsort(out, (size_t)keep, sizeof(int32_t), cmp_i32);
+    for (int64_t i = keep; i < K; ++i) out[i] = -1;
+    free(v);
+    free(s);
+    free(pool);
+  }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Attention                                                                  */
 /* ------------------------------------------------------------------------- */

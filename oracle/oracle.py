@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FULL, REINDEX, REUSE = 0, 1, 2
+FULL, REINDEX, REUSE, REINDEX_POOL = 0, 1, 2, 3
 LAT, ROPE, DQ, DIDX, DSWA, PAGE = 512, 64, 576, 64, 128, 64
 
 
@@ -54,6 +54,10 @@ def lib():
         L.csa2o_topk_from_scores.argtypes = [vp, i64, i32, vp]
         L.csa2o_index_topk.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32,
                                        vp, vp]
+        L.csa2o_pool_positions.restype = i64
+        L.csa2o_pool_positions.argtypes = [vp, i32, i64, vp]
+        L.csa2o_index_topk_pool.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                            i32, vp, i32, vp, vp]
         L.csa2o_sparse_attn.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f64, vp,
                                         i32, vp, vp]
         L.csa2o_swa_attn.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, f64, vp, i32, vp,
@@ -125,6 +129,37 @@ def index_topk(K, max_pages, q_idx, w_idx, k_idx, page_table, seq_id, n_vis, row
     return (out, scores) if want_scores else out
 
 
+def pool_positions(sel_row, n_vis) -> np.ndarray:
+    """Candidate pool of the hierarchical indexer for one row: the union of the aligned
+    8-position blocks that hold the Full layer's selected entries (sel_row, -1 = unused),
+    cut to the n_vis visible entries, ascending.  [summary] Architecture Components,
+    item 3."""
+    sel = _c(sel_row, np.int32)
+    pool = np.empty(max(8 * sel.shape[0], 1), dtype=np.int32)
+    m = lib().csa2o_pool_positions(_p(sel), sel.shape[0], int(n_vis), _p(pool))
+    return pool[:m].copy()
+
+
+def index_topk_pool(K, max_pages, q_idx, w_idx, k_idx, page_table, seq_id, n_vis, sel,
+                    rows=None, want_scores=False):
+    """Reindex scoring + Top-K restricted to the candidate pool built from sel [T, K_sel]
+    (the Full layer's selection).  Returns idx [n_rows, K] (and scores [n_rows,
+    max_pages*64], NaN outside the pool, if want_scores).  [summary] Architecture
+    Components, items 2 and 3."""
+    q_idx = _c(q_idx, np.uint16)
+    T, H_I = q_idx.shape[0], q_idx.shape[1]
+    w_idx, k_idx = _c(w_idx, np.float32), _c(k_idx, np.uint16)
+    pt, sid, nv = _c(page_table, np.int32), _c(seq_id, np.int32), _c(n_vis, np.int32)
+    sel = _c(sel, np.int32)
+    rows = _c(np.arange(T) if rows is None else rows, np.int32)
+    out = np.empty((rows.shape[0], K), dtype=np.int32)
+    scores = (np.full((rows.shape[0], max_pages * PAGE), np.nan) if want_scores else None)
+    lib().csa2o_index_topk_pool(T, H_I, K, max_pages, _p(q_idx), _p(w_idx), _p(k_idx),
+                                _p(pt), _p(sid), _p(nv), _p(sel), sel.shape[1], _p(rows),
+                                rows.shape[0], _p(out), _p(scores) if want_scores else None)
+    return (out, scores) if want_scores else out
+
+
 def sparse_attn(max_pages, q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx,
                 sm_scale=None, rows=None):
     """Global sparse branch.  q bf16 bits [T, H, 576]; planes in physical rows;
@@ -169,7 +204,9 @@ def resolve_sources(modes):
     it reads: KV from the nearest Full layer at or before it, indices from the nearest
     Full or Reindex layer at or before it.  [summary] Architecture Components, item 2
     (Full computes its own main KV, indexer key and Top-K; Reindex reuses the preceding
-    layer's main KV with fresh Top-K; Reuse borrows both from the preceding layer)."""
+    layer's main KV with fresh Top-K; Reuse borrows both from the preceding layer).  A
+    pooled Reindex layer (REINDEX_POOL) is a Reindex layer whose search is the candidate
+    pool of the group's first Full layer (item 3)."""
     if not modes or modes[0] != FULL:
         raise ValueError("the first layer of a group must be Full")
     kv_src, idx_src = [], []
@@ -177,7 +214,7 @@ def resolve_sources(modes):
     for i, m in enumerate(modes):
         if m == FULL:
             last_kv = last_idx = i
-        elif m == REINDEX:
+        elif m in (REINDEX, REINDEX_POOL):
             last_idx = i
         elif m != REUSE:
             raise ValueError(f"unknown mode {m}")
@@ -189,8 +226,9 @@ def resolve_sources(modes):
 def layer_group(layers, K, max_pages, page_table, seq_id, n_vis, swa_start, swa_len,
                 sm_scale=None, sm_scale_swa=None, rows=None):
     """Full / Reindex / Reuse layer group.  `layers` is a list of dicts with 'mode', 'q',
-    'q_swa', 'swa_k', 'swa_v', and for Full/Reindex 'q_idx', 'w_idx', 'k_idx', for Full
-    the planes 'kv_lat', 'kv_scl', 'kv_rope'.  Returns per layer a dict with 'idx'
+    'q_swa', 'swa_k', 'swa_v', and for Full/Reindex/pooled Reindex 'q_idx', 'w_idx',
+    'k_idx', for Full the planes 'kv_lat', 'kv_scl', 'kv_rope'.  Pooled Reindex layers
+    search the pool of layer 0's selection.  Returns per layer a dict with 'idx'
     (the indices it used), 'o', 'lse', 'o_swa', 'lse_swa' for the listed rows."""
     modes = [L["mode"] for L in layers]
     kv_src, idx_src = resolve_sources(modes)
@@ -202,6 +240,10 @@ def layer_group(layers, K, max_pages, page_table, seq_id, n_vis, swa_start, swa_
             # Own scores over all rows the later layers may borrow: compute for all T
             idx_all = index_topk(K, max_pages, L["q_idx"], L["w_idx"], L["k_idx"], page_table,
                                  seq_id, n_vis, rows=np.arange(T))
+        elif L["mode"] == REINDEX_POOL:
+            idx_all = index_topk_pool(K, max_pages, L["q_idx"], L["w_idx"], L["k_idx"],
+                                      page_table, seq_id, n_vis, results[0]["idx_all"],
+                                      rows=np.arange(T))
         else:
             idx_all = results[idx_src[i]]["idx_all"]
         kv = layers[kv_src[i]]

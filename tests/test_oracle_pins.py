@@ -423,7 +423,7 @@ def _group_layers(w, pt, modes, same_q=False, same_indexer=False):
         li = 0 if same_q else i
         L = {"mode": m, "q": w.q(li), "q_swa": w.q_swa(li), "swa_k": w.swa_k(i),
              "swa_v": w.swa_v(i)}
-        if m in (orc.FULL, orc.REINDEX):
+        if m in (orc.FULL, orc.REINDEX, orc.REINDEX_POOL):
             lj = 0 if same_indexer else i
             L.update(q_idx=w.q_idx(lj), w_idx=w.w_idx(lj),
                      k_idx=w.to_physical(lambda b: w.k_idx_seq(b, lj), pt))
@@ -462,6 +462,105 @@ def test_layer_group_reuse_and_reindex_invariants():
     o, lse = orc.sparse_attn(w.P, layers[2]["q"], layers[0]["kv_lat"], layers[0]["kv_scl"],
                              layers[0]["kv_rope"], pt, w.seq_id(), res[1]["idx"])
     np.testing.assert_array_equal(res[2]["o"], o)
+
+
+# ---------------------------------------------------------------- hierarchical pool
+def _pool_golden():
+    cases = []
+    with open(os.path.join(GOLDEN, "pool_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            nv, sel, pool = (part.split() for part in line.split("|"))
+            cases.append((int(nv[0]), np.array([int(v) for v in sel], np.int32),
+                          np.array([int(v) for v in pool], np.int32)))
+    return cases
+
+
+def test_pool_blocks_golden():
+    cases = _pool_golden()
+    assert len(cases) == 7
+    for nv, sel, pool in cases:
+        np.testing.assert_array_equal(orc.pool_positions(sel, nv), pool)
+
+
+def test_pool_size_bound_at_the_pages_sizes():
+    # 2,048 selected entries -> at most 2,048 blocks x 8 = 16,384 positions; exactly that
+    # when every selected entry lies in its own block
+    n_vis, K_sel = 131072, 2048
+    spread = (64 * np.arange(K_sel) + np.arange(K_sel) % 8).astype(np.int32)
+    assert orc.pool_positions(spread, n_vis).size == 16384
+    rng = np.random.default_rng(5)
+    for _ in range(3):
+        sel = np.sort(rng.choice(n_vis, K_sel, replace=False)).astype(np.int32)
+        pool = orc.pool_positions(sel, n_vis)
+        assert pool.size <= 16384 and pool.size % 8 == 0
+        assert np.all(np.diff(pool) > 0) and np.all(np.isin(sel, pool))
+
+
+def _pool_case(seed=41, K=64, E=512):
+    w = _small_workload(K=K, E=E, seed=seed)
+    pt = w.page_table()
+    _, _, _, kidx = _planes(w, pt)
+    return w, pt, kidx
+
+
+def test_pool_topk_brute_force():
+    # selection restricted to the pool: the K best pool positions by (score desc, position
+    # asc), ascending, -1 padded; including a pool smaller than K
+    w, pt, kidx = _pool_case()
+    _, s = orc.index_topk(w.K, w.P, w.q_idx(), w.w_idx(), kidx, pt, w.seq_id(), w.n_vis(),
+                          want_scores=True)
+    rng = np.random.default_rng(9)
+    nv = w.n_vis()
+    for K_sel in (32, 3):
+        sel = np.full((w.T, K_sel), -1, np.int32)
+        for t in range(w.T):
+            m = min(K_sel, int(nv[t]))
+            sel[t, :m] = np.sort(rng.choice(int(nv[t]), m, replace=False))
+        got = orc.index_topk_pool(w.K, w.P, w.q_idx(), w.w_idx(), kidx, pt, w.seq_id(), nv,
+                                  sel)
+        for t in range(w.T):
+            pool = np.array(sorted({8 * (j // 8) + o for j in sel[t] if j >= 0
+                                    for o in range(8) if 8 * (j // 8) + o < nv[t]}))
+            ref = np.full(w.K, -1, np.int32)
+            pick = pool[_lexsort_topk(s[t, pool], w.K)[: min(w.K, pool.size)]]
+            ref[: pick.size] = np.sort(pick)
+            np.testing.assert_array_equal(got[t], ref)
+
+
+def test_pool_covering_everything_equals_full_search():
+    w, pt, kidx = _pool_case()
+    nv = w.n_vis()
+    n_blocks = (int(nv.max()) + 7) // 8
+    sel = np.tile(8 * np.arange(n_blocks, dtype=np.int32), (w.T, 1))
+    sel[sel >= nv[:, None]] = -1
+    sel = np.sort(np.where(sel < 0, np.iinfo(np.int32).max, sel), axis=1)
+    sel[sel == np.iinfo(np.int32).max] = -1
+    a = orc.index_topk(w.K, w.P, w.q_idx(), w.w_idx(), kidx, pt, w.seq_id(), nv)
+    b = orc.index_topk_pool(w.K, w.P, w.q_idx(), w.w_idx(), kidx, pt, w.seq_id(), nv, sel)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_layer_group_pooled_reindex():
+    w = _small_workload()
+    pt = w.page_table()
+    args = (w.K, w.P, pt, w.seq_id(), w.n_vis(), w.swa_start(), w.swa_len())
+    # the same indexer as the Full layer: the Full selection lies inside its own pool, so
+    # the pooled search finds it again
+    layers = _group_layers(w, pt, [orc.FULL, orc.REINDEX_POOL, orc.REUSE], same_indexer=True)
+    res = orc.layer_group(layers, *args)
+    np.testing.assert_array_equal(res[1]["idx"], res[0]["idx"])
+    # its own indexer: every pick lies in the pool of the Full selection; Reuse borrows it
+    layers = _group_layers(w, pt, [orc.FULL, orc.REINDEX_POOL, orc.REUSE])
+    res = orc.layer_group(layers, *args)
+    assert not np.array_equal(res[1]["idx"], res[0]["idx"])
+    np.testing.assert_array_equal(res[2]["idx"], res[1]["idx"])
+    for t in range(w.T):
+        pool = orc.pool_positions(res[0]["idx"][t], w.n_vis()[t])
+        picks = res[1]["idx"][t]
+        assert np.all(np.isin(picks[picks >= 0], pool))
 
 
 # ---------------------------------------------------------------- footprint
