@@ -19,6 +19,7 @@ timed on a sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -78,7 +79,7 @@ class Inputs:
         for li, m in enumerate(w.modes):
             L = {"mode": m, "q": b16(w.q(li)), "q_swa": b16(w.q_swa(li)),
                  "swa_k": b16(w.swa_k(li)), "swa_v": b16(w.swa_v(li))}
-            if m in (0, 1):
+            if m in (0, 1, 3):
                 L["q_idx"], L["w_idx"] = b16(w.q_idx(li)), t(w.w_idx(li))
                 kidx = torch.empty((w.n_pages, rows_per_page, 64), dtype=torch.bfloat16,
                                    device=dev)
@@ -117,14 +118,27 @@ class Inputs:
 
 
 # ------------------------------------------------------------------ algorithmic bytes
-def algorithmic_bytes(w):
+def pool_sizes(w, sel):
+    """Entries in each row's candidate pool: the aligned 8-entry blocks holding the row's
+    selected entries (sel [T, K], -1 unused), cut to the visible entries."""
+    import numpy as np
+    nv = w.n_vis().astype(np.int64)
+    out = np.zeros(w.T, np.int64)
+    for t in range(w.T):
+        blk = np.unique(sel[t][sel[t] >= 0] // 8)
+        out[t] = int(np.minimum(8, nv[t] - 8 * blk).sum())
+    return out
+
+
+def algorithmic_bytes(w, pools=None):
     """Bytes each kernel class must move per step (what the method itself reads/writes once,
     not what an implementation re-reads), returned per kernel name of the library:
     per sequence, its indexer keys up to the largest visibility of its rows (128 B each),
     its distinct selected entries (at most min(E, the rows' selections), 400 B each) and the
     union of its rows' SWA windows (H_kv x 128 x 2 x 2 B per token); per row, queries, the
     Top-K output and fp32 outputs.  With one row per sequence (decode) this is the per-row
-    scan n_vis x 128 B, gather K x 400 B and window n_win x H_kv x 512 B."""
+    scan n_vis x 128 B, gather K x 400 B and window n_win x H_kv x 512 B.  A pooled Reindex
+    layer reads each row's pool (pools[t] entries, 128 B each) and its K selections."""
     import numpy as np
     nv = w.n_vis().astype(np.int64)
     sel = np.minimum(nv, w.K)
@@ -141,34 +155,41 @@ def algorithmic_bytes(w):
             tok[s0:s0 + l] = True
         window += int(tok.sum())
     n_idx_layers = sum(1 for m in w.modes if m in (0, 1))
+    n_pool_layers = sum(1 for m in w.modes if m == 3)
     n_layers = len(w.modes)
     idx_score = n_idx_layers * (keys * 128 + w.T * w.H_I * (64 * 2 + 4))
     topk = n_idx_layers * w.T * w.K * 4
     attn = n_layers * (gathered * 400 + w.T * w.H * (576 * 2 + 512 * 4 + 4))
     swa = n_layers * (window * w.H_kv * 128 * 2 * 2 + w.T * w.H * (128 * 2 + 128 * 4 + 4))
-    return {"idx_score": idx_score, "topk": topk, "sparse_attn": attn, "swa": swa}
+    out = {"idx_score": idx_score, "topk": topk, "sparse_attn": attn, "swa": swa}
+    if n_pool_layers:
+        out["idx_pool_score"] = n_pool_layers * (int(pools.sum()) * 128 + w.T * w.K * 4 +
+                                                 w.T * w.H_I * (64 * 2 + 4))
+        out["topk_pool"] = n_pool_layers * w.T * w.K * 4
+    return out
 
 
-def algorithmic_flops(w):
-    """Matrix-math work per step: indexer 2 H_I 64 n_vis, attention 2 H sel (576 + 512),
-    SWA 2 H len 128 x 2 per row (the fp8 hi/lo query split is not counted)."""
+def algorithmic_flops(w, pools=None):
+    """Matrix-math work per step: indexer 2 H_I 64 n_vis (pool entries for a pooled
+    layer), attention 2 H sel (576 + 512), SWA 2 H len 128 x 2 per row (the fp8 hi/lo query
+    split is not counted)."""
     import numpy as np
     nv = w.n_vis().astype(np.int64)
     sel = np.minimum(nv, w.K)
     win = w.swa_len().astype(np.int64)
     n_idx_layers = sum(1 for m in w.modes if m in (0, 1))
+    n_pool_layers = sum(1 for m in w.modes if m == 3)
     n_layers = len(w.modes)
     return (n_idx_layers * 2 * w.H_I * 64 * int(nv.sum()) +
+            n_pool_layers * 2 * w.H_I * 64 * int(pools.sum() if pools is not None else 0) +
             n_layers * 2 * w.H * 1088 * int(sel.sum()) +
             n_layers * 2 * w.H * 256 * int(win.sum()))
 
 
-def measure_extra(workload, dev, steps, warmup, flush_mb):
-    """Whole-step time and per-kernel times of another named workload (smaller bench)."""
+def measure_extra(w, dev, steps, warmup, flush_mb):
+    """Whole-step time and per-kernel times of another workload (smaller bench)."""
     import torch
-    import synth
     from fp4_compressed_sparse_amd import csa2
-    w = synth.workload(workload)
     inp = Inputs(w, dev)
     for _ in range(warmup):
         inp.step()
@@ -189,10 +210,12 @@ def measure_extra(workload, dev, steps, warmup, flush_mb):
     torch.cuda.synchronize()
     csa2.timing_enable(False)
     kt = csa2.timing_read()
-    algo = algorithmic_bytes(w)
-    flops = algorithmic_flops(w)
+    pools = (pool_sizes(w, inp.layers[0]["idx_out"].cpu().numpy()) if 3 in w.modes else None)
+    algo = algorithmic_bytes(w, pools)
+    flops = algorithmic_flops(w, pools)
     step_bytes = sum(algo.values())
     out = {"workload": w.name, "query_rows": w.T, "entries_per_seq": w.E, "top_k": w.K,
+           "layers": [["full", "reindex", "reuse", "reindex_pool"][m] for m in w.modes],
            "steps": steps, "ms_per_step": round(ms, 4),
            "query_tokens_per_s": round(w.T / (ms * 1e-3), 1),
            "step_algo_bytes": step_bytes,
@@ -203,6 +226,12 @@ def measure_extra(workload, dev, steps, warmup, flush_mb):
            "step_mfma_frac_bf16": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "kernels": {k: {"launches": n, "avg_us": round(t * 1e3 / n, 3)}
                        for k, (n, t) in kt.items()}}
+    for k, v in out["kernels"].items():
+        if k in algo and k not in ("topk", "topk_pool"):
+            v["algo_bytes"] = algo[k] / (v["launches"] / steps)
+            v["gbs"] = round(v["algo_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1)
+    if pools is not None:
+        out["pool_entries_per_row"] = round(float(pools.mean()), 1)
     del inp
     torch.cuda.empty_cache()
     return out
@@ -376,9 +405,13 @@ def main():
     }
     if not args.no_extra and not args.kernel_pass_only:
         result["extra"] = []
-        for wl, steps in ((4, 20), (5, 3)):
-            print(f"[bench] extra workload {wl}", file=sys.stderr, flush=True)
-            result["extra"].append(measure_extra(wl, dev, steps, 2, args.flush_mb))
+        w3 = synth.workload(3)
+        w3p = dataclasses.replace(w3, name=w3.name.replace("reindex", "reindexpool"),
+                                  modes=[0, 3, 2])
+        for wx, steps in ((synth.workload(4), 20), (synth.workload(5), 3), (w3, 10),
+                          (w3p, 10)):
+            print(f"[bench] extra workload {wx.name}", file=sys.stderr, flush=True)
+            result["extra"].append(measure_extra(wx, dev, steps, 2, args.flush_mb))
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, w.T))

@@ -16,8 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 D_LAT, D_ROPE, D_Q, D_IDX, D_SWA, PAGE = 512, 64, 576, 64, 128, 64
-FULL, REINDEX, REUSE = 0, 1, 2
-OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP = 1, 2, 3
+FULL, REINDEX, REUSE, REINDEX_POOL = 0, 1, 2, 3
+OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEX_TOPK_POOL = 1, 2, 3, 4
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_NULL", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_ALIGN",
           4: "CSA2_ERR_MODE", 5: "CSA2_ERR_WORKSPACE", 6: "CSA2_ERR_UNSUPPORTED",
           7: "CSA2_ERR_HIP"}
@@ -31,6 +31,10 @@ class IndexArgs(ctypes.Structure):
     _fields_ = [("T", _i32), ("B", _i32), ("H_I", _i32), ("K", _i32), ("max_pages", _i32),
                 ("n_pages", _i32), ("q_idx", _vp), ("w_idx", _vp), ("k_idx", _vp),
                 ("page_table", _vp), ("seq_id", _vp), ("n_vis", _vp), ("idx_out", _vp)]
+
+
+class PoolArgs(ctypes.Structure):
+    _fields_ = [("ix", IndexArgs), ("sel", _vp), ("K_sel", _i32)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -56,7 +60,7 @@ class GroupArgs(ctypes.Structure):
                 ("swa_len", _vp), ("sm_scale", _f32), ("sm_scale_swa", _f32)]
 
 
-EXPORTS = ["csa2_index_topk", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize",
+EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize",
            "csa2_workspace_bytes", "csa2_last_error", "csa2_status_string", "csa2_abi_version",
            "csa2_timing_enable", "csa2_timing_read"]
 
@@ -67,6 +71,8 @@ def _load():
     L = ctypes.CDLL(LIB_PATH)
     L.csa2_index_topk.restype = _i32
     L.csa2_index_topk.argtypes = [ctypes.POINTER(IndexArgs), _vp, ctypes.c_size_t, _vp]
+    L.csa2_index_topk_pool.restype = _i32
+    L.csa2_index_topk_pool.argtypes = [ctypes.POINTER(PoolArgs), _vp, ctypes.c_size_t, _vp]
     L.csa2_sparse_attn_fp4.restype = _i32
     L.csa2_sparse_attn_fp4.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t, _vp]
     L.csa2_layer_group.restype = _i32
@@ -146,6 +152,23 @@ def index_topk(q_idx, w_idx, k_idx, page_table, seq_id, n_vis, K, idx_out=None, 
     ws = workspace if workspace is not None else _ws(need, q_idx.device)
     _check(lib.csa2_index_topk(ctypes.byref(a), _p(ws), need if workspace is None else
                                ws.numel() * ws.element_size(), _stream(stream)))
+    return idx_out
+
+
+def index_topk_pool(q_idx, w_idx, k_idx, page_table, seq_id, n_vis, K, sel, idx_out=None,
+                    stream=None, workspace=None):
+    """Hierarchical-indexer search: scoring + Top-K over the candidate pool of sel int32
+    [T, K_sel] (ascending entries, -1 tail; e.g. a Full layer's selection).  Other
+    arguments as index_topk.  Returns idx int32 [T, K]."""
+    T = q_idx.shape[0]
+    if idx_out is None:
+        idx_out = torch.empty((T, K), dtype=torch.int32, device=q_idx.device)
+    a = PoolArgs(index_args(q_idx, w_idx, k_idx, page_table, seq_id, n_vis, K, idx_out),
+                 _p(sel), sel.shape[1])
+    need = lib.csa2_workspace_bytes(OP_INDEX_TOPK_POOL, ctypes.byref(a))
+    ws = workspace if workspace is not None else _ws(need, q_idx.device)
+    _check(lib.csa2_index_topk_pool(ctypes.byref(a), _p(ws), need if workspace is None else
+                                    ws.numel() * ws.element_size(), _stream(stream)))
     return idx_out
 
 

@@ -3,6 +3,7 @@
 // so every error path is reachable without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -272,6 +273,69 @@ csa2_status run_index(const csa2_index_args* a, void* ws, hipStream_t s) {
   return run_index_split(a, ws, s, [] { return CSA2_OK; });
 }
 
+// ---------------------------------------------------------------- pooled search
+// Keys [T, pool_key_stride(K_sel)]: 8 slots per selection.
+size_t pool_ws_bytes(int32_t T, int32_t K_sel) {
+  return round_up((size_t)T * (size_t)pool_key_stride(K_sel) * sizeof(uint32_t));
+}
+
+csa2_status validate_pool(const csa2_pool_args* a) {
+  const char* fn = "csa2_index_topk_pool";
+  if (!a) return fail(CSA2_ERR_NULL, "%s: args is NULL", fn);
+  if (a->K_sel < 1 || a->K_sel > kPoolMaxSel)
+    return fail(CSA2_ERR_SHAPE, "%s: K_sel=%d outside [1, %d]", fn, a->K_sel, kPoolMaxSel);
+  if (a->ix.K > kPoolMaxK)
+    return fail(CSA2_ERR_SHAPE, "%s: K=%d above %d", fn, a->ix.K, kPoolMaxK);
+  csa2_status st = validate_index(&a->ix);
+  if (st) {
+    std::string m = g_err;
+    return fail(st, "%s: %s", fn, m.c_str());
+  }
+  if (a->ix.T > 0) REQ(a->sel, "sel");
+  return CSA2_OK;
+}
+
+// Scoring of the pool of sel [T, K_sel], then its Top-K; `between` runs after the scoring
+// launch.
+template <class Between>
+csa2_status run_index_pool_split(const csa2_index_args* a, const int32_t* sel, int K_sel,
+                                 void* ws, hipStream_t s, Between&& between) {
+  if (a->T == 0) return between();
+  IdxScoreParams sp;
+  sp.T = a->T;
+  sp.H_I = a->H_I;
+  sp.max_pages = a->max_pages;
+  sp.chunks = (K_sel + kPoolSelPerBlock - 1) / kPoolSelPerBlock;
+  sp.key_stride = pool_key_stride(K_sel);
+  sp.q_idx = static_cast<const uint16_t*>(a->q_idx);
+  sp.w_idx = a->w_idx;
+  sp.k_idx = static_cast<const uint16_t*>(a->k_idx);
+  sp.page_table = a->page_table;
+  sp.seq_id = a->seq_id;
+  sp.n_vis = a->n_vis;
+  sp.keys = static_cast<uint32_t*>(ws);
+  sp.clear = nullptr;
+  sp.clear_words = 0;
+  sp.trash = nullptr;
+  sp.pool_sel = sel;
+  sp.pool_K = K_sel;
+  csa2_status st = timed("idx_pool_score", s, [&] { return launch_idx_score(sp, s); });
+  if (st) return st;
+  st = between();
+  if (st) return st;
+  TopkParams tp;
+  tp.T = a->T;
+  tp.K = a->K;
+  tp.key_stride = sp.key_stride;
+  tp.keys = sp.keys;
+  tp.n_vis = a->n_vis;
+  tp.idx_out = a->idx_out;
+  tp.ck_hist = tp.ck_counts = tp.ck_sel = nullptr;
+  tp.pool_sel = sel;
+  tp.pool_K = K_sel;
+  return timed("topk_pool", s, [&] { return launch_topk(tp, s); });
+}
+
 // ---------------------------------------------------------------- attention
 csa2_status validate_attn(const csa2_attn_args* a) {
   const char* fn = "csa2_sparse_attn_fp4";
@@ -420,8 +484,12 @@ csa2_status validate_group(const csa2_layer_desc* L, int32_t n_layers, const csa
   for (int i = 0; i < n_layers; ++i) {
     const csa2_layer_desc& d = L[i];
     char what[96];
-    if (d.mode != CSA2_FULL && d.mode != CSA2_REINDEX && d.mode != CSA2_REUSE)
+    if (d.mode != CSA2_FULL && d.mode != CSA2_REINDEX && d.mode != CSA2_REUSE &&
+        d.mode != CSA2_REINDEX_POOL)
       return fail(CSA2_ERR_MODE, "%s: layer %d has unknown mode %d", fn, i, d.mode);
+    if (d.mode == CSA2_REINDEX_POOL && g->K > kPoolMaxSel)
+      return fail(CSA2_ERR_SHAPE, "%s: layer %d searches a pool, which needs K <= %d (K=%d)",
+                  fn, i, kPoolMaxSel, g->K);
     const bool own_idx = d.mode != CSA2_REUSE, own_kv = d.mode == CSA2_FULL;
 #define LAYER_REQ(field)                                            \
     do {                                                            \
@@ -512,6 +580,17 @@ csa2_status validate_group(const csa2_layer_desc* L, int32_t n_layers, const csa
 
 extern "C" {
 
+csa2_status csa2_index_topk_pool(const csa2_pool_args* a, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  csa2_status st = validate_pool(a);
+  if (st) return st;
+  st = check_ws("csa2_index_topk_pool", ws, ws_bytes,
+                a->ix.T ? pool_ws_bytes(a->ix.T, a->K_sel) : 0);
+  if (st) return st;
+  return run_index_pool_split(&a->ix, a->sel, a->K_sel, ws, static_cast<hipStream_t>(stream),
+                              [] { return CSA2_OK; });
+}
+
 csa2_status csa2_index_topk(const csa2_index_args* a, void* ws, size_t ws_bytes, void* stream) {
   csa2_status st = validate_index(a);
   if (st) return st;
@@ -564,7 +643,10 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
       ia.w_idx = L[i].w_idx;
       ia.k_idx = L[i].k_idx;
       ia.idx_out = L[i].idx_out;
-      st = run_index_split(&ia, ws, s, [&] { return swa_now(i); });
+      if (L[i].mode == CSA2_REINDEX_POOL)   // the pool of layer 0's (Full) selection
+        st = run_index_pool_split(&ia, L[0].idx_out, g->K, ws, s, [&] { return swa_now(i); });
+      else
+        st = run_index_split(&ia, ws, s, [&] { return swa_now(i); });
     } else {
       st = swa_now(i);
     }
@@ -614,7 +696,13 @@ size_t csa2_workspace_bytes(int32_t op, const void* args) {
       if (g->T <= 0 || g->max_pages <= 0 || g->K <= 0 || g->H <= 0) return 0;
       const size_t a = index_ws_bytes(g->T, g->max_pages);
       const size_t b = attn_ws_bytes(g->T, g->H, g->K);
-      return a > b ? a : b;
+      const size_t c = g->K <= kPoolMaxSel ? pool_ws_bytes(g->T, g->K) : 0;   // pooled layers
+      return std::max(a, std::max(b, c));
+    }
+    case CSA2_OP_INDEX_TOPK_POOL: {
+      const csa2_pool_args* a = static_cast<const csa2_pool_args*>(args);
+      if (a->ix.T <= 0 || a->K_sel <= 0) return 0;
+      return pool_ws_bytes(a->ix.T, a->K_sel);
     }
     default:
       return 0;

@@ -38,6 +38,11 @@ struct IdxScoreParams {
   uint32_t* clear;                     // optional: words zeroed by the first blocks
   int clear_words;
   uint32_t* trash;                     // row-tiled scoring: 1 KB that masked stores hit
+  // pooled scoring (hierarchical indexer): score the 8-entry blocks of the selections
+  // pool_sel [T, pool_K] instead of every visible entry; key slot 8i + o = entry o of the
+  // block of selection i (chunks then counts workgroups of kPoolSelPerBlock selections)
+  const int32_t* pool_sel = nullptr;
+  int pool_K = 0;
 };
 
 struct TopkParams {
@@ -51,6 +56,10 @@ struct TopkParams {
   uint32_t* ck_hist;                   // [T, kCkHistWords]
   uint32_t* ck_counts;                 // [T, n_chunks, 2]
   uint32_t* ck_sel;                    // [T, 8]
+  // pooled rows: keys are the 8 * pool_K slots of the pooled scoring; the output maps
+  // slot 8i + o to entry 8 * (pool_sel[t, i] / 8) + o
+  const int32_t* pool_sel = nullptr;
+  int pool_K = 0;
 };
 
 // Top-K over few long rows runs chunked: rows longer than 65536 keys with at most
@@ -114,6 +123,12 @@ constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-
 static_assert(kCkMaxRows < kIdxGemmMinRows, "row-tiled scoring reuses the chunked Top-K area");
 constexpr int kSwaTileMinRows = 256;   // from this many rows, SWA runs row-tiled on MFMA
 constexpr int kTopkThreads = 1024;
+constexpr int kPoolBlock = 8;          // entries per pool block (aligned)
+constexpr int kPoolMaxSel = 2048;      // selections that may seed a pool
+constexpr int kPoolMaxK = 8192;        // Top-K size over a pool (staged in LDS)
+constexpr int kPoolSelPerWave = 32;    // selections per wave of the pooled scoring
+constexpr int kPoolSelPerBlock = 4 * kPoolSelPerWave;   // per workgroup (4 waves)
+inline int64_t pool_key_stride(int pool_K) { return ((int64_t)kPoolBlock * pool_K + 63) / 64 * 64; }
 
 // Split plan of the attention launch: `splits` workgroups per row, each covering
 // `per_split` (a multiple of 32, <= 2048) consecutive index slots.

@@ -46,9 +46,8 @@ __device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, i
 // (v_permlane32_swap pairs groups g and g+2, v_permlane16_swap groups g and g+1) leaves
 // lane (g, n) with the whole sum of entry 16g + n, so the page's 64 keys go out in one
 // store.
-__device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa1,
-                                               const float (&w)[4], const u32x4 (&kb)[8],
-                                               int valid, int n, int g, uint32_t* keys) {
+__device__ __forceinline__ float idx_score_64(const u32x4& qa0, const u32x4& qa1,
+                                              const float (&w)[4], const u32x4 (&kb)[8]) {
   float su[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -68,7 +67,13 @@ __device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa
   const float hb = __uint_as_float(b[0]) + __uint_as_float(b[1]);
   // then each row g keeps group u = g from rows g and g ^ 1
   const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(ha), __float_as_uint(hb), false, false);
-  const float tot = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+__device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa1,
+                                               const float (&w)[4], const u32x4 (&kb)[8],
+                                               int valid, int n, int g, uint32_t* keys) {
+  const float tot = idx_score_64(qa0, qa1, w, kb);
   if (16 * g + n < valid) keys[16 * g + n] = float_key(tot);
 }
 
@@ -118,6 +123,87 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
     if (pi + 2 < npages) idx_load_page(p.k_idx, __shfl(my_page, pi + 2), valid_in(pi + 2), n, g, bufA);
     if (pi + 1 < npages)
       idx_score_page(qa0, qa1, w, bufB, valid_in(pi + 1), n, g, keys + kPage * (pi + 1));
+  }
+}
+
+// ---------------------------------------------------------------- pooled scoring
+// Hierarchical indexer ([summary] Architecture Components, item 3): a Reindex layer scores
+// only the candidate pool, the aligned 8-entry blocks that hold the selected entries of
+// the Full layer.  The selections of a row are ascending with -1 at the tail, so entries
+// sharing a block are neighbours: selection i owns key slots 8i .. 8i+7 of the row, which
+// hold the block's scores when i is the first selection in its block and 0 (no candidate)
+// otherwise.  Slot order is entry order, so the Top-K's lowest-slot tie-break keeps the
+// lowest entry.  Each wave takes kPoolSelPerWave consecutive selections, one per lane
+// (block row and visible count resolved once), and scores them in groups of 64 slots; a
+// group is scored like a 64-entry page whose rows come 8 at a time from 8 lanes' blocks.
+// The next group's 8 KB of keys is in flight while the current one is scored.
+__global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
+  const int t = blockIdx.x / p.chunks;
+  const int c = blockIdx.x - t * p.chunks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i0 = c * kPoolSelPerBlock + wave * kPoolSelPerWave;   // first of this wave
+  if (i0 >= p.pool_K) return;                        // wave-uniform; no block barriers
+  const int nv = p.n_vis[t];
+  const int b = p.seq_id[t];
+  const int n = lane & 15, g = lane >> 4;
+  const int32_t* sel = p.pool_sel + (int64_t)t * p.pool_K;
+  const int i = i0 + lane;
+  const int j = (lane < kPoolSelPerWave && i < p.pool_K) ? sel[i] : -1;
+  int prev = __shfl_up(j, 1);
+  if (lane == 0) prev = (i0 > 0) ? sel[i0 - 1] : -1;
+  const bool first = j >= 0 && j < nv && (prev < 0 || (prev >> 3) != (j >> 3));
+  int brow = 0, bvis = 0;        // physical row of the block's entry 0; its visible entries
+  if (first) {
+    const int blk = j >> 3;
+    brow = p.page_table[(int64_t)b * p.max_pages + (blk >> 3)] * kPage + kPoolBlock * (blk & 7);
+    bvis = min(kPoolBlock, nv - kPoolBlock * blk);
+  }
+
+  u32x4 qa0 = {0u, 0u, 0u, 0u}, qa1 = {0u, 0u, 0u, 0u};
+  if (n < p.H_I) {
+    const uint16_t* qp = p.q_idx + ((int64_t)t * p.H_I + n) * kDidx + 16 * g;
+    qa0 = ld_global_16(qp);
+    qa1 = ld_global_16(qp + 8);
+  }
+  float w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int h = 4 * g + q;
+    w[q] = (h < p.H_I) ? p.w_idx[(int64_t)t * p.H_I + h] : 0.f;
+  }
+  uint32_t* keys = p.keys + (int64_t)t * p.key_stride + kPoolBlock * (int64_t)i0;
+  const int ngroups = min(kPoolSelPerWave / 8, (p.pool_K - i0 + 7) / 8);
+
+  // group v, MFMA column block u: lane (g, n) loads entry n & 7 of the block of
+  // selection 8v + 2u + (n >> 3) of this wave
+  auto load_group = [&](int v, u32x4 (&kb)[8]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int src = 8 * v + 2 * u + (n >> 3);
+      const int row = __shfl(brow, src) + (n & 7);
+      if ((n & 7) < __shfl(bvis, src)) {
+        const uint16_t* kp = p.k_idx + (int64_t)row * kDidx + 16 * g;
+        kb[2 * u] = ld_global_16(kp);
+        kb[2 * u + 1] = ld_global_16(kp + 8);
+      } else {
+        kb[2 * u] = u32x4{0u, 0u, 0u, 0u};
+        kb[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // lane (g, n) holds slot 16g + n of the group: entry n & 7 of selection 8v + 2g + (n >> 3)
+  auto score_group = [&](int v, const u32x4 (&kb)[8]) {
+    const float tot = idx_score_64(qa0, qa1, w, kb);
+    const bool ok = (n & 7) < __shfl(bvis, 8 * v + 2 * g + (n >> 3));
+    keys[64 * v + 16 * g + n] = ok ? float_key(tot) : 0u;
+  };
+  u32x4 bufA[8], bufB[8];
+  load_group(0, bufA);
+  for (int v = 0; v < ngroups; v += 2) {
+    if (v + 1 < ngroups) load_group(v + 1, bufB);
+    score_group(v, bufA);
+    if (v + 2 < ngroups) load_group(v + 2, bufA);
+    if (v + 1 < ngroups) score_group(v + 1, bufB);
   }
 }
 
@@ -274,21 +360,27 @@ __device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_
 
 // Rows of at most 4096 * NR keys: thread t keeps keys [4NR t, 4NR (t+1)) in registers,
 // so the row is read from memory once and one block-wide scan orders the output.
-template <int NR>
+// POOL: the row is the 8 * pool_K key slots of the pooled scoring (0 = no candidate); when
+// at most K slots hold a candidate all of them are taken, and slots map back to entries.
+template <int NR, bool POOL>
 __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   constexpr int KPT = 4 * NR;                        // keys per thread
   __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
   __shared__ uint32_t s_digit, s_rem;
   __shared__ uint32_t s_wtot[kTopkWaves];
   const int t = blockIdx.x;
-  const int n = p.n_vis[t];
+  const int n = POOL ? kPoolBlock * p.pool_K : p.n_vis[t];
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (n <= K) {                       // every visible entry is selected
+  if (!POOL && n <= K) {              // every visible entry is selected
     for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
     return;
   }
+  const int32_t* psel = POOL ? p.pool_sel + (int64_t)t * p.pool_K : nullptr;
+  auto entry_of = [&](int slot) {
+    return POOL ? kPoolBlock * (psel[slot >> 3] >> 3) + (slot & 7) : slot;
+  };
   // keys below n are >= float_key(-inf) > 0; 0 marks the slots past n
   const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
   const int i0 = KPT * tid;
@@ -320,22 +412,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) kmax = max(kmax, s_wtot[w]);
-  uint32_t ctop = 0u;
+  uint32_t ctop = 0u, cnz = 0u;
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) ctop += (kv[e] != 0u && (kv[e] >> 28) == (kmax >> 28));
-  uint32_t ctot;
+  for (int e = 0; e < KPT; ++e) {
+    ctop += (kv[e] != 0u && (kv[e] >> 28) == (kmax >> 28));
+    cnz += (kv[e] != 0u);
+  }
+  uint32_t ctot, nzt = 0u;
   (void)wave_prefix_small<7>(ctop, ctot);
+  if (POOL) (void)wave_prefix_small<7>(cnz, nzt);
   __syncthreads();                                   // everyone has read the maxima
-  if (lane == 0) s_wtot[wave] = ctot;
+  if (lane == 0) s_wtot[wave] = ctot | (nzt << 16);  // each part <= 64 * 64
   __syncthreads();
-  ctop = 0u;
+  uint32_t wsum = 0u;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) ctop += s_wtot[w];
+  for (int w = 0; w < kTopkWaves; ++w) wsum += s_wtot[w];
+  const uint32_t n_cand = POOL ? (wsum >> 16) : 0u;  // POOL: slots holding a candidate
+  ctop = POOL ? (wsum & 0xffffu) : wsum;             // (POOL rows hold <= 16384 slots)
+  const bool take_all = POOL && n_cand <= (uint32_t)K;
   const bool narrow = ctop >= (uint32_t)K;
-  uint32_t prefix = narrow ? (kmax & 0xf0000000u) : 0u, remaining = (uint32_t)K;
+  // take_all: tau = 0 with no ties to keep selects every candidate
+  uint32_t prefix = (narrow && !take_all) ? (kmax & 0xf0000000u) : 0u;
+  uint32_t remaining = take_all ? 0u : (uint32_t)K;
   __syncthreads();                                   // s_wtot is reused below
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
+    if (take_all) break;                             // block-uniform
     const int shift = narrow ? (pass == 0 ? 16 : (pass == 1 ? 4 : 0)) : (pass == 0 ? 20 : (pass == 1 ? 8 : 0));
     const int width = narrow ? (pass == 2 ? 4 : 12) : (pass == 2 ? 8 : 12);
     const uint32_t pmask = ~((2u << (shift + width - 1)) - 1u);   // bits above the digit
@@ -385,6 +487,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   uint32_t pos = gtb + min(eqb, need_eq);
   // Stage the ordered output in the (now free) histogram space when it fits, so that the
   // row goes out in coalesced stores; else write it in place.
+  const int n_out = take_all ? (int)n_cand : K;      // the rest is -1 padding
   if (K <= 2 * kHistBins) {
     int32_t* s_out = reinterpret_cast<int32_t*>(&hist[0][0]);
     while (sel) {
@@ -392,12 +495,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
       sel &= sel - 1;
     }
     __syncthreads();
-    for (int i = tid; i < K; i += kTopkThreads) out[i] = s_out[i];
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n_out) ? entry_of(s_out[i]) : -1;
   } else {
     while (sel) {
-      out[pos++] = i0 + (int)__builtin_ctzll(sel);
+      out[pos++] = entry_of(i0 + (int)__builtin_ctzll(sel));
       sel &= sel - 1;
     }
+    for (int i = n_out + tid; i < K; i += kTopkThreads) out[i] = -1;
   }
 }
 
@@ -938,7 +1042,7 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
 }
 
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
-  if (p.T >= kIdxGemmMinRows) {
+  if (p.T >= kIdxGemmMinRows && !p.pool_sel) {
     const int64_t nch = (p.key_stride + kGemmChunk - 1) / kGemmChunk;
     const int hp = p.H_I <= 4 ? 4 : (p.H_I <= 8 ? 8 : 16);
     const int rt = 4 * 8 * (16 / hp);                 // rows per workgroup
@@ -949,7 +1053,8 @@ hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   const int64_t blocks = (int64_t)p.T * p.chunks;
-  CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  if (p.pool_sel) CSA2_LAUNCH(idx_pool_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  else CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   return hipGetLastError();
 }
 
@@ -970,13 +1075,21 @@ hipError_t launch_topk_chunked(const TopkParams& p, int pass, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.T), block(kTopkThreads);
+  if (p.pool_sel) {                                  // at most 8 * kPoolMaxSel slots
+    const int slots = kPoolBlock * p.pool_K;
+    if (slots <= 4 * kTopkThreads) CSA2_LAUNCH((topk_reg_kernel<1, true>), grid, block, s, p);
+    else if (slots <= 8 * kTopkThreads) CSA2_LAUNCH((topk_reg_kernel<2, true>), grid, block, s, p);
+    else if (slots <= 16 * kTopkThreads) CSA2_LAUNCH((topk_reg_kernel<4, true>), grid, block, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   // key_stride bounds every row's n_vis; pick the register-resident variant that holds it
   const int64_t nr = (p.key_stride + 4 * kTopkThreads - 1) / (4 * kTopkThreads);
-  const dim3 grid((unsigned)p.T), block(kTopkThreads);
-  if (nr <= 2) CSA2_LAUNCH(topk_reg_kernel<2>, grid, block, s, p);
-  else if (nr <= 4) CSA2_LAUNCH(topk_reg_kernel<4>, grid, block, s, p);
-  else if (nr <= 8) CSA2_LAUNCH(topk_reg_kernel<8>, grid, block, s, p);
-  else if (nr <= 16) CSA2_LAUNCH(topk_reg_kernel<16>, grid, block, s, p);
+  if (nr <= 2) CSA2_LAUNCH((topk_reg_kernel<2, false>), grid, block, s, p);
+  else if (nr <= 4) CSA2_LAUNCH((topk_reg_kernel<4, false>), grid, block, s, p);
+  else if (nr <= 8) CSA2_LAUNCH((topk_reg_kernel<8, false>), grid, block, s, p);
+  else if (nr <= 16) CSA2_LAUNCH((topk_reg_kernel<16, false>), grid, block, s, p);
   else if (!topk_chunked(p.T, p.key_stride)) CSA2_LAUNCH(topk_stream_kernel, grid, block, s, p);
   else return hipErrorInvalidValue;                  // chunked rows go through launch_topk_chunked
   return hipGetLastError();

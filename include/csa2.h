@@ -70,10 +70,23 @@ typedef enum {
   CSA2_ERR_HIP = 7          /* a HIP call failed; csa2_last_error has HIP's message */
 } csa2_status;
 
-typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+typedef enum {
+  CSA2_FULL = 0,
+  CSA2_REINDEX = 1,
+  CSA2_REUSE = 2,
+  CSA2_REINDEX_POOL = 3  /* Reindex that searches the first Full layer's candidate pool */
+} csa2_mode;
 
 /* Operation codes for csa2_workspace_bytes. */
-enum { CSA2_OP_INDEX_TOPK = 1, CSA2_OP_SPARSE_ATTN = 2, CSA2_OP_LAYER_GROUP = 3 };
+enum {
+  CSA2_OP_INDEX_TOPK = 1,
+  CSA2_OP_SPARSE_ATTN = 2,
+  CSA2_OP_LAYER_GROUP = 3,
+  CSA2_OP_INDEX_TOPK_POOL = 4
+};
+#define CSA2_POOL_BLOCK 8      /* entries per candidate-pool block (aligned) */
+#define CSA2_POOL_MAX_SEL 2048 /* selections that seed a pool: 2048 blocks x 8 positions */
+#define CSA2_POOL_MAX_K 8192   /* Top-K size of a pooled search */
 
 /* Indexer scoring + Top-K ([summary] Architecture Components, item 2: Full and Reindex
  * layers compute fresh Top-K indices from the indexer key).
@@ -95,6 +108,25 @@ typedef struct csa2_index_args {
   const int32_t* n_vis;        /* device i32  [T], visible entries, 0..max_pages*64 */
   int32_t* idx_out;            /* device i32  [T, K] (output) */
 } csa2_index_args;
+
+/* Hierarchical sparse indexer ([summary] Architecture Components, item 3: the first Full
+ * layer's selection defines a candidate pool of up to 2,048 blocks x 8 positions, and the
+ * later Reindex layers search only that pool, so their cost stops growing with context).
+ * Reading of the block: an aligned run of CSA2_POOL_BLOCK entry positions, block b =
+ * {8b .. 8b+7}.  For each row t the pool is the union of the blocks that hold an entry of
+ * sel[t, 0:K_sel], cut to the n_vis[t] visible entries.  The layer's own indexer (ix.q_idx,
+ * ix.w_idx, ix.k_idx, same score as csa2_index_topk) scores every pool entry, and the
+ * min(ix.K, pool size) best by (score desc, index asc) go to ix.idx_out[t, 0:ix.K] in
+ * ascending order, -1 in the unused tail.  Per row the indexer keys read are at most
+ * 8 * K_sel (16,384 entries, 2 MiB at K_sel = 2048), whatever the context length. */
+typedef struct csa2_pool_args {
+  csa2_index_args ix;          /* the searching layer's indexer, shapes and output; ix.K in
+                                  1..CSA2_POOL_MAX_K */
+  const int32_t* sel;          /* device i32 [T, K_sel]: the pool-building selection (e.g. a
+                                  Full layer's idx_out): entries in [0, n_vis[t]) in strictly
+                                  ascending order, then -1 to the end of the row */
+  int32_t K_sel;               /* 1..CSA2_POOL_MAX_SEL */
+} csa2_pool_args;
 
 /* Sparse global attention over the selected FP4 entries plus the bf16 sliding-window
  * branch ([summary] Architecture Components, items 2 and 5; Introduction).
@@ -146,6 +178,8 @@ typedef struct csa2_attn_args {
  * Reindex: main KV of the nearest preceding Full layer, own indexer -> idx_out.
  * Reuse: main KV of the nearest preceding Full layer and the indices of the nearest
  * preceding Full/Reindex layer; it must leave every indexer/KV/idx_out field NULL.
+ * Reindex-pool: a Reindex layer whose Top-K searches only the candidate pool of layer 0's
+ * selection (see csa2_index_topk_pool; needs K <= CSA2_POOL_MAX_SEL).
  * Every layer has its own q, SWA caches and outputs. */
 typedef struct csa2_layer_desc {
   int32_t mode;                /* csa2_mode */
@@ -180,6 +214,10 @@ typedef struct csa2_group_args {
 /* Indexer scoring + Top-K.  Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, a). */
 csa2_status csa2_index_topk(const csa2_index_args* a, void* ws, size_t ws_bytes, void* stream);
 
+/* Hierarchical-indexer search of a candidate pool (scoring + Top-K over the pool).
+ * Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK_POOL, a). */
+csa2_status csa2_index_topk_pool(const csa2_pool_args* a, void* ws, size_t ws_bytes,
+                                 void* stream);
 /* Sparse FP4 global attention + SWA.  Workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, a)
  * (may be 0, then ws may be NULL). */
 csa2_status csa2_sparse_attn_fp4(const csa2_attn_args* a, void* ws, size_t ws_bytes,
@@ -201,7 +239,8 @@ csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint
                                 const int64_t* dst_row, void* stream);
 
 /* Workspace bytes for an operation; args points to the op's argument struct
- * (csa2_index_args, csa2_attn_args or csa2_group_args).  Returns 0 for NULL args. */
+ * (csa2_index_args, csa2_attn_args, csa2_group_args or csa2_pool_args).  Returns 0 for
+ * NULL args. */
 size_t csa2_workspace_bytes(int32_t op, const void* args);
 
 /* Thread-local description of the last failure on this thread ("" if none). */

@@ -232,6 +232,33 @@ class Workload:
         return normal_bf16(self.seed, 9 + 16 * layer, 0, n).reshape(
             self.B, self.L_swa, self.H_kv, D_SWA)
 
+    def selection(self, K_sel: int, stream: int = 48) -> np.ndarray:
+        """int32 [T, K_sel]: a seeded selection per row shaped like a Top-K output (distinct
+        visible entries, ascending, -1 tail): min(K_sel, n_vis) entries, half of them in
+        runs of 8 consecutive entries at seeded offsets (so that several fall in one
+        aligned 8-entry block, as selections around hot regions do), the rest uniform."""
+        nv = self.n_vis()
+        out = np.full((self.T, K_sel), -1, dtype=np.int32)
+        for t in range(self.T):
+            n = int(nv[t])
+            m = min(K_sel, n)
+            if m == n:
+                out[t, :m] = np.arange(n, dtype=np.int32)
+                continue
+            picks = set()
+            r = 0
+            while n >= 16 and len(picks) < m // 2:
+                start = u64(self.seed, stream, (t << 20) + r) % (n - 7)
+                picks.update(range(start, start + 8))
+                r += 1
+            rest = sample(self.seed, stream + 1 + 4096 * t, n, min(n, 2 * m))
+            for j in rest.tolist():
+                if len(picks) >= m:
+                    break
+                picks.add(j)
+            out[t, :m] = np.sort(np.fromiter(picks, dtype=np.int64))[:m]
+        return out
+
     # ---- paging ------------------------------------------------------------
     def physical_rows(self, b: int, pt: np.ndarray | None = None) -> np.ndarray:
         """Physical cache row of each logical entry of sequence b."""

@@ -19,7 +19,8 @@ import numpy as np
 import synth
 from oracle import oracle as orc
 
-FULL, REINDEX, REUSE = 0, 1, 2
+FULL, REINDEX, REUSE, REINDEX_POOL = 0, 1, 2, 3
+OWN_INDEX = (FULL, REINDEX, REINDEX_POOL)
 O_MAX_ABS, O_REL_L2, LSE_MAX_ABS, TOPK_REL = 2e-3, 1e-3, 1e-3, 1e-5
 
 
@@ -48,7 +49,7 @@ class HostWorkload:
         w, m = self.w, self.modes[li]
         L = {"mode": m, "q": w.q(li), "q_swa": w.q_swa(li), "swa_k": w.swa_k(li),
              "swa_v": w.swa_v(li)}
-        if m in (FULL, REINDEX):
+        if m in OWN_INDEX:
             L.update(q_idx=w.q_idx(li), w_idx=w.w_idx(li),
                      k_idx=w.to_physical(lambda b: w.k_idx_seq(b, li), self.pt))
         if m == FULL:
@@ -63,16 +64,39 @@ class HostWorkload:
                               w.seq_id(), w.n_vis(), rows=rows, want_scores=True)
         return s
 
+    def pool_search(self, li, rows, sel):
+        """Oracle pooled search of layer li for `rows` over the pool of sel [T, K_sel]:
+        (idx [n_rows, K], scores [n_rows, E] with NaN outside the pool)."""
+        w = self.w
+        L = self.layer_inputs(li)
+        return orc.index_topk_pool(w.K, w.P, L["q_idx"], L["w_idx"], L["k_idx"], self.pt,
+                                   w.seq_id(), w.n_vis(), sel, rows=rows, want_scores=True)
+
     def run_layer_group(self, rows):
         """Oracle Top-K scores of the listed rows for every layer (the scores of the layer
-        whose indices it uses)."""
+        whose indices it uses).  A pooled Reindex layer searches the pool of the oracle's
+        own layer-0 selection: its entry has the pooled 'scores' (NaN outside the pool),
+        'pooled' True, and layer 0's selection of the rows as 'sel0'."""
         kv_src, idx_src = orc.resolve_sources(self.modes)
         out, cache = [], {}
+        sel0 = None
         for li in range(len(self.modes)):
             src = idx_src[li]
             if src not in cache:
-                cache[src] = self.scores(src, rows)
-            out.append({"scores": cache[src]})
+                if self.modes[src] == REINDEX_POOL:
+                    if sel0 is None:
+                        s0 = cache[0]
+                        sel0 = -np.ones((self.w.T, self.w.K), np.int32)
+                        for r, t in enumerate(rows):
+                            n = int(self.w.n_vis()[t])
+                            sel0[t] = orc.topk_from_scores(s0[r, :n], self.w.K)
+                    cache[src] = self.pool_search(src, rows, sel0)[1]
+                else:
+                    cache[src] = self.scores(src, rows)
+            ent = {"scores": cache[src], "pooled": self.modes[src] == REINDEX_POOL}
+            if ent["pooled"]:
+                ent["sel0"] = sel0[rows]
+            out.append(ent)
         return out
 
     def attn_on(self, idx_rows, li, rows):
@@ -116,7 +140,7 @@ class DeviceWorkload:
         for li, m in enumerate(self.modes):
             L = {"mode": m, "q": b16(w.q(li)), "q_swa": b16(w.q_swa(li)),
                  "swa_k": b16(w.swa_k(li)), "swa_v": b16(w.swa_v(li))}
-            if m in (FULL, REINDEX):
+            if m in OWN_INDEX:
                 L["q_idx"] = b16(w.q_idx(li))
                 L["w_idx"] = t(w.w_idx(li))
                 L["k_idx"] = b16(w.to_physical(lambda b: w.k_idx_seq(b, li), pt)).view(
@@ -199,6 +223,36 @@ def check_topk(idx_gpu, scores, K, n_vis, rows=None):
             assert bad.size == 0, (f"row {t}: {bad.size} index differences beyond the score "
                                    f"tolerance (tau={tau}, worst gap "
                                    f"{np.abs(s[bad] - tau).max()})")
+            n_boundary += diff.size
+    return n_boundary
+
+
+def check_topk_pool(idx_gpu, scores, K, rows=None):
+    """Pooled search: scores [n_rows, E] hold the oracle's scores on the pool and NaN
+    elsewhere.  Same rules as check_topk, over the pool: min(K, pool size) picks, all in
+    the pool, ascending, -1 padded; equal to the oracle's pooled selection except within
+    the score tolerance of its K-th pool score."""
+    rows = np.arange(scores.shape[0]) if rows is None else np.asarray(rows)
+    n_boundary = 0
+    for r, t in enumerate(rows):
+        s = scores[r]
+        pool = np.flatnonzero(~np.isnan(s))
+        g = np.asarray(idx_gpu[t] if idx_gpu.shape[0] != len(rows) else idx_gpu[r])
+        m = min(K, pool.size)
+        assert np.all(g[m:] == -1), f"row {t}: padding"
+        sel = g[:m]
+        assert np.all(np.isin(sel, pool)), f"row {t}: pick outside the pool"
+        assert np.all(np.diff(sel) > 0), f"row {t}: not strictly ascending"
+        sp = s[pool]
+        order = np.lexsort((pool, -sp))
+        ref = pool[order[:m]]
+        diff = np.setxor1d(sel, ref)
+        if diff.size:
+            tau = sp[order[m - 1]]
+            tol = TOPK_REL * (abs(tau) if tau != 0 else np.abs(sp).max())
+            bad = diff[np.abs(s[diff] - tau) > tol]
+            assert bad.size == 0, (f"row {t}: {bad.size} pooled index differences beyond the "
+                                   f"score tolerance (tau={tau})")
             n_boundary += diff.size
     return n_boundary
 

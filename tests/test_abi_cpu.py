@@ -35,7 +35,8 @@ def test_exports_every_declared_function(c):
 
 def test_struct_layout_matches_header(c, tmp_path):
     structs = {"csa2_index_args": c.IndexArgs, "csa2_attn_args": c.AttnArgs,
-               "csa2_layer_desc": c.LayerDesc, "csa2_group_args": c.GroupArgs}
+               "csa2_layer_desc": c.LayerDesc, "csa2_group_args": c.GroupArgs,
+               "csa2_pool_args": c.PoolArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(){']
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -112,6 +113,43 @@ def test_index_alignment_and_workspace(c):
 def test_t_zero_is_noop(c):
     a = good_index(c, T=0, q_idx=None, idx_out=None)
     assert call_index(c, a)[0] == 0
+
+
+def call_pool(c, a, ws=None, ws_bytes=0):
+    st = c.lib.csa2_index_topk_pool(ctypes.byref(a), ws, ws_bytes, None)
+    return st, c.lib.csa2_last_error().decode()
+
+
+def test_pool_validation_and_workspace(c):
+    good = lambda **kw: c.PoolArgs(good_index(c, **kw), fake(8), 2048)
+    # pool size limits: 1..2048 selections, Top-K up to 8192
+    for K_sel in (0, 2049):
+        a = good()
+        a.K_sel = K_sel
+        st, msg = call_pool(c, a)
+        assert st == 2 and "K_sel" in msg
+    st, msg = call_pool(c, good(K=8193))
+    assert st == 2 and "K=8193" in msg
+    # the searching layer's indexer arguments go through the index validation
+    st, msg = call_pool(c, good(q_idx=None))
+    assert st == 1 and "q_idx" in msg
+    a = good()
+    a.sel = None
+    st, msg = call_pool(c, a)
+    assert st == 1 and "sel" in msg
+    a = good()
+    a.sel = ctypes.c_void_p(FAKE + 4)
+    assert call_pool(c, a)[0] == 3
+    # keys: 8 slots per selection and row, whatever the context
+    a = good()
+    need = c.lib.csa2_workspace_bytes(c.OP_INDEX_TOPK_POOL, ctypes.byref(a))
+    assert need == 4 * 8 * 2048 * 4
+    st, msg = call_pool(c, a, fake(9), need - 1)
+    assert st == 5 and "needed" in msg
+    # T = 0: nothing to do, no buffers needed
+    a = c.PoolArgs(good_index(c, T=0, q_idx=None, idx_out=None), None, 16)
+    assert call_pool(c, a)[0] == 0
+    assert c.lib.csa2_index_topk_pool(None, None, 0, None) == 1
 
 
 def good_attn(c, **kw):
@@ -208,6 +246,12 @@ def test_group_mode_rules(c):
     assert st == 5, msg
     need = c.lib.csa2_workspace_bytes(c.OP_LAYER_GROUP, ctypes.byref(g))
     assert need >= 4 * 16 * 64 * 4
+    # a pooled Reindex layer: valid with K <= 2048, rejected above
+    pooled = [layer(c, F), layer(c, c.REINDEX_POOL), layer(c, U)]
+    assert call_group(c, pooled, g)[0] == 5
+    st, msg = call_group(c, pooled, group(c, K=4096))
+    assert st == 2 and "pool" in msg
+    assert call_group(c, [layer(c, F), layer(c, c.REINDEX_POOL, kv_lat=fake(50))], g)[0] == 4
     # shapes are validated per op
     assert call_group(c, ok, group(c, H=40))[0] == 2
     assert call_group(c, ok, group(c, H_I=99))[0] == 2

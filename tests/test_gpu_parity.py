@@ -320,7 +320,10 @@ def _group_case(csa2, dev, w, rows, name):
     ref = h.run_layer_group(rows)
     nb = 0
     for li in range(len(w.modes)):
-        nb += tl.check_topk(res[li]["idx"], ref[li]["scores"], w.K, w.n_vis(), rows=rows)
+        if ref[li]["pooled"]:
+            nb += _check_pooled_layer(res[li]["idx"], res[0]["idx"], ref[li], w, rows)
+        else:
+            nb += tl.check_topk(res[li]["idx"], ref[li]["scores"], w.K, w.n_vis(), rows=rows)
         oref = h.attn_on(res[li]["idx"][rows], li, rows)
         tl.check_attn(res[li], oref, rows=rows)
     # Reuse borrows Reindex's indices; Reindex's differ from Full's (independent indexers)
@@ -330,10 +333,79 @@ def _group_case(csa2, dev, w, rows, name):
     return d, res, nb
 
 
+def _check_pooled_layer(idxp, idx0, ref, w, rows):
+    """Selection idxp of a pooled Reindex layer (or of a Reuse layer borrowing it); the
+    oracle searched the pool of its own layer-0 selection ref["sel0"].  Rows whose GPU
+    layer-0 selection idx0 is the same set (all, unless a near-tie moved a boundary entry)
+    are compared with the oracle; the others must still pick inside the pool of the GPU's
+    own layer-0 selection, ascending."""
+    same = np.array([np.array_equal(idx0[t], ref["sel0"][r]) for r, t in enumerate(rows)])
+    assert same.mean() >= 0.75, "too few rows with the oracle's layer-0 selection"
+    nb = tl.check_topk_pool(idxp[rows[same]], ref["scores"][same], w.K)
+    for t in rows[~same]:
+        pool = orc.pool_positions(idx0[t], w.n_vis()[t])
+        g = idxp[t][idxp[t] >= 0]
+        assert np.all(np.isin(g, pool)) and np.all(np.diff(g) > 0)
+    return nb
+
+
 def test_layer_group_full_reindex_reuse(csa2, dev):
     w = W(name="group_small", B=4, T=4, E=2048, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
           modes=[0, 1, 2])
     _group_case(csa2, dev, w, np.arange(4), "group_small")
+
+
+POOL = {
+    # name: (workload, K_sel)
+    "pool_small_k256": (W(B=2, T=4, E=2048, K=256, H_I=8), 256),
+    "pool_ragged_take_all": (W(B=3, T=5, E=1536, K=100, H_I=3, seq_id_rows=[0, 1, 2, 1, 0],
+                               n_vis_rows=[1536, 700, 33, 1100, 1]), 64),
+    "pool_k_above_pool": (W(B=2, T=3, E=1024, K=300, H_I=4), 32),
+    "pool_sel_not_mult8": (W(B=2, T=3, E=4096, K=512, H_I=8, n_vis_rows=[4096, 3001, 2047],
+                             seq_id_rows=[0, 1, 0]), 300),
+    "pool_sel_1": (W(B=1, T=2, E=512, K=16, H_I=2), 1),
+    "pool_2048_on_32k": (W(B=8, T=8, E=32768, K=2048, H_I=8, n_hot=328), 2048),
+}
+
+
+def _pool_parity(csa2, dev, w, K_sel, name, rows=None, empty_row=None):
+    _say("index_topk_pool", name)
+    rows = np.arange(w.T) if rows is None else rows
+    sel = w.selection(K_sel)
+    if empty_row is not None:
+        sel[empty_row] = -1
+    w1 = synth.Workload(**{**w.__dict__, "modes": [0, 3]})
+    d = tl.DeviceWorkload(w1, dev)
+    L = d.layers[1]
+    idx = csa2.index_topk_pool(L["q_idx"], L["w_idx"], L["k_idx"], d.page_table, d.seq_id,
+                               d.n_vis, w.K, torch.from_numpy(sel).to(dev))
+    torch.cuda.synchronize()
+    h = tl.HostWorkload(w1)
+    ref, scores = h.pool_search(1, rows, sel)
+    idx = idx.cpu().numpy()
+    tl.check_topk_pool(idx, scores, w.K, rows=rows)
+    return idx, ref
+
+
+@pytest.mark.parametrize("name", list(POOL))
+def test_index_topk_pool_parity(csa2, dev, name):
+    w, K_sel = POOL[name]
+    _pool_parity(csa2, dev, w, K_sel, name, empty_row=(1 if name == "pool_small_k256" else None))
+
+
+def test_full_size_pool_64x128k_sampled(csa2, dev):
+    """Pooled search at the headline decode shape: 64 rows over 32768 entries, K = 2048,
+    pools from 2048 selections (16384 key slots per row); the oracle checks sampled rows."""
+    w = synth.workload(2)
+    idx, _ = _pool_parity(csa2, dev, w, 2048, "pool_" + w.name, rows=np.array([0, 5, 31, 63]))
+    assert np.all(idx >= 0)
+
+
+def test_layer_group_pooled_reindex(csa2, dev):
+    w = W(name="group_pool", B=4, T=4, E=4096, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
+          modes=[0, 3, 2])
+    d, res, _ = _group_case(csa2, dev, w, np.arange(4), "group_pool")
+    np.testing.assert_array_equal(res[2]["idx"], res[1]["idx"])
 
 
 def test_determinism(csa2, dev):
@@ -365,6 +437,13 @@ def test_full_size_decode_4x1m(csa2, dev):
 
 def test_full_size_group_32x256k_sampled(csa2, dev):
     w = synth.workload(3)
+    _group_case(csa2, dev, w, np.array([0, 13, 31]), w.name)
+
+
+def test_full_size_group_pooled_32x256k_sampled(csa2, dev):
+    """The 32 x 256K group with its Reindex layer searching the Full layer's pool."""
+    w = synth.workload(3)
+    w = synth.Workload(**{**w.__dict__, "name": w.name + "_pool", "modes": [0, 3, 2]})
     _group_case(csa2, dev, w, np.array([0, 13, 31]), w.name)
 
 
