@@ -18,7 +18,9 @@
  *
  * Parity-unpinned parts: the decomposition of the pages' 890 bytes/token figure
  * into per-layer pieces (the footprint function is pinned only on its structural
- * values); the whole path against the pages (they print no worked example).
+ * values); the block-pooling formula of the KV append path (csa2o_kv_pool: the
+ * pages name C and Z but print no pooling rule; pinned only on the mathematics of
+ * the reading); the whole path against the pages (they print no worked example).
  */
 #include <math.h>
 #include <stdint.h>
@@ -147,6 +149,61 @@ void csa2o_mxfp4_dequantize(const uint8_t* lat, const uint8_t* scl, int64_t rows
       int code = (c & 1) ? (byte >> 4) : (byte & 15);
       out[r * LAT + c] = csa2o_e2m1_decode(code) * csa2o_e8m0_decode(scl[r * NBLK + c / BLK]);
     }
+}
+
+/* ------------------------------------------------------------------------- */
+/* KV append: block pooling                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* One compressed entry from a block of R raw tokens ([summary] Architecture
+ * Components, item 1, Eq. 1: the decoder's global KV entries come from the
+ * projections C = H W^KV and Z = H W^Z; [card] block-based sequence compression;
+ * compression ratio 4).  The pooling formula is not on the pages (parity unpinned
+ * against them).  Reading: Z holds one pooling logit per token and channel, and
+ * the entry is the softmax-over-the-block weighted sum of the tokens' C:
+ *   y[ch] = sum_i w_i[ch] c_i[ch],  w_i[ch] = exp(z_i[ch]) / sum_k exp(z_k[ch]).
+ * c, z: [n, R, D] fp32; out: [n, D] double. */
+void csa2o_kv_pool(const float* c, const float* z, int64_t n, int R, int D, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < n; ++e) {
+    for (int ch = 0; ch < D; ++ch) {
+      double m = -INFINITY;
+      for (int i = 0; i < R; ++i) {
+        double zi = z[(e * R + i) * D + ch];
+        if (zi > m) m = zi;
+      }
+      double num = 0.0, den = 0.0;
+      for (int i = 0; i < R; ++i) {
+        double w = exp((double)z[(e * R + i) * D + ch] - m);
+        num += w * (double)c[(e * R + i) * D + ch];
+        den += w;
+      }
+      out[e * D + ch] = num / den;
+    }
+  }
+}
+
+/* Round to bfloat16 (8 significant bits), to nearest with ties to the even
+ * significand; finite inputs whose result is a normal bf16 or zero. */
+uint16_t csa2o_round_bf16(double x) {
+  if (x == 0.0) return signbit(x) ? 0x8000u : 0u;
+  int ex;
+  double m = frexp(fabs(x), &ex);              /* |x| = m 2^ex, m in [0.5, 1) */
+  double q = m * 256.0;                         /* 8 significant bits */
+  double r = floor(q);
+  double frac = q - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  double v = ldexp(r, ex - 8);
+  float f = (float)v;                           /* exact: v has 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u >>= 16;
+  if (x < 0) u |= 0x8000u;
+  return (uint16_t)u;
+}
+
+void csa2o_round_bf16_array(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = csa2o_round_bf16(x[i]);
 }
 
 /* ------------------------------------------------------------------------- */

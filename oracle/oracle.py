@@ -9,7 +9,8 @@ Sources are cited by page and section: [summary] is the picx.dev whiteboard summ
 repost of the blog article of that title.
 
 Parity unpinned: the decomposition of the pages' 890 bytes/token into per-layer pieces;
-the whole path against the pages (they print no worked example).
+the block-pooling formula of the KV append path (kv_pool: a reading, pinned only on its
+own mathematics); the whole path against the pages (they print no worked example).
 """
 from __future__ import annotations
 
@@ -54,6 +55,8 @@ def lib():
         L.csa2o_topk_from_scores.argtypes = [vp, i64, i32, vp]
         L.csa2o_index_topk.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32,
                                        vp, vp]
+        L.csa2o_kv_pool.argtypes = [vp, vp, i64, i32, i32, vp]
+        L.csa2o_round_bf16_array.argtypes = [vp, i64, vp]
         L.csa2o_pool_positions.restype = i64
         L.csa2o_pool_positions.argtypes = [vp, i32, i64, vp]
         L.csa2o_index_topk_pool.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
@@ -101,6 +104,41 @@ def mxfp4_dequantize(lat: np.ndarray, scl: np.ndarray) -> np.ndarray:
     scl = _c(scl, np.uint8).reshape(-1, LAT // 32)
     out = np.empty((lat.shape[0], LAT), dtype=np.float64)
     lib().csa2o_mxfp4_dequantize(_p(lat), _p(scl), lat.shape[0], _p(out))
+    return out
+
+
+def kv_pool(c, z) -> np.ndarray:
+    """Block pooling of the KV append path: c, z fp32 [n, R, D] -> [n, D] float64, the
+    softmax(z)-over-the-block weighted sum of c per channel.  [summary] Architecture
+    Components, item 1 (Eq. 1: C and Z projections); the formula itself is a reading
+    (parity unpinned against the pages)."""
+    c, z = _c(c, np.float32), _c(z, np.float32)
+    n, R, D = c.shape
+    out = np.empty((n, D), dtype=np.float64)
+    lib().csa2o_kv_pool(_p(c), _p(z), n, R, D, _p(out))
+    return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns (round to nearest, ties to even)."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().csa2o_round_bf16_array(_p(x), x.size, _p(out))
+    return out
+
+
+def kv_append(c, z, c_idx=None, z_idx=None):
+    """KV append of n entries, each pooled from 4 raw tokens: c, z fp32 [n, 4, 576]
+    (latent 512 ; rope 64), c_idx, z_idx fp32 [n, 4, 64] or None.  Returns the pooled values
+    (float64) and the cache contents: MXFP4 latent (of the pooled value rounded to fp32, the
+    precision the cache write decides in), bf16 rope and bf16 indexer key."""
+    y = kv_pool(c, z)
+    lat, scl = mxfp4_quantize(y[:, :LAT].astype(np.float32))
+    out = {"pooled": y, "lat": lat, "scl": scl, "rope": round_bf16(y[:, LAT:])}
+    if c_idx is not None:
+        yi = kv_pool(c_idx, z_idx)
+        out["pooled_idx"] = yi
+        out["k_idx"] = round_bf16(yi)
     return out
 
 

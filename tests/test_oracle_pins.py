@@ -563,6 +563,65 @@ def test_layer_group_pooled_reindex():
         assert np.all(np.isin(picks[picks >= 0], pool))
 
 
+# ---------------------------------------------------------------- KV append (block pooling)
+def _append_inputs(n=6, D=576, seed=21):
+    c = synth.normal_f32(seed, 1, 0, n * 4 * D).reshape(n, 4, D)
+    z = (2.0 * synth.normal_f32(seed, 2, 0, n * 4 * D)).reshape(n, 4, D).astype(np.float32)
+    return c, z
+
+
+def test_kv_pool_equal_logits_is_mean():
+    c, z = _append_inputs()
+    z[:] = 0.75
+    np.testing.assert_allclose(orc.kv_pool(c, z), c.astype(np.float64).mean(axis=1),
+                               rtol=1e-14, atol=1e-15)
+
+
+def test_kv_pool_dominant_token_and_two_token_weights():
+    c, z = _append_inputs()
+    z[:] = -1e4
+    z[:, 2] = 0.0                                   # exp(-1e4) underflows to 0 in fp64
+    np.testing.assert_array_equal(orc.kv_pool(c, z), c[:, 2].astype(np.float64))
+    # logits log 3 and log 1 on tokens 0 and 1: weights 3/4 and 1/4
+    z[:] = -1e4
+    z[:, 0] = np.float32(np.log(3.0))
+    z[:, 1] = 0.0
+    w0 = 1.0 / (1.0 + np.exp(-np.float64(np.float32(np.log(3.0)))))
+    ref = w0 * c[:, 0] + (1 - w0) * c[:, 1]
+    np.testing.assert_allclose(orc.kv_pool(c, z), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_kv_pool_shift_and_permutation_invariance_and_convexity():
+    c, z = _append_inputs()
+    z = (np.round(z * 64) / 64).astype(np.float32)  # exact after adding 7.5
+    y = orc.kv_pool(c, z)
+    np.testing.assert_allclose(orc.kv_pool(c, z + np.float32(7.5)), y, rtol=1e-14, atol=1e-15)
+    perm = [3, 0, 2, 1]
+    np.testing.assert_allclose(orc.kv_pool(c[:, perm], z[:, perm]), y, rtol=1e-14, atol=1e-15)
+    assert np.all(y <= c.max(axis=1) + 1e-12) and np.all(y >= c.min(axis=1) - 1e-12)
+
+
+def test_round_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 6, 2000),
+                        1.0 + np.arange(16) * 2.0 ** -9, -(1.0 + np.arange(16) * 2.0 ** -9),
+                        [0.0, -0.0]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(orc.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_kv_append_composes_pooling_with_the_cache_formats():
+    c, z = _append_inputs()
+    ci, zi = _append_inputs(D=64, seed=22)
+    out = orc.kv_append(c, z, ci, zi)
+    y = orc.kv_pool(c, z)
+    lat, scl = orc.mxfp4_quantize(y[:, :512].astype(np.float32))
+    np.testing.assert_array_equal(out["lat"], lat)
+    np.testing.assert_array_equal(out["scl"], scl)
+    np.testing.assert_array_equal(out["rope"], orc.round_bf16(y[:, 512:]))
+    np.testing.assert_array_equal(out["k_idx"], orc.round_bf16(orc.kv_pool(ci, zi)))
+
+
 # ---------------------------------------------------------------- footprint
 def test_footprint_structure():
     # one entry = 256 B of E2M1 codes + 16 E8M0 scale bytes + 64 bf16 rope = 400 B
