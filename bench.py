@@ -237,6 +237,47 @@ def measure_extra(w, dev, steps, warmup, flush_mb):
     return out
 
 
+def measure_append(dev, n, steps, flush_mb):
+    """The KV append kernel alone: n entries, each pooled from 4 raw tokens (C and Z of
+    576 channels, indexer key and logits of 64), written to scattered cache rows."""
+    import numpy as np
+    import torch
+    import synth
+    from fp4_compressed_sparse_amd import csa2
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    c = t(synth.normal_f32(7, 1, 0, n * 4 * 576).reshape(n, 4, 576))
+    z = t(synth.normal_f32(7, 2, 0, n * 4 * 576).reshape(n, 4, 576))
+    ci = t(synth.normal_f32(7, 3, 0, n * 4 * 64).reshape(n, 4, 64))
+    zi = t(synth.normal_f32(7, 4, 0, n * 4 * 64).reshape(n, 4, 64))
+    rows = t(synth.permutation(7, 5, n).astype(np.int64))
+    lat = torch.empty((n, 256), dtype=torch.uint8, device=dev)
+    scl = torch.empty((n, 16), dtype=torch.uint8, device=dev)
+    rope = torch.empty((n, 64), dtype=torch.int16, device=dev)
+    kidx = torch.empty((n, 64), dtype=torch.int16, device=dev)
+    run = lambda: csa2.kv_append(c, z, lat, scl, rope, dst_row=rows, c_idx=ci, z_idx=zi,
+                                 k_idx=kidx)
+    run()
+    scratch = (torch.ones(flush_mb << 18, dtype=torch.float32, device=dev)
+               if flush_mb > 0 else None)
+    torch.cuda.synchronize()
+    csa2.timing_read()
+    csa2.timing_enable(True)
+    for _ in range(steps):
+        if scratch is not None:
+            scratch.sum()
+        run()
+    torch.cuda.synchronize()
+    csa2.timing_enable(False)
+    launches, ms = csa2.timing_read()["kv_append"]
+    us = ms * 1e3 / launches
+    algo = n * (2 * 4 * 576 * 4 + 2 * 4 * 64 * 4 + 8 + 256 + 16 + 128 + 128)
+    return {"workload": f"kv_append_{n}", "entries": n, "raw_tokens": 4 * n,
+            "kernels": {"kv_append": {"launches": launches, "avg_us": round(us, 3),
+                                      "algo_bytes": algo,
+                                      "gbs": round(algo / (us * 1e-6) / 1e9, 1)}},
+            "entries_per_s": round(n / (us * 1e-6), 1)}
+
+
 def kernel_source_sha(name):
     src = {"idx_score": "k_index.hip", "topk": "k_index.hip", "sparse_attn": "k_attn.hip",
            "attn_merge": "k_attn.hip", "swa": "k_swa.hip"}.get(name)
@@ -412,6 +453,8 @@ def main():
                           (w3p, 10)):
             print(f"[bench] extra workload {wx.name}", file=sys.stderr, flush=True)
             result["extra"].append(measure_extra(wx, dev, steps, 2, args.flush_mb))
+        print("[bench] extra: KV append", file=sys.stderr, flush=True)
+        result["extra"].append(measure_append(dev, 32768, 20, args.flush_mb))
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, w.T))

@@ -37,6 +37,12 @@ class PoolArgs(ctypes.Structure):
     _fields_ = [("ix", IndexArgs), ("sel", _vp), ("K_sel", _i32)]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("c", _vp), ("z", _vp), ("c_idx", _vp), ("z_idx", _vp),
+                ("dst_row", _vp), ("kv_lat", _vp), ("kv_scl", _vp), ("kv_rope", _vp),
+                ("k_idx", _vp)]
+
+
 class AttnArgs(ctypes.Structure):
     _fields_ = [("T", _i32), ("B", _i32), ("H", _i32), ("K", _i32), ("max_pages", _i32),
                 ("n_pages", _i32), ("q", _vp), ("kv_lat", _vp), ("kv_scl", _vp),
@@ -60,7 +66,7 @@ class GroupArgs(ctypes.Structure):
                 ("swa_len", _vp), ("sm_scale", _f32), ("sm_scale_swa", _f32)]
 
 
-EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize",
+EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize", "csa2_kv_append",
            "csa2_workspace_bytes", "csa2_last_error", "csa2_status_string", "csa2_abi_version",
            "csa2_timing_enable", "csa2_timing_read"]
 
@@ -78,6 +84,8 @@ def _load():
     L.csa2_layer_group.restype = _i32
     L.csa2_layer_group.argtypes = [ctypes.POINTER(LayerDesc), _i32, ctypes.POINTER(GroupArgs),
                                    _vp, ctypes.c_size_t, _vp]
+    L.csa2_kv_append.restype = _i32
+    L.csa2_kv_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
     L.csa2_mxfp4_quantize.restype = _i32
     L.csa2_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]
     L.csa2_workspace_bytes.restype = ctypes.c_size_t
@@ -246,6 +254,16 @@ def mxfp4_quantize(x, lat, scl, dst_row=None, stream=None):
     """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 16] at rows dst_row (int64) or 0..rows-1."""
     rows = x.shape[0]
     _check(lib.csa2_mxfp4_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row), _stream(stream)))
+
+
+def kv_append(c, z, kv_lat, kv_scl, kv_rope, dst_row=None, c_idx=None, z_idx=None,
+              k_idx=None, stream=None):
+    """KV append: entries pooled from blocks of 4 raw tokens.  c, z f32 [n, 4, 576];
+    c_idx, z_idx f32 [n, 4, 64] (optional, with k_idx); writes rows dst_row (int64) or
+    0..n-1 of kv_lat u8 [*, 256], kv_scl u8 [*, 16], kv_rope bf16 [*, 64], k_idx bf16 [*, 64]."""
+    a = AppendArgs(c.shape[0], _p(c), _p(z), _p(c_idx), _p(z_idx), _p(dst_row), _p(kv_lat),
+                   _p(kv_scl), _p(kv_rope), _p(k_idx))
+    _check(lib.csa2_kv_append(ctypes.byref(a), _stream(stream)))
 
 
 def workspace_bytes(op: int, args) -> int:

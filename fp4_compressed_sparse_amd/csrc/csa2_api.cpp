@@ -678,6 +678,34 @@ csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint
   return timed("mxfp4_quantize", s, [&] { return launch_quantize(p, s); });
 }
 
+csa2_status csa2_kv_append(const csa2_append_args* a, void* stream) {
+  const char* fn = "csa2_kv_append";
+  if (!a) return fail(CSA2_ERR_NULL, "%s: args is NULL", fn);
+  if (a->n < 0) return fail(CSA2_ERR_SHAPE, "%s: n=%lld < 0", fn, (long long)a->n);
+  if (a->n > (int64_t)0xffffffff * 4)
+    return fail(CSA2_ERR_SHAPE, "%s: n=%lld too large", fn, (long long)a->n);
+  if ((a->c_idx != nullptr) != (a->z_idx != nullptr) ||
+      (a->c_idx != nullptr) != (a->k_idx != nullptr))
+    return fail(CSA2_ERR_MODE, "%s: c_idx, z_idx and k_idx must be all set or all NULL", fn);
+  if (a->n == 0) return CSA2_OK;
+  REQ(a->c, "c");
+  REQ(a->z, "z");
+  REQ(a->kv_lat, "kv_lat");
+  REQ(a->kv_scl, "kv_scl");
+  REQ(a->kv_rope, "kv_rope");
+  if (a->c_idx) {
+    REQ(a->c_idx, "c_idx");
+    REQ(a->z_idx, "z_idx");
+    REQ(a->k_idx, "k_idx");
+  }
+  if (a->dst_row && misaligned(a->dst_row))
+    return fail(CSA2_ERR_ALIGN, "%s: dst_row is not 16-byte aligned", fn);
+  AppendParams p{a->n, a->c, a->z, a->c_idx, a->z_idx, a->dst_row, a->kv_lat, a->kv_scl,
+                 static_cast<uint16_t*>(a->kv_rope), static_cast<uint16_t*>(a->k_idx)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed("kv_append", s, [&] { return launch_kv_append(p, s); });
+}
+
 size_t csa2_workspace_bytes(int32_t op, const void* args) {
   if (!args) return 0;
   switch (op) {

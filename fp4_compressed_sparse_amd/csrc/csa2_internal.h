@@ -117,6 +117,19 @@ struct QuantParams {
   const int64_t* dst_row;              // may be null
 };
 
+struct AppendParams {
+  int64_t n;                           // entries
+  const float* c;                      // [n, 4, 576] token projections C
+  const float* z;                      // [n, 4, 576] pooling logits Z
+  const float* c_idx;                  // [n, 4, 64] or null
+  const float* z_idx;                  // [n, 4, 64] or null
+  const int64_t* dst_row;              // [n] physical rows, or null = 0..n-1
+  uint8_t* lat;                        // [*, 256]
+  uint8_t* scl;                        // [*, 16]
+  uint16_t* rope;                      // [*, 64] bf16
+  uint16_t* k_idx;                     // [*, 64] bf16, or null
+};
+
 // ---------------------------------------------------------------- launch geometry
 constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
 constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-tiled
@@ -145,5 +158,6 @@ hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_swa(const SwaParams& p, hipStream_t s);
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 
 }  // namespace csa2

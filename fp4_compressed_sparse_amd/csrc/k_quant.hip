@@ -15,13 +15,10 @@
 
 namespace csa2 {
 
-__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= p.rows) return;
-  const int lane = threadIdx.x & 63;
-  const f32x4* xp = reinterpret_cast<const f32x4*>(p.x + r * kLat + 8 * lane);
-  const f32x4 a = xp[0], b = xp[1];
-  float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// Lane l of a wave holds channels 8l .. 8l+7 of a row (x); four consecutive lanes form a
+// 32-channel scale block.  Returns the E2M1 codes as one dword and the block's shared
+// exponent X (scale byte X + 127).
+__device__ __forceinline__ uint32_t mxfp4_encode_lane(const float (&x)[8], int& X) {
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
@@ -29,7 +26,6 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
   amax = fmaxf(amax, __shfl_xor(amax, 2));
 
   const uint32_t ab = __float_as_uint(amax);
-  int X;
   if (ab == 0u) {
     X = -127;
   } else {
@@ -48,9 +44,99 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
     code |= (__float_as_uint(x[e]) >> 31) << 3;
     word |= code << (4 * e);
   }
+  return word;
+}
+
+__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= p.rows) return;
+  const int lane = threadIdx.x & 63;
+  const f32x4* xp = reinterpret_cast<const f32x4*>(p.x + r * kLat + 8 * lane);
+  const f32x4 a = xp[0], b = xp[1];
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  int X;
+  const uint32_t word = mxfp4_encode_lane(x, X);
   const int64_t dst = p.dst_row ? p.dst_row[r] : r;
   *reinterpret_cast<uint32_t*>(p.lat + dst * kLatBytes + 4 * lane) = word;
   if ((lane & 3) == 0) p.scl[dst * kScl + (lane >> 2)] = (uint8_t)(X + 127);
+}
+
+// ---------------------------------------------------------------- KV append
+// One cache entry from a block of 4 raw tokens ([summary] Architecture Components, item 1,
+// Eq. 1: the global KV entries come from the projections C and Z of the encoder's hidden
+// state; [card] block-based sequence compression, 4:1).  The pages print no pooling rule;
+// the one read here is a softmax over the block's tokens per channel, the entry being the
+// weighted sum of the tokens' C.  The pooled latent is written in MXFP4 (as above), the rope
+// and indexer-key parts in bf16 (round to nearest even).
+//
+// One wave per entry: lane l pools latent channels 8l .. 8l+7, rope channel l and indexer
+// channel l from the four tokens, in fp32.
+__device__ __forceinline__ float pool4(const float (&z)[4], const float (&c)[4]) {
+  const float m = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w = __builtin_amdgcn_exp2f((z[i] - m) * 1.4426950408889634f);
+    num = fmaf(w, c[i], num);
+    den += w;
+  }
+  return num / den;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= p.n) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int D = kLat + kRope;                    // channels per token
+  const float* c = p.c + e * 4 * D;
+  const float* z = p.z + e * 4 * D;
+  float cl[4][8], zl[4][8], cr[4], zr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4* cp = reinterpret_cast<const f32x4*>(c + i * D + 8 * lane);
+    const f32x4* zp = reinterpret_cast<const f32x4*>(z + i * D + 8 * lane);
+    const f32x4 c0 = cp[0], c1 = cp[1], z0 = zp[0], z1 = zp[1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cl[i][k] = c0[k]; cl[i][4 + k] = c1[k];
+      zl[i][k] = z0[k]; zl[i][4 + k] = z1[k];
+    }
+    cr[i] = c[i * D + kLat + lane];
+    zr[i] = z[i * D + kLat + lane];
+  }
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float zk[4] = {zl[0][k], zl[1][k], zl[2][k], zl[3][k]};
+    const float ck[4] = {cl[0][k], cl[1][k], cl[2][k], cl[3][k]};
+    y[k] = pool4(zk, ck);
+  }
+  int X;
+  const uint32_t word = mxfp4_encode_lane(y, X);
+  const int64_t dst = p.dst_row ? p.dst_row[e] : e;
+  *reinterpret_cast<uint32_t*>(p.lat + dst * kLatBytes + 4 * lane) = word;
+  if ((lane & 3) == 0) p.scl[dst * kScl + (lane >> 2)] = (uint8_t)(X + 127);
+  p.rope[dst * kRope + lane] = bf16_rne(pool4(zr, cr));
+  if (p.c_idx) {
+    float ci[4], zi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ci[i] = p.c_idx[(e * 4 + i) * kDidx + lane];
+      zi[i] = p.z_idx[(e * 4 + i) * kDidx + lane];
+    }
+    p.k_idx[dst * kDidx + lane] = bf16_rne(pool4(zi, ci));
+  }
+}
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
+  const int64_t blocks = (p.n + 3) / 4;
+  CSA2_LAUNCH(kv_append_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {

@@ -238,6 +238,32 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
 csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
                                 const int64_t* dst_row, void* stream);
 
+/* KV append: one compressed cache entry from each block of CSA2_APPEND_TOKENS raw tokens,
+ * written straight into the paged cache planes (a Full layer computing its own KV:
+ * [summary] Architecture Components, item 1, Eq. 1 -- the global KV entries are projections
+ * C = H W^KV with companion projections Z = H W^Z -- and item 2; [card] block-based
+ * sequence compression; 4:1 compression).  The pages print no pooling formula; the reading
+ * here, per channel ch of entry e over its block's tokens i:
+ *   y[e, ch] = sum_i softmax_i(z[e, i, ch]) * c[e, i, ch]
+ * computed in fp32.  Channels 0..511 of y are written as MXFP4 to kv_lat/kv_scl (the
+ * csa2_mxfp4_quantize rule), channels 512..575 as bf16 (round to nearest even) to kv_rope;
+ * with c_idx, the 64-d indexer key is pooled the same way and written as bf16 to k_idx.
+ * Inputs must be finite.  Rows dst_row[e] (NULL = 0..n-1) of every written plane are
+ * overwritten; distinct entries must have distinct rows. */
+#define CSA2_APPEND_TOKENS 4
+typedef struct csa2_append_args {
+  int64_t n;                   /* entries, >= 0 */
+  const float* c;              /* device f32 [n, 4, 576] token projections (latent ; rope) */
+  const float* z;              /* device f32 [n, 4, 576] pooling logits */
+  const float* c_idx;          /* device f32 [n, 4, 64] indexer-key projections, or NULL */
+  const float* z_idx;          /* device f32 [n, 4, 64] their logits; NULL iff c_idx is */
+  const int64_t* dst_row;      /* device i64 [n] physical cache rows, or NULL */
+  uint8_t* kv_lat;             /* device u8   [rows, 256] (output) */
+  uint8_t* kv_scl;             /* device u8   [rows, 16]  (output) */
+  void* kv_rope;               /* device bf16 [rows, 64]  (output) */
+  void* k_idx;                 /* device bf16 [rows, 64]  (output); NULL iff c_idx is */
+} csa2_append_args;
+csa2_status csa2_kv_append(const csa2_append_args* a, void* stream);
 /* Workspace bytes for an operation; args points to the op's argument struct
  * (csa2_index_args, csa2_attn_args, csa2_group_args or csa2_pool_args).  Returns 0 for
  * NULL args. */

@@ -36,7 +36,7 @@ def test_exports_every_declared_function(c):
 def test_struct_layout_matches_header(c, tmp_path):
     structs = {"csa2_index_args": c.IndexArgs, "csa2_attn_args": c.AttnArgs,
                "csa2_layer_desc": c.LayerDesc, "csa2_group_args": c.GroupArgs,
-               "csa2_pool_args": c.PoolArgs}
+               "csa2_pool_args": c.PoolArgs, "csa2_append_args": c.AppendArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(){']
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -265,6 +265,26 @@ def test_quantize_validation(c):
     assert q(ctypes.c_void_p(FAKE + 4), 4, fake(1), fake(2), None, None) == 3
     assert q(fake(0), 4, fake(1), fake(2), ctypes.c_void_p(FAKE + 8), None) == 3
     assert q(None, 0, None, None, None, None) == 0
+
+
+def test_kv_append_validation(c):
+    def call(**kw):
+        a = c.AppendArgs(8, fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7),
+                         fake(8), fake(9))
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return c.lib.csa2_kv_append(ctypes.byref(a), None), c.lib.csa2_last_error().decode()
+    assert call(n=-1)[0] == 2
+    st, msg = call(z_idx=None)
+    assert st == 4 and "c_idx" in msg
+    assert call(k_idx=None)[0] == 4
+    st, msg = call(c=None)
+    assert st == 1 and "c" in msg
+    assert call(kv_rope=None)[0] == 1
+    assert call(kv_scl=ctypes.c_void_p(FAKE + 4))[0] == 3
+    assert call(dst_row=ctypes.c_void_p(FAKE + 8))[0] == 3
+    assert call(n=0, c=None, z=None)[0] == 0                 # nothing to write
+    assert c.lib.csa2_kv_append(None, None) == 1
 
 
 def test_workspace_sizes_of_named_workloads(c):

@@ -87,6 +87,110 @@ def test_quantize_bit_exact(csa2, dev):
     np.testing.assert_array_equal(scl2.cpu().numpy()[perm], scl_ref)
 
 
+# ---------------------------------------------------------------- KV append
+def _e2m1_midpoints():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "e2m1_codes.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    grid = sorted({abs(float(r[1])) for r in rows})
+    return (np.array(grid[1:]) + np.array(grid[:-1])) / 2
+
+
+def _check_append(got, y, tol):
+    """got: GPU planes (lat, scl, rope, k_idx) of the written rows; y: the oracle's pooled
+    values (float64 [n, 576] and [n, 64]); tol: absolute pooling tolerance per element.
+    Codes, scales and bf16 values must equal the oracle's cache write of y except where y
+    lies within tol of a decision boundary (a grid midpoint, a power of two for the shared
+    exponent, a bf16 midpoint); there the GPU may take the neighbouring value."""
+    n = y.shape[0]
+    y_lat, t_lat = y[:, :512], tol[:, :512]
+    ref_lat, ref_scl = orc.mxfp4_quantize(y_lat.astype(np.float32))
+    Xg = got["scl"].astype(np.int64) - 127
+    Xr = ref_scl.astype(np.int64) - 127
+    amax = np.abs(y_lat).reshape(n, 16, 32).max(-1)
+    tmax = t_lat.reshape(n, 16, 32).max(-1)
+    same_x = Xg == Xr
+    edge = np.abs(amax - 2.0 ** (np.maximum(Xg, Xr) + 2)) <= tmax
+    assert np.all(same_x | edge), "shared exponent differs away from a power of two"
+    unpack = lambda lat: np.stack([lat & 15, lat >> 4], -1).reshape(n, 512)
+    cg, cr = unpack(got["lat"]), unpack(ref_lat)
+    mids = _e2m1_midpoints()
+    sc = 2.0 ** -np.repeat(Xr, 32, axis=1)
+    tt = np.abs(y_lat) * sc
+    near = (np.abs(tt[..., None] - mids).min(-1) <= t_lat * sc) | (np.abs(y_lat) <= t_lat)
+    blk_ok = np.repeat(same_x, 32, axis=1)
+    bad = blk_ok & (cg != cr) & ~near
+    assert not bad.any(), f"{bad.sum()} MXFP4 codes differ away from a rounding boundary"
+    adj = np.abs((cg & 7).astype(int) - (cr & 7).astype(int)) <= 1
+    assert np.all(adj | ~blk_ok), "a code differs by more than one grid step"
+    n_edge = int((blk_ok & (cg != cr)).sum()) + int((~same_x).sum())
+    for key, yy, tt_ in (("rope", y[:, 512:], tol[:, 512:]), ("k_idx", got.get("y_idx"),
+                                                                 got.get("t_idx"))):
+        if yy is None:
+            continue
+        g = got[key]
+        r = orc.round_bf16(yy)
+        gv = synth.bf16_bits_to_f32(g).astype(np.float64)
+        # a differing value must be the rounding of something within tol of y: at most
+        # tol plus half a bf16 step (<= |y| 2^-8 + |gv| 2^-8) away
+        near = np.abs(gv - yy) <= tt_ + (np.abs(yy) + np.abs(gv)) * 2.0 ** -8
+        assert np.all((g == r) | near), f"{key}: bf16 value outside the tolerance"
+        n_edge += int((g != r).sum())
+    return n_edge
+
+
+def _append_case(n, seed, with_idx=True, dst=True):
+    c = synth.normal_f32(seed, 1, 0, n * 4 * 576).reshape(n, 4, 576)
+    z = (2.0 * synth.normal_f32(seed, 2, 0, n * 4 * 576)).reshape(n, 4, 576).astype(np.float32)
+    if n >= 40:
+        z[0:10] = 0.5                                # equal logits: the mean
+        z[10:20] = 0.0
+        z[10:20, 2] = 30.0                           # one token dominates
+        c[20:25, :, 64:96] = 0.0                     # an all-zero scale block
+        c[25:30] *= np.float32(2.0 ** 20)
+        c[30:35] *= np.float32(2.0 ** -20)
+        z[35:40] *= np.float32(40.0)                 # near-hard selections
+    ci = zi = None
+    if with_idx:
+        ci = synth.normal_f32(seed, 3, 0, n * 4 * 64).reshape(n, 4, 64)
+        zi = (2.0 * synth.normal_f32(seed, 4, 0, n * 4 * 64)).reshape(n, 4, 64).astype(np.float32)
+    rows = (np.random.default_rng(seed).permutation(n + 50)[:n].astype(np.int64) if dst
+            else np.arange(n, dtype=np.int64))
+    return c, z, ci, zi, rows
+
+
+@pytest.mark.parametrize("n,with_idx,dst", [(1000, True, True), (5, False, False),
+                                            (1, True, True)])
+def test_kv_append_parity(csa2, dev, n, with_idx, dst):
+    _say("kv_append", n, with_idx, dst)
+    c, z, ci, zi, rows = _append_case(n, 17 + n, with_idx, dst)
+    R = int(rows.max()) + 1
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    lat = torch.zeros((R, 256), dtype=torch.uint8, device=dev)
+    scl = torch.zeros((R, 16), dtype=torch.uint8, device=dev)
+    rope = torch.zeros((R, 64), dtype=torch.int16, device=dev)
+    kidx = torch.zeros((R, 64), dtype=torch.int16, device=dev) if with_idx else None
+    csa2.kv_append(t(c), t(z), lat, scl, rope, dst_row=t(rows) if dst else None, c_idx=t(ci),
+                   z_idx=t(zi), k_idx=kidx)
+    torch.cuda.synchronize()
+    ref = orc.kv_append(c, z, ci, zi)
+    tol = 4e-6 * np.abs(c).max(axis=1).astype(np.float64) + 1e-37
+    got = {"lat": lat.cpu().numpy()[rows], "scl": scl.cpu().numpy()[rows],
+           "rope": rope.cpu().numpy().view(np.uint16)[rows]}
+    if with_idx:
+        got["k_idx"] = kidx.cpu().numpy().view(np.uint16)[rows]
+        got["y_idx"] = ref["pooled_idx"]
+        got["t_idx"] = 4e-6 * np.abs(ci).max(axis=1).astype(np.float64) + 1e-37
+    n_edge = _check_append(got, ref["pooled"], tol)
+    assert n_edge <= max(2, n * 576 // 1000), f"{n_edge} boundary cases"
+    if n >= 40:   # equal logits give the mean, exactly representable cases stay exact
+        np.testing.assert_array_equal(got["scl"][20:25, 2:3], 0)   # zero block: scale 2^-127
+    # rows not written stay untouched
+    if dst:
+        untouched = np.setdiff1d(np.arange(R), rows)
+        assert not lat.cpu().numpy()[untouched].any()
+
+
 def _index_parity(csa2, dev, w, name):
     _say("index_topk", name)
     d = tl.DeviceWorkload(w, dev)
