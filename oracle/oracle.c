@@ -152,6 +152,95 @@ void csa2o_mxfp4_dequantize(const uint8_t* lat, const uint8_t* scl, int64_t rows
 }
 
 /* ------------------------------------------------------------------------- */
+/* FP4 with E4M3 scales per 16 channels                                       */
+/* ------------------------------------------------------------------------- */
+
+/* E4M3 (OCP 8-bit floating point, E4M3 variant): 1 sign bit, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent field 0 encodes subnormals m 2^-9; no
+ * infinities; S.1111.111 is NaN, so the largest magnitude is 1.75 * 2^8 = 448.
+ * The literal format of [summary] Architecture Components, item 5 (one E4M3 scale
+ * per 16 channels; its range 2688 = 6 * 448). */
+double csa2o_e4m3_decode(int byte) {
+  int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* Non-negative v -> the nearest E4M3 value (ties to the even mantissa), saturating
+ * at 448.  Returns the byte. */
+int csa2o_e4m3_round(double v) {
+  if (v >= 448.0) return 0x7e;
+  if (v < ldexp(1.0, -6)) {                     /* subnormal range: steps of 2^-9 */
+    double k = v * 512.0, fl = floor(k), frac = k - fl;
+    int q = (int)fl;
+    if (frac > 0.5 || (frac == 0.5 && (q & 1))) q += 1;
+    return q;                                   /* q = 8 is the smallest normal, 0x08 */
+  }
+  int ex;
+  frexp(v, &ex);                                /* v in [2^(ex-1), 2^ex) */
+  int e = ex - 1;                               /* floor(log2 v) >= -6 */
+  double k = ldexp(v, 3 - e), fl = floor(k), frac = k - fl;   /* k in [8, 16) */
+  int q = (int)fl;
+  if (frac > 0.5 || (frac == 0.5 && (q & 1))) q += 1;
+  if (q == 16) { q = 8; e += 1; }
+  if (e > 8) return 0x7e;
+  return ((e + 7) << 3) | (q - 8);
+}
+
+/* One 16-channel block: scale s = E4M3(max|x| / 6) (nearest, ties to even); each
+ * element |x| / s rounded to E2M1 (ties to the even code, saturating at 6), sign
+ * bit from x.  A scale that rounds to 0 encodes the block as (signed) zeros.
+ * Returns -1 on NaN/Inf. */
+static int quant_block16_e4m3(const float* x, uint8_t* scale_byte, uint8_t codes[16]) {
+  double amax = 0.0;
+  for (int i = 0; i < 16; ++i) {
+    if (!isfinite(x[i])) return -1;
+    double a = fabs((double)x[i]);
+    if (a > amax) amax = a;
+  }
+  int sb = csa2o_e4m3_round(amax / 6.0);
+  *scale_byte = (uint8_t)sb;
+  double sv = csa2o_e4m3_decode(sb);
+  for (int i = 0; i < 16; ++i) {
+    int mag = (sv > 0.0) ? e2m1_round_mag(fabs((double)x[i]) / sv) : 0;
+    codes[i] = (uint8_t)(((signbit(x[i]) ? 1 : 0) << 3) | mag);
+  }
+  return 0;
+}
+
+/* Rows [rows, 512] -> lat [rows, 256] (as the MXFP4 layout) and scl [rows, 32]
+ * (one E4M3 byte per 16 channels).  Returns -1 if any input is NaN/Inf. */
+int csa2o_fp4e4m3_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl) {
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int b = 0; b < LAT / 16; ++b) {
+      uint8_t codes[16];
+      if (quant_block16_e4m3(x + r * LAT + b * 16, &scl[r * (LAT / 16) + b], codes)) {
+        bad = 1;
+        continue;
+      }
+      for (int k = 0; k < 8; ++k)
+        lat[r * (LAT / 2) + b * 8 + k] = (uint8_t)(codes[2 * k] | (codes[2 * k + 1] << 4));
+    }
+  }
+  return bad ? -1 : 0;
+}
+
+/* v[c] = e2m1(code c) * e4m3(scale byte c / 16), exact in double. */
+void csa2o_fp4e4m3_dequantize(const uint8_t* lat, const uint8_t* scl, int64_t rows,
+                              double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < LAT; ++c) {
+      uint8_t byte = lat[r * (LAT / 2) + c / 2];
+      int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      out[r * LAT + c] =
+          csa2o_e2m1_decode(code) * csa2o_e4m3_decode(scl[r * (LAT / 16) + c / 16]);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* KV append: block pooling                                                   */
 /* ------------------------------------------------------------------------- */
 
@@ -403,12 +492,14 @@ static void softmax_combine(const double* l, const double* v, int64_t n, int dv,
  *   logit = sm_scale * q . key.
  * [summary] Architecture Components, item 2 (CSA2) and item 5 (FP4 main KV);
  * [blog] introduction (sparse attention covering the whole context).
+ * fmt 0: MXFP4 planes (E8M0 scale per 32 channels, kv_scl [*, 16]); fmt 1: FP4 with
+ * an E4M3 scale per 16 channels (kv_scl [*, 32]).
  * o_out: [n_rows, H, 512]; lse_out: [n_rows, H]. */
-void csa2o_sparse_attn(int H, int K, int max_pages, const uint16_t* q, const uint8_t* kv_lat,
-                       const uint8_t* kv_scl, const uint16_t* kv_rope,
-                       const int32_t* page_table, const int32_t* seq_id, const int32_t* idx,
-                       double sm_scale, const int32_t* rows, int n_rows, double* o_out,
-                       double* lse_out) {
+void csa2o_sparse_attn_fmt(int H, int K, int max_pages, const uint16_t* q,
+                           const uint8_t* kv_lat, const uint8_t* kv_scl, int fmt,
+                           const uint16_t* kv_rope, const int32_t* page_table,
+                           const int32_t* seq_id, const int32_t* idx, double sm_scale,
+                           const int32_t* rows, int n_rows, double* o_out, double* lse_out) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int r = 0; r < n_rows; ++r) {
     int t = rows[r];
@@ -423,7 +514,11 @@ void csa2o_sparse_attn(int H, int K, int max_pages, const uint16_t* q, const uin
     for (int i = 0; i < K; ++i) {
       if (sel[i] < 0) continue;
       int64_t pr = phys_row(page_table, max_pages, b, sel[i]);
-      csa2o_mxfp4_dequantize(kv_lat + pr * (LAT / 2), kv_scl + pr * NBLK, 1, v + k * LAT);
+      if (fmt == 1)
+        csa2o_fp4e4m3_dequantize(kv_lat + pr * (LAT / 2), kv_scl + pr * (LAT / 16), 1,
+                                 v + k * LAT);
+      else
+        csa2o_mxfp4_dequantize(kv_lat + pr * (LAT / 2), kv_scl + pr * NBLK, 1, v + k * LAT);
       for (int c = 0; c < ROPE; ++c) rope[k * ROPE + c] = bf16_val(kv_rope[pr * ROPE + c]);
       ++k;
     }
@@ -444,6 +539,15 @@ void csa2o_sparse_attn(int H, int K, int max_pages, const uint16_t* q, const uin
     free(rope);
     free(l);
   }
+}
+
+void csa2o_sparse_attn(int H, int K, int max_pages, const uint16_t* q, const uint8_t* kv_lat,
+                       const uint8_t* kv_scl, const uint16_t* kv_rope,
+                       const int32_t* page_table, const int32_t* seq_id, const int32_t* idx,
+                       double sm_scale, const int32_t* rows, int n_rows, double* o_out,
+                       double* lse_out) {
+  csa2o_sparse_attn_fmt(H, K, max_pages, q, kv_lat, kv_scl, 0, kv_rope, page_table, seq_id,
+                        idx, sm_scale, rows, n_rows, o_out, lse_out);
 }
 
 /* Sliding-window branch for the listed rows: head h of row t attends over the

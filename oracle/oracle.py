@@ -56,6 +56,15 @@ def lib():
         L.csa2o_index_topk.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32,
                                        vp, vp]
         L.csa2o_kv_pool.argtypes = [vp, vp, i64, i32, i32, vp]
+        L.csa2o_e4m3_decode.restype = f64
+        L.csa2o_e4m3_decode.argtypes = [i32]
+        L.csa2o_e4m3_round.restype = i32
+        L.csa2o_e4m3_round.argtypes = [f64]
+        L.csa2o_fp4e4m3_quantize.restype = i32
+        L.csa2o_fp4e4m3_quantize.argtypes = [vp, i64, vp, vp]
+        L.csa2o_fp4e4m3_dequantize.argtypes = [vp, vp, i64, vp]
+        L.csa2o_sparse_attn_fmt.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp,
+                                            f64, vp, i32, vp, vp]
         L.csa2o_round_bf16_array.argtypes = [vp, i64, vp]
         L.csa2o_pool_positions.restype = i64
         L.csa2o_pool_positions.argtypes = [vp, i32, i64, vp]
@@ -104,6 +113,35 @@ def mxfp4_dequantize(lat: np.ndarray, scl: np.ndarray) -> np.ndarray:
     scl = _c(scl, np.uint8).reshape(-1, LAT // 32)
     out = np.empty((lat.shape[0], LAT), dtype=np.float64)
     lib().csa2o_mxfp4_dequantize(_p(lat), _p(scl), lat.shape[0], _p(out))
+    return out
+
+
+def e4m3_decode(byte: int) -> float:
+    return lib().csa2o_e4m3_decode(int(byte))
+
+
+def e4m3_round(v: float) -> int:
+    return lib().csa2o_e4m3_round(float(v))
+
+
+def fp4e4m3_quantize(x: np.ndarray):
+    """fp32 [rows, 512] -> (lat uint8 [rows, 256], scl uint8 [rows, 32]): E2M1 codes with
+    one E4M3 scale per 16 channels.  [summary] Architecture Components, item 5 (its literal
+    format)."""
+    x = _c(x, np.float32).reshape(-1, LAT)
+    rows = x.shape[0]
+    lat = np.zeros((rows, LAT // 2), dtype=np.uint8)
+    scl = np.zeros((rows, LAT // 16), dtype=np.uint8)
+    if lib().csa2o_fp4e4m3_quantize(_p(x), rows, _p(lat), _p(scl)) != 0:
+        raise ValueError("FP4/E4M3 quantization of a non-finite value")
+    return lat, scl
+
+
+def fp4e4m3_dequantize(lat: np.ndarray, scl: np.ndarray) -> np.ndarray:
+    lat = _c(lat, np.uint8).reshape(-1, LAT // 2)
+    scl = _c(scl, np.uint8).reshape(-1, LAT // 16)
+    out = np.empty((lat.shape[0], LAT), dtype=np.float64)
+    lib().csa2o_fp4e4m3_dequantize(_p(lat), _p(scl), lat.shape[0], _p(out))
     return out
 
 
@@ -199,9 +237,10 @@ def index_topk_pool(K, max_pages, q_idx, w_idx, k_idx, page_table, seq_id, n_vis
 
 
 def sparse_attn(max_pages, q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx,
-                sm_scale=None, rows=None):
-    """Global sparse branch.  q bf16 bits [T, H, 576]; planes in physical rows;
-    idx i32 [T, K].  Returns (o [n_rows, H, 512], lse [n_rows, H]) in float64."""
+                sm_scale=None, rows=None, fmt=0):
+    """Global sparse branch.  q bf16 bits [T, H, 576]; planes in physical rows (kv_scl
+    [*, 16] E8M0 for fmt 0, [*, 32] E4M3 for fmt 1); idx i32 [T, K].  Returns
+    (o [n_rows, H, 512], lse [n_rows, H]) in float64."""
     q = _c(q, np.uint16)
     T, H = q.shape[0], q.shape[1]
     idx = _c(idx, np.int32)
@@ -213,9 +252,9 @@ def sparse_attn(max_pages, q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx,
     lse = np.empty((rows.shape[0], H), dtype=np.float64)
     lat, scl = _c(kv_lat, np.uint8), _c(kv_scl, np.uint8)
     rope, pt, sid = _c(kv_rope, np.uint16), _c(page_table, np.int32), _c(seq_id, np.int32)
-    lib().csa2o_sparse_attn(H, K, max_pages, _p(q), _p(lat), _p(scl), _p(rope), _p(pt),
-                            _p(sid), _p(idx), float(sm_scale), _p(rows), rows.shape[0], _p(o),
-                            _p(lse))
+    lib().csa2o_sparse_attn_fmt(H, K, max_pages, _p(q), _p(lat), _p(scl), int(fmt), _p(rope),
+                                _p(pt), _p(sid), _p(idx), float(sm_scale), _p(rows),
+                                rows.shape[0], _p(o), _p(lse))
     return o, lse
 
 

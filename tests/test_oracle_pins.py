@@ -563,6 +563,105 @@ def test_layer_group_pooled_reindex():
         assert np.all(np.isin(picks[picks >= 0], pool))
 
 
+# ---------------------------------------------------------------- FP4 with E4M3 scales / 16
+def test_e4m3_golden_and_all_bytes():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "e4m3_codes.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 11
+    for b, v in rows:
+        got = orc.e4m3_decode(int(b, 16))
+        assert got == float(v) and np.signbit(got) == np.signbit(float(v)), b
+    assert np.isnan(orc.e4m3_decode(0x7f)) and np.isnan(orc.e4m3_decode(0xff))
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for b in range(256):
+        got = orc.e4m3_decode(b)
+        assert (np.isnan(got) and np.isnan(ref[b])) or got == ref[b], hex(b)
+
+
+def test_e4m3_round_nearest_even_and_saturating():
+    grid = np.array([orc.e4m3_decode(b) for b in range(0x7f)])          # 0 .. 448, ascending
+    mids = (grid[1:] + grid[:-1]) / 2
+    # every midpoint goes to the neighbour with the even mantissa (even byte)
+    for k, m in enumerate(mids):
+        assert orc.e4m3_round(m) == (k if k % 2 == 0 else k + 1), m
+    rng = np.random.default_rng(4)
+    v = np.abs(rng.standard_normal(4000)) * 10.0 ** rng.integers(-4, 3, 4000)
+    for x in v:
+        b = orc.e4m3_round(x)
+        if x >= 448:
+            assert b == 0x7e
+        else:
+            assert abs(grid[b] - x) <= np.abs(grid - x).min()
+    assert orc.e4m3_round(1e9) == 0x7e and orc.e4m3_round(0.0) == 0
+
+
+def _e2m1_nearest(y):
+    """Brute force: nearest E2M1 magnitude code to y >= 0, ties to the even code."""
+    mags = np.array([orc.e2m1_decode(c) for c in range(8)])
+    d = np.abs(mags - min(y, 6.0))
+    best = np.flatnonzero(d == d.min())
+    return int(best[0] if best.size == 1 else best[best % 2 == 0][0])
+
+
+def test_fp4e4m3_quantizer_brute_force():
+    rng = np.random.default_rng(8)
+    rows = 6
+    x = rng.standard_normal((rows, 512)).astype(np.float32)
+    x *= (2.0 ** rng.integers(-12, 6, (rows, 32, 1))).repeat(16, -1).reshape(rows, 512)
+    x[0, :16] = 0.0
+    x[1, 16:32] = np.float32(1e-6) * rng.standard_normal(16)   # scale rounds to 0
+    x[2, 32:48] = [6.0, 0.75, 0.25, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, -0.75, 0, 0, 0, 0, 0, 0]
+    lat, scl = orc.fp4e4m3_quantize(x)
+    for r in range(rows):
+        for b in range(32):
+            blk = x[r, 16 * b: 16 * b + 16].astype(np.float64)
+            sb = orc.e4m3_round(np.abs(blk).max() / 6.0)
+            assert scl[r, b] == sb
+            sv = orc.e4m3_decode(sb)
+            for i in range(16):
+                byte = lat[r, 8 * b + i // 2]
+                code = (byte >> 4) if i % 2 else (byte & 15)
+                mag = _e2m1_nearest(abs(blk[i]) / sv) if sv > 0 else 0
+                assert code == (mag | (8 if np.signbit(blk[i]) else 0)), (r, b, i)
+
+
+def test_fp4e4m3_range_and_error_bound():
+    # the format's largest magnitude is 6 x 448 = 2688, the range the page gives
+    top = np.zeros((1, 512), np.float32)
+    top[0, 0] = 2688.0
+    top[0, 1] = -2688.0
+    lat, scl = orc.fp4e4m3_quantize(top)
+    assert scl[0, 0] == 0x7e
+    np.testing.assert_array_equal(orc.fp4e4m3_dequantize(lat, scl)[0, :2], [2688.0, -2688.0])
+    # |x| <= sqrt(512) never reaches the scale's saturation; the error stays within half a
+    # grid step at the block's scale, plus the clipping above 6 s
+    rng = np.random.default_rng(9)
+    x = np.clip(rng.standard_normal((64, 512)) * 8, -22.6, 22.6).astype(np.float32)
+    lat, scl = orc.fp4e4m3_quantize(x)
+    assert scl.max() < 0x7e
+    v = orc.fp4e4m3_dequantize(lat, scl)
+    s = np.array([[orc.e4m3_decode(b) for b in row] for row in scl]).repeat(16, axis=1)
+    a = np.abs(x.astype(np.float64))
+    half = np.where(a < 2 * s, 0.25, np.where(a < 4 * s, 0.5, 1.0)) * s
+    err = np.abs(v - x)
+    assert np.all(err <= np.maximum(half, a - 6 * s) + 1e-12)
+
+
+def test_attention_e4m3_planes_dense():
+    w = _small_workload(B=1, T=1, E=192, K=256, shuffle=True)
+    pt = w.page_table()
+    l, s = orc.fp4e4m3_quantize(w.latent_seq(0))
+    lat = w.to_physical(lambda b: l, pt)
+    scl = w.to_physical(lambda b: s, pt)
+    rope = w.to_physical(w.rope_seq, pt)
+    idx = np.concatenate([np.arange(192), -np.ones(64)]).astype(np.int32)[None]
+    o, lse = orc.sparse_attn(w.P, w.q(), lat, scl, rope, pt, w.seq_id(), idx, fmt=1)
+    ro, rl = _dense_reference(w.q()[0], orc.fp4e4m3_dequantize(l, s), _f(w.rope_seq(0)),
+                              1 / 24.0)
+    np.testing.assert_allclose(o[0], ro, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse[0], rl, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- KV append (block pooling)
 def _append_inputs(n=6, D=576, seed=21):
     c = synth.normal_f32(seed, 1, 0, n * 4 * D).reshape(n, 4, D)
