@@ -62,7 +62,7 @@ class Inputs:
     """Device-resident inputs of one workload, built from the seeded generator; the MXFP4
     planes are written by the library's own quantizer."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, fmt=0):
         import numpy as np
         import torch
         from fp4_compressed_sparse_amd import csa2
@@ -89,11 +89,13 @@ class Inputs:
                 L["idx_out"] = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
             if m == 0:
                 lat = torch.empty((w.n_pages, 64, 256), dtype=torch.uint8, device=dev)
-                scl = torch.empty((w.n_pages, 64, 16), dtype=torch.uint8, device=dev)
+                scl = torch.empty((w.n_pages, 64, 32 if fmt else 16), dtype=torch.uint8,
+                                  device=dev)
                 rope = torch.empty((w.n_pages, 64, 64), dtype=torch.bfloat16, device=dev)
+                quant = csa2.fp4e4m3_quantize if fmt else csa2.mxfp4_quantize
                 for b in range(w.B):
                     dst = t(w.physical_rows(b, pt))
-                    csa2.mxfp4_quantize(t(w.latent_seq(b, li)), lat, scl, dst)
+                    quant(t(w.latent_seq(b, li)), lat, scl, dst)
                     rope.view(-1, 64)[dst] = b16(w.rope_seq(b, li))
                 L["kv_lat"], L["kv_scl"], L["kv_rope"] = lat, scl, rope
             L["o"] = torch.empty((w.T, w.H, 512), dtype=torch.float32, device=dev)
@@ -103,7 +105,7 @@ class Inputs:
             self.layers.append(L)
         self.g = csa2.group_args(w.T, w.B, w.H, w.H_I, w.K, w.H_kv, w.L_swa, w.P, w.n_pages,
                                  self.page_table, self.seq_id, self.n_vis, self.swa_start,
-                                 self.swa_len)
+                                 self.swa_len, kv_format=fmt)
         self.descs = [csa2.layer_desc(
             L["mode"], L["q"], L["o"], L["lse"], q_swa=L["q_swa"], q_idx=L.get("q_idx"),
             w_idx=L.get("w_idx"), k_idx=L.get("k_idx"), kv_lat=L.get("kv_lat"),
@@ -130,7 +132,7 @@ def pool_sizes(w, sel):
     return out
 
 
-def algorithmic_bytes(w, pools=None):
+def algorithmic_bytes(w, pools=None, fmt=0):
     """Bytes each kernel class must move per step (what the method itself reads/writes once,
     not what an implementation re-reads), returned per kernel name of the library:
     per sequence, its indexer keys up to the largest visibility of its rows (128 B each),
@@ -159,7 +161,8 @@ def algorithmic_bytes(w, pools=None):
     n_layers = len(w.modes)
     idx_score = n_idx_layers * (keys * 128 + w.T * w.H_I * (64 * 2 + 4))
     topk = n_idx_layers * w.T * w.K * 4
-    attn = n_layers * (gathered * 400 + w.T * w.H * (576 * 2 + 512 * 4 + 4))
+    entry = 416 if fmt else 400                      # E4M3 per 16: 32 scale bytes, not 16
+    attn = n_layers * (gathered * entry + w.T * w.H * (576 * 2 + 512 * 4 + 4))
     swa = n_layers * (window * w.H_kv * 128 * 2 * 2 + w.T * w.H * (128 * 2 + 128 * 4 + 4))
     out = {"idx_score": idx_score, "topk": topk, "sparse_attn": attn, "swa": swa}
     if n_pool_layers:
@@ -186,11 +189,11 @@ def algorithmic_flops(w, pools=None):
             n_layers * 2 * w.H * 256 * int(win.sum()))
 
 
-def measure_extra(w, dev, steps, warmup, flush_mb):
+def measure_extra(w, dev, steps, warmup, flush_mb, fmt=0):
     """Whole-step time and per-kernel times of another workload (smaller bench)."""
     import torch
     from fp4_compressed_sparse_amd import csa2
-    inp = Inputs(w, dev)
+    inp = Inputs(w, dev, fmt)
     for _ in range(warmup):
         inp.step()
     torch.cuda.synchronize()
@@ -211,10 +214,11 @@ def measure_extra(w, dev, steps, warmup, flush_mb):
     csa2.timing_enable(False)
     kt = csa2.timing_read()
     pools = (pool_sizes(w, inp.layers[0]["idx_out"].cpu().numpy()) if 3 in w.modes else None)
-    algo = algorithmic_bytes(w, pools)
+    algo = algorithmic_bytes(w, pools, fmt)
     flops = algorithmic_flops(w, pools)
     step_bytes = sum(algo.values())
     out = {"workload": w.name, "query_rows": w.T, "entries_per_seq": w.E, "top_k": w.K,
+           "kv_format": "E2M1 + E4M3 per 16" if fmt else "MXFP4 (E2M1 + E8M0 per 32)",
            "layers": [["full", "reindex", "reuse", "reindex_pool"][m] for m in w.modes],
            "steps": steps, "ms_per_step": round(ms, 4),
            "query_tokens_per_s": round(w.T / (ms * 1e-3), 1),
@@ -449,10 +453,11 @@ def main():
         w3 = synth.workload(3)
         w3p = dataclasses.replace(w3, name=w3.name.replace("reindex", "reindexpool"),
                                   modes=[0, 3, 2])
-        for wx, steps in ((synth.workload(4), 20), (synth.workload(5), 3), (w3, 10),
-                          (w3p, 10)):
+        w2e = dataclasses.replace(synth.workload(2), name=synth.workload(2).name + "_e4m3")
+        for wx, steps, fmt in ((synth.workload(4), 20, 0), (synth.workload(5), 3, 0),
+                               (w3, 10, 0), (w3p, 10, 0), (w2e, 20, 1)):
             print(f"[bench] extra workload {wx.name}", file=sys.stderr, flush=True)
-            result["extra"].append(measure_extra(wx, dev, steps, 2, args.flush_mb))
+            result["extra"].append(measure_extra(wx, dev, steps, 2, args.flush_mb, fmt))
         print("[bench] extra: KV append", file=sys.stderr, flush=True)
         result["extra"].append(measure_append(dev, 32768, 20, args.flush_mb))
     if args.cpu_rows > 0:

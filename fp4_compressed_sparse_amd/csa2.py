@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 D_LAT, D_ROPE, D_Q, D_IDX, D_SWA, PAGE = 512, 64, 576, 64, 128, 64
 FULL, REINDEX, REUSE, REINDEX_POOL = 0, 1, 2, 3
+KV_MXFP4, KV_FP4_E4M3 = 0, 1
 OP_INDEX_TOPK, OP_SPARSE_ATTN, OP_LAYER_GROUP, OP_INDEX_TOPK_POOL = 1, 2, 3, 4
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_NULL", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_ALIGN",
           4: "CSA2_ERR_MODE", 5: "CSA2_ERR_WORKSPACE", 6: "CSA2_ERR_UNSUPPORTED",
@@ -49,7 +50,8 @@ class AttnArgs(ctypes.Structure):
                 ("kv_rope", _vp), ("page_table", _vp), ("seq_id", _vp), ("idx", _vp),
                 ("sm_scale", _f32), ("o", _vp), ("lse", _vp), ("H_kv", _i32), ("L_swa", _i32),
                 ("q_swa", _vp), ("swa_k", _vp), ("swa_v", _vp), ("swa_start", _vp),
-                ("swa_len", _vp), ("sm_scale_swa", _f32), ("o_swa", _vp), ("lse_swa", _vp)]
+                ("swa_len", _vp), ("sm_scale_swa", _f32), ("o_swa", _vp), ("lse_swa", _vp),
+                ("kv_format", _i32)]
 
 
 class LayerDesc(ctypes.Structure):
@@ -63,10 +65,11 @@ class GroupArgs(ctypes.Structure):
     _fields_ = [("T", _i32), ("B", _i32), ("H", _i32), ("H_I", _i32), ("K", _i32),
                 ("H_kv", _i32), ("L_swa", _i32), ("max_pages", _i32), ("n_pages", _i32),
                 ("page_table", _vp), ("seq_id", _vp), ("n_vis", _vp), ("swa_start", _vp),
-                ("swa_len", _vp), ("sm_scale", _f32), ("sm_scale_swa", _f32)]
+                ("swa_len", _vp), ("sm_scale", _f32), ("sm_scale_swa", _f32),
+                ("kv_format", _i32)]
 
 
-EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize", "csa2_kv_append",
+EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize", "csa2_kv_append", "csa2_fp4e4m3_quantize",
            "csa2_workspace_bytes", "csa2_last_error", "csa2_status_string", "csa2_abi_version",
            "csa2_timing_enable", "csa2_timing_read"]
 
@@ -84,6 +87,8 @@ def _load():
     L.csa2_layer_group.restype = _i32
     L.csa2_layer_group.argtypes = [ctypes.POINTER(LayerDesc), _i32, ctypes.POINTER(GroupArgs),
                                    _vp, ctypes.c_size_t, _vp]
+    L.csa2_fp4e4m3_quantize.restype = _i32
+    L.csa2_fp4e4m3_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]
     L.csa2_kv_append.restype = _i32
     L.csa2_kv_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
     L.csa2_mxfp4_quantize.restype = _i32
@@ -182,7 +187,7 @@ def index_topk_pool(q_idx, w_idx, k_idx, page_table, seq_id, n_vis, K, sel, idx_
 
 def attn_args(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, o, lse, sm_scale=None,
               q_swa=None, swa_k=None, swa_v=None, swa_start=None, swa_len=None,
-              sm_scale_swa=None, o_swa=None, lse_swa=None):
+              sm_scale_swa=None, o_swa=None, lse_swa=None, kv_format=KV_MXFP4):
     T, H = q.shape[0], q.shape[1]
     K = idx.shape[1]
     if sm_scale is None:
@@ -194,12 +199,13 @@ def attn_args(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, o, lse, sm_sc
     return AttnArgs(T, page_table.shape[0], H, K, page_table.shape[1], kv_lat.shape[0],
                     _p(q), _p(kv_lat), _p(kv_scl), _p(kv_rope), _p(page_table), _p(seq_id),
                     _p(idx), sm_scale, _p(o), _p(lse), H_kv, L_swa, _p(q_swa), _p(swa_k),
-                    _p(swa_v), _p(swa_start), _p(swa_len), sm_scale_swa, _p(o_swa), _p(lse_swa))
+                    _p(swa_v), _p(swa_start), _p(swa_len), sm_scale_swa, _p(o_swa), _p(lse_swa),
+                    kv_format)
 
 
 def sparse_attn_fp4(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, sm_scale=None,
                     q_swa=None, swa_k=None, swa_v=None, swa_start=None, swa_len=None,
-                    sm_scale_swa=None, stream=None, out=None):
+                    sm_scale_swa=None, stream=None, out=None, kv_format=KV_MXFP4):
     """Sparse FP4 global attention (+ SWA when q_swa is given).
     kv_lat u8 [n_pages, 64, 256]; kv_scl u8 [n_pages, 64, 16]; kv_rope bf16 [n_pages, 64, 64].
     Returns (o, lse) or (o, lse, o_swa, lse_swa)."""
@@ -213,7 +219,7 @@ def sparse_attn_fp4(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, sm_scal
             out["lse_swa"] = torch.empty((T, H), dtype=torch.float32, device=dev)
     a = attn_args(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, out["o"], out["lse"],
                   sm_scale, q_swa, swa_k, swa_v, swa_start, swa_len, sm_scale_swa,
-                  out.get("o_swa"), out.get("lse_swa"))
+                  out.get("o_swa"), out.get("lse_swa"), kv_format)
     need = lib.csa2_workspace_bytes(OP_SPARSE_ATTN, ctypes.byref(a))
     ws = _ws(need, dev)
     _check(lib.csa2_sparse_attn_fp4(ctypes.byref(a), _p(ws), need, _stream(stream)))
@@ -223,13 +229,14 @@ def sparse_attn_fp4(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, sm_scal
 
 
 def group_args(T, B, H, H_I, K, H_kv, L_swa, max_pages, n_pages, page_table, seq_id, n_vis,
-               swa_start, swa_len, sm_scale=None, sm_scale_swa=None):
+               swa_start, swa_len, sm_scale=None, sm_scale_swa=None, kv_format=KV_MXFP4):
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D_Q)
     if sm_scale_swa is None:
         sm_scale_swa = 1.0 / math.sqrt(D_SWA)
     return GroupArgs(T, B, H, H_I, K, H_kv, L_swa, max_pages, n_pages, _p(page_table),
-                     _p(seq_id), _p(n_vis), _p(swa_start), _p(swa_len), sm_scale, sm_scale_swa)
+                     _p(seq_id), _p(n_vis), _p(swa_start), _p(swa_len), sm_scale, sm_scale_swa,
+                     kv_format)
 
 
 def layer_desc(mode, q, o, lse, q_swa=None, q_idx=None, w_idx=None, k_idx=None, kv_lat=None,
@@ -254,6 +261,14 @@ def mxfp4_quantize(x, lat, scl, dst_row=None, stream=None):
     """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 16] at rows dst_row (int64) or 0..rows-1."""
     rows = x.shape[0]
     _check(lib.csa2_mxfp4_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row), _stream(stream)))
+
+
+def fp4e4m3_quantize(x, lat, scl, dst_row=None, stream=None):
+    """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 32] (E4M3 per 16 channels) at rows
+    dst_row (int64) or 0..rows-1."""
+    rows = x.shape[0]
+    _check(lib.csa2_fp4e4m3_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row),
+                                     _stream(stream)))
 
 
 def kv_append(c, z, kv_lat, kv_scl, kv_rope, dst_row=None, c_idx=None, z_idx=None,

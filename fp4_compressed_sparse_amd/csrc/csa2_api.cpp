@@ -348,6 +348,9 @@ csa2_status validate_attn(const csa2_attn_args* a) {
   csa2_status st = check_paging(fn, a->B, a->max_pages, a->n_pages);
   if (st) return st;
   if (!std::isfinite(a->sm_scale)) return fail(CSA2_ERR_SHAPE, "%s: sm_scale not finite", fn);
+  if (a->kv_format != CSA2_KV_MXFP4 && a->kv_format != CSA2_KV_FP4_E4M3)
+    return fail(CSA2_ERR_UNSUPPORTED, "%s: kv_format=%d is not a known format", fn,
+                a->kv_format);
   const bool swa = a->q_swa != nullptr;
   if (swa) {
     if (a->H_kv < 1 || a->H % a->H_kv != 0)
@@ -398,6 +401,7 @@ csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
   ap.max_pages = a->max_pages;
   ap.splits = S;
   ap.per_split = per;
+  ap.fmt = a->kv_format;
   ap.sm_scale_log2 = a->sm_scale * 1.4426950408889634f;
   ap.q = static_cast<const uint16_t*>(a->q);
   ap.kv_lat = a->kv_lat;
@@ -545,6 +549,7 @@ csa2_status validate_group(const csa2_layer_desc* L, int32_t n_layers, const csa
     aa[i].page_table = g->page_table;
     aa[i].seq_id = g->seq_id;
     aa[i].sm_scale = g->sm_scale;
+    aa[i].kv_format = g->kv_format;
     aa[i].o = L[i].o;
     aa[i].lse = L[i].lse;
     aa[i].H_kv = g->H_kv;
@@ -704,6 +709,23 @@ csa2_status csa2_kv_append(const csa2_append_args* a, void* stream) {
                  static_cast<uint16_t*>(a->kv_rope), static_cast<uint16_t*>(a->k_idx)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed("kv_append", s, [&] { return launch_kv_append(p, s); });
+}
+
+csa2_status csa2_fp4e4m3_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
+                                  const int64_t* dst_row, void* stream) {
+  const char* fn = "csa2_fp4e4m3_quantize";
+  if (rows < 0) return fail(CSA2_ERR_SHAPE, "%s: rows=%lld < 0", fn, (long long)rows);
+  if (rows > (int64_t)0xffffffff * 4)
+    return fail(CSA2_ERR_SHAPE, "%s: rows=%lld too large", fn, (long long)rows);
+  if (rows == 0) return CSA2_OK;
+  REQ(x, "x");
+  REQ(lat, "lat");
+  REQ(scl, "scl");
+  if (dst_row && misaligned(dst_row))
+    return fail(CSA2_ERR_ALIGN, "%s: dst_row is not 16-byte aligned", fn);
+  QuantParams p{rows, x, lat, scl, dst_row};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed("fp4e4m3_quantize", s, [&] { return launch_fp4e4m3_quantize(p, s); });
 }
 
 size_t csa2_workspace_bytes(int32_t op, const void* args) {

@@ -74,6 +74,7 @@ inline int64_t topk_chunks(int64_t key_stride) { return (key_stride + kCkKeys - 
 
 struct AttnParams {
   int T, H, K, max_pages, splits, per_split;   // per_split: idx slots per split
+  int fmt = 0;                                  // 0: E8M0 per 32; 1: E4M3 per 16
   float sm_scale_log2;                          // sm_scale * log2(e)
   const uint16_t* q;                            // [T, H, 576]
   const uint8_t* kv_lat;
@@ -159,5 +160,6 @@ hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_swa(const SwaParams& p, hipStream_t s);
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_fp4e4m3_quantize(const QuantParams& p, hipStream_t s);
 
 }  // namespace csa2

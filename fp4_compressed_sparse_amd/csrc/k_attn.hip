@@ -48,8 +48,9 @@ constexpr int kNPre = 2;             // loop unroll: the tile parity picks the P
                                      // buffers statically
 constexpr int kRing = 4;             // raw tiles in LDS: one read, one ready, two in flight
 constexpr float kRaise = 12.f;       // log2 headroom before the running maximum is raised
-// raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16]
-constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 12800;
+// raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16] (E8M0
+// per 32 channels) or [32][32] (E4M3 per 16 channels)
+constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 13312;
 constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rope, 1 scales
 constexpr int kRawSlot = kRawBytes + 1024;   // a raw tile and the 1 KB its dead loads fill
 constexpr int kVtStride = 80;        // LDS bytes per V^T channel row (32 fp16 + 16 pad)
@@ -98,8 +99,31 @@ __device__ __forceinline__ int xcd_linear(int b, int n) {
   return (x < r8) ? x * (q8 + 1) + slot : r8 * (q8 + 1) + (x - r8) * q8 + slot;
 }
 
-template <int NHB>   // 16-head blocks per workgroup: 1, 2 or 4 (blockIdx.y picks 64-head groups)
-__global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
+// E4M3 scale byte -> (a power of two, for the conversions that apply a scale's exponent
+// only, and the remaining significand 1 + m/8, or m for the subnormals m 2^-9)
+__device__ __forceinline__ void e4m3_split(uint32_t b, float& pow2, _Float16& mant) {
+  const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+  pow2 = __uint_as_float((uint32_t)((e ? e - 7 : -9) + 127) << 23);
+  mant = (_Float16)(e ? 1.f + 0.125f * (float)m : (float)m);
+}
+
+// 8 E2M1 codes times an E4M3 scale -> 4 packed f16 pairs (exact: at most 6 significant bits,
+// magnitudes in [2^-10, 2688]).
+__device__ __forceinline__ void fp4x8_e4m3_to_f16_pairs(uint32_t w, uint32_t sbyte,
+                                                        uint32_t out[4]) {
+  float pow2;
+  _Float16 mant;
+  e4m3_split(sbyte, pow2, mant);
+  fp4x8_to_f16_pairs(w, pow2, out);
+  const f16x2 mm = {mant, mant};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    out[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, out[k]) * mm);
+}
+
+// FMT 0: MXFP4 (E8M0 scale per 32 channels); FMT 1: FP4 with an E4M3 scale per 16 channels
+template <int NHB, int FMT>   // NHB: 16-head blocks per workgroup, 1, 2 or 4 (blockIdx.y
+__global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // picks 64-head groups)
   constexpr int NW = 12;
   constexpr int NT = 64 * NW;
   constexpr int NV = 8;                              // value waves
@@ -140,7 +164,18 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   const int hb = min(wave, NHB - 1);
   const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
   u32x4 qraw[4][2][2], qrope0, qrope1;
-  if (scorer_role) {
+  if (scorer_role && FMT == 1) {
+    // FMT 1: per 128-channel chunk kk and step j, B lane (g, n) carries query channels
+    // 32(4kk + g) + 8j .. +7, the channels A lane (g, n) dequantizes from the 16-byte code
+    // slot of block 4kk + g (dword j)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qraw[kk][j >> 1][j & 1] = ld_global_16(qp + 32 * (4 * kk + g) + 8 * j);
+    qrope0 = ld_global_16(qp + kLat + 8 * g);
+    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
+  } else if (scorer_role) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
@@ -187,8 +222,12 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
       const int e = 4 * eq + k;
       const uint32_t w = *reinterpret_cast<const uint32_t*>(
           raw + kRawLat + 256 * e + 16 * lat_slot(co >> 2, e) + 4 * (co & 3));
-      const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);   // block co / 4
-      fp4x8_to_f16_pairs(w, sc, hv[k]);
+      if (FMT == 1) {
+        fp4x8_e4m3_to_f16_pairs(w, raw[kRawScl + 32 * e + (co >> 1)], hv[k]);   // group co/2
+      } else {
+        const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);        // block co/4
+        fp4x8_to_f16_pairs(w, sc, hv[k]);
+      }
     }
     uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
 #pragma unroll
@@ -217,8 +256,23 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     // bf16 value within 2^9 of the block maximum, and within 2^-16 of it below that.
     i32x8 qhi[4], qlo[4];
     int qscp = 0;                                    // byte kk: E8M0 scale of block 4kk + g
+    f16x8 qf[4][4];                                  // FMT 1: the query in fp16
+    if (FMT == 1) {
+      // bf16 -> fp16, to nearest: exact for magnitudes in [2^-14, 65504]
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = qraw[kk][j >> 1][j & 1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qf[kk][j][2 * e] = (_Float16)__uint_as_float(v[e] << 16);
+            qf[kk][j][2 * e + 1] = (_Float16)__uint_as_float(v[e] & 0xffff0000u);
+          }
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4 && FMT == 0; ++kk) {
       float x[2][16];
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
@@ -287,7 +341,8 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
             for (int mb = 0; mb < 2; ++mb) {
               ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
               al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-              ksc[mb] = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * (16 * mb + n));
+              if (FMT == 0)
+                ksc[mb] = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * (16 * mb + n));
             }
             // A scale: block 4kk + g = byte g of dword kk, shifted down (op_sel 0); B scale:
             // op_sel = kk picks byte kk of qscp
@@ -303,11 +358,37 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
     al[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[kk], al[mb], 4, 0, 0,  \
                                                                asc, kk, qscp);              \
   }
-            CSA2_QK_CHUNK(0)
-            CSA2_QK_CHUNK(1)
-            CSA2_QK_CHUNK(2)
-            CSA2_QK_CHUNK(3)
+            // FMT 1: the lane dequantizes its 8 codes of step j (dword j of the slot of block
+            // 4kk + g, E4M3 group 8kk + 2g + j/2) into fp16; fp16 MFMA; steps alternate
+            // between the two accumulators
+#define CSA2_QK_E4M3(kk)                                                                      \
+  _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                        \
+    const int e = 16 * mb + n;                                                              \
+    const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
+        raw + kRawLat + 256 * e + 16 * lat_slot(4 * (kk) + g, e));                          \
+    const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(                                \
+        raw + kRawScl + 32 * e + 8 * (kk) + 2 * g);                                         \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
+      uint32_t kv[4];                                                                       \
+      fp4x8_e4m3_to_f16_pairs(w4[j], (sc2 >> (8 * (j >> 1))) & 0xffu, kv);                  \
+      const f16x8 ka = __builtin_bit_cast(f16x8, u32x4{kv[0], kv[1], kv[2], kv[3]});        \
+      if (j & 1) al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][j], al[mb], 0, 0, 0); \
+      else ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][j], ah[mb], 0, 0, 0);  \
+    }                                                                                       \
+  }
+            if (FMT == 0) {
+              CSA2_QK_CHUNK(0)
+              CSA2_QK_CHUNK(1)
+              CSA2_QK_CHUNK(2)
+              CSA2_QK_CHUNK(3)
+            } else {
+              CSA2_QK_E4M3(0)
+              CSA2_QK_E4M3(1)
+              CSA2_QK_E4M3(2)
+              CSA2_QK_E4M3(3)
+            }
 #undef CSA2_QK_CHUNK
+#undef CSA2_QK_E4M3
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
               const int chunk = 4 * s2 + g;
@@ -389,7 +470,8 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   // by choosing what each lane fetches:
   //   j < 8      : codes of entries 4j + l/16; LDS slot l%16 holds chunk lat_slot(l%16, e)
   //   8 <= j < 12: rope of entries 8(j-8) + l/8; slot l%8 holds chunk (l%8) ^ (e%8)
-  //   j == 12    : the 16 scale bytes of entry l (lanes >= 32 fill the tile's tail)
+  //   j == 12    : the 16 scale bytes of entry l (lanes >= 32 fill the tile's tail), or
+  //                with E4M3 scales the 32 bytes of entry l/2, half l%2
   // Value wave v owns units j = v + 8c; the units past 12 load the zero row into the tail,
   // so that every value wave issues the same number of loads per tile and can wait for a
   // tile with one counter value.  Row indices are read from LDS one tile ahead.
@@ -400,12 +482,14 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {
   for (int c = 0; c < CPW; ++c) {
     const int j = rid + NV * c;
     const bool codes = j < 8, rope = !codes && j < 12, scl = j == 12;
-    const int e = codes ? 4 * j + (lane >> 4) : (rope ? 8 * (j - 8) + (lane >> 3) : (lane & 31));
+    const int e = codes ? 4 * j + (lane >> 4)
+                        : (rope ? 8 * (j - 8) + (lane >> 3) : (FMT == 1 ? lane >> 1 : lane & 31));
     u_entry[c] = e;
-    u_live[c] = codes || rope || (scl && lane < 32);
+    u_live[c] = codes || rope || (scl && (FMT == 1 || lane < 32));
     u_base[c] = codes ? p.kv_lat : (rope ? reinterpret_cast<const uint8_t*>(p.kv_rope) : p.kv_scl);
-    u_stride[c] = codes ? kLatBytes : (rope ? 2 * kRope : kScl);
-    u_goff[c] = codes ? 16 * lat_slot(lane & 15, e) : (rope ? 16 * ((lane & 7) ^ (e & 7)) : 0);
+    u_stride[c] = codes ? kLatBytes : (rope ? 2 * kRope : (FMT == 1 ? 2 * kScl : kScl));
+    u_goff[c] = codes ? 16 * lat_slot(lane & 15, e)
+                      : (rope ? 16 * ((lane & 7) ^ (e & 7)) : (FMT == 1 ? 16 * (lane & 1) : 0));
     u_dst[c] = __builtin_amdgcn_readfirstlane(codes ? kRawLat + 1024 * j
                                               : rope ? kRawRope + 1024 * (j - 8)
                                               : scl ? kRawScl : kRawBytes);
@@ -546,16 +630,23 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   if (c == 0) p.lse[(int64_t)t * p.H + h] = lse2 * 0.69314718055994530942f;
 }
 
-hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
+template <int FMT>
+hipError_t launch_sparse_attn_fmt(const AttnParams& p, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * p.splits);
   switch (p.H) {
-    case 16: CSA2_LAUNCH((sparse_attn_kernel<1>), dim3(blocks), dim3(768), s, p); break;
-    case 32: CSA2_LAUNCH((sparse_attn_kernel<2>), dim3(blocks), dim3(768), s, p); break;
-    case 64: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks), dim3(768), s, p); break;
-    case 128: CSA2_LAUNCH((sparse_attn_kernel<4>), dim3(blocks, 2), dim3(768), s, p); break;
+    case 16: CSA2_LAUNCH((sparse_attn_kernel<1, FMT>), dim3(blocks), dim3(768), s, p); break;
+    case 32: CSA2_LAUNCH((sparse_attn_kernel<2, FMT>), dim3(blocks), dim3(768), s, p); break;
+    case 64: CSA2_LAUNCH((sparse_attn_kernel<4, FMT>), dim3(blocks), dim3(768), s, p); break;
+    case 128: CSA2_LAUNCH((sparse_attn_kernel<4, FMT>), dim3(blocks, 2), dim3(768), s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
+  if (p.fmt == 1) return launch_sparse_attn_fmt<1>(p, s);
+  if (p.fmt == 0) return launch_sparse_attn_fmt<0>(p, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s) {

@@ -61,6 +61,66 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
   if ((lane & 3) == 0) p.scl[dst * kScl + (lane >> 2)] = (uint8_t)(X + 127);
 }
 
+// ---------------------------------------------------------------- E4M3 scales per 16
+// The literal format of [summary] item 5: E2M1 codes with one E4M3 scale per 16 channels
+// (OCP FP8 E4M3: bias 7, subnormals m 2^-9, largest 448).  Scale s = E4M3(max|x| / 6),
+// nearest with ties to the even significand, saturating at 448; each element |x| / s
+// rounded to the E2M1 grid with ties to the even code, saturating at 6; the sign bit is x's
+// sign; a scale that rounds to 0 leaves (signed) zeros.  Decisions are exact: max|x| / 6 is
+// taken in fp64 (its rounding to E4M3 then equals the rounding of the exact quotient), and
+// each element is compared with s times a grid midpoint, a product exact in fp32.
+__device__ __forceinline__ uint32_t e4m3_round_rne(double q) {   // q >= 0
+  if (q >= 448.0) return 0x7eu;
+  if (q < 0.015625) return (uint32_t)__builtin_rint(q * 512.0);  // subnormals, 8 = 2^-6
+  const int e = (int)((__double_as_longlong(q) >> 52) & 0x7ff) - 1023;   // floor(log2 q)
+  double k = __builtin_rint(q * __longlong_as_double((long long)(1023 + 3 - e) << 52));
+  int ee = e;
+  if (k == 16.0) { k = 8.0; ee += 1; }
+  if (ee > 8) return 0x7eu;
+  return (uint32_t)(((ee + 7) << 3) | ((int)k - 8));
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+  return e ? __uint_as_float((uint32_t)(e - 7 + 127) << 23) * (1.f + 0.125f * (float)m)
+           : 0.001953125f * (float)m;
+}
+
+__global__ __launch_bounds__(256) void fp4e4m3_quantize_kernel(QuantParams p) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= p.rows) return;
+  const int lane = threadIdx.x & 63;
+  const f32x4* xp = reinterpret_cast<const f32x4*>(p.x + r * kLat + 8 * lane);
+  const f32x4 a = xp[0], b = xp[1];
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));          // lanes 2k, 2k+1: one 16-channel group
+  const uint32_t sb = e4m3_round_rne((double)amax / 6.0);
+  const float s = e4m3_value(sb);
+  uint32_t word = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = fabsf(x[e]);
+    uint32_t code = (s > 0.f) ? (y > 0.25f * s) + (y >= 0.75f * s) + (y > 1.25f * s) +
+                                    (y >= 1.75f * s) + (y > 2.5f * s) + (y >= 3.5f * s) +
+                                    (y > 5.0f * s)
+                              : 0u;
+    code |= (__float_as_uint(x[e]) >> 31) << 3;
+    word |= code << (4 * e);
+  }
+  const int64_t dst = p.dst_row ? p.dst_row[r] : r;
+  *reinterpret_cast<uint32_t*>(p.lat + dst * kLatBytes + 4 * lane) = word;
+  if ((lane & 1) == 0) p.scl[dst * 2 * kScl + (lane >> 1)] = (uint8_t)sb;
+}
+
+hipError_t launch_fp4e4m3_quantize(const QuantParams& p, hipStream_t s) {
+  const int64_t blocks = (p.rows + 3) / 4;
+  CSA2_LAUNCH(fp4e4m3_quantize_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- KV append
 // One cache entry from a block of 4 raw tokens ([summary] Architecture Components, item 1,
 // Eq. 1: the global KV entries come from the projections C and Z of the encoder's hidden

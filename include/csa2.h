@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 #define CSA2_D_LAT 512   /* latent channels per entry (MXFP4) */
 #define CSA2_D_ROPE 64   /* rope channels per entry (bf16) */
@@ -58,6 +58,12 @@ extern "C" {
 #define CSA2_PAGE 64     /* entries per page */
 #define CSA2_MAX_H_I 16  /* indexer heads */
 #define CSA2_MAX_K 65536 /* Top-K size */
+/* Main-KV cache formats (kv_format): E2M1 codes (256 B per entry) with
+ *   CSA2_KV_MXFP4:     one E8M0 scale per 32 channels (kv_scl [*, 16]; OCP MXFP4), or
+ *   CSA2_KV_FP4_E4M3:  one E4M3 scale per 16 channels (kv_scl [*, 32]), the literal
+ *                      format of [summary] item 5 (largest magnitude 6 x 448 = 2688). */
+#define CSA2_KV_MXFP4 0
+#define CSA2_KV_FP4_E4M3 1
 
 typedef enum {
   CSA2_OK = 0,
@@ -139,10 +145,12 @@ typedef struct csa2_pool_args {
  *   keys/values at positions [swa_start[t], swa_start[t] + swa_len[t]) of sequence
  *   seq_id[t], KV head h * H_kv / H, logit = sm_scale_swa * q_swa . k;
  *   o_swa = softmax-weighted values (128-d), lse_swa; empty window: 0 / -inf.
- * Numerics: q.k in bf16 MFMA with fp32 accumulation; the probability-value product in
- * fp16 MFMA with fp32 accumulation (dequantized values are exact in fp16 for scale
- * bytes 104..140, i.e. |v| <= 49152 -- the pages bound KV magnitudes by ~22.6);
- * softmax and outputs in fp32. */
+ * Numerics: the latent q.k on the MX-scaled fp4 x fp8 matrix path (the bf16 query split
+ * into two fp8 parts; CSA2_KV_MXFP4) or in fp16 MFMA with the bf16 query rounded to fp16
+ * (CSA2_KV_FP4_E4M3: exact for query magnitudes in [2^-14, 65504]); rope q.k in bf16 MFMA;
+ * the probability-value product in fp16 MFMA with fp32 accumulation (dequantized values
+ * are exact in fp16 for E8M0 scale bytes 104..140, i.e. |v| <= 49152, and for every E4M3
+ * scale -- the pages bound KV magnitudes by ~22.6); softmax and outputs in fp32. */
 typedef struct csa2_attn_args {
   int32_t T;          /* query rows */
   int32_t B;          /* sequences */
@@ -171,6 +179,8 @@ typedef struct csa2_attn_args {
   float sm_scale_swa;          /* e.g. 1/sqrt(128) */
   float* o_swa;                /* device f32 [T, H, 128] (output) */
   float* lse_swa;              /* device f32 [T, H]      (output) */
+  int32_t kv_format;           /* CSA2_KV_MXFP4 (kv_scl [n_pages, 64, 16]) or
+                                  CSA2_KV_FP4_E4M3 (kv_scl [n_pages, 64, 32]) */
 } csa2_attn_args;
 
 /* One layer of a Full / Reindex / Reuse group ([summary] Architecture Components,
@@ -209,6 +219,7 @@ typedef struct csa2_group_args {
   const int32_t* swa_start;    /* [T] */
   const int32_t* swa_len;      /* [T] */
   float sm_scale, sm_scale_swa;
+  int32_t kv_format;           /* format of every Full layer's main-KV planes */
 } csa2_group_args;
 
 /* Indexer scoring + Top-K.  Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, a). */
@@ -264,6 +275,14 @@ typedef struct csa2_append_args {
   void* k_idx;                 /* device bf16 [rows, 64]  (output); NULL iff c_idx is */
 } csa2_append_args;
 csa2_status csa2_kv_append(const csa2_append_args* a, void* stream);
+/* Cache write in the CSA2_KV_FP4_E4M3 format ([summary] item 5, literal reading): rows
+ * x [rows, 512] -> lat [*, 256] (as csa2_mxfp4_quantize) and scl [*, 32], one E4M3 byte per
+ * 16 channels: s = E4M3(max|x| / 6), to nearest with ties to the even significand,
+ * saturating at 448; each element |x| / s rounded to E2M1 (ties to the even code,
+ * saturating at 6), sign kept; a scale that rounds to 0 gives (signed) zero codes.
+ * dst_row as for csa2_mxfp4_quantize.  Inputs must be finite. */
+csa2_status csa2_fp4e4m3_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
+                                  const int64_t* dst_row, void* stream);
 /* Workspace bytes for an operation; args points to the op's argument struct
  * (csa2_index_args, csa2_attn_args, csa2_group_args or csa2_pool_args).  Returns 0 for
  * NULL args. */

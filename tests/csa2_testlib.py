@@ -27,16 +27,18 @@ O_MAX_ABS, O_REL_L2, LSE_MAX_ABS, TOPK_REL = 2e-3, 1e-3, 1e-3, 1e-5
 class HostWorkload:
     """Oracle-side inputs and results for a synth.Workload."""
 
-    def __init__(self, w: synth.Workload, modes=None):
+    def __init__(self, w: synth.Workload, modes=None, fmt=0):
         self.w = w
+        self.fmt = fmt
         self.modes = list(modes if modes is not None else w.modes)
         self.pt = w.page_table()
         self.kv = {}
+        quant = orc.fp4e4m3_quantize if fmt == 1 else orc.mxfp4_quantize
         for li, m in enumerate(self.modes):
             if m == FULL:
                 lat_l, scl_l = [], []
                 for b in range(w.B):
-                    l, s = orc.mxfp4_quantize(w.latent_seq(b, li))
+                    l, s = quant(w.latent_seq(b, li))
                     lat_l.append(l)
                     scl_l.append(s)
                 lat = w.to_physical(lambda b: lat_l[b], self.pt)
@@ -110,7 +112,7 @@ class HostWorkload:
         idx_full[rows] = idx_rows
         q, q_swa = w.q(li), w.q_swa(li)
         o, lse = orc.sparse_attn(w.P, q, lat, scl, rope, self.pt, w.seq_id(), idx_full,
-                                 rows=rows)
+                                 rows=rows, fmt=self.fmt)
         ow, lw = orc.swa_attn(q_swa, w.swa_k(li), w.swa_v(li), w.seq_id(), w.swa_start(),
                               w.swa_len(), rows=rows)
         return {"o": o, "lse": lse, "o_swa": ow, "lse_swa": lw}
@@ -119,11 +121,12 @@ class HostWorkload:
 class DeviceWorkload:
     """GPU-side inputs (device tensors) for a synth.Workload, quantized by the library."""
 
-    def __init__(self, w: synth.Workload, device, modes=None):
+    def __init__(self, w: synth.Workload, device, modes=None, fmt=0):
         import torch
         from fp4_compressed_sparse_amd import csa2
         self.torch, self.csa2 = torch, csa2
         self.w, self.dev = w, device
+        self.fmt = fmt
         self.modes = list(modes if modes is not None else w.modes)
         pt = w.page_table()
         self.pt_host = pt
@@ -148,11 +151,13 @@ class DeviceWorkload:
                 L["idx_out"] = torch.empty((w.T, w.K), dtype=torch.int32, device=device)
             if m == FULL:
                 lat = torch.empty((w.n_pages, 64, 256), dtype=torch.uint8, device=device)
-                scl = torch.empty((w.n_pages, 64, 16), dtype=torch.uint8, device=device)
+                scl = torch.empty((w.n_pages, 64, 32 if fmt == 1 else 16), dtype=torch.uint8,
+                                  device=device)
+                quant = csa2.fp4e4m3_quantize if fmt == 1 else csa2.mxfp4_quantize
                 for b in range(w.B):
                     x = t(w.latent_seq(b, li))
                     dst = t(w.physical_rows(b, pt).astype(np.int64))
-                    csa2.mxfp4_quantize(x, lat, scl, dst)
+                    quant(x, lat, scl, dst)
                 L["kv_lat"], L["kv_scl"] = lat, scl
                 L["kv_rope"] = b16(w.to_physical(lambda b: w.rope_seq(b, li), pt)).view(
                     w.n_pages, 64, 64)
@@ -165,13 +170,13 @@ class DeviceWorkload:
     def planes_host(self, li=0):
         L = self.layers[li]
         return (L["kv_lat"].cpu().numpy().reshape(-1, 256),
-                L["kv_scl"].cpu().numpy().reshape(-1, 16))
+                L["kv_scl"].cpu().numpy().reshape(-1, L["kv_scl"].shape[-1]))
 
     def group_args(self):
         w = self.w
         return self.csa2.group_args(w.T, w.B, w.H, w.H_I, w.K, w.H_kv, w.L_swa, w.P, w.n_pages,
                                     self.page_table, self.seq_id, self.n_vis, self.swa_start,
-                                    self.swa_len)
+                                    self.swa_len, kv_format=self.fmt)
 
     def descs(self):
         c = self.csa2

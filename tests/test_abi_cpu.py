@@ -56,7 +56,7 @@ def test_struct_layout_matches_header(c, tmp_path):
 
 
 def test_version_and_strings(c):
-    assert c.abi_version() == 1
+    assert c.abi_version() == 2
     for st, name in c.STATUS.items():
         assert c.lib.csa2_status_string(st).decode() == name
 
@@ -176,6 +176,17 @@ def test_attn_validation(c, field, value, status):
     a = good_attn(c, **{field: value})
     st, msg = call_attn(c, a)
     assert st == status, msg
+
+
+def test_attn_kv_format(c):
+    st, msg = call_attn(c, good_attn(c, kv_format=2))
+    assert st == 6 and "kv_format" in msg
+    assert call_attn(c, good_attn(c, kv_format=1))[0] == 5       # valid: reaches workspace
+    q = c.lib.csa2_fp4e4m3_quantize
+    assert q(None, 4, fake(1), fake(2), None, None) == 1
+    assert q(fake(0), -1, fake(1), fake(2), None, None) == 2
+    assert q(fake(0), 4, fake(1), ctypes.c_void_p(FAKE + 4), None, None) == 3
+    assert q(None, 0, None, None, None, None) == 0
 
 
 def test_attn_swa_disabled_must_be_consistent(c):

@@ -191,14 +191,60 @@ def test_kv_append_parity(csa2, dev, n, with_idx, dst):
         assert not lat.cpu().numpy()[untouched].any()
 
 
-def _index_parity(csa2, dev, w, name):
+def test_fp4e4m3_quantize_bit_exact(csa2, dev):
+    """The E4M3-per-16 cache write against the oracle, bit for bit: random blocks over a
+    wide range of magnitudes, elements exactly at s x a grid midpoint, maxima whose /6
+    falls exactly between two E4M3 values, scales that round to 0, saturate at 448 or are
+    subnormal, zero blocks and signed zeros."""
+    _say("fp4e4m3_quantize_bit_exact")
+    rng = np.random.default_rng(2)
+    rows = 512
+    x = synth.normal_f32(6, 1, 0, rows * 512).reshape(rows, 512)
+    mult = (2.0 ** rng.integers(-24, 12, size=(rows, 32))).astype(np.float32)
+    x = (x.reshape(rows, 32, 16) * mult[:, :, None]).reshape(rows, 512).astype(np.float32)
+    e4 = np.array([orc.e4m3_decode(b) for b in range(0x7f)])
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for r in range(rows):
+        g = rng.integers(0, 32)
+        sb = int(rng.integers(1, 0x7e))
+        sv = np.float32(e4[sb])
+        blk = np.zeros(16, np.float32)
+        blk[0] = np.float32(6.0) * sv                      # max -> scale exactly sv
+        blk[1:8] = mids * sv * rng.choice([-1, 1], 7)      # ties at s x midpoints
+        blk[8:] = rng.standard_normal(8).astype(np.float32) * sv
+        x[r, 16 * g: 16 * g + 16] = blk
+        g2 = (g + 1) % 32                                  # max / 6 on an E4M3 midpoint
+        k = int(rng.integers(1, 0x7d))
+        x[r, 16 * g2] = np.float32(6.0 * (e4[k] + e4[k + 1]) / 2)
+    x[0, :16] = 0.0
+    x[0, 3] = -0.0
+    x[1, :16] = np.float32(1e-5) * np.arange(16)          # max / 6 below half of 2^-9: zeros
+    x[2, 16:32] = np.float32(3e4) * rng.choice([-1, 1], 16)  # scale saturates at 448
+    x[3, 32:48] = np.float32(0.01) * rng.standard_normal(16).astype(np.float32)  # subnormal
+    lat_ref, scl_ref = orc.fp4e4m3_quantize(x)
+    xd = torch.from_numpy(x).to(dev)
+    lat = torch.zeros((rows, 256), dtype=torch.uint8, device=dev)
+    scl = torch.zeros((rows, 32), dtype=torch.uint8, device=dev)
+    csa2.fp4e4m3_quantize(xd, lat, scl)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scl.cpu().numpy(), scl_ref)
+    np.testing.assert_array_equal(lat.cpu().numpy(), lat_ref)
+    perm = rng.permutation(rows + 5)[:rows]
+    lat2 = torch.zeros((rows + 5, 256), dtype=torch.uint8, device=dev)
+    scl2 = torch.zeros((rows + 5, 32), dtype=torch.uint8, device=dev)
+    csa2.fp4e4m3_quantize(xd, lat2, scl2, torch.from_numpy(perm.astype(np.int64)).to(dev))
+    np.testing.assert_array_equal(lat2.cpu().numpy()[perm], lat_ref)
+    np.testing.assert_array_equal(scl2.cpu().numpy()[perm], scl_ref)
+
+
+def _index_parity(csa2, dev, w, name, fmt=0):
     _say("index_topk", name)
-    d = tl.DeviceWorkload(w, dev)
+    d = tl.DeviceWorkload(w, dev, fmt=fmt)
     L = d.layers[0]
     idx = csa2.index_topk(L["q_idx"], L["w_idx"], L["k_idx"], d.page_table, d.seq_id, d.n_vis,
                           w.K)
     torch.cuda.synchronize()
-    h = tl.HostWorkload(w)
+    h = tl.HostWorkload(w, fmt=fmt)
     rows = np.arange(w.T)
     tl.check_topk(idx.cpu().numpy(), h.scores(0, rows), w.K, w.n_vis())
     return d, h, idx
@@ -209,16 +255,18 @@ def test_index_topk_parity(csa2, dev, name):
     _index_parity(csa2, dev, SMALL[name], name)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_sparse_attn_parity(csa2, dev, name):
+def test_sparse_attn_parity(csa2, dev, name, fmt):
     w = SMALL[name]
-    d, h, idx = _index_parity(csa2, dev, w, name)
-    _say("sparse_attn", name)
+    d, h, idx = _index_parity(csa2, dev, w, name, fmt=fmt)
+    _say("sparse_attn", name, "kv_format", fmt)
     L = d.layers[0]
     o, lse, ow, lw = csa2.sparse_attn_fp4(L["q"], L["kv_lat"], L["kv_scl"], L["kv_rope"],
                                           d.page_table, d.seq_id, idx, q_swa=L["q_swa"],
                                           swa_k=L["swa_k"], swa_v=L["swa_v"],
-                                          swa_start=d.swa_start, swa_len=d.swa_len)
+                                          swa_start=d.swa_start, swa_len=d.swa_len,
+                                          kv_format=fmt)
     torch.cuda.synchronize()
     rows = np.arange(w.T)
     ref = h.attn_on(idx.cpu().numpy(), 0, rows)
@@ -415,12 +463,12 @@ def test_empty_rows_and_windows(csa2, dev):
     assert z.shape == (0, w.K)
 
 
-def _group_case(csa2, dev, w, rows, name):
-    _say("layer_group", name)
-    d = tl.DeviceWorkload(w, dev)
+def _group_case(csa2, dev, w, rows, name, fmt=0):
+    _say("layer_group", name, "kv_format", fmt)
+    d = tl.DeviceWorkload(w, dev, fmt=fmt)
     res = d.run_layer_group()
     torch.cuda.synchronize()
-    h = tl.HostWorkload(w)
+    h = tl.HostWorkload(w, fmt=fmt)
     ref = h.run_layer_group(rows)
     nb = 0
     for li in range(len(w.modes)):
@@ -532,6 +580,18 @@ def test_full_size_decode_64x128k_sampled(csa2, dev):
     d, res, _ = _group_case(csa2, dev, w, rows, w.name)
     idx = res[0]["idx"]
     assert np.all(np.diff(idx, axis=1) > 0) and idx.min() >= 0 and idx.max() < w.E
+
+
+def test_full_size_decode_64x128k_e4m3_sampled(csa2, dev):
+    """The headline decode with the main KV in the E4M3-per-16 format."""
+    w = synth.workload(2)
+    _group_case(csa2, dev, w, np.array([0, 31, 63]), w.name + "_e4m3", fmt=1)
+
+
+def test_layer_group_e4m3_group_small(csa2, dev):
+    w = W(name="group_small_e4m3", B=4, T=4, E=2048, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
+          modes=[0, 1, 2])
+    _group_case(csa2, dev, w, np.arange(4), "group_small_e4m3", fmt=1)
 
 
 def test_full_size_decode_4x1m(csa2, dev):
