@@ -52,6 +52,12 @@ def parse_args():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines for the 1M-context decode and the chunked "
                          "prefill workloads")
+    ap.add_argument("--kv-format", type=int, default=0, choices=(0, 1),
+                    help="main-KV cache format of the timed workload: 0 = MXFP4 (E8M0 per 32), "
+                         "1 = E2M1 with an E4M3 scale per 16 channels")
+    ap.add_argument("--reindex-pool", action="store_true",
+                    help="the workload's Reindex layers search the candidate pool of its Full "
+                         "layer (workload 3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -283,8 +289,9 @@ def measure_append(dev, n, steps, flush_mb):
 
 
 def kernel_source_sha(name):
-    src = {"idx_score": "k_index.hip", "topk": "k_index.hip", "sparse_attn": "k_attn.hip",
-           "attn_merge": "k_attn.hip", "swa": "k_swa.hip"}.get(name)
+    src = {"idx_score": "k_index.hip", "topk": "k_index.hip", "idx_pool_score": "k_index.hip",
+           "topk_pool": "k_index.hip", "sparse_attn": "k_attn.hip", "attn_merge": "k_attn.hip",
+           "swa": "k_swa.hip", "kv_append": "k_quant.hip"}.get(name)
     if src is None:
         return None
     path = os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", src)
@@ -363,8 +370,13 @@ def main():
 
     from fp4_compressed_sparse_amd import csa2
     w = synth.workload(args.workload)
+    if args.reindex_pool:
+        w = dataclasses.replace(w, name=w.name.replace("reindex", "reindexpool"),
+                                modes=[3 if m == 1 else m for m in w.modes])
+    if args.kv_format:
+        w = dataclasses.replace(w, name=w.name + "_e4m3")
     t_build = time.perf_counter()
-    inp = Inputs(w, dev)
+    inp = Inputs(w, dev, args.kv_format)
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
     print(f"[bench] {w.name}: inputs built in {t_build:.1f} s", file=sys.stderr, flush=True)
@@ -404,7 +416,8 @@ def main():
     qtok_s = w.T / (ms_step * 1e-3)
     if args.kernel_pass_only:
         ms_step = qtok_s = None
-    algo = algorithmic_bytes(w)
+    pools = (pool_sizes(w, inp.layers[0]["idx_out"].cpu().numpy()) if 3 in w.modes else None)
+    algo = algorithmic_bytes(w, pools, args.kv_format)
     step_bytes = sum(algo.values())
     kernels = {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 3)} for k, (n, ms) in kt.items()}
     for k, v in kernels.items():
@@ -438,9 +451,10 @@ def main():
         "config": {"workload": w.name, "batch": w.T, "context_tokens": 4 * w.E,
                    "entries_per_seq": w.E, "top_k": w.K, "heads": w.H, "head_dim": 576,
                    "indexer_heads": w.H_I, "swa_window": w.n_win, "swa_kv_heads": w.H_kv,
-                   "kv_format": "MXFP4 (E2M1, E8M0 per 32) latent 512 + bf16 rope 64",
-                   "layers": ["full", "reindex", "reuse"][:len(w.modes)] if len(w.modes) > 1
-                   else ["full"], "parallelism": "single GPU"},
+                   "kv_format": ("E2M1 + E4M3 per 16" if args.kv_format else
+                                 "MXFP4 (E2M1, E8M0 per 32)") + " latent 512 + bf16 rope 64",
+                   "layers": [["full", "reindex", "reuse", "reindex_pool"][m] for m in w.modes],
+                   "parallelism": "single GPU"},
         "step_algo_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1) if ms_step else None,
         "step_hbm_frac": (round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
