@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
 // stream copies them, with their indices and in index order, into an LDS list; the last two
 // digits are then found on the list and the emission walks the list: two streams of the row
 // in all.  Otherwise the remaining digit passes and the emission each stream the row.
-constexpr int kTopkListCap = 8192;
+constexpr int kTopkListCap = 4096;
 
 __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p) {
   __shared__ TopkShared sh;
@@ -540,6 +540,135 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
       }
     }
   };
+  // Radix select of the `rank`-th largest of the first L keys of the LDS list over the
+  // first `passes` digits (3: the exact key and how many keys equal to it to keep; 2: the
+  // key with its low 8 bits cleared).
+  auto list_select = [&](int L, uint32_t rank, int passes, uint32_t& key, uint32_t& keep) {
+    uint32_t pre = 0u, rem = rank;
+#pragma unroll
+    for (int ps = 0; ps < 3; ++ps) {
+      if (ps == passes) break;                       // block-uniform
+      const uint32_t pmask = topk_prefix_mask(ps);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
+      __syncthreads();
+      for (int i = tid; i < L; i += kTopkThreads) {
+        const uint32_t k = s_lkey[i];
+        if ((k & pmask) == pre) atomicAdd(&sh.hist[topk_digit(k, ps)], 1u);
+      }
+      __syncthreads();
+      topk_find_digit(sh, rem);
+      pre |= topk_place(sh.digit, ps);
+      rem = sh.remaining;
+    }
+    key = pre;
+    keep = rem;
+  };
+  // The ordered emission from the list (it holds every key >= tau, in index order).
+  auto emit_list = [&](int L, uint32_t tau, uint32_t need_eq) {
+    uint32_t gt_base = 0u, eq_base = 0u;
+    for (int b0 = 0; b0 < L; b0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+      bool valid[4];
+      int idx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = b0 + 4 * tid + e;
+        valid[e] = i < L;
+        kv[e] = valid[e] ? s_lkey[i] : 0u;
+        idx[e] = valid[e] ? s_lidx[i] : 0;
+      }
+      topk_emit_tile(sh, kv, valid, idx, tau, need_eq, gt_base, eq_base, out);
+    }
+  };
+  // The second stream: keys >= thr into the list in index order (at most kTopkListCap are
+  // stored); returns how many there are.
+  auto compact = [&](uint32_t thr) -> uint32_t {
+    uint32_t base = 0u;
+    constexpr int kAhead = 3;                        // tiles of loads in flight
+    constexpr int kTile = 4 * kTopkThreads;
+    uint32_t kn[kAhead][4];
+    bool vn[kAhead][4];
+#pragma unroll
+    for (int a = 0; a < kAhead; ++a) load4(4 * tid + a * kTile, kn[a], vn[a]);
+    for (int t0 = 0; t0 < n; t0 += kAhead * kTile) {
+#pragma unroll
+      for (int a = 0; a < kAhead; ++a) {             // static buffer index: no register moves
+        const int tile = t0 + a * kTile;
+        if (tile >= n) break;                        // block-uniform
+        const int i0 = tile + 4 * tid;
+        uint32_t f = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f |= (uint32_t)(vn[a][e] && kn[a][e] >= thr) << e;
+        uint32_t wtot;
+        const uint32_t pre = wave_prefix_small<3>((uint32_t)__popc(f), wtot);
+        if (lane == 0) sh.wave_tot[wave] = wtot;
+        __syncthreads();
+        uint32_t off = 0u, tot = 0u;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) {
+          const uint32_t x = sh.wave_tot[w];
+          off += (w < wave) ? x : 0u;
+          tot += x;
+        }
+        uint32_t pos = base + off + pre;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((f >> e) & 1u) {
+            if (pos < (uint32_t)kTopkListCap) {
+              s_lkey[pos] = kn[a][e];
+              s_lidx[pos] = i0 + e;
+            }
+            ++pos;
+          }
+        }
+        base += tot;
+        load4(i0 + kAhead * kTile, kn[a], vn[a]);    // past n: no load
+        __syncthreads();                             // wave_tot is reused by the next tile
+      }
+    }
+    return base;
+  };
+
+  // ---- sampled threshold.  A sample of the row (one 16-key segment in every `gap`, at
+  // most kTopkListCap keys) goes to the list; its r-th largest key (to 24 bits), with r
+  // chosen so that about 1.3 K + 8 n / sample keys of the row are expected at or above
+  // it, becomes the threshold of a single full stream into the list.  When that stream holds at least
+  // K and at most kTopkListCap keys, the exact selection runs on the list; otherwise the
+  // passes below run as if no sample had been taken.
+  {
+    const int nseg = n >> 4;
+    const int gap = (nseg + kTopkListCap / 16 - 1) / (kTopkListCap / 16);
+    const int sseg = (nseg + gap - 1) / gap;         // sampled segments, <= kTopkListCap / 16
+    const int ns = 16 * sseg;
+    const uint32_t r = (uint32_t)((1.3 * (double)K * ns) / n) + 8u;
+    if (nseg > 0 && r <= (uint32_t)ns) {
+      // at most two segments' quarters per thread, both loads in flight at once
+      const int q0 = tid >> 2, q1 = q0 + kTopkThreads / 4;
+      u32x4 v0 = u32x4{0u, 0u, 0u, 0u}, v1 = u32x4{0u, 0u, 0u, 0u};
+      if (q0 < sseg) v0 = k4[((int64_t)q0 * gap * 16 + 4 * (tid & 3)) >> 2];
+      if (q1 < sseg) v1 = k4[((int64_t)q1 * gap * 16 + 4 * (tid & 3)) >> 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (q0 < sseg) s_lkey[16 * q0 + 4 * (tid & 3) + e] = v0[e];
+        if (q1 < sseg) s_lkey[16 * q1 + 4 * (tid & 3) + e] = v1[e];
+      }
+      __syncthreads();
+      uint32_t thr, unused;
+      list_select(ns, r, 2, thr, unused);
+      (void)unused;
+      __syncthreads();                               // the sample is read by all
+      const uint32_t L = compact(thr);
+      if (L >= (uint32_t)K && L <= (uint32_t)kTopkListCap) {
+        uint32_t tau, need_eq;
+        list_select((int)L, (uint32_t)K, 3, tau, need_eq);
+        emit_list((int)L, tau, need_eq);
+        return;
+      }
+      __syncthreads();
+    }
+  }
+
   uint32_t prefix = 0u, remaining = (uint32_t)K;
   int pass = 0;
   for (; pass < 3; ++pass) {
@@ -547,14 +676,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
 #pragma unroll
     for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
     __syncthreads();
-    for (int i0 = 4 * tid; i0 < n; i0 += 4 * kTopkThreads) {
-      uint32_t kv[4];
-      bool valid[4];
-      load4(i0, kv, valid);
+    // four tiles of loads in flight per thread
+    for (int i0 = 4 * tid; i0 < n; i0 += 16 * kTopkThreads) {
+      uint32_t kv[4][4];
+      bool valid[4][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (valid[e] && (kv[e] & pmask) == prefix)
-          atomicAdd(&sh.hist[topk_digit(kv[e], pass)], 1u);
+      for (int u = 0; u < 4; ++u) load4(i0 + 4 * kTopkThreads * u, kv[u], valid[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (valid[u][e] && (kv[u][e] & pmask) == prefix)
+            atomicAdd(&sh.hist[topk_digit(kv[u][e], pass)], 1u);
     }
     __syncthreads();
     topk_find_digit(sh, remaining);
@@ -570,39 +703,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
   if (pass == 0) {
     // ---- second stream: keys with top digit >= d0 into the LDS list, in index order
     const uint32_t d0 = prefix >> 20;
-    uint32_t base = 0u;
-    for (int tile = 0; tile < n; tile += 4 * kTopkThreads) {
-      const int i0 = tile + 4 * tid;
-      uint32_t kv[4];
-      bool valid[4];
-      load4(i0, kv, valid);
-      uint32_t f = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f |= (uint32_t)(valid[e] && (kv[e] >> 20) >= d0) << e;
-      uint32_t wtot;
-      const uint32_t pre = wave_prefix_small<3>((uint32_t)__popc(f), wtot);
-      if (lane == 0) sh.wave_tot[wave] = wtot;
-      __syncthreads();
-      uint32_t off = 0u, tot = 0u;
-#pragma unroll
-      for (int w = 0; w < kTopkWaves; ++w) {
-        const uint32_t x = sh.wave_tot[w];
-        off += (w < wave) ? x : 0u;
-        tot += x;
-      }
-      uint32_t pos = base + off + pre;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((f >> e) & 1u) {
-          s_lkey[pos] = kv[e];
-          s_lidx[pos] = i0 + e;
-          ++pos;
-        }
-      }
-      base += tot;
-      __syncthreads();                               // wave_tot is reused by the next tile
-    }
-    const int L = (int)base;                         // = K - rank + hist[d0] <= cap
+    const int L = (int)compact(d0 << 20);            // = K - rank + hist[d0] <= cap
     // ---- the last two digits among the list's keys in bin d0
 #pragma unroll
     for (int sub = 1; sub < 3; ++sub) {
@@ -619,21 +720,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
       prefix |= topk_place(sh.digit, sub);
       remaining = sh.remaining;
     }
-    // ---- emission from the list (it holds every key >= tau, in index order)
-    uint32_t gt_base = 0u, eq_base = 0u;
-    for (int b0 = 0; b0 < L; b0 += 4 * kTopkThreads) {
-      uint32_t kv[4];
-      bool valid[4];
-      int idx[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = b0 + 4 * tid + e;
-        valid[e] = i < L;
-        kv[e] = valid[e] ? s_lkey[i] : 0u;
-        idx[e] = valid[e] ? s_lidx[i] : 0;
-      }
-      topk_emit_tile(sh, kv, valid, idx, prefix, remaining, gt_base, eq_base, out);
-    }
+    emit_list(L, prefix, remaining);
     return;
   }
   uint32_t gt_base = 0u, eq_base = 0u;

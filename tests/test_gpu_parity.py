@@ -422,6 +422,38 @@ def test_topk_streamed_all_equal_scores(csa2, dev):
         np.testing.assert_array_equal(idx[r], np.arange(K))
 
 
+@pytest.mark.parametrize("boost", ["sampled", "unsampled"])
+def test_topk_streamed_sample_misses(csa2, dev, boost):
+    """Rows whose sample misleads the streamed Top-K's threshold: the keys at the sampled
+    16-entry segments (one in every ceil(E/16/256)) scaled x8, so the threshold keeps fewer
+    than K keys, or every other key scaled x8, so it keeps more than the list holds.  Both
+    must fall back to the exact passes and match the oracle."""
+    _say("topk_streamed_sample_misses", boost)
+    E, K, T = 65600, 512, 66
+    nseg = E // 16
+    gap = -(-nseg // 256)
+    seg = np.zeros(E // 16, bool)
+    seg[::gap] = True
+    in_sample = np.repeat(seg, 16)
+    kf = np.abs(synth.normal_f32(11, 1, 0, E * 64)).reshape(E, 64)
+    kf[in_sample if boost == "sampled" else ~in_sample] *= 8.0
+    kb = synth.f32_to_bf16_bits(kf)
+    qb = synth.f32_to_bf16_bits(np.abs(synth.normal_f32(11, 2, 0, T * 64)).reshape(T, 1, 64))
+    wv = np.ones((T, 1), np.float32)
+    pt = np.arange(E // 64, dtype=np.int32)[None]
+    sid = np.zeros(T, np.int32)
+    nv = np.full(T, E, np.int32)
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    ti = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    idx = csa2.index_topk(t16(qb), ti(wv), t16(kb).view(E // 64, 64, 64), ti(pt), ti(sid),
+                          ti(nv), K).cpu().numpy()
+    rows = np.array([0, 1, 33, 65])
+    _, s_ref = orc.index_topk(K, E // 64, qb, wv, kb, pt, sid, nv, rows=rows, want_scores=True)
+    tl.check_topk(idx[rows], s_ref, K, nv, rows=rows)
+    assert np.all(np.diff(idx, axis=1) > 0)
+
+
 def test_topk_chunked_all_equal_scores(csa2, dev):
     """Equal scores over many chunks: the lowest K indices win, in order, also when the
     selection spans several chunks."""
