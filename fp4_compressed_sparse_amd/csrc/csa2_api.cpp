@@ -164,14 +164,15 @@ csa2_status check_paging(const char* fn, int32_t B, int32_t max_pages, int32_t n
 }
 
 // Keys [T, E]; for the chunked Top-K also row histograms [T, kCkHistWords], per-chunk
-// counts [T, chunks, 2] and per-row digits [T, 8].
+// counts [T, chunks], per-row digits [T, 8] and candidate keys and indices [T, E] each.
 size_t index_ws_bytes(int32_t T, int32_t max_pages) {
   const int64_t E = (int64_t)max_pages * CSA2_PAGE;
   size_t b = round_up((size_t)T * (size_t)E * sizeof(uint32_t));
   if (topk_chunked(T, E))
     b += round_up((size_t)T * kCkHistWords * sizeof(uint32_t)) +
-         round_up((size_t)T * topk_chunks(E) * 2 * sizeof(uint32_t)) +
-         round_up((size_t)T * 8 * sizeof(uint32_t));
+         round_up((size_t)T * topk_chunks(E) * sizeof(uint32_t)) +
+         round_up((size_t)T * 8 * sizeof(uint32_t)) +
+         2 * round_up((size_t)T * (size_t)E * sizeof(uint32_t));
   if (T >= kIdxGemmMinRows) b += round_up(1024);   // the row-tiled scoring's store sink
   return b;
 }
@@ -205,6 +206,11 @@ csa2_status validate_index(const csa2_index_args* a) {
     return fail(CSA2_ERR_SHAPE, "%s: K=%d outside [1, %d]", fn, a->K, CSA2_MAX_K);
   csa2_status st = check_paging(fn, a->B, a->max_pages, a->n_pages);
   if (st) return st;
+  const int64_t E = (int64_t)a->max_pages * CSA2_PAGE;
+  if (topk_chunked(a->T, E) && topk_chunks(E) > kCkMaxChunks)
+    return fail(CSA2_ERR_UNSUPPORTED, "%s: %d rows of up to %lld entries: at most %d rows "
+                "longer than 65536 entries support up to %lld entries", fn, a->T,
+                (long long)E, kCkMaxRows, (long long)kCkMaxChunks * kCkKeys);
   if (a->T == 0) return CSA2_OK;
   REQ(a->q_idx, "q_idx");
   REQ(a->w_idx, "w_idx");
@@ -252,17 +258,21 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   tp.keys = sp.keys;
   tp.n_vis = a->n_vis;
   tp.idx_out = a->idx_out;
-  tp.ck_hist = tp.ck_counts = tp.ck_sel = nullptr;
+  tp.ck_hist = tp.ck_counts = tp.ck_sel = tp.ck_ckey = nullptr;
+  tp.ck_cidx = nullptr;
   if (!chunked) return timed("topk", s, [&] { return launch_topk(tp, s); });
   tp.ck_hist = ck;
   char* w = reinterpret_cast<char*>(ck);
   w += round_up((size_t)a->T * kCkHistWords * sizeof(uint32_t));
   tp.ck_counts = reinterpret_cast<uint32_t*>(w);
-  w += round_up((size_t)a->T * topk_chunks(E) * 2 * sizeof(uint32_t));
+  w += round_up((size_t)a->T * topk_chunks(E) * sizeof(uint32_t));
   tp.ck_sel = reinterpret_cast<uint32_t*>(w);
-  static const char* const names[6] = {"", "topk_ck_hist0", "topk_ck_hist1",
-                                       "topk_ck_hist2", "topk_ck_count", "topk_ck_emit"};
-  for (int pass = 1; pass < 6; ++pass) {
+  w += round_up((size_t)a->T * 8 * sizeof(uint32_t));
+  tp.ck_ckey = reinterpret_cast<uint32_t*>(w);
+  w += round_up((size_t)a->T * (size_t)E * sizeof(uint32_t));
+  tp.ck_cidx = reinterpret_cast<int32_t*>(w);
+  static const char* const names[4] = {"", "topk_ck_hist", "topk_ck_compact", "topk_ck_select"};
+  for (int pass = 1; pass < 4; ++pass) {
     st = timed(names[pass], s, [&] { return launch_topk_chunked(tp, pass, s); });
     if (st) return st;
   }
@@ -330,7 +340,8 @@ csa2_status run_index_pool_split(const csa2_index_args* a, const int32_t* sel, i
   tp.keys = sp.keys;
   tp.n_vis = a->n_vis;
   tp.idx_out = a->idx_out;
-  tp.ck_hist = tp.ck_counts = tp.ck_sel = nullptr;
+  tp.ck_hist = tp.ck_counts = tp.ck_sel = tp.ck_ckey = nullptr;
+  tp.ck_cidx = nullptr;
   tp.pool_sel = sel;
   tp.pool_K = K_sel;
   return timed("topk_pool", s, [&] { return launch_topk(tp, s); });

@@ -51,11 +51,14 @@ struct TopkParams {
   const uint32_t* keys;
   const int32_t* n_vis;
   int32_t* idx_out;                    // [T, K]
-  // chunked path (few long rows): workspace for per-row histograms, per-chunk counts and
-  // the digits found so far; null otherwise
+  // chunked path (few long rows): workspace for per-row histograms, per-chunk candidate
+  // counts, the digit found, and candidate keys and indices (a segment of kCkKeys per
+  // chunk, laid out like the keys); null otherwise
   uint32_t* ck_hist;                   // [T, kCkHistWords]
-  uint32_t* ck_counts;                 // [T, n_chunks, 2]
+  uint32_t* ck_counts;                 // [T, n_chunks]
   uint32_t* ck_sel;                    // [T, 8]
+  uint32_t* ck_ckey = nullptr;         // [T, key_stride]
+  int32_t* ck_cidx = nullptr;          // [T, key_stride]
   // pooled rows: keys are the 8 * pool_K slots of the pooled scoring; the output maps
   // slot 8i + o to entry 8 * (pool_sel[t, i] / 8) + o
   const int32_t* pool_sel = nullptr;
@@ -63,14 +66,16 @@ struct TopkParams {
 };
 
 // Top-K over few long rows runs chunked: rows longer than 65536 keys with at most
-// kCkMaxRows rows are split into 4096-key chunks, one workgroup each.
+// kCkMaxRows rows are split into 4096-key chunks, one workgroup each (rows of at most
+// kCkMaxChunks chunks).
 constexpr int kCkKeys = 4096;
-constexpr int kCkHistWords = 4096 + 4096 + 256;
+constexpr int kCkHistWords = 4096;
 constexpr int kCkMaxRows = 64;
+constexpr int kCkMaxChunks = 4096;
 inline bool topk_chunked(int T, int64_t key_stride) {
   return key_stride > 65536 && T <= kCkMaxRows;
 }
-inline int64_t topk_chunks(int64_t key_stride) { return (key_stride + kCkKeys - 1) / kCkKeys; }
+__host__ __device__ inline int64_t topk_chunks(int64_t key_stride) { return (key_stride + kCkKeys - 1) / kCkKeys; }
 
 struct AttnParams {
   int T, H, K, max_pages, splits, per_split;   // per_split: idx slots per split

@@ -737,13 +737,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stream_kernel(TopkParams p)
 }
 
 // ---------------------------------------------------------------- chunked Top-K
-// Few long rows: every pass runs on 4096-key chunks, one workgroup of 256 threads each
-// (16 keys per thread), so a row's work spreads over many CUs.  Passes (one launch each),
-// after the scoring launch has zeroed the row histograms: histogram of bits 31..20 (chunk histograms in LDS, non-zero bins
-// added to the row's histogram in memory); bits 19..8 of the keys under the chosen top
-// digit; bits 7..0 under the chosen 24-bit prefix; per-chunk counts above and at tau;
-// ordered emission, each chunk at the offset its predecessors' counts give.  Every pass
-// re-reads its chunk (4 B per key, L2-resident at these sizes).
+// Few long rows: the work of a row spreads over many CUs in 4096-key chunks, one
+// workgroup of 256 threads each (16 keys per thread), in three launches:
+//   1. histogram of the top digit (bits 31..20): chunk histograms in LDS, non-zero bins
+//      added to the row's histogram in memory (zeroed by the scoring launch);
+//   2. every chunk finds the digit d0 holding the K-th key from the row histogram and
+//      copies its keys with top digit >= d0, and their indices, in index order, to its own
+//      candidate segment, with a count;
+//   3. one workgroup per row finds the last two digits among the candidates of bin d0 and
+//      emits the selection chunk by chunk (candidate segments in chunk order are in index
+//      order), each chunk's candidates one emission tile.
+// Every key >= tau is a candidate, so the emission sees all it needs.
 constexpr int kCkThreads = 256;
 constexpr int kCkPerThread = kCkKeys / kCkThreads;   // 16
 
@@ -764,175 +768,222 @@ __device__ __forceinline__ void ck_load(const TopkParams& p, int t, int ch, int 
   }
 }
 
-// Digit holding the remaining-th key of a row histogram in memory (bins beyond `nbins`
-// read as zero); all threads get the digit and the rank left inside it.
-__device__ __forceinline__ void ck_find(const uint32_t* ghist, int nbins, uint32_t remaining,
-                                        uint32_t* s_hist, uint32_t* s_digit, uint32_t* s_rem,
-                                        uint32_t& digit, uint32_t& rem) {
-  for (int i = threadIdx.x; i < kHistBins; i += kCkThreads) s_hist[i] = (i < nbins) ? ghist[i] : 0u;
-  __syncthreads();
-  if (threadIdx.x < 64) topk_find_digit_w0(s_hist, remaining, s_digit, s_rem);
-  __syncthreads();
-  digit = *s_digit;
-  rem = *s_rem;
-  __syncthreads();                                   // s_hist is reused by the caller
-}
-
-// PASS 0, 1, 2: histogram of bits 31..20, 19..8, 7..0 among the keys under the prefix
-template <int PASS>
-__global__ __launch_bounds__(kCkThreads) void topk_ck_pass_kernel(TopkParams p) {
+// 1: histogram of bits 31..20 of the chunk's keys, added to the row histogram
+__global__ __launch_bounds__(kCkThreads) void topk_ck_hist_kernel(TopkParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
-  __shared__ uint32_t s_digit, s_rem;
-  const int nch = (int)((p.key_stride + kCkKeys - 1) / kCkKeys);
+  const int nch = (int)topk_chunks(p.key_stride);
   const int t = blockIdx.x / nch, ch = blockIdx.x - t * nch;
   const int n = p.n_vis[t];
   if (n <= p.K || ch * kCkKeys >= n) return;         // uniform per workgroup
-  uint32_t* hrow = p.ck_hist + (int64_t)t * kCkHistWords;
-  uint32_t* sel = p.ck_sel + (int64_t)t * 8;
   uint32_t kv[kCkPerThread];
-  ck_load(p, t, ch, n, kv);                          // in flight while the digit is found
-  uint32_t prefix = 0u, pmask = 0u;
-  if (PASS == 1) {                                   // top digit from the row histogram
-    uint32_t d0, r0;
-    ck_find(hrow, 4096, (uint32_t)p.K, s_hist, &s_digit, &s_rem, d0, r0);
-    prefix = d0 << 20;
-    pmask = 0xfff00000u;
-    if (ch == 0 && threadIdx.x == 0) { sel[0] = d0; sel[1] = r0; }
-  } else if (PASS == 2) {                            // top digit as the last launch found it
-    uint32_t d1, r1;
-    ck_find(hrow + 4096, 4096, sel[1], s_hist, &s_digit, &s_rem, d1, r1);
-    prefix = (sel[0] << 20) | (d1 << 8);
-    pmask = 0xffffff00u;
-    if (ch == 0 && threadIdx.x == 0) { sel[2] = d1; sel[3] = r1; }
-  }
+  ck_load(p, t, ch, n, kv);
   for (int i = threadIdx.x; i < kHistBins; i += kCkThreads) s_hist[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kCkPerThread; ++e) {
-    if (kv[e] != 0u && (kv[e] & pmask) == prefix) {
-      const uint32_t d = PASS == 0 ? (kv[e] >> 20) : (PASS == 1 ? ((kv[e] >> 8) & 0xfffu) : (kv[e] & 0xffu));
-      atomicAdd(&s_hist[d], 1u);
-    }
-  }
+  for (int e = 0; e < kCkPerThread; ++e)
+    if (kv[e] != 0u) atomicAdd(&s_hist[kv[e] >> 20], 1u);
   __syncthreads();
-  uint32_t* g = hrow + (PASS == 0 ? 0 : (PASS == 1 ? 4096 : 8192));
-  const int nbins = PASS == 2 ? 256 : 4096;
-  for (int i = threadIdx.x; i < nbins; i += kCkThreads) {
+  uint32_t* g = p.ck_hist + (int64_t)t * kCkHistWords;
+  for (int i = threadIdx.x; i < kHistBins; i += kCkThreads) {
     const uint32_t c = s_hist[i];
     if (c) atomicAdd(&g[i], c);
   }
 }
 
-// counts above and at tau per chunk; tau and need_eq per row
-__global__ __launch_bounds__(kCkThreads) void topk_ck_count_kernel(TopkParams p) {
+// 2: candidates of the chunk (top digit >= d0) in index order, and their count
+__global__ __launch_bounds__(kCkThreads) void topk_ck_compact_kernel(TopkParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
   __shared__ uint32_t s_digit, s_rem;
   __shared__ uint32_t s_w[kCkThreads / 64];
-  const int nch = (int)((p.key_stride + kCkKeys - 1) / kCkKeys);
+  const int nch = (int)topk_chunks(p.key_stride);
   const int t = blockIdx.x / nch, ch = blockIdx.x - t * nch;
   const int n = p.n_vis[t];
-  if (n <= p.K) return;
-  uint32_t* sel = p.ck_sel + (int64_t)t * 8;
+  if (n <= p.K || ch * kCkKeys >= n) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kv[kCkPerThread];
-  ck_load(p, t, ch, n, kv);
-  uint32_t d2, r2;
-  ck_find(p.ck_hist + (int64_t)t * kCkHistWords + 8192, 256, sel[3], s_hist, &s_digit, &s_rem, d2, r2);
-  const uint32_t tau = (sel[0] << 20) | (sel[2] << 8) | d2;
-  if (ch == 0 && threadIdx.x == 0) { sel[4] = tau; sel[5] = r2; }
-  uint32_t cg = 0u, ce = 0u;
+  ck_load(p, t, ch, n, kv);                          // in flight while the digit is found
+  for (int i = tid; i < kHistBins; i += kCkThreads)
+    s_hist[i] = p.ck_hist[(int64_t)t * kCkHistWords + i];
+  __syncthreads();
+  if (tid < 64) topk_find_digit_w0(s_hist, (uint32_t)p.K, &s_digit, &s_rem);
+  __syncthreads();
+  const uint32_t d0 = s_digit;
+  if (ch == 0 && tid == 0) {
+    uint32_t* sel = p.ck_sel + (int64_t)t * 8;
+    sel[0] = d0;
+    sel[1] = s_rem;
+  }
+  const uint32_t thr = d0 << 20;
+  uint32_t f = 0u;
+#pragma unroll
+  for (int e = 0; e < kCkPerThread; ++e) f |= (uint32_t)(kv[e] != 0u && kv[e] >= thr) << e;
+  uint32_t wtot;
+  const uint32_t pre = wave_prefix_small<5>((uint32_t)__popc(f), wtot);
+  if (lane == 0) s_w[wave] = wtot;
+  __syncthreads();
+  uint32_t off = 0u, tot = 0u;
+#pragma unroll
+  for (int w = 0; w < kCkThreads / 64; ++w) {
+    off += (w < wave) ? s_w[w] : 0u;
+    tot += s_w[w];
+  }
+  const int64_t seg = (int64_t)t * p.key_stride + (int64_t)ch * kCkKeys;
+  uint32_t pos = off + pre;
+  const int i0 = ch * kCkKeys + kCkPerThread * tid;
 #pragma unroll
   for (int e = 0; e < kCkPerThread; ++e) {
-    cg += kv[e] > tau;
-    ce += kv[e] == tau;
+    if ((f >> e) & 1u) {
+      p.ck_ckey[seg + pos] = kv[e];
+      p.ck_cidx[seg + pos] = i0 + e;
+      ++pos;
+    }
   }
-  const uint32_t packed = wave_sum_u32(cg | (ce << 16));
-  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = packed;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0u;
-#pragma unroll
-    for (int w = 0; w < kCkThreads / 64; ++w) tot += s_w[w];
-    uint32_t* c = p.ck_counts + ((int64_t)t * nch + ch) * 2;
-    c[0] = tot & 0xffffu;
-    c[1] = tot >> 16;
-  }
+  if (tid == 0) p.ck_counts[(int64_t)t * nch + ch] = tot;
 }
 
-// ordered emission: chunk ch writes its selected indices after those of chunks < ch
-__global__ __launch_bounds__(kCkThreads) void topk_ck_emit_kernel(TopkParams p) {
-  __shared__ int32_t s_out[kCkKeys];
-  __shared__ uint32_t s_w[kCkThreads / 64];
-  __shared__ uint32_t s_base[2];
-  const int nch = (int)((p.key_stride + kCkKeys - 1) / kCkKeys);
-  const int t = blockIdx.x / nch, ch = blockIdx.x - t * nch;
+// 3: one workgroup per row: the last two digits among the candidates, then the emission.
+// The candidates usually fit an LDS list: they are gathered there once (each thread takes
+// list positions, finds their chunk by binary search over the chunks' offsets, and has all
+// its loads in flight at once); otherwise the passes and the emission read the candidate
+// segments in memory.
+constexpr int kCkListCap = 8192;
+
+__global__ __launch_bounds__(kTopkThreads) void topk_ck_select_kernel(TopkParams p) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t s_cnt[kCkMaxChunks];
+  __shared__ uint32_t s_off[kCkMaxChunks + 1];
+  __shared__ uint32_t s_lkey[kCkListCap];
+  __shared__ int32_t s_lidx[kCkListCap];
+  const int t = blockIdx.x;
   const int n = p.n_vis[t];
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (n <= K) {                                      // every visible entry is selected
-    for (int i = ch * kCkKeys + tid; i < min((ch + 1) * kCkKeys, K); i += kCkThreads)
-      out[i] = (i < n) ? i : -1;
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
     return;
   }
-  const uint32_t* sel = p.ck_sel + (int64_t)t * 8;
-  const uint32_t tau = sel[4], need_eq = sel[5];
-  // keys above / at tau in the chunks before this one
-  if (wave == 0) {
-    uint32_t gt = 0u, eq = 0u;
-    for (int c = lane; c < ch; c += 64) {
-      gt += p.ck_counts[((int64_t)t * nch + c) * 2];
-      eq += p.ck_counts[((int64_t)t * nch + c) * 2 + 1];
+  const int nch = (int)topk_chunks(p.key_stride);
+  const int nrow = (n + kCkKeys - 1) / kCkKeys;      // chunks holding visible keys
+  // counts and their exclusive prefix: thread tid owns chunks 4 tid .. 4 tid + 3
+  uint32_t c4[4], own = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = 4 * tid + e;
+    c4[e] = (c < nrow) ? p.ck_counts[(int64_t)t * nch + c] : 0u;
+    own += c4[e];
+  }
+  const uint32_t incl = wave_incl_scan(own);
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - own, total = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t x = sh.wave_tot[w];
+    before += (w < wave) ? x : 0u;
+    total += x;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = 4 * tid + e;
+    if (c < nrow) {
+      s_cnt[c] = c4[e];
+      s_off[c] = before;
     }
-    gt = wave_sum_u32(gt);
-    eq = wave_sum_u32(eq);
-    if (lane == 0) { s_base[0] = gt; s_base[1] = eq; }
+    before += c4[e];
   }
-  uint32_t kv[kCkPerThread];
-  ck_load(p, t, ch, n, kv);
-  uint32_t gtm = 0u, eqm = 0u;
+  if (tid == 0) s_off[nrow] = total;
+  const uint32_t* sel = p.ck_sel + (int64_t)t * 8;
+  uint32_t prefix = sel[0] << 20, remaining = sel[1];
+  const uint32_t* ckey = p.ck_ckey + (int64_t)t * p.key_stride;
+  const int32_t* cidx = p.ck_cidx + (int64_t)t * p.key_stride;
+  __syncthreads();                                   // s_cnt, s_off; wave_tot read by all
+  const bool in_lds = total <= (uint32_t)kCkListCap;
+  if (in_lds) {
+    const int L = (int)total;
+    for (int p0 = tid; p0 < L; p0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+      int iv[4];
 #pragma unroll
-  for (int e = 0; e < kCkPerThread; ++e) {
-    gtm |= (uint32_t)(kv[e] > tau) << e;
-    eqm |= (uint32_t)(kv[e] == tau) << e;
-  }
-  const uint32_t cg = (uint32_t)__popc(gtm), ce = (uint32_t)__popc(eqm);
-  uint32_t wg, we;
-  const uint32_t pg = wave_prefix_small<5>(cg, wg);
-  const uint32_t pe = wave_prefix_small<5>(ce, we);
-  if (lane == 0) s_w[wave] = wg | (we << 16);
-  __syncthreads();
-  uint32_t off = 0u;
-  for (int w = 0; w < wave; ++w) off += s_w[w];
-  uint32_t chunk_sel = 0u;                           // selected in this chunk
-  const uint32_t gt0 = s_base[0], eq0 = s_base[1];
-  {
-    uint32_t tot = 0u;
+      for (int u = 0; u < 4; ++u) {                  // four loads of each kind in flight
+        const int pos = p0 + u * kTopkThreads;
+        if (pos < L) {
+          int lo = 0, hi = nrow;                     // last chunk with s_off[c] <= pos
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= (uint32_t)pos) lo = mid; else hi = mid;
+          }
+          const int64_t at = (int64_t)lo * kCkKeys + (pos - (int)s_off[lo]);
+          kv[u] = ckey[at];
+          iv[u] = cidx[at];
+        }
+      }
 #pragma unroll
-    for (int w = 0; w < kCkThreads / 64; ++w) tot += s_w[w];
-    const uint32_t tg = tot & 0xffffu, te = tot >> 16;
-    const uint32_t eq_sel = min(sub_sat_u32(need_eq, eq0), te);
-    chunk_sel = tg + eq_sel;
+      for (int u = 0; u < 4; ++u) {
+        const int pos = p0 + u * kTopkThreads;
+        if (pos < L) {
+          s_lkey[pos] = kv[u];
+          s_lidx[pos] = iv[u];
+        }
+      }
+    }
   }
-  const uint32_t gtb = (off & 0xffffu) + pg;         // within the chunk
-  const uint32_t eqb = eq0 + (off >> 16) + pe;       // global rank of this thread's first tie
-  uint32_t r = min(sub_sat_u32(need_eq, eqb), ce);
-  uint32_t selm = gtm;
-  while (r--) {
-    const uint32_t low = eqm & (0u - eqm);
-    selm |= low;
-    eqm ^= low;
+#pragma unroll
+  for (int sub = 1; sub < 3; ++sub) {
+    const uint32_t pmask = topk_prefix_mask(sub);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
+    __syncthreads();                                 // (also: the list is written)
+    if (in_lds) {
+      for (int i = tid; i < (int)total; i += kTopkThreads) {
+        const uint32_t k = s_lkey[i];
+        if ((k & pmask) == prefix) atomicAdd(&sh.hist[topk_digit(k, sub)], 1u);
+      }
+    } else {
+      for (int c = 0; c < nrow; ++c) {
+        const int cnt = (int)s_cnt[c];
+        for (int j = tid; j < cnt; j += kTopkThreads) {
+          const uint32_t k = ckey[(int64_t)c * kCkKeys + j];
+          if ((k & pmask) == prefix) atomicAdd(&sh.hist[topk_digit(k, sub)], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    topk_find_digit(sh, remaining);
+    prefix |= topk_place(sh.digit, sub);
+    remaining = sh.remaining;
   }
-  const uint32_t eq_before = min(eqb, need_eq) - min(eq0, need_eq);
-  uint32_t pos = gtb + eq_before;                    // position within the chunk's output
-  const int i0 = ch * kCkKeys + kCkPerThread * tid;
-  while (selm) {
-    s_out[pos++] = i0 + (int)__builtin_ctz(selm);
-    selm &= selm - 1;
+  uint32_t gt_base = 0u, eq_base = 0u;
+  if (in_lds) {
+    for (int b0 = 0; b0 < (int)total; b0 += 4 * kTopkThreads) {
+      uint32_t kv[4];
+      bool valid[4];
+      int idx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = b0 + 4 * tid + e;
+        valid[e] = i < (int)total;
+        kv[e] = valid[e] ? s_lkey[i] : 0u;
+        idx[e] = valid[e] ? s_lidx[i] : 0;
+      }
+      topk_emit_tile(sh, kv, valid, idx, prefix, remaining, gt_base, eq_base, out);
+    }
+    return;
   }
-  __syncthreads();
-  const uint32_t base = gt0 + min(eq0, need_eq);     // selected before this chunk
-  for (uint32_t i = tid; i < chunk_sel && base + i < (uint32_t)K; i += kCkThreads)
-    out[base + i] = s_out[i];
+  for (int c = 0; c < nrow; ++c) {                   // each chunk's candidates one tile
+    const int cnt = (int)s_cnt[c];
+    uint32_t kv[4];
+    bool valid[4];
+    int idx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * tid + e;
+      valid[e] = j < cnt;
+      kv[e] = valid[e] ? ckey[(int64_t)c * kCkKeys + j] : 0u;
+      idx[e] = valid[e] ? cidx[(int64_t)c * kCkKeys + j] : 0;
+    }
+    topk_emit_tile(sh, kv, valid, idx, prefix, remaining, gt_base, eq_base, out);
+  }
 }
 
 // ---------------------------------------------------------------- scoring, many rows
@@ -1145,17 +1196,15 @@ hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One pass of the chunked Top-K (1..3: digit passes, 4: counts, 5: emit); the row
-// histograms must be zero before pass 1.
+// One launch of the chunked Top-K (1: top-digit histogram, 2: candidates, 3: selection and
+// emission); the row histograms must be zero before launch 1.
 hipError_t launch_topk_chunked(const TopkParams& p, int pass, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)p.T * topk_chunks(p.key_stride));
   const dim3 block(kCkThreads);
   switch (pass) {
-    case 1: CSA2_LAUNCH(topk_ck_pass_kernel<0>, dim3(blocks), block, s, p); break;
-    case 2: CSA2_LAUNCH(topk_ck_pass_kernel<1>, dim3(blocks), block, s, p); break;
-    case 3: CSA2_LAUNCH(topk_ck_pass_kernel<2>, dim3(blocks), block, s, p); break;
-    case 4: CSA2_LAUNCH(topk_ck_count_kernel, dim3(blocks), block, s, p); break;
-    case 5: CSA2_LAUNCH(topk_ck_emit_kernel, dim3(blocks), block, s, p); break;
+    case 1: CSA2_LAUNCH(topk_ck_hist_kernel, dim3(blocks), block, s, p); break;
+    case 2: CSA2_LAUNCH(topk_ck_compact_kernel, dim3(blocks), block, s, p); break;
+    case 3: CSA2_LAUNCH(topk_ck_select_kernel, dim3((unsigned)p.T), dim3(kTopkThreads), s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
