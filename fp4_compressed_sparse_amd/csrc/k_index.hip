@@ -12,7 +12,13 @@
 // order, -1 padded.  Radix select over order-preserving u32 keys (digits of 12, 12 and
 // 8 bits) finds the K-th key tau and how many keys equal to tau to keep; an ordered
 // block-wide scan then compacts the selected indices in index order.  Rows of up to 64K
-// entries are read once into registers; longer rows are streamed per pass.
+// entries are read once into registers; few longer rows spread over many workgroups in
+// 4096-key chunks; many longer rows are streamed, one workgroup each, through a list of
+// candidates above a sampled threshold.
+//
+// Pooled search (hierarchical indexer, [summary] item 3): the same scoring over the
+// aligned 8-entry blocks that hold a Full layer's selection, then the register Top-K over
+// those slots.
 #include "csa2_internal.h"
 #include "csa2_device.h"
 

@@ -222,7 +222,9 @@ typedef struct csa2_group_args {
   int32_t kv_format;           /* format of every Full layer's main-KV planes */
 } csa2_group_args;
 
-/* Indexer scoring + Top-K.  Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, a). */
+/* Indexer scoring + Top-K.  Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, a).
+ * CSA2_ERR_UNSUPPORTED: at most 64 rows with max_pages * 64 above 16,777,216 entries (few
+ * long rows are split into 4096-entry chunks, at most 4096 of them per row). */
 csa2_status csa2_index_topk(const csa2_index_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /* Hierarchical-indexer search of a candidate pool (scoring + Top-K over the pool).
