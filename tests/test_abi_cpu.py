@@ -110,6 +110,14 @@ def test_index_alignment_and_workspace(c):
     assert c.lib.csa2_index_topk(None, None, 0, None) == 1
 
 
+def test_index_chunked_row_length_limit(c):
+    # few rows longer than 65536 entries run chunked, at most 4096 chunks of 4096 per row
+    st, msg = call_index(c, good_index(c, max_pages=262145))
+    assert st == 6 and "entries" in msg
+    assert call_index(c, good_index(c, max_pages=262144))[0] == 5     # valid: workspace next
+    assert call_index(c, good_index(c, T=65, max_pages=262145))[0] == 5   # streamed rows
+
+
 def test_t_zero_is_noop(c):
     a = good_index(c, T=0, q_idx=None, idx_out=None)
     assert call_index(c, a)[0] == 0
