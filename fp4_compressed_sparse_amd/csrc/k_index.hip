@@ -76,17 +76,10 @@ __device__ __forceinline__ float idx_score_64(const u32x4& qa0, const u32x4& qa1
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-__device__ __forceinline__ void idx_score_page(const u32x4& qa0, const u32x4& qa1,
-                                               const float (&w)[4], const u32x4 (&kb)[8],
-                                               int valid, int n, int g, uint32_t* keys) {
-  const float tot = idx_score_64(qa0, qa1, w, kb);
-  if (16 * g + n < valid) keys[16 * g + n] = float_key(tot);
-}
-
 // One workgroup scores kIdxChunk consecutive entries of one row, each wave a run of whole
 // pages.  The wave resolves its pages' physical numbers once (one page-table entry per
 // lane, broadcast by shuffle) and keeps the next page's 8 KB of keys in flight while it
-// scores the current one.
+// scores the current one; the run's keys are stored at its end.
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
   // zero a workspace area for the Top-K that follows
   for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
@@ -121,15 +114,24 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
 
   const int span = j_end - j_begin;           // valid entries of page pi: span - 64*pi
   auto valid_in = [&](int pi) { return min(kPage, span - kPage * pi); };
-  u32x4 bufA[8], bufB[8];
-  idx_load_page(p.k_idx, __shfl(my_page, 0), valid_in(0), n, g, bufA);
-  for (int pi = 0; pi < npages; pi += 2) {
-    if (pi + 1 < npages) idx_load_page(p.k_idx, __shfl(my_page, pi + 1), valid_in(pi + 1), n, g, bufB);
-    idx_score_page(qa0, qa1, w, bufA, valid_in(pi), n, g, keys + kPage * pi);
-    if (pi + 2 < npages) idx_load_page(p.k_idx, __shfl(my_page, pi + 2), valid_in(pi + 2), n, g, bufA);
-    if (pi + 1 < npages)
-      idx_score_page(qa0, qa1, w, bufB, valid_in(pi + 1), n, g, keys + kPage * (pi + 1));
+  // The scores stay in registers until the last page: a store inside the loop would sit
+  // among the memory operations that each page's wait counts, so every page would also
+  // wait for the previous page's store to be acknowledged.
+  float sc[kIdxPagesPerWave];
+  u32x4 buf[2][8];
+  idx_load_page(p.k_idx, __shfl(my_page, 0), valid_in(0), n, g, buf[0]);
+#pragma unroll
+  for (int pi = 0; pi < kIdxPagesPerWave; ++pi) {
+    sc[pi] = 0.f;
+    if (pi < npages) {                        // wave-uniform
+      if (pi + 1 < npages)
+        idx_load_page(p.k_idx, __shfl(my_page, pi + 1), valid_in(pi + 1), n, g, buf[(pi + 1) & 1]);
+      sc[pi] = idx_score_64(qa0, qa1, w, buf[pi & 1]);
+    }
   }
+#pragma unroll
+  for (int pi = 0; pi < kIdxPagesPerWave; ++pi)
+    if (pi < npages && 16 * g + n < valid_in(pi)) keys[kPage * pi + 16 * g + n] = float_key(sc[pi]);
 }
 
 // ---------------------------------------------------------------- pooled scoring
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
 // lowest entry.  Each wave takes kPoolSelPerWave consecutive selections, one per lane
 // (block row and visible count resolved once), and scores them in groups of 64 slots; a
 // group is scored like a 64-entry page whose rows come 8 at a time from 8 lanes' blocks.
-// The next group's 8 KB of keys is in flight while the current one is scored.
+// The next group's 8 KB of keys is in flight while the current one is scored; the keys are
+// stored after the last group.
 __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
   const int t = blockIdx.x / p.chunks;
   const int c = blockIdx.x - t * p.chunks;
@@ -197,19 +200,26 @@ __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
       }
     }
   };
-  // lane (g, n) holds slot 16g + n of the group: entry n & 7 of selection 8v + 2g + (n >> 3)
-  auto score_group = [&](int v, const u32x4 (&kb)[8]) {
-    const float tot = idx_score_64(qa0, qa1, w, kb);
-    const bool ok = (n & 7) < __shfl(bvis, 8 * v + 2 * g + (n >> 3));
-    keys[64 * v + 16 * g + n] = ok ? float_key(tot) : 0u;
-  };
-  u32x4 bufA[8], bufB[8];
-  load_group(0, bufA);
-  for (int v = 0; v < ngroups; v += 2) {
-    if (v + 1 < ngroups) load_group(v + 1, bufB);
-    score_group(v, bufA);
-    if (v + 2 < ngroups) load_group(v + 2, bufA);
-    if (v + 1 < ngroups) score_group(v + 1, bufB);
+  // lane (g, n) holds slot 16g + n of the group: entry n & 7 of selection 8v + 2g + (n >> 3);
+  // the keys are stored after the last group (no store among the loads' waits)
+  constexpr int kGroups = kPoolSelPerWave / 8;
+  float sc[kGroups];
+  u32x4 buf[2][8];
+  load_group(0, buf[0]);
+#pragma unroll
+  for (int v = 0; v < kGroups; ++v) {
+    sc[v] = 0.f;
+    if (v < ngroups) {                               // wave-uniform
+      if (v + 1 < ngroups) load_group(v + 1, buf[(v + 1) & 1]);
+      sc[v] = idx_score_64(qa0, qa1, w, buf[v & 1]);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < kGroups; ++v) {
+    if (v < ngroups) {
+      const bool ok = (n & 7) < __shfl(bvis, 8 * v + 2 * g + (n >> 3));
+      keys[64 * v + 16 * g + n] = ok ? float_key(sc[v]) : 0u;
+    }
   }
 }
 
