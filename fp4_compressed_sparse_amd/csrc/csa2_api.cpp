@@ -403,8 +403,10 @@ csa2_status validate_attn(const csa2_attn_args* a) {
 
 csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
   if (a->T == 0) return CSA2_OK;
+  // with an SWA branch on persistent workgroups beside it, plan for the CUs they leave
+  const int swa_wgs = a->q_swa ? swa_persist_wgs(a->T, a->H, a->H_kv) : 0;
   int S, per;
-  attn_plan(a->T, a->H, a->K, &S, &per);
+  attn_plan(a->T, a->H, a->K, &S, &per, kNumCus - swa_wgs);
   AttnParams ap;
   ap.T = a->T;
   ap.H = a->H;
@@ -459,6 +461,7 @@ csa2_status run_swa(const csa2_attn_args* a, hipStream_t s) {
     wp.len = a->swa_len;
     wp.o = a->o_swa;
     wp.lse = a->lse_swa;
+    wp.wgs = swa_persist_wgs(a->T, a->H, a->H_kv);
     st = timed("swa", s, [&] { return launch_swa(wp, s); });
     if (st) return st;
   }

@@ -113,6 +113,8 @@ struct SwaParams {
   const int32_t* len;
   float* o;                            // [T, H, 128]
   float* lse;                          // [T, H]
+  int wgs = 0;                         // > 0: that many one-per-CU workgroups (decode rows,
+                                       // H == H_kv); 0: one per (row, KV head)
 };
 
 struct QuantParams {
@@ -150,8 +152,20 @@ constexpr int kPoolSelPerBlock = 4 * kPoolSelPerWave;   // per workgroup (4 wave
 inline int64_t pool_key_stride(int pool_K) { return ((int64_t)kPoolBlock * pool_K + 63) / 64 * 64; }
 
 // Split plan of the attention launch: `splits` workgroups per row, each covering
-// `per_split` (a multiple of 32, <= 2048) consecutive index slots.
-void attn_plan(int T, int H, int K, int* splits, int* per_split);
+// `per_split` (a multiple of 32, <= 2048) consecutive index slots, sized to fill `cus`
+// CUs (a smaller budget never gives more splits).
+constexpr int kNumCus = 256;
+void attn_plan(int T, int H, int K, int* splits, int* per_split, int cus = kNumCus);
+
+// The SWA branch beside the global one, for decode rows with H == H_kv: this many
+// persistent one-per-CU workgroups (16 (row, KV head) units in flight each), or 0 for the
+// one-workgroup-per-unit launch.  The attention beside it is planned for the other CUs.
+constexpr int kSwaPMaxWgs = 128;
+inline int swa_persist_wgs(int T, int H, int H_kv) {
+  if (T <= 0 || T >= kSwaTileMinRows || H != H_kv) return 0;
+  const int64_t w = ((int64_t)T * H_kv + 15) / 16;
+  return (int)(w < kSwaPMaxWgs ? w : kSwaPMaxWgs);
+}
 // 64-head workgroups per (row, split) of the sparse attention kernel
 inline int attn_head_groups(int H) { return H > 64 ? H / 64 : 1; }
 

@@ -55,11 +55,14 @@ constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rop
 constexpr int kRawSlot = kRawBytes + 1024;   // a raw tile and the 1 KB its dead loads fill
 constexpr int kVtStride = 80;        // LDS bytes per V^T channel row (32 fp16 + 16 pad)
 
-void attn_plan(int T, int H, int K, int* splits, int* per_split) {
+void attn_plan(int T, int H, int K, int* splits, int* per_split, int cus) {
   const int groups = attn_head_groups(H);
   const int min_s = (K + kMaxPerSplit - 1) / kMaxPerSplit;
   const int max_s = max(1, (K + 2 * kTE - 1) / (2 * kTE));   // >= 2 tiles per split
-  int s = (T > 0) ? (256 + T * groups - 1) / (T * groups) : 1;
+  cus = max(1, min(cus, kNumCus));
+  // as many splits as fit the CUs in one round (a second round of a few workgroups would
+  // cost a whole split's time)
+  int s = (T > 0) ? max(1, cus / (T * groups)) : 1;
   s = min(s, max_s);
   s = max(s, min_s);
   // whole tiles per split; the split count follows from the rounded slot count
