@@ -69,6 +69,10 @@ hipEvent_t timing_event() {
 
 // Launch `fn` (returning hipError_t, one kernel launch) on `s`; while timing is on, the
 // launch itself records a start and a stop event, so the pair brackets the kernel alone.
+// With kernel timing off: an event that the next launch records as it completes (set to
+// fork the side stream off a kernel without a separate event packet in the stream).
+thread_local hipEvent_t g_stop_next = nullptr;
+
 template <class F>
 csa2_status timed(const char* name, hipStream_t s, F&& fn) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -81,6 +85,9 @@ csa2_status timed(const char* name, hipStream_t s, F&& fn) {
   if (e0 && e1) {
     csa2::g_launch_events[0] = e0;
     csa2::g_launch_events[1] = e1;
+  } else if (g_stop_next) {
+    csa2::g_launch_events[1] = g_stop_next;
+    g_stop_next = nullptr;
   }
   hipError_t err = fn();
   csa2::g_launch_events[0] = csa2::g_launch_events[1] = nullptr;
@@ -648,10 +655,18 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
   Side* sd = (any_swa && !g_timing.on) ? side_for_current_device() : nullptr;
   csa2_status st_swa = CSA2_OK;
   bool forked = false;
-  auto swa_now = [&](int i) -> csa2_status {
+  // The fork event is recorded by the scoring launch itself when there is one (an event
+  // record of its own would add a packet, and a gap, between the scoring and Top-K).
+  auto swa_now = [&](int i, bool after_launch) -> csa2_status {
     if (!sd) return CSA2_OK;
-    csa2_status f = fork_to(sd, s);
-    if (f) return f;
+    if (after_launch && g_stop_next == nullptr) {    // the scoring launch took the event
+      hipError_t e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+      if (e != hipSuccess) return fail(CSA2_ERR_HIP, "side stream fork: %s", hipGetErrorString(e));
+    } else {
+      g_stop_next = nullptr;
+      csa2_status f = fork_to(sd, s);
+      if (f) return f;
+    }
     forked = true;
     if (!st_swa) st_swa = run_swa(&aa[i], sd->s);
     return CSA2_OK;
@@ -662,12 +677,14 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
       ia.w_idx = L[i].w_idx;
       ia.k_idx = L[i].k_idx;
       ia.idx_out = L[i].idx_out;
+      if (sd) g_stop_next = sd->fork;
       if (L[i].mode == CSA2_REINDEX_POOL)   // the pool of layer 0's (Full) selection
-        st = run_index_pool_split(&ia, L[0].idx_out, g->K, ws, s, [&] { return swa_now(i); });
+        st = run_index_pool_split(&ia, L[0].idx_out, g->K, ws, s, [&] { return swa_now(i, true); });
       else
-        st = run_index_split(&ia, ws, s, [&] { return swa_now(i); });
+        st = run_index_split(&ia, ws, s, [&] { return swa_now(i, true); });
+      g_stop_next = nullptr;
     } else {
-      st = swa_now(i);
+      st = swa_now(i, false);
     }
     if (!st) st = run_attn(&aa[i], ws, s);
   }
