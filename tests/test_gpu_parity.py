@@ -390,6 +390,24 @@ def test_layer_group_rowtiled_swa_and_scoring(csa2, dev):
     assert np.all(res[0]["o_swa"][empty] == 0) and np.all(np.isneginf(res[0]["lse_swa"][empty]))
 
 
+_SW2 = _swa_windows(200, 400, 17)
+
+
+def test_layer_group_persistent_swa_ragged(csa2, dev):
+    """Decode-shaped rows with H = H_kv: the SWA branch runs on 128 persistent workgroups
+    (3200 (row, KV head) units over 2048 waves, so some waves take two units), with empty,
+    one-token and long windows over three sequences; attention runs beside it on the CUs
+    left."""
+    w = W(name="persist_swa_t200_b3_h16", B=3, T=200, E=1024, H=16, H_I=4, K=64, H_kv=16,
+          L_swa=400, seq_id_rows=(np.arange(200) % 3).astype(np.int32),
+          n_vis_rows=_gemm_nvis(200, 1024, 18), swa_start_rows=_SW2[0],
+          swa_len_rows=_SW2[1])
+    d, res, _ = _group_case(csa2, dev, w, np.arange(200), w.name)
+    empty = w.swa_len() == 0
+    assert empty.any()
+    assert np.all(res[0]["o_swa"][empty] == 0) and np.all(np.isneginf(res[0]["lse_swa"][empty]))
+
+
 # Many rows longer than 65536 keys: the streamed Top-K.  Distinct scores take the path that
 # gathers the keys at or above the top digit into LDS; all-equal scores overflow that list
 # and take the streamed digit passes.
