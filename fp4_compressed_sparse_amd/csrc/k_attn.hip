@@ -586,8 +586,9 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
 }
 
 // o = sum_s 2^(lse2_s - lse2) o_s, lse = ln 2 * lse2 with lse2 = log2 sum_s 2^lse2_s.
-// Workgroup: 2 heads of one row; the splits' log2-sum-exps go through LDS first, then each
-// thread (4 channels of one head) issues kMergeUnroll partial loads at a time.
+// Workgroup: 2 heads of one row; the splits' log2-sum-exps go through LDS, and each thread
+// (4 channels of one head) loads the partials of up to kMergeUnroll splits at a time, the
+// first batch together with the log2-sum-exps.
 constexpr int kMergeUnroll = 16;
 constexpr int kMergeMaxSplits = 512;
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
@@ -600,6 +601,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   const int h = (lin - t * per_row) * hpb + hh;
   const int c = 4 * (threadIdx.x & 127);
   const int S = p.splits;
+  // the first kMergeUnroll splits' partials are loaded before the log2-sum-exps are
+  // awaited (they do not depend on them), so both round trips overlap
+  const float* op = p.o_part + ((int64_t)t * S * p.H + h) * kLat + c;
+  f32x4 v0[kMergeUnroll];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u)                 // (u < S is uniform)
+    v0[u] = (u < S) ? *reinterpret_cast<const f32x4*>(op + (int64_t)u * p.H * kLat)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
   const float* lp = p.lse_part + (int64_t)t * S * p.H + (lin - t * per_row) * hpb;
   for (int i = threadIdx.x; i < hpb * S; i += 256) s_lse[i % hpb][i / hpb] = lp[(int64_t)(i / hpb) * p.H + (i % hpb)];
   __syncthreads();
@@ -614,15 +623,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
   float z = 0.f;
   for (int s = 0; s < S; ++s) z += __builtin_amdgcn_exp2f(s_lse[hh][s] - mx);
   const float lse2 = mx + __log2f(z);
-  const float* op = p.o_part + ((int64_t)t * S * p.H + h) * kLat + c;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += kMergeUnroll) {
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const float wgt = (u < S) ? __builtin_amdgcn_exp2f(s_lse[hh][min(u, S - 1)] - lse2) : 0.f;
+    acc += wgt * v0[u];
+  }
+  for (int s0 = kMergeUnroll; s0 < S; s0 += kMergeUnroll) {
     f32x4 v[kMergeUnroll];
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const int s = min(s0 + u, S - 1);
-      v[u] = *reinterpret_cast<const f32x4*>(op + (int64_t)s * p.H * kLat);
-    }
+    for (int u = 0; u < kMergeUnroll; ++u)
+      v[u] = (s0 + u < S) ? *reinterpret_cast<const f32x4*>(op + (int64_t)(s0 + u) * p.H * kLat)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const float wgt = (s0 + u < S) ? __builtin_amdgcn_exp2f(s_lse[hh][min(s0 + u, S - 1)] - lse2) : 0.f;
