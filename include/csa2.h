@@ -27,7 +27,9 @@
  *     returns.  The SWA branch runs on a library-owned stream of the current device
  *     (one per host thread, created on first use), forked from `stream` and joined back
  *     into it with events before the call returns; work queued on `stream` afterwards
- *     sees every output.  Fork and join are capturable.
+ *     sees every output.  Fork and join are capturable.  For fewer than 256 rows with
+ *     H == H_kv the branch runs on at most 128 persistent workgroups, one per CU, and the
+ *     global branch's attention is planned for the CUs left.
  *   - "device" pointers are device memory and must be 16-byte aligned.
  *   - bf16 tensors are raw 16-bit patterns; all layouts are dense row-major.
  *   - Paged caches: 64 entries per page; entry j of sequence b lives in physical row
