@@ -350,6 +350,31 @@ def cpu_baseline(w, rows, min_seconds=10.0):
                       f"repeated {reps} times: {dt:.2f} s wall"}
 
 
+def measure_hbm(dev, reps=5):
+    """A reference rate of this GPU's HBM, to read the achieved rates against besides the
+    8 TB/s peak: a 1 GiB fp32 copy (1 GiB read + 1 GiB written; bytes moved / time), the
+    median of `reps` event-timed runs on torch's stream."""
+    import torch
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        y.copy_(x)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del x, y
+    tc = sorted(ts)[reps // 2]
+    return {"copy_gbs": round(8 * n / tc / 1e9, 1),
+            "how": "median of 5 event-timed 1 GiB fp32 copies, (read + written bytes) / time"}
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse_args()
@@ -469,6 +494,13 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if not args.kernel_pass_only:
+        hbm = measure_hbm(dev)
+        hbm["step_frac_of_copy"] = (round(result["step_hbm_gbs"] / hbm["copy_gbs"], 4)
+                                    if ms_step else None)
+        hbm["roofline_frac_of_copy"] = (round(achieved / hbm["copy_gbs"], 4)
+                                        if achieved else None)
+        result["hbm_measured"] = hbm
     if not args.no_extra and not args.kernel_pass_only:
         result["extra"] = []
         w3 = synth.workload(3)
