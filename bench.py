@@ -125,6 +125,23 @@ class Inputs:
         self.csa2.layer_group(self.descs, self.g, workspace=self.ws)
 
 
+
+LLC_BYTES = 256 << 20                        # MI355X last-level cache (Infinity Cache)
+
+
+def input_sets(w, dev, fmt=0):
+    """Independent copies of the workload's device inputs (same values, own memory), enough
+    that the whole-step clock, cycling through them, streams at least twice the last-level
+    cache between two steps on the same copy: a step then finds nothing of its inputs left
+    in the cache by the previous step on them, as in a model where the other layers' data
+    passes through the cache between two steps of one layer.  (Bytes per step: the
+    algorithmic bytes, a pooled layer counted as a dense one.)"""
+    wd = dataclasses.replace(w, modes=[1 if m == 3 else m for m in w.modes])
+    per_step = sum(algorithmic_bytes(wd, None, fmt).values())
+    n = max(2, min(8, 1 + -(-2 * LLC_BYTES // max(per_step, 1))))
+    return [Inputs(w, dev, fmt) for _ in range(n)]
+
+
 # ------------------------------------------------------------------ algorithmic bytes
 def pool_sizes(w, sel):
     """Entries in each row's candidate pool: the aligned 8-entry blocks holding the row's
@@ -199,13 +216,14 @@ def measure_extra(w, dev, steps, warmup, flush_mb, fmt=0):
     """Whole-step time and per-kernel times of another workload (smaller bench)."""
     import torch
     from fp4_compressed_sparse_amd import csa2
-    inp = Inputs(w, dev, fmt)
-    for _ in range(warmup):
-        inp.step()
+    sets = input_sets(w, dev, fmt)
+    inp = sets[0]
+    for i in range(warmup):
+        sets[i % len(sets)].step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        inp.step()
+    for i in range(steps):
+        sets[i % len(sets)].step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     scratch = (torch.ones(flush_mb << 18, dtype=torch.float32, device=dev)
@@ -224,6 +242,7 @@ def measure_extra(w, dev, steps, warmup, flush_mb, fmt=0):
     flops = algorithmic_flops(w, pools)
     step_bytes = sum(algo.values())
     out = {"workload": w.name, "query_rows": w.T, "entries_per_seq": w.E, "top_k": w.K,
+           "input_copies": len(sets),
            "kv_format": "E2M1 + E4M3 per 16" if fmt else "MXFP4 (E2M1 + E8M0 per 32)",
            "layers": [["full", "reindex", "reuse", "reindex_pool"][m] for m in w.modes],
            "steps": steps, "ms_per_step": round(ms, 4),
@@ -406,26 +425,30 @@ def main():
     if args.kv_format:
         w = dataclasses.replace(w, name=w.name + "_e4m3")
     t_build = time.perf_counter()
-    inp = Inputs(w, dev, args.kv_format)
+    sets = (input_sets(w, dev, args.kv_format) if not args.kernel_pass_only
+            else [Inputs(w, dev, args.kv_format)])
+    inp = sets[0]
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
-    print(f"[bench] {w.name}: inputs built in {t_build:.1f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: {len(sets)} input set(s) built in {t_build:.1f} s",
+          file=sys.stderr, flush=True)
 
     scratch = (torch.ones(args.flush_mb << 18, dtype=torch.float32, device=dev)
                if args.flush_mb > 0 else None)
     if args.kernel_pass_only:
         csa2.timing_enable(True)
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         if args.kernel_pass_only and scratch is not None:
             scratch.sum()          # read-only sweep: no dirty lines left behind
-        inp.step()
+        sets[i % len(sets)].step()
     torch.cuda.synchronize()
     elapsed = float("nan")
     if not args.kernel_pass_only:
-        # whole-step clock: no per-kernel events inside the timed region
+        # whole-step clock: no per-kernel events inside the timed region; consecutive steps
+        # run on different input copies, so none finds its inputs in the last-level cache
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            inp.step()
+        for i in range(args.steps):
+            sets[i % len(sets)].step()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr,
@@ -491,6 +514,7 @@ def main():
         "step_hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1) if ms_step else None,
         "step_hbm_frac": (round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                           if ms_step else None),
+        "input_copies": len(sets),
         "kernels": kernels,
         "roofline": roofline,
     }

@@ -60,6 +60,11 @@ __device__ __forceinline__ u32x4 ld_global_16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// 16-byte streaming load (non-temporal: data read once, not kept in the caches for reuse)
+__device__ __forceinline__ u32x4 ld_global_16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // 16-byte load from an address held as an integer, kept in the global address space (a
 // generic pointer would become a flat load, which also counts against LDS waits).
 __device__ __forceinline__ u32x4 ld_global_16_addr(uint64_t a) {

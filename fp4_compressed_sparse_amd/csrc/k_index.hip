@@ -30,15 +30,16 @@ constexpr int kIdxPagesPerWave = kIdxPerWave / kPage;
 static_assert(kIdxPagesPerWave <= 64, "one page-table entry per lane");
 
 // Keys of one 64-entry page for the MFMA B operand: group u (entries 16u .. 16u+15 of the
-// page), lane (g, n) holds entry 16u + n, channels [16g, 16g+8) and [16g+8, 16g+16).
+// page), lane (g, n) holds entry 16u + n, channels [16g, 16g+8) and [16g+8, 16g+16).  The
+// keys are streamed once per step: non-temporal loads.
 __device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, int valid,
                                               int n, int g, u32x4 (&kb)[8]) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (16 * u + n < valid) {
       const uint16_t* kp = k_idx + ((int64_t)page * kPage + 16 * u + n) * kDidx + 16 * g;
-      kb[2 * u] = ld_global_16(kp);
-      kb[2 * u + 1] = ld_global_16(kp + 8);
+      kb[2 * u] = ld_global_16_nt(kp);
+      kb[2 * u + 1] = ld_global_16_nt(kp + 8);
     } else {
       kb[2 * u] = u32x4{0u, 0u, 0u, 0u};
       kb[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};

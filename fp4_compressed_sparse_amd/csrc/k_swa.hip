@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void swa_kernel(SwaParams p) {
     for (int u = 0; u < kSwaUnroll; ++u) {
       const int tok = 4 * (q0 + kSwaWaves * u) + g;
       if (tok < len) {
-        kv[u] = ld_global_16(p.k + base + tok * tok_stride);
-        vv[u] = ld_global_16(p.v + base + tok * tok_stride);
+        kv[u] = ld_global_16_nt(p.k + base + tok * tok_stride);
+        vv[u] = ld_global_16_nt(p.v + base + tok * tok_stride);
       } else {
         kv[u] = u32x4{0u, 0u, 0u, 0u};
         vv[u] = u32x4{0u, 0u, 0u, 0u};
@@ -158,7 +158,9 @@ __global__ __launch_bounds__(256) void swa_kernel(SwaParams p) {
 // the global branch's attention, whose workgroups each need a whole CU, runs on the rest,
 // instead of waiting for the branch's many small workgroups to drain.  One wave per unit:
 // lane (g, d) takes token 4*quad + g, channels 8d .. 8d+7, as above; the four lane groups
-// merge by shuffles and the wave writes the unit's outputs itself.
+// merge by shuffles and the wave writes the unit's outputs itself.  Window rows are read
+// once: non-temporal loads (they then displace less of what the global branch beside them
+// keeps in the caches).
 constexpr int kSwaPWaves = 16;
 constexpr int kSwaPHold = 96 * 1024;    // LDS reserved per workgroup (more than half a CU's)
 constexpr int kSwaPUnroll = 4;          // token quads in flight per wave
@@ -200,8 +202,8 @@ __global__ __launch_bounds__(64 * kSwaPWaves) void swa_persist_kernel(SwaParams 
       for (int i = 0; i < kSwaPUnroll; ++i) {
         const int tok = 4 * (q0 + i) + g;
         if (tok < len) {
-          kv[i] = ld_global_16(p.k + base + tok * tok_stride);
-          vv[i] = ld_global_16(p.v + base + tok * tok_stride);
+          kv[i] = ld_global_16_nt(p.k + base + tok * tok_stride);
+          vv[i] = ld_global_16_nt(p.v + base + tok * tok_stride);
         } else {
           kv[i] = u32x4{0u, 0u, 0u, 0u};
           vv[i] = u32x4{0u, 0u, 0u, 0u};
