@@ -10,7 +10,9 @@ with 64 KV heads of dim 128.  Seeded synthetic N(0,1) data, 1% hot indexer keys.
 One step = one Full-mode CSA2 layer through csa2_layer_group: indexer scoring, Top-K,
 FP4 gather attention (+ split merge) and the SWA branch (on the library's side stream,
 concurrent with the others), inputs resident in HBM.  The step clock runs without
-per-kernel events; a second pass of the same steps brackets every launch with HIP events
+per-kernel events and cycles through independent copies of the inputs, so that no step
+finds its inputs in the last-level cache; a second pass of the same steps brackets every
+launch with HIP events
 on the stream it runs on, after a read sweep that evicts the last-level cache before each
 step.  Prints one JSON line (metric: decode query-tokens/s), with the roofline of the
 dominant kernel of the critical path (the global branch; algorithmic bytes / its average
