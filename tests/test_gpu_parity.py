@@ -620,6 +620,28 @@ def test_determinism(csa2, dev):
         np.testing.assert_array_equal(a[k], b[k])
 
 
+def test_side_stream_schedule_matches_sequential(csa2, dev):
+    """The SWA branch on the side stream (persistent workgroups beside attention) and the
+    same layer group run in sequence on one stream (kernel timing on) give bit-identical
+    outputs: the branches share no buffer and the launch shapes are the same."""
+    _say("side_stream_vs_sequential")
+    w = W(name="sched_t96_b3", B=3, T=96, E=2048, K=512, H=64, H_I=8, H_kv=64,
+          seq_id_rows=(np.arange(96) % 3).astype(np.int32), modes=[0, 1, 2])
+    d = tl.DeviceWorkload(w, dev)
+    a = d.run_layer_group()
+    torch.cuda.synchronize()
+    csa2.timing_enable(True)
+    try:
+        b = d.run_layer_group()
+        torch.cuda.synchronize()
+    finally:
+        csa2.timing_enable(False)
+        csa2.timing_read()
+    for la, lb in zip(a, b):
+        for k in la:
+            np.testing.assert_array_equal(la[k], lb[k])
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_size_decode_64x128k_sampled(csa2, dev):
     """The headline decode workload (64 rows, 32768 entries each, K=2048, H=64) in the same
