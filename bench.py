@@ -131,17 +131,22 @@ class Inputs:
 LLC_BYTES = 256 << 20                        # MI355X last-level cache (Infinity Cache)
 
 
-def input_sets(w, dev, fmt=0):
-    """Independent copies of the workload's device inputs (same values, own memory), enough
-    that the whole-step clock, cycling through them, streams at least twice the last-level
-    cache between two steps on the same copy: a step then finds nothing of its inputs left
-    in the cache by the previous step on them, as in a model where the other layers' data
-    passes through the cache between two steps of one layer.  (Bytes per step: the
-    algorithmic bytes, a pooled layer counted as a dense one.)"""
+def input_copies(w, fmt=0):
+    """How many independent copies of the inputs the whole-step clock cycles through: enough
+    that at least twice the last-level cache is streamed between two steps on the same
+    copy (bytes per step: the algorithmic bytes, a pooled layer counted as a dense one);
+    2 to 8."""
     wd = dataclasses.replace(w, modes=[1 if m == 3 else m for m in w.modes])
     per_step = sum(algorithmic_bytes(wd, None, fmt).values())
-    n = max(2, min(8, 1 + -(-2 * LLC_BYTES // max(per_step, 1))))
-    return [Inputs(w, dev, fmt) for _ in range(n)]
+    return max(2, min(8, 1 + -(-2 * LLC_BYTES // max(per_step, 1))))
+
+
+def input_sets(w, dev, fmt=0):
+    """Independent copies of the workload's device inputs (same values, own memory): a step
+    then finds nothing of its inputs left in the last-level cache by the previous step on
+    them, as in a model where the other layers' data passes through that cache between two
+    steps of one layer."""
+    return [Inputs(w, dev, fmt) for _ in range(input_copies(w, fmt))]
 
 
 # ------------------------------------------------------------------ algorithmic bytes
