@@ -8,10 +8,15 @@
 //
 // Decode-shaped work: one query vector per head against <= a few hundred keys is a
 // matrix-vector product (about 1 flop per byte), so it runs on wavefront reductions, not
-// MFMA.  One workgroup per (row, KV head) serves the G query heads that share the KV head
-// so each K/V byte is read once.  Lane (g, d): token 4*quad + g, channels 8d .. 8d+7, so
-// each 16-lane group reads one 256-byte key row contiguously.  Waves take interleaved
-// token quads with an online softmax, then merge through LDS.
+// MFMA.  Lane (g, d): token 4*quad + g, channels 8d .. 8d+7, so each 16-lane group reads
+// one 256-byte key row contiguously.  Three forms:
+//   swa_kernel<G>       one workgroup per (row, KV head) serves the G query heads that
+//                       share the KV head, so each K/V byte is read once; waves take
+//                       interleaved token quads with an online softmax, then merge
+//                       through LDS (GQA decode rows);
+//   swa_persist_kernel  H == H_kv decode rows beside the global branch: a fixed set of
+//                       one-per-CU workgroups, one wave per (row, KV head) unit;
+//   swa_tile_kernel     many rows (prefill): row tiles on MFMA.
 #include "csa2_internal.h"
 #include "csa2_device.h"
 
