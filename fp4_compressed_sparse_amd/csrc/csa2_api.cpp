@@ -657,9 +657,10 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
   bool forked = false;
   // The fork event is recorded by the scoring launch itself when there is one (an event
   // record of its own would add a packet, and a gap, between the scoring and Top-K).
+  bool armed = false;                                // g_stop_next set for the scoring
   auto swa_now = [&](int i, bool after_launch) -> csa2_status {
     if (!sd) return CSA2_OK;
-    if (after_launch && g_stop_next == nullptr) {    // the scoring launch took the event
+    if (after_launch && armed && g_stop_next == nullptr) {   // the scoring launch took it
       hipError_t e = hipStreamWaitEvent(sd->s, sd->fork, 0);
       if (e != hipSuccess) return fail(CSA2_ERR_HIP, "side stream fork: %s", hipGetErrorString(e));
     } else {
@@ -671,13 +672,19 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
     if (!st_swa) st_swa = run_swa(&aa[i], sd->s);
     return CSA2_OK;
   };
+  // Under stream capture the fork is an explicit event record (a graph records event
+  // nodes, not a kernel's own completion event).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const bool capturing =
+      sd && hipStreamIsCapturing(s, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
   for (int i = 0; i < n_layers && !st; ++i) {
     if (L[i].mode != CSA2_REUSE) {
       ia.q_idx = L[i].q_idx;
       ia.w_idx = L[i].w_idx;
       ia.k_idx = L[i].k_idx;
       ia.idx_out = L[i].idx_out;
-      if (sd) g_stop_next = sd->fork;
+      armed = sd && !capturing;
+      if (armed) g_stop_next = sd->fork;
       if (L[i].mode == CSA2_REINDEX_POOL)   // the pool of layer 0's (Full) selection
         st = run_index_pool_split(&ia, L[0].idx_out, g->K, ws, s, [&] { return swa_now(i, true); });
       else

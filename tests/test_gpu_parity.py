@@ -642,6 +642,47 @@ def test_side_stream_schedule_matches_sequential(csa2, dev):
             np.testing.assert_array_equal(la[k], lb[k])
 
 
+def test_layer_group_graph_capture(csa2, dev):
+    """The layer group recorded in a HIP graph (through torch's capture): each replay, with
+    the outputs cleared eagerly and the device synchronized in between, gives the eager
+    call's bits, SWA branch (side stream, forked and joined by events) included."""
+    _say("layer_group_graph_capture")
+    w = W(name="graph_t16_b2", B=2, T=16, E=2048, K=256, H=64, H_I=8, H_kv=64,
+          seq_id_rows=(np.arange(16) % 2).astype(np.int32), modes=[0, 1, 2])
+    d = tl.DeviceWorkload(w, dev)
+    ref = d.run_layer_group()
+    torch.cuda.synchronize()
+    descs, g = d.descs(), d.group_args()
+    need = csa2.workspace_bytes(csa2.OP_LAYER_GROUP, g)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # warm-up on the capture stream
+        csa2.layer_group(descs, g, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        csa2.layer_group(descs, g, workspace=ws)
+    outs = [k for k in ("o", "lse", "o_swa", "lse_swa")]
+    for rep in range(3):
+        for L in d.layers:
+            for k in outs:
+                L[k].zero_()
+            if "idx_out" in L:
+                L["idx_out"].fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _, idx_src = tl.orc.resolve_sources(w.modes)
+        for li, L in enumerate(d.layers):
+            np.testing.assert_array_equal(d.layers[idx_src[li]]["idx_out"].cpu().numpy(),
+                                          ref[li]["idx"], err_msg=f"replay {rep} layer {li}")
+            for k in outs:
+                np.testing.assert_array_equal(L[k].cpu().numpy(), ref[li][k],
+                                              err_msg=f"replay {rep} layer {li} {k}")
+
+
 # ---------------------------------------------------------------- full sizes
 def test_full_size_decode_64x128k_sampled(csa2, dev):
     """The headline decode workload (64 rows, 32768 entries each, K=2048, H=64) in the same
