@@ -60,6 +60,8 @@ def parse_args():
     ap.add_argument("--reindex-pool", action="store_true",
                     help="the workload's Reindex layers search the candidate pool of its Full "
                          "layer (workload 3)")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only measure this GPU's MFMA and LDS peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -401,6 +403,26 @@ def measure_hbm(dev, reps=5):
             "how": "median of 5 event-timed 1 GiB fp32 copies, (read + written bytes) / time"}
 
 
+def measure_peaks():
+    """Peaks measured on this GPU (libcsa2_peaks.so): dense MFMA TFLOP/s per operand type,
+    from a loop of independent MFMAs on every SIMD, and the LDS read bandwidth in TB/s.
+    Context beside the published peaks that the roofline fractions use."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp4_compressed_sparse_amd", "libcsa2_peaks.so"))
+    lib.csa2peak_mfma_tflops.restype = ctypes.c_double
+    lib.csa2peak_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.csa2peak_lds_tbs.restype = ctypes.c_double
+    lib.csa2peak_lds_tbs.argtypes = []
+    kinds = {"bf16_16x16x32": 0, "f16_16x16x32": 1, "fp8xfp4_scaled_16x16x128": 2,
+             "fp8_scaled_16x16x128": 3, "fp4_scaled_16x16x128": 4}
+    out = {f"mfma_{k}_tflops": round(lib.csa2peak_mfma_tflops(v, 2), 1) for k, v in kinds.items()}
+    out["lds_read_tbs"] = round(lib.csa2peak_lds_tbs(), 2)
+    out["how"] = ("two 4-wave workgroups per CU, 8 independent MFMA chains per wave, 2048 "
+                  "iterations; LDS: one 1024-thread workgroup per CU reading 16 B per lane per "
+                  "step, conflict-free; event-timed, median-free mean of 5 launches")
+    return out
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse_args()
@@ -412,6 +434,10 @@ def main():
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+
+    if args.peaks_only:
+        print(json.dumps(measure_peaks()))
+        return
 
     if args.calibrate_copy:
         n = 1 << 28                          # 1 GiB of fp32 read + 1 GiB written per copy
@@ -532,6 +558,7 @@ def main():
         hbm["roofline_frac_of_copy"] = (round(achieved / hbm["copy_gbs"], 4)
                                         if achieved else None)
         result["hbm_measured"] = hbm
+        result["peaks_measured"] = measure_peaks()
     if not args.no_extra and not args.kernel_pass_only:
         result["extra"] = []
         w3 = synth.workload(3)

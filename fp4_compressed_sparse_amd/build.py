@@ -1,4 +1,5 @@
-"""Build libcsa2.so (the gfx950 CSA2 library) in-tree with hipcc.
+"""Build libcsa2.so (the gfx950 CSA2 library) and libcsa2_peaks.so (measured MFMA and LDS
+peaks, for the benchmark) in-tree with hipcc.
 
 Each source compiles to its own object (in parallel), then one shared library is linked.
 HIP code is built with packed-fp32 instruction generation disabled.
@@ -14,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
 BUILD_DIR = os.path.join(HERE, "_build")
+# the peak-measurement kernels that bench.py reads the library's kernels against (own library)
+PEAKS_SRC = os.path.join(HERE, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "libcsa2_peaks.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,13 +49,18 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        peaks = ex.submit(_compile, PEAKS_SRC)
         objs = list(ex.map(_compile, srcs))
+        peaks_obj = peaks.result()
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp"
+    subprocess.check_call([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", peaks_obj, "-o", tmp])
+    os.replace(tmp, PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

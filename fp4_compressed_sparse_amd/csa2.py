@@ -69,9 +69,9 @@ class GroupArgs(ctypes.Structure):
                 ("kv_format", _i32)]
 
 
-EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_mxfp4_quantize", "csa2_kv_append", "csa2_fp4e4m3_quantize",
+EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_layer_group_noalloc", "csa2_mxfp4_quantize", "csa2_kv_append", "csa2_fp4e4m3_quantize",
            "csa2_workspace_bytes", "csa2_last_error", "csa2_status_string", "csa2_abi_version",
-           "csa2_timing_enable", "csa2_timing_read"]
+           "csa2_plan_cus", "csa2_timing_enable", "csa2_timing_read"]
 
 
 def _load():
@@ -87,6 +87,9 @@ def _load():
     L.csa2_layer_group.restype = _i32
     L.csa2_layer_group.argtypes = [ctypes.POINTER(LayerDesc), _i32, ctypes.POINTER(GroupArgs),
                                    _vp, ctypes.c_size_t, _vp]
+    L.csa2_layer_group_noalloc.restype = _i32
+    L.csa2_layer_group_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _i32,
+                                           ctypes.POINTER(GroupArgs), _vp]
     L.csa2_fp4e4m3_quantize.restype = _i32
     L.csa2_fp4e4m3_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]
     L.csa2_kv_append.restype = _i32
@@ -100,6 +103,8 @@ def _load():
     L.csa2_status_string.restype = ctypes.c_char_p
     L.csa2_status_string.argtypes = [_i32]
     L.csa2_abi_version.restype = _i32
+    L.csa2_plan_cus.restype = _i32
+    L.csa2_plan_cus.argtypes = []
     L.csa2_timing_enable.restype = _i32
     L.csa2_timing_enable.argtypes = [_i32]
     L.csa2_timing_read.restype = _i32
@@ -257,6 +262,17 @@ def layer_group(descs, g: GroupArgs, stream=None, workspace=None, device=None):
                                 need if workspace is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def layer_group_noalloc(descs, g: GroupArgs, stream=None):
+    """The layer group with the library's static device scratch as its workspace (no
+    allocation by the library or here)."""
+    n = len(descs)
+    arr = (LayerDesc * n)(*descs)
+    _check(lib.csa2_layer_group_noalloc(arr, n, ctypes.byref(g), _stream(stream)))
+
+
 def mxfp4_quantize(x, lat, scl, dst_row=None, stream=None):
     """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 16] at rows dst_row (int64) or 0..rows-1."""
     rows = x.shape[0]
@@ -304,3 +320,8 @@ def timing_read(max_kernels: int = 32):
 
 def abi_version() -> int:
     return lib.csa2_abi_version()
+
+
+def plan_cus() -> int:
+    """Compute units the library's launch plans assume for the current device."""
+    return lib.csa2_plan_cus()

@@ -20,7 +20,40 @@ using namespace csa2;
 
 namespace csa2 {
 thread_local hipEvent_t g_launch_events[2] = {nullptr, nullptr};
+
+// The device property cache: compute units per device ordinal, each queried once.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCus;
+  std::call_once(once[dev], [dev] {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                    hipSuccess && n > 0) ? n : kDefaultCus;
+  });
+  return cus[dev];
 }
+}
+
+namespace csa2 {
+bool side_create(Side* sd) {
+  *sd = Side{};
+  const unsigned fl = hipEventDisableTiming | hipEventDisableSystemFence;
+  if (hipStreamCreateWithFlags(&sd->s, hipStreamNonBlocking) != hipSuccess) sd->s = nullptr;
+  if (sd->s && hipEventCreateWithFlags(&sd->fork, fl) != hipSuccess) sd->fork = nullptr;
+  if (sd->fork && hipEventCreateWithFlags(&sd->join, fl) != hipSuccess) sd->join = nullptr;
+  if (!sd->join) {                                   // partial failure: release, no side
+    if (sd->fork) (void)hipEventDestroy(sd->fork);
+    if (sd->s) (void)hipStreamDestroy(sd->s);
+    *sd = Side{};
+    return false;
+  }
+  sd->ok = true;
+  return true;
+}
+}  // namespace csa2
 
 namespace {
 
@@ -103,29 +136,19 @@ csa2_status timed(const char* name, hipStream_t s, F&& fn) {
 // The SWA branch depends only on its own inputs, so it runs on a library-owned stream of
 // the current device (default priority), forked from and joined back into the caller's
 // stream with events.  Both are capturable, so a caller may record the calls in a graph.
-// One side stream and event pair per host thread and device.  The events only order work
-// between two streams of one device and are never inspected from the host, so they skip
-// the system-scope fence on record (its cache write-back measured about 1% of a decode
-// step); device-scope visibility comes from the kernels' own completion.
-struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ok = false;
-};
-
+// This is the library's one piece of state besides the device property cache: one side
+// stream and event pair per host thread and device, created on first use and kept (a
+// pool of one) for the life of the thread.  If creating them fails, whatever was created
+// is destroyed and the branch runs on the caller's stream instead.  The events only order
+// work between two streams of one device and are never inspected from the host, so they
+// skip the system-scope fence on record (its cache write-back measured about 1% of a
+// decode step); device-scope visibility comes from the kernels' own completion.
 Side* side_for_current_device() {
   thread_local std::map<int, Side> sides;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   Side& sd = sides[dev];
-  if (!sd.ok) {
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    const unsigned fl = hipEventDisableTiming | hipEventDisableSystemFence;
-    if (hipEventCreateWithFlags(&sd.fork, fl) != hipSuccess ||
-        hipEventCreateWithFlags(&sd.join, fl) != hipSuccess)
-      return nullptr;
-    sd.ok = true;
-  }
+  if (!sd.ok && !side_create(&sd)) return nullptr;
   return &sd;
 }
 
@@ -186,7 +209,7 @@ size_t index_ws_bytes(int32_t T, int32_t max_pages) {
 
 size_t attn_ws_bytes(int32_t T, int32_t H, int32_t K) {
   int S, per;
-  attn_plan(T, H, K, &S, &per);
+  attn_plan(T, H, K, &S, &per, device_cus());   // the most splits any plan below uses
   if (S <= 1) return 0;
   return round_up((size_t)T * S * H * CSA2_D_LAT * sizeof(float)) +
          round_up((size_t)T * S * H * sizeof(float));
@@ -411,9 +434,10 @@ csa2_status validate_attn(const csa2_attn_args* a) {
 csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
   if (a->T == 0) return CSA2_OK;
   // with an SWA branch on persistent workgroups beside it, plan for the CUs they leave
-  const int swa_wgs = a->q_swa ? swa_persist_wgs(a->T, a->H, a->H_kv) : 0;
+  const int cus = device_cus();
+  const int swa_wgs = a->q_swa ? swa_persist_wgs(a->T, a->H, a->H_kv, cus) : 0;
   int S, per;
-  attn_plan(a->T, a->H, a->K, &S, &per, kNumCus - swa_wgs);
+  attn_plan(a->T, a->H, a->K, &S, &per, cus - swa_wgs);
   AttnParams ap;
   ap.T = a->T;
   ap.H = a->H;
@@ -468,7 +492,7 @@ csa2_status run_swa(const csa2_attn_args* a, hipStream_t s) {
     wp.len = a->swa_len;
     wp.o = a->o_swa;
     wp.lse = a->lse_swa;
-    wp.wgs = swa_persist_wgs(a->T, a->H, a->H_kv);
+    wp.wgs = swa_persist_wgs(a->T, a->H, a->H_kv, device_cus());
     st = timed("swa", s, [&] { return launch_swa(wp, s); });
     if (st) return st;
   }
@@ -635,24 +659,37 @@ csa2_status csa2_sparse_attn_fp4(const csa2_attn_args* a, void* ws, size_t ws_by
   return run_with_swa(a, 1, s, [&] { return run_attn(a, ws, s); });
 }
 
-csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
-                             const csa2_group_args* g, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace csa2 {
+csa2_status layer_group_validate(const csa2_layer_desc* L, int32_t n_layers,
+                                 const csa2_group_args* g) {
+  if (n_layers > kMaxGroupLayers)
+    return fail(CSA2_ERR_SHAPE, "csa2_layer_group: n_layers=%d > %d", n_layers, kMaxGroupLayers);
   csa2_index_args ia;
-  if (n_layers > 64) return fail(CSA2_ERR_SHAPE, "csa2_layer_group: n_layers=%d > 64", n_layers);
-  csa2_attn_args aa[64];
+  csa2_attn_args aa[kMaxGroupLayers];
+  return validate_group(L, n_layers, g, &ia, aa);
+}
+
+csa2_status layer_group_run(const csa2_layer_desc* L, int32_t n_layers,
+                            const csa2_group_args* g, void* ws, size_t ws_bytes,
+                            hipStream_t s, Side* side) {
+  csa2_index_args ia;
+  if (n_layers > kMaxGroupLayers)
+    return fail(CSA2_ERR_SHAPE, "csa2_layer_group: n_layers=%d > %d", n_layers, kMaxGroupLayers);
+  csa2_attn_args aa[kMaxGroupLayers];
   csa2_status st = validate_group(L, n_layers, g, &ia, aa);
   if (st) return st;
   if (g->T == 0) return CSA2_OK;
   st = check_ws("csa2_layer_group", ws, ws_bytes,
                 csa2_workspace_bytes(CSA2_OP_LAYER_GROUP, g));
   if (st) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   // Layer i's SWA branch goes to the side stream once layer i's indexer scoring is queued:
   // both stream from HBM, so SWA overlaps Top-K, attention and the merge instead (forking
   // before the scoring or after Top-K measured slower).
   bool any_swa = false;
   for (int i = 0; i < n_layers; ++i) any_swa |= (aa[i].q_swa != nullptr);
-  Side* sd = (any_swa && !g_timing.on) ? side_for_current_device() : nullptr;
+  Side* sd = (any_swa && !g_timing.on) ? side : nullptr;
   csa2_status st_swa = CSA2_OK;
   bool forked = false;
   // The fork event is recorded by the scoring launch itself when there is one (an event
@@ -702,6 +739,22 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
   if (!sd)
     for (int i = 0; i < n_layers && !st; ++i) st = run_swa(&aa[i], s);
   return st ? st : st_swa;
+}
+
+csa2_status set_error(csa2_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace csa2
+
+extern "C" {
+
+csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
+                             const csa2_group_args* g, void* ws, size_t ws_bytes, void* stream) {
+  // the side stream is made (once per host thread and device) only when a branch needs it
+  csa2_status st = layer_group_validate(L, n_layers, g);
+  if (st) return st;
+  bool any_swa = false;
+  for (int i = 0; i < n_layers; ++i) any_swa |= (L[i].q_swa != nullptr);
+  Side* sd = (g->T > 0 && any_swa && !g_timing.on) ? side_for_current_device() : nullptr;
+  return layer_group_run(L, n_layers, g, ws, ws_bytes, static_cast<hipStream_t>(stream), sd);
 }
 
 csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
@@ -814,6 +867,8 @@ const char* csa2_status_string(csa2_status s) {
 }
 
 int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+int32_t csa2_plan_cus(void) { return device_cus(); }
 
 csa2_status csa2_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_timing.mu);

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/csa2.h"
+
 namespace csa2 {
 
 // Start/stop events that the next kernel launch records itself (null = none): set by the
@@ -151,23 +153,53 @@ constexpr int kPoolSelPerWave = 32;    // selections per wave of the pooled scor
 constexpr int kPoolSelPerBlock = 4 * kPoolSelPerWave;   // per workgroup (4 waves)
 inline int64_t pool_key_stride(int pool_K) { return ((int64_t)kPoolBlock * pool_K + 63) / 64 * 64; }
 
+// Compute units of the current device, queried once per device (std::call_once) and used
+// by every launch plan; kDefaultCus (MI355X) when no device can be queried, e.g. when a
+// host-only caller sizes a workspace.
+constexpr int kDefaultCus = 256;
+int device_cus();
+
 // Split plan of the attention launch: `splits` workgroups per row, each covering
 // `per_split` (a multiple of 32, <= 2048) consecutive index slots, sized to fill `cus`
 // CUs (a smaller budget never gives more splits).
-constexpr int kNumCus = 256;
-void attn_plan(int T, int H, int K, int* splits, int* per_split, int cus = kNumCus);
+void attn_plan(int T, int H, int K, int* splits, int* per_split, int cus);
 
 // The SWA branch beside the global one, for decode rows with H == H_kv: this many
-// persistent one-per-CU workgroups (16 (row, KV head) units in flight each), or 0 for the
-// one-workgroup-per-unit launch.  The attention beside it is planned for the other CUs.
+// persistent one-per-CU workgroups (16 (row, KV head) units in flight each, each holding a
+// whole CU through its LDS reservation), or 0 for the one-workgroup-per-unit launch.  At
+// most half the device's CUs; the attention beside it is planned for the others.
 constexpr int kSwaPMaxWgs = 128;
-inline int swa_persist_wgs(int T, int H, int H_kv) {
+inline int swa_persist_wgs(int T, int H, int H_kv, int cus) {
   if (T <= 0 || T >= kSwaTileMinRows || H != H_kv) return 0;
   const int64_t w = ((int64_t)T * H_kv + 15) / 16;
-  return (int)(w < kSwaPMaxWgs ? w : kSwaPMaxWgs);
+  int cap = cus / 2 < kSwaPMaxWgs ? cus / 2 : kSwaPMaxWgs;
+  cap = cap < 1 ? 1 : cap;
+  return (int)(w < cap ? w : cap);
 }
 // 64-head workgroups per (row, split) of the sparse attention kernel
 inline int attn_head_groups(int H) { return H > 64 ? H / 64 : 1; }
+
+// ---------------------------------------------------------------- host-side runners
+// A side stream of the current device with its fork and join events (default priority;
+// the events skip the system-scope fence), on which a layer's SWA branch runs beside the
+// global branch.  side_create makes one and returns false (having released any part it
+// made) on failure.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false;
+};
+bool side_create(Side* sd);
+
+// The layer group's validation and its run on `s` with the given workspace; `side` null
+// runs the SWA branches on `s` after the global ones.  Both set the thread's last error.
+constexpr int kMaxGroupLayers = 64;
+csa2_status layer_group_validate(const csa2_layer_desc* L, int32_t n_layers,
+                                 const csa2_group_args* g);
+csa2_status layer_group_run(const csa2_layer_desc* L, int32_t n_layers, const csa2_group_args* g,
+                            void* ws, size_t ws_bytes, hipStream_t s, Side* side);
+// Sets the thread's last error message and returns st.
+csa2_status set_error(csa2_status st, const char* msg);
 
 // ---------------------------------------------------------------- launchers
 // Each launcher enqueues one kernel on `s` and returns hipGetLastError().

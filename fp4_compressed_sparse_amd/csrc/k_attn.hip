@@ -9,16 +9,19 @@
 // value = latent (512).
 //
 // One workgroup per (row, split of the K index slots, 64-head group) with twelve waves: four
-// score waves and eight value waves, three waves per SIMD, so that one wave's LDS and VALU
-// work hides behind the others' matrix work.  The query operands of a score wave and the
-// accumulators of a value wave occupy the same registers.
-//   gather  : the split's physical rows are resolved once into LDS.  Each 32-entry tile
-//             (8 KB codes, 4 KB rope, 0.5 KB scales) goes straight from memory into a ring
-//             of four LDS tiles by LDS DMA (16 bytes per lane, three tiles ahead), the lanes
-//             fetching in an XOR-swizzled order of 16-byte slots so that the operand reads
-//             below are bank-conflict free; no registers or LDS store instructions are spent
-//             on staging.
-//   QK^T    : score wave hb computes S^T[32 entries x 16 heads 16hb..] over all 576
+// score waves and eight value waves, three waves per SIMD.  Entries go in tiles of 64, one
+// barrier per tile.
+//   gather  : the split's physical rows are resolved once into LDS (by the value waves,
+//             while the score waves load and split the query).  Each tile (16 KB codes,
+//             8 KB rope, 1 KB scales) goes straight from memory into a ring of four LDS
+//             tiles by LDS DMA, 16 bytes per lane, in a column-major image: column s of the
+//             codes holds channels 32s..32s+31 of all 64 entries, each entry's 16 bytes at
+//             an XOR-swizzled position, so that both the matrix-operand reads of the score
+//             waves and the transposing reads of the value waves are bank-conflict free.
+//             Value wave v fetches the two code columns that only it reads, so it refills
+//             a ring slot as soon as its own reads of that slot are done: three tiles are
+//             in flight while one is consumed.
+//   QK^T    : score wave hb computes S^T[64 entries x 16 heads 16hb..] over all 576
 //             channels.  The latent part runs on the MXFP4 matrix path (v_mfma_scale
 //             16x16x128: A = the cached E2M1 codes with their own E8M0 block scales,
 //             dequantized inside the MFMA); the query enters as two fp8 (E4M3) parts with
@@ -28,12 +31,13 @@
 //             is raised only when a tile exceeds it by more than 2^12 (fp16 P <= 4096).
 //             The wave publishes P (fp16) and, when it raised a maximum, the rescale factors.
 //   PV      : value wave v accumulates O^T[64 channels 64v.. x all heads] += V^T P^T on
-//             fp16 MFMA 16x16x32 with fp32 accumulation; each V^T operand (one 16-byte LDS
-//             read) feeds every 16-head block.  V^T is dequantized once per tile into LDS
-//             (fp16, channel-major, entries in the order the P^T operand has in registers)
-//             by the value waves, one tile ahead.  fp16 rather than bf16 for P: bf16
-//             rounding of P alone would put the output's relative error near 1.7e-3.
-// Shared buffers are double-buffered by tile parity, so each tile needs one barrier.  Splits
+//             fp16 MFMA 16x16x32 with fp32 accumulation.  The V^T operand comes straight
+//             from the staged codes: a transposing LDS read (ds_read_b64_tr_b4) gives each
+//             lane 16 entries of one channel, converted in registers to fp16 (scale 1, exact)
+//             and multiplied by each entry's block scale (fp16, from a per-tile table the
+//             value waves build from the staged scale bytes).  fp16 rather than bf16 for P:
+//             bf16 rounding of P alone would put the output's relative error near 1.7e-3.
+// P, the rescale factors and the scale table are double-buffered by tile parity.  Splits
 // write normalized partial outputs plus log2-sum-exp, and a merge kernel combines them.
 // Both kernels number their workgroups so that everything of a row runs on one XCD, whose
 // L2 then serves the row's shared query and its partial outputs.
@@ -42,24 +46,23 @@
 
 namespace csa2 {
 
-constexpr int kTE = 32;              // entries per tile
+constexpr int kTE = 64;              // entries per tile
 constexpr int kMaxPerSplit = 2048;   // idx slots per split (LDS row table size)
-constexpr int kNPre = 2;             // loop unroll: the tile parity picks the P and V^T
-                                     // buffers statically
-constexpr int kRing = 4;             // raw tiles in LDS: one read, one ready, two in flight
+constexpr int kNPre = 2;             // loop unroll: the tile parity picks buffers statically
+constexpr int kRing = 4;             // raw tiles in LDS: one consumed, three in flight
 constexpr float kRaise = 12.f;       // log2 headroom before the running maximum is raised
-// raw tile layout in LDS (bytes): codes [32][256], rope [32][128], scales [32][16] (E8M0
-// per 32 channels) or [32][32] (E4M3 per 16 channels)
-constexpr int kRawLat = 0, kRawRope = 8192, kRawScl = 12288, kRawBytes = 13312;
-constexpr int kChunks = 13;          // 1 KB load units per tile: 8 codes, 4 rope, 1 scales
-constexpr int kRawSlot = kRawBytes + 1024;   // a raw tile and the 1 KB its dead loads fill
-constexpr int kVtStride = 80;        // LDS bytes per V^T channel row (32 fp16 + 16 pad)
+// raw tile layout in LDS (bytes): 16 code columns [16][64 entries][16 B] (column s holds
+// channels 32s..32s+31), 8 rope columns [8][64][16 B] (column r holds rope channels
+// 8r..8r+7), then the scale bytes: one unit [64][16 B] of E8M0 scales, or two units of
+// E4M3 scales (unit u holds bytes 16u..16u+15 of each entry's 32); entry e of a column
+// sits at position ent_pos(e).  Each 1 KB unit is one LDS DMA instruction per wave.
+constexpr int kRawLat = 0, kRawRope = 16384, kRawScl = 24576, kRawBytes = 26624;
 
 void attn_plan(int T, int H, int K, int* splits, int* per_split, int cus) {
   const int groups = attn_head_groups(H);
   const int min_s = (K + kMaxPerSplit - 1) / kMaxPerSplit;
   const int max_s = max(1, (K + 2 * kTE - 1) / (2 * kTE));   // >= 2 tiles per split
-  cus = max(1, min(cus, kNumCus));
+  cus = max(1, cus);
   // as many splits as fit the CUs in one round (a second round of a few workgroups would
   // cost a whole split's time)
   int s = (T > 0) ? max(1, cus / (T * groups)) : 1;
@@ -75,10 +78,11 @@ void attn_plan(int T, int H, int K, int* splits, int* per_split, int cus) {
 // An all-zero row stands in for empty index slots (so staged tiles never hold garbage).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[256];
 
-// LDS swizzle of a staged tile's codes: entry e's 16-byte slot c sits at slot
-// c ^ (e & 15) ^ (e >> 4), so readers that take entries e and e + 16 in one access hit
-// different banks.  (The map is its own inverse.)
-__device__ __forceinline__ int lat_slot(int c, int e) { return c ^ (e & 15) ^ (e >> 4); }
+// Position of entry e (0..63) in a column of the staged tile: 16 (e/16) + ((e%16) ^
+// 4 (e/16)).  Readers that take 16 entries {16a + 4G + b : a, b in 0..3} (G fixed), and
+// readers that take 16 consecutive entries, both hit 16 distinct 16-byte positions of a
+// 256-byte bank period.  The map is its own inverse.
+__device__ __forceinline__ int ent_pos(int e) { return (e & 48) | ((e & 15) ^ ((e >> 2) & 12)); }
 
 // Barrier for the tile loop: this wave's LDS accesses are complete, no wait on vector
 // memory (the raw tiles arrive by LDS DMA, whose completion the loading waves await
@@ -86,12 +90,6 @@ __device__ __forceinline__ int lat_slot(int c, int e) { return c ^ (e & 15) ^ (e
 // `raw` is passed so that the DMA-filled buffer counts as written by it.
 __device__ __forceinline__ void tile_barrier(const void* raw) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : "v"(raw) : "memory");
-}
-
-// Position of entry e of a tile in a V^T row: the P^T operand of lane group g carries
-// entries 4g..4g+3 then 16+4g..16+4g+3, so contraction slots 8g..8g+7 map to those.
-__device__ __forceinline__ int vt_pos(int e) {
-  return (e < 16) ? (8 * (e >> 2) + (e & 3)) : (8 * ((e - 16) >> 2) + 4 + (e & 3));
 }
 
 // Workgroup b of n runs on XCD b % 8; return the index of the b-th workgroup when XCD x
@@ -124,24 +122,41 @@ __device__ __forceinline__ void fp4x8_e4m3_to_f16_pairs(uint32_t w, uint32_t sby
     out[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, out[k]) * mm);
 }
 
+// Scale byte -> the fp16 bit pattern of the scale it encodes: E8M0 2^(b - 127) (FMT 0;
+// exponents below -24 give 0, above 15 give +inf, so that a value the fp16 product cannot
+// hold shows as a non-finite output rather than a wrong finite one), or the E4M3 value
+// (FMT 1; every E4M3 value is exact in fp16).
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_f16_bits(uint32_t b) {
+  if (FMT == 1) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e) return ((e + 8u) << 10) | (m << 7);       // 2^(e-7) (1 + m/8)
+    // m 2^-9: normal fp16 2^(j-9) (1 + (m - 2^j) / 2^j) with j = floor(log2 m)
+    if (m == 0u) return 0u;
+    const uint32_t j = 31u - (uint32_t)__builtin_clz(m);
+    return ((j + 6u) << 10) | (((m << (10u - j)) & 0x3ffu));
+  }
+  const int k = (int)b - 127;
+  if (k > 15) return 0x7c00u;
+  if (k >= -14) return (uint32_t)(k + 15) << 10;
+  if (k >= -24) return 1u << (k + 24);
+  return 0u;
+}
+
 // FMT 0: MXFP4 (E8M0 scale per 32 channels); FMT 1: FP4 with an E4M3 scale per 16 channels
 template <int NHB, int FMT>   // NHB: 16-head blocks per workgroup, 1, 2 or 4 (blockIdx.y
 __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // picks 64-head groups)
-  constexpr int NW = 12;
-  constexpr int NT = 64 * NW;
   constexpr int NV = 8;                              // value waves
-  constexpr int CPW = (kChunks + NV - 1) / NV;       // load units per value wave and tile
-  static_assert((kTE / 4) * (kLat / 8) == 64 * NV, "one V^T unit per value thread");
+  constexpr int kSclBlocks = FMT == 1 ? 32 : 16;     // scale-table rows (channel blocks)
 
-  // ring of raw tiles, each followed by 1 KB that dead loads write to
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRing][kRawSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[2][kLat * kVtStride];
-  __shared__ __attribute__((aligned(16))) u32x4 s_p[2][NHB][64];     // P^T operands
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRing][kRawBytes];
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[2][NHB][2][64];   // P^T operands
+  __shared__ __attribute__((aligned(16))) uint16_t s_sclt[2][kSclBlocks * kTE];   // fp16
   __shared__ float s_alpha[2][NHB][16];              // rescale factors of a raise
   __shared__ float s_l[NHB][16];
   __shared__ uint32_t s_flag[3];                     // per tile mod 3: blocks that raised
   __shared__ int32_t s_rows[kMaxPerSplit];
-  __shared__ uint32_t s_tmask[kMaxPerSplit / kTE];
+  __shared__ uint64_t s_tmask[kMaxPerSplit / kTE];
 
   // blockIdx.x -> (row, split): XCD x takes the x-th contiguous range of (row, split)
   const int lin = xcd_linear((int)blockIdx.x, p.T * p.splits);
@@ -153,17 +168,16 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
   const int n = lane & 15, g = lane >> 4;
   const int h0 = 16 * NHB * blockIdx.y;              // first head of this workgroup
   const int ntiles = (nslots + kTE - 1) / kTE;
-  // the loops run whole groups of kNPre tiles (static buffer parity and staging slot, and
-  // no path on which a tile of a group is skipped, so the compiler counts loads in flight
-  // exactly); a padding tile has no valid entry
+  // the loops run whole groups of kNPre tiles (static buffer parity, and no path on which a
+  // tile of a group is skipped, so the compiler counts loads in flight exactly); a padding
+  // tile has no valid entry
   const int ntiles2 = (ntiles + kNPre - 1) / kNPre * kNPre;
   // Roles: waves 0..3 score (one per SIMD, as waves go to the SIMDs in turn), waves 4..11
   // are value waves (two per SIMD).  Each role runs its own loop; both loops pass the same
   // barriers in the same order.
   const bool scorer_role = wave < 4;
 
-  // ---- the score waves' query loads go out first, so that their latency overlaps the
-  //      row resolution below
+  // ---- the score waves' query loads
   const int hb = min(wave, NHB - 1);
   const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
   u32x4 qraw[4][2][2], qrope0, qrope1;
@@ -190,61 +204,34 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
     }
     qrope0 = ld_global_16(qp + kLat + 8 * g);
     qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
-  }
-
-  // ---- resolve the split's physical rows once (-1 = empty slot); one validity bit per
-  //      entry of each tile
-  {
+  } else {
+    // ---- value waves: resolve the split's physical rows (-1 = empty slot), all index
+    //      loads first, then all page-table loads; one validity bit per entry of a tile
     const int b = p.seq_id[t];
     const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
     const int32_t* idx = p.idx + (int64_t)t * p.K + k0;
-    for (int i = tid; i < ntiles2 * kTE; i += NT) {
-      int32_t row = -1;
-      if (i < nslots) {
-        const int j = idx[i];
-        if (j >= 0) row = pt[j >> 6] * kPage + (j & 63);
-      }
-      s_rows[i] = row;
-      const uint64_t bal = __ballot(row >= 0);      // 64 slots = two tiles per wave step
-      if (lane == 0) s_tmask[i >> 5] = (uint32_t)bal;
-      if (lane == 32) s_tmask[i >> 5] = (uint32_t)(bal >> 32);
+    const int tv = tid - 256;
+    constexpr int kPer = kMaxPerSplit / (64 * NV);   // slots per value thread
+    int j[kPer], row[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tv + 64 * NV * r;
+      j[r] = (i < nslots) ? idx[i] : -1;
     }
-    if (tid < 3) s_flag[tid] = 0u;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) row[r] = (j[r] >= 0) ? pt[j[r] >> 6] * kPage + (j[r] & 63) : -1;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tv + 64 * NV * r;                // tile i / 64 = wave - 4 + 8r
+      if (i < ntiles2 * kTE) {
+        s_rows[i] = row[r];
+        const uint64_t bal = __ballot(row[r] >= 0);
+        if (lane == 0) s_tmask[i >> 6] = bal;
+      }
+    }
+    if (tid == 256) s_flag[0] = s_flag[1] = s_flag[2] = 0u;
   }
   __syncthreads();                                   // s_rows ready
-
-  // V^T (fp16, channel-major, entries at vt_pos order) of the tile staged in `raw`, built
-  // by the value waves, one tile ahead: unit u = 64 (wave - 4) + lane = (eq, co) converts
-  // entries 4eq..4eq+3 x channels 8co..8co+7
-  auto build_vt_unit = [&](const uint8_t* raw, uint8_t* vtb, int u) {
-    const int eq = u & 7;
-    const int co = u >> 3;
-    uint32_t hv[4][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = 4 * eq + k;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(
-          raw + kRawLat + 256 * e + 16 * lat_slot(co >> 2, e) + 4 * (co & 3));
-      if (FMT == 1) {
-        fp4x8_e4m3_to_f16_pairs(w, raw[kRawScl + 32 * e + (co >> 1)], hv[k]);   // group co/2
-      } else {
-        const float sc = e8m0_to_f32(raw[kRawScl + 16 * e + (co >> 2)]);        // block co/4
-        fp4x8_to_f16_pairs(w, sc, hv[k]);
-      }
-    }
-    uint8_t* dst = vtb + 8 * co * kVtStride + 2 * vt_pos(4 * eq);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      u32x2 lo, hi;   // channel 8co+2k and 8co+2k+1, entries 4eq..4eq+3
-      lo[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(hv[1][k], hv[0][k], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(hv[3][k], hv[2][k], 0x07060302u);
-      *reinterpret_cast<u32x2*>(dst + (2 * k) * kVtStride) = lo;
-      *reinterpret_cast<u32x2*>(dst + (2 * k + 1) * kVtStride) = hi;
-    }
-  };
-
 
   const float sc_log2 = p.sm_scale_log2;
   if (scorer_role) {
@@ -265,12 +252,12 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 v = qraw[kk][j >> 1][j & 1];
+        for (int jj = 0; jj < 4; ++jj) {
+          const u32x4 v = qraw[kk][jj >> 1][jj & 1];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            qf[kk][j][2 * e] = (_Float16)__uint_as_float(v[e] << 16);
-            qf[kk][j][2 * e + 1] = (_Float16)__uint_as_float(v[e] & 0xffff0000u);
+            qf[kk][jj][2 * e] = (_Float16)__uint_as_float(v[e] << 16);
+            qf[kk][jj][2 * e + 1] = (_Float16)__uint_as_float(v[e] & 0xffff0000u);
           }
         }
     }
@@ -325,6 +312,10 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
         }
       }
     }
+    // this lane's entry positions in the staged columns: entry 16mb + n
+    int epos[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) epos[mb] = 16 * ent_pos(16 * mb + n);
     // running state per head n; a finite initial maximum keeps fully masked tiles at
     // 2^(-inf) = 0 instead of -inf - (-inf)
     float m_run = -1.0e30f, l_run = 0.f;
@@ -334,26 +325,23 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
 #pragma unroll
       for (int bb = 0; bb < kNPre; ++bb) {           // bb & 1 = i & 1: static buffer parity
         const int i = i0 + bb;
-        {
-          if (active) {
-            // ---- S^T[entries 16mb + 4g + k][head n]: four independent chains
-            const uint8_t* raw = s_raw[i & (kRing - 1)];
-            f32x4 ah[2], al[2];
-            u32x4 ksc[2];                              // the 16 block scales of entry e
+        if (active) {
+          // ---- S^T[entries 16mb + 4g + k][head n]: eight independent chains
+          const uint8_t* raw = s_raw[i & (kRing - 1)];
+          f32x4 ah[4], al[4];
+          u32x4 ksc[4];                              // the 16 block scales of entry e
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-              ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-              al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-              if (FMT == 0)
-                ksc[mb] = *reinterpret_cast<const u32x4*>(raw + kRawScl + 16 * (16 * mb + n));
-            }
-            // A scale: block 4kk + g = byte g of dword kk, shifted down (op_sel 0); B scale:
-            // op_sel = kk picks byte kk of qscp
+          for (int mb = 0; mb < 4; ++mb) {
+            ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (FMT == 0) ksc[mb] = *reinterpret_cast<const u32x4*>(raw + kRawScl + epos[mb]);
+          }
+          // A scale: block 4kk + g = byte g of dword kk, shifted down (op_sel 0); B scale:
+          // op_sel = kk picks byte kk of qscp
 #define CSA2_QK_CHUNK(kk)                                                                     \
-  _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                        \
-    const int e = 16 * mb + n;                                                              \
+  _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                        \
     const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
-        raw + kRawLat + 256 * e + 16 * lat_slot(4 * (kk) + g, e));                          \
+        raw + kRawLat + 1024 * (4 * (kk) + g) + epos[mb]);                                  \
     const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};          \
     const int asc = (int)(ksc[mb][kk] >> (8 * g));                                          \
     ah[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[kk], ah[mb], 4, 0, 0,  \
@@ -361,93 +349,91 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
     al[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[kk], al[mb], 4, 0, 0,  \
                                                                asc, kk, qscp);              \
   }
-            // FMT 1: the lane dequantizes its 8 codes of step j (dword j of the slot of block
-            // 4kk + g, E4M3 group 8kk + 2g + j/2) into fp16; fp16 MFMA; steps alternate
-            // between the two accumulators
+          // FMT 1: the lane dequantizes its 8 codes of step j (dword j of the slot of block
+          // 4kk + g, E4M3 group 8kk + 2g + j/2) into fp16; fp16 MFMA; steps alternate
+          // between the two accumulators
 #define CSA2_QK_E4M3(kk)                                                                      \
-  _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                        \
-    const int e = 16 * mb + n;                                                              \
+  _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                        \
     const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
-        raw + kRawLat + 256 * e + 16 * lat_slot(4 * (kk) + g, e));                          \
+        raw + kRawLat + 1024 * (4 * (kk) + g) + epos[mb]);                                  \
     const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(                                \
-        raw + kRawScl + 32 * e + 8 * (kk) + 2 * g);                                         \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
+        raw + kRawScl + 1024 * ((kk) >> 1) + epos[mb] + ((8 * (kk) + 2 * g) & 15));          \
+    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                                      \
       uint32_t kv[4];                                                                       \
-      fp4x8_e4m3_to_f16_pairs(w4[j], (sc2 >> (8 * (j >> 1))) & 0xffu, kv);                  \
+      fp4x8_e4m3_to_f16_pairs(w4[jj], (sc2 >> (8 * (jj >> 1))) & 0xffu, kv);                \
       const f16x8 ka = __builtin_bit_cast(f16x8, u32x4{kv[0], kv[1], kv[2], kv[3]});        \
-      if (j & 1) al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][j], al[mb], 0, 0, 0); \
-      else ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][j], ah[mb], 0, 0, 0);  \
+      if (jj & 1) al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][jj], al[mb], 0, 0, 0); \
+      else ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][jj], ah[mb], 0, 0, 0); \
     }                                                                                       \
   }
-            if (FMT == 0) {
-              CSA2_QK_CHUNK(0)
-              CSA2_QK_CHUNK(1)
-              CSA2_QK_CHUNK(2)
-              CSA2_QK_CHUNK(3)
-            } else {
-              CSA2_QK_E4M3(0)
-              CSA2_QK_E4M3(1)
-              CSA2_QK_E4M3(2)
-              CSA2_QK_E4M3(3)
-            }
+          if (FMT == 0) {
+            CSA2_QK_CHUNK(0)
+            CSA2_QK_CHUNK(1)
+            CSA2_QK_CHUNK(2)
+            CSA2_QK_CHUNK(3)
+          } else {
+            CSA2_QK_E4M3(0)
+            CSA2_QK_E4M3(1)
+            CSA2_QK_E4M3(2)
+            CSA2_QK_E4M3(3)
+          }
 #undef CSA2_QK_CHUNK
 #undef CSA2_QK_E4M3
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              const int chunk = 4 * s2 + g;
-              const bf16x8 qr = as_bf16x8(s2 == 0 ? qrope0 : qrope1);
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 qr = as_bf16x8(s2 == 0 ? qrope0 : qrope1);
 #pragma unroll
-              for (int mb = 0; mb < 2; ++mb) {
-                const int e = 16 * mb + n;
-                const u32x4 rv = *reinterpret_cast<const u32x4*>(
-                    raw + kRawRope + 128 * e + 16 * (chunk ^ (e & 7)));
-                if (s2 == 0) ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, ah[mb], 0, 0, 0);
-                else al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, al[mb], 0, 0, 0);
-              }
+            for (int mb = 0; mb < 4; ++mb) {
+              const u32x4 rv = *reinterpret_cast<const u32x4*>(
+                  raw + kRawRope + 1024 * (4 * s2 + g) + epos[mb]);
+              if (s2 == 0) ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, ah[mb], 0, 0, 0);
+              else al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, al[mb], 0, 0, 0);
             }
-            // ---- online softmax; masked slots get -inf (exp2 -> 0)
-            const uint32_t tm = s_tmask[i];
-            float x[8];
-            bool raise_lane = false;
+          }
+          // ---- online softmax; masked slots get -inf (exp2 -> 0)
+          const uint64_t tm = s_tmask[i];
+          float x[16];
+          bool raise_lane = false;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-              const uint32_t bits = tm >> (16 * mb + 4 * g);
+          for (int mb = 0; mb < 4; ++mb) {
+            const uint32_t bits = (uint32_t)(tm >> (16 * mb + 4 * g));
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const float v = ((bits >> k) & 1u) ? (ah[mb][k] + al[mb][k]) * sc_log2 : -INFINITY;
-                x[4 * mb + k] = v;
-                raise_lane |= v > m_run + kRaise;
-              }
+            for (int k = 0; k < 4; ++k) {
+              const float v = ((bits >> k) & 1u) ? (ah[mb][k] + al[mb][k]) * sc_log2 : -INFINITY;
+              x[4 * mb + k] = v;
+              raise_lane |= v > m_run + kRaise;
             }
-            if (__ballot(raise_lane)) {              // rare after the first tile
-              float tmax = x[0];
+          }
+          if (__ballot(raise_lane)) {                // rare after the first tile
+            float tmax = x[0];
 #pragma unroll
-              for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, x[k]);
-              tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-              tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-              float alpha = 1.f;
-              if (tmax > m_run + kRaise) {
-                alpha = __builtin_amdgcn_exp2f(m_run - tmax);
-                m_run = tmax;
-                l_run *= alpha;
-              }
-              if (g == 0) s_alpha[bb & 1][hb][n] = alpha;
-              if (lane == 0) atomicOr(&s_flag[i % 3], 1u << hb);
+            for (int k = 1; k < 16; ++k) tmax = fmaxf(tmax, x[k]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            float alpha = 1.f;
+            if (tmax > m_run + kRaise) {
+              alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+              m_run = tmax;
+              l_run *= alpha;
             }
+            if (g == 0) s_alpha[bb & 1][hb][n] = alpha;
+            if (lane == 0) atomicOr(&s_flag[i % 3], 1u << hb);
+          }
+          float ps = 0.f;
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {              // P^T operand of PV step m: blocks 2m, 2m+1
             f16x8 pb;
-            float ps = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              const float pv = __builtin_amdgcn_exp2f(x[k] - m_run);
+              const float pv = __builtin_amdgcn_exp2f(x[8 * m + k] - m_run);
               ps += pv;
               pb[k] = (_Float16)pv;
             }
-            l_run += ps;
-            s_p[bb & 1][hb][lane] = __builtin_bit_cast(u32x4, pb);
+            s_p[bb & 1][hb][m][lane] = __builtin_bit_cast(u32x4, pb);
           }
-
-          tile_barrier(s_raw);           // P(i), rescale factors, raw(i+1), V^T(i) visible
+          l_run += ps;
         }
+        tile_barrier(s_raw);             // P(i), rescale factors, scale table(i), raw(i+1)
       }
     }
     // ---- epilogue: publish the softmax denominators
@@ -468,68 +454,97 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
 
   // ========================================================== value waves
   const int rid = wave - 4;                          // 0..7: channels 64rid .. 64rid+63
-  // ---- gather by LDS DMA: load unit j of a tile = 1 KB, one 16-byte global load per lane
-  // whose data the hardware writes to LDS at (unit base + 16 lane), so the swizzle is applied
-  // by choosing what each lane fetches:
-  //   j < 8      : codes of entries 4j + l/16; LDS slot l%16 holds chunk lat_slot(l%16, e)
-  //   8 <= j < 12: rope of entries 8(j-8) + l/8; slot l%8 holds chunk (l%8) ^ (e%8)
-  //   j == 12    : the 16 scale bytes of entry l (lanes >= 32 fill the tile's tail), or
-  //                with E4M3 scales the 32 bytes of entry l/2, half l%2
-  // Value wave v owns units j = v + 8c; the units past 12 load the zero row into the tail,
-  // so that every value wave issues the same number of loads per tile and can wait for a
-  // tile with one counter value.  Row indices are read from LDS one tile ahead.
-  const uint8_t* u_base[CPW];
-  int u_stride[CPW], u_goff[CPW], u_dst[CPW], u_entry[CPW];
-  bool u_live[CPW];
+  const int tv = tid - 256;
+  // ---- gather by LDS DMA: a load unit is 1 KB, one 16-byte global load per lane whose data
+  // the hardware writes to LDS at (unit base + 16 lane).  Lane l fetches entry ent_pos(l)
+  // (the column position l holds) in every unit.  Value wave v loads code columns 2v and
+  // 2v+1 (the ones only it reads), rope column v, and value waves 0 (and 1, with E4M3
+  // scales) the scale unit(s).
+  constexpr int kMaxUnits = 4;
+  const int nunits = 3 + ((rid == 0 || (FMT == 1 && rid == 1)) ? 1 : 0);
+  const int my_e = ent_pos(lane);
+  const uint8_t* u_base[kMaxUnits];
+  int u_stride[kMaxUnits], u_dst[kMaxUnits];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int j = rid + NV * c;
-    const bool codes = j < 8, rope = !codes && j < 12, scl = j == 12;
-    const int e = codes ? 4 * j + (lane >> 4)
-                        : (rope ? 8 * (j - 8) + (lane >> 3) : (FMT == 1 ? lane >> 1 : lane & 31));
-    u_entry[c] = e;
-    u_live[c] = codes || rope || (scl && (FMT == 1 || lane < 32));
-    u_base[c] = codes ? p.kv_lat : (rope ? reinterpret_cast<const uint8_t*>(p.kv_rope) : p.kv_scl);
-    u_stride[c] = codes ? kLatBytes : (rope ? 2 * kRope : (FMT == 1 ? 2 * kScl : kScl));
-    u_goff[c] = codes ? 16 * lat_slot(lane & 15, e)
-                      : (rope ? 16 * ((lane & 7) ^ (e & 7)) : (FMT == 1 ? 16 * (lane & 1) : 0));
-    u_dst[c] = __builtin_amdgcn_readfirstlane(codes ? kRawLat + 1024 * j
-                                              : rope ? kRawRope + 1024 * (j - 8)
-                                              : scl ? kRawScl : kRawBytes);
+  for (int c = 0; c < kMaxUnits; ++c) {
+    if (c < 2) {                                     // code column 2rid + c
+      u_base[c] = p.kv_lat + 16 * (2 * rid + c);
+      u_stride[c] = kLatBytes;
+      u_dst[c] = kRawLat + 1024 * (2 * rid + c);
+    } else if (c == 2) {                             // rope column rid
+      u_base[c] = reinterpret_cast<const uint8_t*>(p.kv_rope) + 16 * rid;
+      u_stride[c] = 2 * kRope;
+      u_dst[c] = kRawRope + 1024 * rid;
+    } else {                                         // scale unit rid (0, or 1 for E4M3)
+      u_base[c] = p.kv_scl + 16 * rid;
+      u_stride[c] = FMT == 1 ? 2 * kScl : kScl;
+      u_dst[c] = kRawScl + 1024 * rid;
+    }
   }
-  auto rows_of = [&](int tile, int (&rr)[CPW]) {
+  auto row_of = [&](int tile) { return (tile < ntiles) ? s_rows[tile * kTE + my_e] : -1; };
+  // an empty slot loads the zero row; the select is done on the address bits, so that every
+  // lane issues the same load instructions (one per unit) whatever the tile's slots hold
+  const uint64_t zero_addr = reinterpret_cast<uint64_t>(g_zero_row);
+  auto dma_tile = [&](int row, int slot) {
+    const uint64_t keep = (uint64_t)0 - (uint64_t)(row >= 0);
+    const uint64_t rowu = (uint64_t)(int64_t)max(row, 0);
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
-      rr[c] = (tile < ntiles && u_live[c]) ? s_rows[tile * kTE + u_entry[c]] : -1;
-  };
-  auto dma_tile = [&](const int (&rr)[CPW], int slot) {
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const uint8_t* src = rr[c] >= 0 ? u_base[c] + (int64_t)rr[c] * u_stride[c] + u_goff[c]
-                                      : g_zero_row;
-      __builtin_amdgcn_global_load_lds(src, &s_raw[slot][0] + u_dst[c], 16, 0, 0);
+    for (int c = 0; c < kMaxUnits; ++c) {
+      if (c < nunits) {
+        const uint64_t a = reinterpret_cast<uint64_t>(u_base[c]) + rowu * (uint64_t)u_stride[c];
+        const uint8_t* src = reinterpret_cast<const uint8_t*>((a & keep) | (zero_addr & ~keep));
+        __builtin_amdgcn_global_load_lds(src, &s_raw[slot][0] + u_dst[c], 16, 0, 0);
+      }
     }
   };
-  // loads issued after those of the tile awaited: two tiles of CPW loads
-  auto wait_ready = [] { __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * CPW)); };
-  int rr[CPW];
+  // wait until the tile issued two tiles before the latest (i.e. all but the two latest
+  // tiles' loads) has landed
+  auto wait_ready = [&] {
+    if (nunits == 4) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);
+    else __builtin_amdgcn_s_waitcnt(0x0f70 | 6);
+  };
+  // per-lane offsets of the transposing code reads: lane (G, q) supplies the row of entry
+  // E = 16 (q/4) + 4G + q%4, so that nibble q of every lane's result is that entry, the
+  // order of the P^T operand (slot 8m + j of lane group G = entry 16(2m + j/4) + 4G + j%4)
+  const int tq = lane & 15, tg = lane >> 4;
+  const int tr_off = 16 * ent_pos(16 * (tq >> 2) + 4 * tg + (tq & 3));
 #pragma unroll
-  for (int b = 0; b < kRing - 1; ++b) {
-    rows_of(b, rr);
-    dma_tile(rr, b);
-  }
-  rows_of(kRing - 1, rr);                            // rows of the first loop load
-  // O^T accumulators: channels 64rid + 16c + 4g + i, head h0 + 16b + n
+  for (int b = 0; b < kRing - 1; ++b) dma_tile(row_of(b), b);
+  int next_row = row_of(kRing - 1);                  // rows of the first loop load
+  // O^T accumulators: channels 64rid + 16c + 4g + r, head h0 + 16b + n
   f32x4 acc[4][NHB];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int b = 0; b < NHB; ++b) acc[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  wait_ready();                                      // raw(0) in LDS
+  if (nunits == 4) __builtin_amdgcn_s_waitcnt(0x0f70 | 8);   // raw(0) in LDS
+  else __builtin_amdgcn_s_waitcnt(0x0f70 | 6);
   tile_barrier(s_raw);                               // prologue: raw(0) staged
 
-  // rescale (rare), then O^T += V^T P^T for tile `pt` (parity `par`)
-  auto pv_tile = [&](int pt, int par) {
+  // fp16 scale table of tile `tile` (parity par) from its staged scale bytes: row cb holds
+  // the scale of channel block cb (32 channels; 16 with E4M3 scales) for entries 0..63
+  auto build_sclt = [&](const uint8_t* raw, uint16_t* tb) {
+    if (FMT == 0) {
+      const int cb = tv >> 5, ep = tv & 31;
+      const uint32_t b0 = raw[kRawScl + 16 * ent_pos(2 * ep) + cb];
+      const uint32_t b1 = raw[kRawScl + 16 * ent_pos(2 * ep + 1) + cb];
+      *reinterpret_cast<uint32_t*>(tb + cb * kTE + 2 * ep) =
+          scale_f16_bits<0>(b0) | (scale_f16_bits<0>(b1) << 16);
+    } else {
+      const int cb = tv >> 4, eq = tv & 15;
+      uint32_t v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = scale_f16_bits<1>(raw[kRawScl + 1024 * (cb >> 4) + 16 * ent_pos(4 * eq + k) + (cb & 15)]);
+      *reinterpret_cast<u32x2*>(tb + cb * kTE + 4 * eq) = u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+    }
+  };
+
+  // Period i (between barriers i-1 and i): rescale (rare), then O^T += V^T P^T for tile
+  // i-1 (parity par): transposing reads of its codes, its P^T operands and scales; once
+  // this wave's reads of raw(i-1) are done, the loads of raw(i+3) into that slot; the
+  // conversions and MFMAs; then the scale table of tile i, and the wait for raw(i+1).
+  auto pv_tile = [&](int pt, int par, bool refill, int refill_row, int refill_slot) {
     const uint32_t flag = s_flag[pt % 3];
     if (flag) {
 #pragma unroll
@@ -541,35 +556,74 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
         }
       }
     }
-    f16x8 pbs[NHB];
-#pragma unroll
-    for (int b = 0; b < NHB; ++b) pbs[b] = as_f16x8(s_p[par][b][lane]);
-    const uint8_t* vt = s_vt[par] + (64 * rid + n) * kVtStride + 16 * g;
+    const uint8_t* raw = s_raw[pt & (kRing - 1)];
+    u32x2 code[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f16x8 va = as_f16x8(*reinterpret_cast<const u32x4*>(vt + 16 * c * kVtStride));
+      const int cg = 4 * rid + c;
+      code[c] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(
+              const_cast<uint8_t*>(raw) + kRawLat + 1024 * (cg >> 1) + tr_off + 8 * (cg & 1))));
+    }
+    f16x8 pbs[NHB][2];
 #pragma unroll
-      for (int b = 0; b < NHB; ++b)
-        acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b], acc[c][b], 0, 0, 0);
+    for (int b = 0; b < NHB; ++b)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) pbs[b][m] = as_f16x8(s_p[par][b][m][lane]);
+    // scales of the lane's entries, per channel block and PV step: pairs (slot 2k, 2k+1)
+    constexpr int NSB = FMT == 1 ? 4 : 2;            // channel blocks of this wave
+    u32x2 scl[NSB][2][2];
+    const uint16_t* tb = s_sclt[par];
+#pragma unroll
+    for (int s = 0; s < NSB; ++s) {
+      const int cb = (FMT == 1) ? 4 * rid + s : 2 * rid + s;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          scl[s][m][h] = *reinterpret_cast<const u32x2*>(tb + cb * kTE + 32 * m + 16 * h + 4 * tg);
+    }
+    if (refill) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): this wave's reads done
+      dma_tile(refill_row, refill_slot);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int s = (FMT == 1) ? c : (c >> 1);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint32_t v4[4];                              // slots (2k, 2k+1), scale 1: exact
+        fp4x8_to_f16_pairs(code[c][m], 1.f, v4);
+        f16x8 va;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f16x2 w = __builtin_bit_cast(f16x2, v4[k]) *
+                          __builtin_bit_cast(f16x2, (uint32_t)scl[s][m][k >> 1][k & 1]);
+          va[2 * k] = w[0];
+          va[2 * k + 1] = w[1];
+        }
+#pragma unroll
+        for (int b = 0; b < NHB; ++b)
+          acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbs[b][m], acc[c][b], 0, 0, 0);
+      }
     }
   };
 
-  // Between barriers i-1 and i: PV(i-1), V^T(i) from raw(i), the loads of raw(i+3) into the
-  // slot raw(i-1) left, and the wait for raw(i+1).
   for (int i0 = 0; i0 < ntiles2; i0 += kNPre) {
 #pragma unroll
     for (int bb = 0; bb < kNPre; ++bb) {             // bb & 1 = i & 1: static buffer parity
       const int i = i0 + bb;
       if (tid == 256) s_flag[(i + 1) % 3] = 0u;      // tile i-2's requests, all read by now
-      if (i > 0) pv_tile(i - 1, bb ^ 1);
-      build_vt_unit(s_raw[i & (kRing - 1)], s_vt[bb], 64 * rid + lane);
-      dma_tile(rr, (i + kRing - 1) & (kRing - 1));
-      rows_of(i + kRing, rr);                        // for the next tile's loads
+      const int slot = (i + kRing - 1) & (kRing - 1);   // raw(i-1)'s slot gets raw(i+3)
+      if (i > 0) pv_tile(i - 1, bb ^ 1, true, next_row, slot);
+      else dma_tile(next_row, slot);
+      next_row = row_of(i + kRing);                  // for the next tile's loads
+      build_sclt(s_raw[i & (kRing - 1)], s_sclt[bb]);
       wait_ready();                                  // raw(i+1) in LDS
-      tile_barrier(s_raw);               // P(i), rescale factors, raw(i+1), V^T(i) visible
+      tile_barrier(s_raw);               // P(i), rescale factors, scale table(i), raw(i+1)
     }
   }
-  pv_tile(ntiles2 - 1, (ntiles2 - 1) & 1);
+  pv_tile(ntiles2 - 1, (ntiles2 - 1) & 1, false, 0, 0);
   wait_vmem_all();                                   // no LDS DMA may outlive the workgroup
   __syncthreads();                                   // denominators published
   // ---- epilogue: normalize and write
@@ -577,9 +631,9 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
   for (int b = 0; b < NHB; ++b) {
     const float l_tot = s_l[b][n];
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int64_t row = (p.splits == 1) ? ((int64_t)t * p.H + h0 + 16 * b + n)
-                                        : (((int64_t)t * p.splits + sp) * p.H + h0 + 16 * b + n);
-    float* obase = ((p.splits == 1) ? p.o : p.o_part) + row * kLat + 64 * rid + 4 * g;
+    const int64_t orow = (p.splits == 1) ? ((int64_t)t * p.H + h0 + 16 * b + n)
+                                         : (((int64_t)t * p.splits + sp) * p.H + h0 + 16 * b + n);
+    float* obase = ((p.splits == 1) ? p.o : p.o_part) + orow * kLat + 64 * rid + 4 * g;
 #pragma unroll
     for (int c = 0; c < 4; ++c) *reinterpret_cast<f32x4*>(obase + 16 * c) = acc[c][b] * inv;
   }

@@ -28,8 +28,9 @@
  *     (one per host thread, created on first use), forked from `stream` and joined back
  *     into it with events before the call returns; work queued on `stream` afterwards
  *     sees every output.  Fork and join are capturable.  For fewer than 256 rows with
- *     H == H_kv the branch runs on at most 128 persistent workgroups, one per CU, and the
- *     global branch's attention is planned for the CUs left.
+ *     H == H_kv the branch runs on persistent workgroups, one per CU, on at most half the
+ *     device's CUs (128 on MI355X), and the global branch's attention is planned for the
+ *     CUs left (csa2_plan_cus).
  *   - "device" pointers are device memory and must be 16-byte aligned.
  *   - bf16 tensors are raw 16-bit patterns; all layouts are dense row-major.
  *   - Paged caches: 64 entries per page; entry j of sequence b lives in physical row
@@ -244,6 +245,23 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
                              const csa2_group_args* g, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* The layer group without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, semantics, kernels and results as csa2_layer_group; the
+ * workspace is instead a fixed array of CSA2_NOALLOC_SCRATCH_BYTES in the library's device
+ * code, one per device, held until the process ends.  The first call on a device (with it
+ * current) takes the array's address and makes the device's side stream; after that no
+ * call allocates anything.  Errors: CSA2_ERR_WORKSPACE when the group needs more workspace
+ * than the array holds (csa2_workspace_bytes(CSA2_OP_LAYER_GROUP, g) above the limit: every
+ * decode group of up to 64 rows x 32,768 entries, 32 x 65,536 or 4 x 262,144 fits; a
+ * 4096-row prefill does not), CSA2_ERR_HIP when the set-up fails; otherwise as
+ * csa2_layer_group.  All calls on one device share its array (and its side stream), whose
+ * contents persist between calls: calls that overlap on one device, from several host
+ * threads or streams, race and must be serialized by the caller. */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+csa2_status csa2_layer_group_noalloc(const csa2_layer_desc* L, int32_t n_layers,
+                                     const csa2_group_args* g, void* stream);
+
 /* MXFP4 cache write ([summary] Architecture Components, item 5): quantizes `rows` fp32
  * latent rows x [rows, 512] into physical rows dst_row[r] of the planes
  * lat [*, 256] and scl [*, 16] (OCP MX: shared exponent floor(log2 max|x|) - 2 over each
@@ -296,6 +314,13 @@ size_t csa2_workspace_bytes(int32_t op, const void* args);
 const char* csa2_last_error(void);
 const char* csa2_status_string(csa2_status s);
 int32_t csa2_abi_version(void);
+
+/* Compute units of the current device that the launch plans (attention splits, the SWA
+ * branch's persistent workgroups) and therefore csa2_workspace_bytes assume: queried once
+ * per device (hipDeviceAttributeMultiprocessorCount) and cached for the process; 256 (one
+ * MI355X) when no device can be queried.  Size a workspace with the device current that
+ * the call will run on. */
+int32_t csa2_plan_cus(void);
 
 /* Kernel timing: while enabled, every kernel launch of the library records a start and a
  * stop event itself (hipExtLaunchKernel), and the elapsed time accumulates per kernel

@@ -55,6 +55,16 @@ def test_struct_layout_matches_header(c, tmp_path):
             assert int(got[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
 
 
+def test_plan_cus_without_a_device(c):
+    """With no device to query, the launch plans (and so the workspace sizes) assume one
+    MI355X: 256 compute units."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is visible; the GPU test checks the queried count")
+    assert c.plan_cus() == 256
+    assert c.plan_cus() == 256          # cached
+
+
 def test_version_and_strings(c):
     assert c.abi_version() == 2
     for st, name in c.STATUS.items():
@@ -275,6 +285,27 @@ def test_group_mode_rules(c):
     assert call_group(c, ok, group(c, H=40))[0] == 2
     assert call_group(c, ok, group(c, H_I=99))[0] == 2
     assert c.lib.csa2_layer_group(None, 1, ctypes.byref(g), None, 0, None) == 1
+
+
+def test_noalloc_group_validation_and_limit(c):
+    """The allocation-free layer group validates like csa2_layer_group, is a no-op for T = 0,
+    and rejects a group whose workspace exceeds its static scratch (a 4096-row prefill over
+    132,096 entries: 2 GiB) before any HIP call."""
+    F, R, U = c.FULL, c.REINDEX, c.REUSE
+    noalloc = c.lib.csa2_layer_group_noalloc
+
+    def call(layers, g):
+        arr = (c.LayerDesc * len(layers))(*layers)
+        return noalloc(arr, len(layers), ctypes.byref(g), None), c.lib.csa2_last_error().decode()
+
+    assert call([layer(c, R)], group(c))[0] == 4
+    assert call([layer(c, F, q=None)], group(c))[0] == 1
+    assert call([layer(c, F), layer(c, U)], group(c, T=0))[0] == 0
+    big = group(c, T=4096, B=1, max_pages=2064, n_pages=2064)
+    need = c.lib.csa2_workspace_bytes(c.OP_LAYER_GROUP, ctypes.byref(big))
+    assert need > c.NOALLOC_SCRATCH_BYTES
+    st, msg = call([layer(c, F), layer(c, R), layer(c, U)], big)
+    assert st == 5 and "static scratch" in msg, msg
 
 
 def test_quantize_validation(c):
