@@ -304,6 +304,110 @@ def test_attn_arbitrary_index_lists(csa2, dev):
     assert np.all(res["o"][1] == 0) and np.all(np.isneginf(res["lse"][1]))
 
 
+def _planes_from(csa2, dev, w, x, h, d):
+    """Quantize latent rows x [E, 512] of the single sequence of w on both sides (library
+    quantizer on the GPU, oracle quantizer on the host) into each side's planes."""
+    pt = w.page_table()
+    lat, scl = orc.mxfp4_quantize(x)
+    _, _, rope = h.kv[0]
+    h.kv[0] = (w.to_physical(lambda b: lat, pt), w.to_physical(lambda b: scl, pt), rope)
+    L = d.layers[0]
+    dst = torch.from_numpy(w.physical_rows(0, pt).astype(np.int64)).to(dev)
+    csa2.mxfp4_quantize(torch.from_numpy(x).to(dev), L["kv_lat"], L["kv_scl"], dst)
+    torch.cuda.synchronize()
+    got = L["kv_scl"].cpu().numpy().reshape(-1, 16)
+    np.testing.assert_array_equal(got, h.kv[0][1])
+    return scl
+
+
+def test_attn_latent_scale_range(csa2, dev):
+    """Latent blocks at the edges of the range in which the value product is exact in fp16
+    (E8M0 scale bytes 104..140): values are exact from byte 104 up, so rows over blocks of
+    bytes 104..140 meet the usual tolerances; below byte 104 a value rounds to fp16's
+    subnormal grid (absolute error at most 2^-25 per value), so a row whose picks are all
+    such blocks is held to that absolute bound; above byte 140 the product overflows and the
+    affected output channels are non-finite (a loud failure, never a wrong finite value)."""
+    _say("attn_latent_scale_range")
+    w = W(B=1, T=4, E=512, K=128, H=64, seq_id_rows=[0, 0, 0, 0], shuffle=False)
+    d = tl.DeviceWorkload(w, dev)
+    h = tl.HostWorkload(w)
+    rng = np.random.default_rng(17)
+    x = w.latent_seq(0).astype(np.float32).reshape(512, 16, 32).copy()
+    # entries 0..127: blocks scaled by 2^-27..2^-22 (bytes 98..104); 128..255: by 2^10..2^13
+    # (bytes up to 140); 256..383: unscaled; 384: one block at 2^16 (byte 141 or more)
+    x[:128] *= (2.0 ** rng.integers(-27, -21, size=(128, 16, 1))).astype(np.float32)
+    x[128:256] *= (2.0 ** rng.integers(10, 14, size=(128, 16, 1))).astype(np.float32)
+    x[384, 3] *= np.float32(2.0 ** 16)
+    x[255, 0, 0] = np.float32(7.9 * 2.0 ** 13)                  # a block at byte 140
+    x = x.reshape(512, 512)
+    scl = _planes_from(csa2, dev, w, x, h, d)
+    assert scl[:128].min() <= 100 and scl[:128].max() == 104
+    assert scl[128:256].max() == 140
+    assert scl[384, 3] >= 141
+    idx = -np.ones((4, 128), np.int32)
+    idx[0] = np.arange(128)                                     # all below byte 104
+    idx[1] = np.r_[np.arange(0, 128, 2), np.arange(256, 320)]   # small + unscaled
+    idx[2] = np.arange(128, 256)                                # bytes up to 140
+    idx[3, :64] = np.r_[np.arange(320, 383), 384]               # one block above 140
+    L = d.layers[0]
+    _, _, rope = h.kv[0]
+    lat_h, scl_h, _ = h.kv[0]
+    pt = w.page_table()
+    # blocks of 2^13 give logits near 10^4, where fp32 accumulation alone exceeds the lse
+    # tolerance: row 2 runs with the logit scale reduced by 2^-13 on both sides
+    for sm, rows in ((1.0 / 24.0, [0, 1, 3]), (2.0 ** -13 / 24.0, [2])):
+        o, lse = csa2.sparse_attn_fp4(L["q"], L["kv_lat"], L["kv_scl"], L["kv_rope"],
+                                      d.page_table, d.seq_id, torch.from_numpy(idx).to(dev),
+                                      sm_scale=sm)
+        torch.cuda.synchronize()
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        ro, rl = orc.sparse_attn(w.P, w.q(), lat_h, scl_h, rope, pt, w.seq_id(), idx,
+                                 sm_scale=sm, rows=np.arange(4))
+        for t in rows:
+            if t == 0:
+                assert np.all(np.isfinite(o[0]))
+                err0 = np.abs(o[0] - ro[0]).max()             # 2^-25 per value, plus
+                assert err0 <= 2.0 ** -24, err0               # fp32 accumulation
+                tl._cmp_lse("lse row 0", lse[:1], rl[:1])
+            elif t == 3:
+                bad = ~np.isfinite(o[3])
+                assert bad[:, 96:128].any() and not bad[:, :96].any() and not bad[:, 128:].any()
+            else:
+                # outputs in units of the picked blocks' scale (2^13 for row 2), the scale
+                # the absolute tolerance is stated for
+                u = 2.0 ** 13 if t == 2 else 1.0
+                tl.check_attn({"o": o / u, "lse": lse}, {"o": ro[[t]] / u, "lse": rl[[t]]},
+                              rows=np.array([t]), swa=False)
+
+
+def test_workspace_contents_do_not_matter(csa2, dev):
+    """The layer group's outputs do not depend on what the workspace held before the call:
+    a zeroed and an all-0xFF workspace give bit-identical outputs.  Rows longer than 65,536
+    entries (the chunked Top-K and its histograms), a pooled Reindex layer, split
+    attention."""
+    _say("workspace_contents_do_not_matter")
+    w = W(name="poison", B=2, T=4, E=70016, K=512, H=64, H_I=8, H_kv=64, n_hot=300,
+          seq_id_rows=[0, 1, 1, 0], modes=[0, 3, 2])
+    d = tl.DeviceWorkload(w, dev)
+    need = csa2.workspace_bytes(csa2.OP_LAYER_GROUP, d.group_args())
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=dev)
+        for L in d.layers:
+            for k in ("o", "lse", "o_swa", "lse_swa"):
+                L[k].fill_(float("nan"))
+            if "idx_out" in L:
+                L["idx_out"].fill_(-7)
+        csa2.layer_group(d.descs(), d.group_args(), workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([{k: L[k].cpu().numpy() for k in ("o", "lse", "o_swa", "lse_swa")} |
+                     ({"idx": L["idx_out"].cpu().numpy()} if "idx_out" in L else {})
+                     for L in d.layers])
+    for li, (a, b) in enumerate(zip(*outs)):
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k], err_msg=f"layer {li} {k}")
+
+
 def test_topk_all_equal_scores(csa2, dev):
     """Every entry scores the same: the lowest K indices win, in order."""
     _say("topk_all_equal_scores")
