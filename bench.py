@@ -60,6 +60,12 @@ def parse_args():
     ap.add_argument("--reindex-pool", action="store_true",
                     help="the workload's Reindex layers search the candidate pool of its Full "
                          "layer (workload 3)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="fold rocprofv3 --pmc output directories of this workload into "
+                         "profiles/counters_<workload>.json and exit")
+    ap.add_argument("--calibration-dirs", nargs="*", default=[],
+                    help="with --summarize-counters: FETCH_SIZE and WRITE_SIZE runs of "
+                         "--calibrate-copy")
     ap.add_argument("--peaks-only", action="store_true",
                     help="only measure this GPU's MFMA and LDS peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -316,26 +322,132 @@ def measure_append(dev, n, steps, flush_mb):
             "entries_per_s": round(n / (us * 1e-6), 1)}
 
 
+KERNEL_SOURCES = {"idx_score": "k_index.hip", "topk": "k_index.hip",
+                  "idx_pool_score": "k_index.hip", "topk_pool": "k_index.hip",
+                  "topk_ck_hist": "k_index.hip", "topk_ck_compact": "k_index.hip",
+                  "topk_ck_select": "k_index.hip", "sparse_attn": "k_attn.hip",
+                  "attn_merge": "k_attn.hip", "swa": "k_swa.hip", "kv_append": "k_quant.hip",
+                  "mxfp4_quantize": "k_quant.hip"}
+
+
 def kernel_source_sha(name):
-    src = {"idx_score": "k_index.hip", "topk": "k_index.hip", "idx_pool_score": "k_index.hip",
-           "topk_pool": "k_index.hip", "sparse_attn": "k_attn.hip", "attn_merge": "k_attn.hip",
-           "swa": "k_swa.hip", "kv_append": "k_quant.hip"}.get(name)
+    src = KERNEL_SOURCES.get(name)
     if src is None:
         return None
     path = os.path.join(ROOT, "fp4_compressed_sparse_amd", "csrc", src)
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def counter_traffic(workload_name, kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there
-    is none for this kernel or the kernel's source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+def library_kernel(device_name):
+    """The library's timing name of a device kernel symbol (as rocprofv3 prints it)."""
+    n = device_name
+    for pat, key in (("idx_score_kernel", "idx_score"), ("idx_gemm_kernel", "idx_score"),
+                     ("idx_pool_score_kernel", "idx_pool_score"), ("topk_stream_kernel", "topk"),
+                     ("topk_ck_hist", "topk_ck_hist"), ("topk_ck_compact", "topk_ck_compact"),
+                     ("topk_ck_select", "topk_ck_select"), ("sparse_attn_kernel", "sparse_attn"),
+                     ("attn_merge_kernel", "attn_merge"), ("swa_", "swa"),
+                     ("kv_append", "kv_append"), ("mxfp4_quantize", "mxfp4_quantize")):
+        if pat in n:
+            return key
+    if "topk_reg_kernel" in n:
+        return "topk_pool" if "true>" in n else "topk"
+    return None
+
+
+def counter_record(workload_name, kernel):
+    """The committed rocprofv3 counter summary of a kernel on a workload
+    (profiles/counters_<workload>.json), or None if there is none or the kernel's source
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload_name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(kernel)
     if not rec or rec.get("source_sha") != kernel_source_sha(kernel):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def counter_traffic(workload_name, kernel):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from the committed counter
+    summary, or None."""
+    rec = counter_record(workload_name, kernel)
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+MFMA_PEAK_TFLOPS = {"f8": 5000.0, "f16": 2500.0, "bf16": 2500.0, "f6f4": 10100.0}
+
+
+def counter_mfma(workload_name, kernel, avg_us):
+    """Matrix-core use of a kernel from its committed counters: FLOPs per launch by operand
+    type (SQ_INSTS_VALU_MFMA_MOPS_*, 512 FLOPs per unit) and the fraction of the kernel's
+    duration that the whole device's matrix cores need for them at the published dense peak
+    of each type (1.0 = every matrix core busy for the whole kernel)."""
+    rec = counter_record(workload_name, kernel)
+    if not rec or "mfma_flops_per_launch" not in rec:
+        return None
+    fl = rec["mfma_flops_per_launch"]
+    busy_s = sum(v / (MFMA_PEAK_TFLOPS[k] * 1e12) for k, v in fl.items() if k in MFMA_PEAK_TFLOPS)
+    return {"flops_per_launch": fl, "tflops": round(sum(fl.values()) / (avg_us * 1e-6) / 1e12, 1),
+            "frac_of_device_peak": round(busy_s / (avg_us * 1e-6), 4)}
+
+
+def summarize_counters(name, dirs, calib_dirs=None):
+    """Fold rocprofv3 --pmc runs of bench.py (dirs holding run_counter_collection.csv; one
+    counter group per run) into profiles/counters_<name>.json: per library kernel, the mean
+    per dispatch of every counter, calibrated HBM bytes and matrix-core FLOPs by type, with
+    the hash of the kernel's source.  calib_dirs: FETCH_SIZE and WRITE_SIZE runs of
+    --calibrate-copy (1 GiB read and 1 GiB written per dispatch)."""
+    import csv
+    import glob
+    sums, counts, dev_names = {}, {}, {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = library_kernel(r["Kernel_Name"])
+                if k is None:
+                    continue
+                c = r["Counter_Name"]
+                sums.setdefault(k, {}).setdefault(c, 0.0)
+                sums[k][c] += float(r["Counter_Value"])
+                counts.setdefault(k, {}).setdefault(c, 0)
+                counts[k][c] += 1
+                dev_names[k] = r["Kernel_Name"].split("(")[0]
+    fetch_factor, write_factor = 2.0, 1.0
+    calib = {}
+    for d in calib_dirs or []:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                # the in-place add reads and writes the 1 GiB buffer; the fill before it
+                # only writes it
+                if "_add<" in r["Kernel_Name"]:
+                    calib.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if calib.get("FETCH_SIZE"):
+        fetch_factor = (1 << 30) / 1024 / (sum(calib["FETCH_SIZE"]) / len(calib["FETCH_SIZE"]))
+    if calib.get("WRITE_SIZE"):
+        write_factor = (1 << 30) / 1024 / (sum(calib["WRITE_SIZE"]) / len(calib["WRITE_SIZE"]))
+    out = {"_calibration": {"fetch_factor": round(fetch_factor, 4),
+                            "write_factor": round(write_factor, 4),
+                            "how": "a 1 GiB fp32 copy (bench.py --calibrate-copy) read back: "
+                                   "bytes = FETCH_SIZE x 1024 x fetch_factor, "
+                                   "WRITE_SIZE x 1024 x write_factor"}}
+    for k, cs in sums.items():
+        mean = {c: v / counts[k][c] for c, v in cs.items()}
+        rec = {"kernel": dev_names[k], "dispatches": max(counts[k].values()),
+               "source_sha": kernel_source_sha(k),
+               "counters_per_dispatch": {c: round(v, 1) for c, v in sorted(mean.items())}}
+        if "FETCH_SIZE" in mean and "WRITE_SIZE" in mean:
+            rd = mean["FETCH_SIZE"] * 1024 * fetch_factor
+            wr = mean["WRITE_SIZE"] * 1024 * write_factor
+            rec.update(hbm_read_bytes_per_launch=int(rd), hbm_write_bytes_per_launch=int(wr),
+                       hbm_bytes_per_launch=int(rd + wr))
+        mops = {t: mean.get(f"SQ_INSTS_VALU_MFMA_MOPS_{t.upper()}") for t in ("f8", "f16",
+                                                                             "bf16", "f6f4")}
+        if any(v is not None for v in mops.values()):
+            rec["mfma_flops_per_launch"] = {t: int(v * 512) for t, v in mops.items() if v}
+        out[k] = rec
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.json")
+    json.dump(out, open(path, "w"), indent=1)
+    return path
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -430,6 +542,14 @@ def main():
         print(f"bench.py measures one GPU only (the hot path shards by sequence with no "
               f"exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        import synth
+        w = synth.workload(args.workload)
+        if args.kv_format:
+            w = dataclasses.replace(w, name=w.name + "_e4m3")
+        print(summarize_counters(w.name, args.summarize_counters, args.calibration_dirs))
+        return
+
     import torch
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -511,17 +631,31 @@ def main():
             per_launch = algo[k] / (v["launches"] / args.steps)
             v["algo_bytes"] = per_launch
             v["gbs"] = round(per_launch / (v["avg_us"] * 1e-6) / 1e9, 1)
-    # the roofline kernel: the longest kernel of the global branch, the step's critical
-    # path (the SWA branch runs beside it on its own CUs; its rate is in kernels["swa"])
-    dominant = max((k for k in kt if k != "swa"), key=lambda k: kt[k][1])
-    dk = kernels[dominant]
-    achieved = dk.get("gbs")
-    traffic = counter_traffic(w.name, dominant)
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                "traffic": traffic,
-                "algo_bytes_per_launch": dk.get("algo_bytes"), "avg_us": dk["avg_us"]}
+    flops_attn = 2 * w.H * 1088 * int(min(w.E, w.K)) * w.T        # per launch (one layer)
+
+    def roof(kernel):
+        dk = kernels[kernel]
+        achieved = dk.get("gbs")
+        r = {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+             "traffic": counter_traffic(w.name, kernel),
+             "algo_bytes_per_launch": dk.get("algo_bytes"), "avg_us": dk["avg_us"]}
+        cm = counter_mfma(w.name, kernel, dk["avg_us"])
+        if cm:
+            r["mfma_counters"] = cm
+        return r
+
+    # the roofline kernel: the FP4 gather-attention (the kernel the hot path is built
+    # around; it sits at the ridge, so its matrix-core use is reported too); the longest
+    # kernel of the global branch, the step's critical path, is reported beside it
+    roofline = roof("sparse_attn")
+    roofline["mfma_algorithmic"] = {
+        "flops_per_launch": flops_attn,
+        "tflops": round(flops_attn / (kernels["sparse_attn"]["avg_us"] * 1e-6) / 1e12, 1),
+        "frac_bf16_peak": round(flops_attn / (kernels["sparse_attn"]["avg_us"] * 1e-6) / 1e12
+                                / MFMA_BF16_PEAK_TFLOPS, 4)}
+    critical = max((k for k in kt if k != "swa"), key=lambda k: kt[k][1])
+    roofline_cp = roof(critical)
 
     result = {
         "metric": "decode query-tokens/s and achieved HBM GB/s (% peak) at 128K ctx, Top-K 2048",
@@ -550,6 +684,7 @@ def main():
         "input_copies": len(sets),
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_critical_path": roofline_cp,
     }
     if not args.kernel_pass_only:
         hbm = measure_hbm(dev)
