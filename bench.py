@@ -690,6 +690,7 @@ def main():
         hbm = measure_hbm(dev)
         hbm["step_frac_of_copy"] = (round(result["step_hbm_gbs"] / hbm["copy_gbs"], 4)
                                     if ms_step else None)
+        achieved = roofline["achieved"]
         hbm["roofline_frac_of_copy"] = (round(achieved / hbm["copy_gbs"], 4)
                                         if achieved else None)
         result["hbm_measured"] = hbm

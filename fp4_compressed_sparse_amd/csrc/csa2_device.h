@@ -72,7 +72,8 @@ __device__ __forceinline__ u32x4 ld_global_16_addr(uint64_t a) {
   return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(a);
 }
 
-// Wait until every vector memory load issued so far has returned.
+// Wait until every vector memory access issued so far has completed (the counter covers
+// loads and stores on this architecture).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (Hillis-Steele within
