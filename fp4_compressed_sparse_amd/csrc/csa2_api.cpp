@@ -193,6 +193,11 @@ csa2_status check_paging(const char* fn, int32_t B, int32_t max_pages, int32_t n
   return CSA2_OK;
 }
 
+// Row-tiled rows long enough select through sampled candidates (see kCandMinKeys).
+bool cand_path(int32_t T, int64_t E) {
+  return T >= kIdxGemmMinRows && E >= kCandMinKeys && !topk_chunked(T, E);
+}
+
 // Keys [T, E]; for the chunked Top-K also row histograms [T, kCkHistWords], per-chunk
 // counts [T, chunks], per-row digits [T, 8] and candidate keys and indices [T, E] each.
 size_t index_ws_bytes(int32_t T, int32_t max_pages) {
@@ -204,6 +209,7 @@ size_t index_ws_bytes(int32_t T, int32_t max_pages) {
          round_up((size_t)T * 8 * sizeof(uint32_t)) +
          2 * round_up((size_t)T * (size_t)E * sizeof(uint32_t));
   if (T >= kIdxGemmMinRows) b += round_up(1024);   // the row-tiled scoring's store sink
+  if (cand_path(T, E)) b += 2 * round_up((size_t)T * sizeof(uint32_t));   // thresholds, flags
   return b;
 }
 
@@ -277,10 +283,6 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   sp.clear = chunked ? ck : nullptr;
   sp.clear_words = chunked ? a->T * kCkHistWords : 0;
   sp.trash = (a->T >= kIdxGemmMinRows) ? ck : nullptr;   // chunked and row-tiled never meet
-  csa2_status st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
-  if (st) return st;
-  st = between();
-  if (st) return st;
   TopkParams tp;
   tp.T = a->T;
   tp.K = a->K;
@@ -290,6 +292,73 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   tp.idx_out = a->idx_out;
   tp.ck_hist = tp.ck_counts = tp.ck_sel = tp.ck_ckey = nullptr;
   tp.ck_cidx = nullptr;
+  csa2_status st;
+  if (cand_path(a->T, E)) {
+    // Sampled candidates.  Inside the keys area (written only by the exact path at the
+    // end): first the packed sample, then, once the thresholds are known, the candidate
+    // counts, keys and indices.  Thresholds and flags sit after the store sink.
+    const int G = cand_page_gap(E);
+    const int64_t ns = (((E + kPage - 1) / kPage + G - 1) / G) * kPage;
+    const int nch = (int)((E + kGemmChunk - 1) / kGemmChunk);
+    char* w = static_cast<char*>(ws);
+    uint32_t* sample = reinterpret_cast<uint32_t*>(w);
+    uint32_t* ccnt = reinterpret_cast<uint32_t*>(w);
+    w += round_up((size_t)a->T * nch * sizeof(uint32_t));
+    uint32_t* ckey = reinterpret_cast<uint32_t*>(w);
+    w += round_up((size_t)a->T * nch * kCandCap * sizeof(uint32_t));
+    int32_t* cidx = reinterpret_cast<int32_t*>(w);
+    char* w2 = reinterpret_cast<char*>(ck) + round_up(1024);
+    uint32_t* thr = reinterpret_cast<uint32_t*>(w2);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(w2 + round_up((size_t)a->T * sizeof(uint32_t)));
+
+    IdxScoreParams s1 = sp;                          // 1: the sample
+    s1.gemm_mode = kGemmSample;
+    s1.page_gap = G;
+    s1.key_stride = ns;
+    s1.keys = sample;
+    st = timed("idx_sample", s, [&] { return launch_idx_score(s1, s); });
+    if (st) return st;
+    TopkParams t1 = tp;                              // 2: thresholds
+    t1.key_stride = ns;
+    t1.keys = sample;
+    t1.thr = thr;
+    t1.row_flags = flags;
+    t1.page_gap = G;
+    st = timed("topk_thr", s, [&] { return launch_topk_thr(t1, s); });
+    if (st) return st;
+    IdxScoreParams s3 = sp;                          // 3: scoring into candidates
+    s3.gemm_mode = kGemmCand;
+    s3.thr = thr;
+    s3.row_flags = flags;
+    s3.cand_key = ckey;
+    s3.cand_idx = cidx;
+    s3.cand_cnt = ccnt;
+    s3.n_chunks = nch;
+    st = timed("idx_score", s, [&] { return launch_idx_score(s3, s); });
+    if (st) return st;
+    st = between();
+    if (st) return st;
+    TopkParams t4 = tp;                              // 4: the exact Top-K of the candidates
+    t4.cand_key = ckey;
+    t4.cand_idx = cidx;
+    t4.cand_cnt = ccnt;
+    t4.row_flags = flags;
+    t4.n_chunks = nch;
+    st = timed("topk", s, [&] { return launch_topk_cand(t4, s); });
+    if (st) return st;
+    // 5, 6: the exact path for flagged rows only (the other workgroups leave at once)
+    IdxScoreParams s5 = sp;
+    s5.row_flags = flags;
+    st = timed("idx_exact", s, [&] { return launch_idx_score(s5, s); });
+    if (st) return st;
+    TopkParams t6 = tp;
+    t6.row_flags = flags;
+    return timed("topk_exact", s, [&] { return launch_topk(t6, s); });
+  }
+  st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
+  if (st) return st;
+  st = between();
+  if (st) return st;
   if (!chunked) return timed("topk", s, [&] { return launch_topk(tp, s); });
   tp.ck_hist = ck;
   char* w = reinterpret_cast<char*>(ck);

@@ -88,6 +88,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// Inclusive prefix sum within each 16-lane row of the wave (the first four steps above).
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return v;
+}
+
 // max(a - b, 0) for unsigned values, written without a comparison-guarded subtraction:
 // this compiler has been seen to hoist the subtraction of `a > b ? f(a - b) : 0` with a
 // no-wrap flag and then treat b <= a as known elsewhere (dropping a later min(b, a)).

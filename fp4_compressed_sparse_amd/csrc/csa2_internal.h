@@ -45,7 +45,23 @@ struct IdxScoreParams {
   // block of selection i (chunks then counts workgroups of kPoolSelPerBlock selections)
   const int32_t* pool_sel = nullptr;
   int pool_K = 0;
+  // row-tiled scoring only (prefill): what the tiles produce
+  //   kGemmKeys:  every visible key (row_flags, if set: only tiles holding a flagged row run)
+  //   kGemmSample: the keys of every page_gap-th page, packed ([T, key_stride], 0 = masked)
+  //   kGemmCand:  the keys >= thr[t] with their entries, per 2048-entry chunk in entry
+  //               order, at most kCandCap each ([T, n_chunks, kCandCap]); cand_cnt gets
+  //               the full count, and a chunk that overflows sets row_flags[t]
+  int gemm_mode = 0;
+  int page_gap = 1;
+  int n_chunks = 0;
+  const uint32_t* thr = nullptr;       // [T]
+  uint32_t* row_flags = nullptr;       // [T]
+  uint32_t* cand_key = nullptr;
+  int32_t* cand_idx = nullptr;
+  uint32_t* cand_cnt = nullptr;        // [T, n_chunks]
 };
+
+constexpr int kGemmKeys = 0, kGemmSample = 1, kGemmCand = 2;
 
 struct TopkParams {
   int T, K;
@@ -65,6 +81,15 @@ struct TopkParams {
   // slot 8i + o to entry 8 * (pool_sel[t, i] / 8) + o
   const int32_t* pool_sel = nullptr;
   int pool_K = 0;
+  // sampled-candidate path (prefill): per-row thresholds, candidates and flags as in
+  // IdxScoreParams; row_flags also restricts the exact (fallback) kernels to flagged rows
+  const uint32_t* cand_key = nullptr;
+  const int32_t* cand_idx = nullptr;
+  const uint32_t* cand_cnt = nullptr;
+  uint32_t* thr = nullptr;
+  uint32_t* row_flags = nullptr;
+  int n_chunks = 0;
+  int page_gap = 1;
 };
 
 // Top-K over few long rows runs chunked: rows longer than 65536 keys with at most
@@ -143,6 +168,20 @@ struct AppendParams {
 // ---------------------------------------------------------------- launch geometry
 constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
 constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-tiled
+// Row-tiled rows of at least kCandMinKeys keys select through sampled candidates: the keys
+// of every page_gap-th page (at most kSamplePages pages) set a per-row threshold, the
+// scoring keeps only the keys at or above it (at most kCandCap per 2048-entry chunk), and
+// the exact selection runs on those (at most kCandList); rows where that fails go through
+// the exact path again.
+constexpr int kGemmChunk = 2048;       // entries per row-tiled scoring workgroup
+constexpr int kCandMinKeys = 16384;
+constexpr int kSamplePages = 64;
+constexpr int kCandCap = 128;
+constexpr int kCandList = 6144;
+inline int cand_page_gap(int64_t key_stride) {
+  const int64_t pages = (key_stride + kPage - 1) / kPage;
+  return (int)((pages + kSamplePages - 1) / kSamplePages);
+}
 static_assert(kCkMaxRows < kIdxGemmMinRows, "row-tiled scoring reuses the chunked Top-K area");
 constexpr int kSwaTileMinRows = 256;   // from this many rows, SWA runs row-tiled on MFMA
 constexpr int kTopkThreads = 1024;
@@ -205,6 +244,8 @@ csa2_status set_error(csa2_status st, const char* msg);
 // Each launcher enqueues one kernel on `s` and returns hipGetLastError().
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_topk_thr(const TopkParams& p, hipStream_t s);
+hipError_t launch_topk_cand(const TopkParams& p, hipStream_t s);
 hipError_t launch_topk_chunked(const TopkParams& p, int pass, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t s);

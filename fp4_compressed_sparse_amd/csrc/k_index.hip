@@ -386,6 +386,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   __shared__ uint32_t s_digit, s_rem;
   __shared__ uint32_t s_wtot[kTopkWaves];
   const int t = blockIdx.x;
+  if (!POOL && p.row_flags && !p.row_flags[t]) return;   // selected on the candidate path
   const int n = POOL ? kPoolBlock * p.pool_K : p.n_vis[t];
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
@@ -522,6 +523,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   }
 }
 
+// Radix select of the `rank`-th largest of the first L keys of an LDS list over the first
+// `passes` digits (3: the exact key and how many keys equal to it to keep; 2: the key with
+// its low 8 bits cleared).  Block-wide (kTopkThreads threads).
+__device__ __forceinline__ void topk_list_select(TopkShared& sh, const uint32_t* lkey, int L,
+                                                 uint32_t rank, int passes, uint32_t& key,
+                                                 uint32_t& keep) {
+  const int tid = threadIdx.x;
+  uint32_t pre = 0u, rem = rank;
+#pragma unroll
+  for (int ps = 0; ps < 3; ++ps) {
+    if (ps == passes) break;                         // block-uniform
+    const uint32_t pmask = topk_prefix_mask(ps);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
+    __syncthreads();
+    for (int i = tid; i < L; i += kTopkThreads) {
+      const uint32_t k = lkey[i];
+      if ((k & pmask) == pre) atomicAdd(&sh.hist[topk_digit(k, ps)], 1u);
+    }
+    __syncthreads();
+    topk_find_digit(sh, rem);
+    pre |= topk_place(sh.digit, ps);
+    rem = sh.remaining;
+  }
+  key = pre;
+  keep = rem;
+}
+
+// The ordered emission from an LDS list that holds every key >= tau in index order.
+__device__ __forceinline__ void topk_emit_list(TopkShared& sh, const uint32_t* lkey,
+                                               const int32_t* lidx, int L, uint32_t tau,
+                                               uint32_t need_eq, int32_t* out) {
+  const int tid = threadIdx.x;
+  uint32_t gt_base = 0u, eq_base = 0u;
+  for (int b0 = 0; b0 < L; b0 += 4 * kTopkThreads) {
+    uint32_t kv[4];
+    bool valid[4];
+    int idx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = b0 + 4 * tid + e;
+      valid[e] = i < L;
+      kv[e] = valid[e] ? lkey[i] : 0u;
+      idx[e] = valid[e] ? lidx[i] : 0;
+    }
+    topk_emit_tile(sh, kv, valid, idx, tau, need_eq, gt_base, eq_base, out);
+  }
+}
+
 // Rows of any length, streamed from memory.  The first pass histograms the top digit (bits
 // 31..20).  When the keys at or above the chosen digit fit in LDS (kTopkListCap), a second
 // stream copies them, with their indices and in index order, into an LDS list; the last two
@@ -538,6 +588,7 @@ void topk_stream_kernel(TopkParams p) {
   __shared__ uint32_t s_lkey[kTopkListCap];
   __shared__ int32_t s_lidx[kTopkListCap];
   const int t = blockIdx.x;
+  if (p.row_flags && !p.row_flags[t]) return;        // selected on the candidate path
   const int n = p.n_vis[t];
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
@@ -561,46 +612,11 @@ void topk_stream_kernel(TopkParams p) {
       }
     }
   };
-  // Radix select of the `rank`-th largest of the first L keys of the LDS list over the
-  // first `passes` digits (3: the exact key and how many keys equal to it to keep; 2: the
-  // key with its low 8 bits cleared).
   auto list_select = [&](int L, uint32_t rank, int passes, uint32_t& key, uint32_t& keep) {
-    uint32_t pre = 0u, rem = rank;
-#pragma unroll
-    for (int ps = 0; ps < 3; ++ps) {
-      if (ps == passes) break;                       // block-uniform
-      const uint32_t pmask = topk_prefix_mask(ps);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = 0u;
-      __syncthreads();
-      for (int i = tid; i < L; i += kTopkThreads) {
-        const uint32_t k = s_lkey[i];
-        if ((k & pmask) == pre) atomicAdd(&sh.hist[topk_digit(k, ps)], 1u);
-      }
-      __syncthreads();
-      topk_find_digit(sh, rem);
-      pre |= topk_place(sh.digit, ps);
-      rem = sh.remaining;
-    }
-    key = pre;
-    keep = rem;
+    topk_list_select(sh, s_lkey, L, rank, passes, key, keep);
   };
-  // The ordered emission from the list (it holds every key >= tau, in index order).
   auto emit_list = [&](int L, uint32_t tau, uint32_t need_eq) {
-    uint32_t gt_base = 0u, eq_base = 0u;
-    for (int b0 = 0; b0 < L; b0 += 4 * kTopkThreads) {
-      uint32_t kv[4];
-      bool valid[4];
-      int idx[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = b0 + 4 * tid + e;
-        valid[e] = i < L;
-        kv[e] = valid[e] ? s_lkey[i] : 0u;
-        idx[e] = valid[e] ? s_lidx[i] : 0;
-      }
-      topk_emit_tile(sh, kv, valid, idx, tau, need_eq, gt_base, eq_base, out);
-    }
+    topk_emit_list(sh, s_lkey, s_lidx, L, tau, need_eq, out);
   };
   // The second stream: keys >= thr into the list in index order (at most kTopkListCap are
   // stored); returns how many there are.
@@ -755,6 +771,156 @@ void topk_stream_kernel(TopkParams p) {
     for (int e = 0; e < 4; ++e) idx[e] = i0 + e;
     topk_emit_tile(sh, kv, valid, idx, prefix, remaining, gt_base, eq_base, out);
   }
+}
+
+// ---------------------------------------------------------------- sampled candidates
+// Per row, from the packed sample of every page_gap-th page (zeros = masked): the
+// threshold, the r-th largest sampled key to 24 bits with r chosen so that about 1.5 K +
+// 16 page_gap 64 of the row's keys are expected at or above it.  Rows where that cannot
+// work (r above the sample) are flagged for the exact path; rows with at most K visible
+// entries need no threshold.
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_thr_kernel(TopkParams p) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t s_lkey[kSamplePages * kPage];
+  __shared__ uint32_t s_cnt;
+  const int t = blockIdx.x;
+  const int n = p.n_vis[t];
+  const int tid = threadIdx.x;
+  if (n <= p.K) {
+    if (tid == 0) {
+      p.thr[t] = 0xffffffffu;
+      p.row_flags[t] = 0u;
+    }
+    return;
+  }
+  const int G = p.page_gap;
+  const int nsp = ((n + kPage - 1) / kPage + G - 1) / G;   // sampled pages with visible keys
+  const int ns = min(nsp, kSamplePages) * kPage;
+  if (tid == 0) s_cnt = 0u;
+  __syncthreads();
+  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
+  uint32_t c = 0u;
+  for (int i = tid; i < ns; i += kTopkThreads) {
+    const uint32_t k = keys[i];
+    s_lkey[i] = k;
+    c += (k != 0u);
+  }
+  c = wave_sum_u32(c);
+  if ((tid & 63) == 0) atomicAdd(&s_cnt, c);
+  __syncthreads();
+  const uint32_t nsv = s_cnt;                        // valid sampled keys
+  const uint32_t r = (uint32_t)((1.5 * (double)p.K * nsv) / n) + 16u;
+  if (r > nsv) {
+    if (tid == 0) {
+      p.thr[t] = 0u;
+      p.row_flags[t] = 1u;
+    }
+    return;
+  }
+  uint32_t thr, unused;
+  topk_list_select(sh, s_lkey, ns, r, 2, thr, unused);
+  (void)unused;
+  if (tid == 0) {
+    p.thr[t] = thr;
+    p.row_flags[t] = 0u;
+  }
+}
+
+// Per row: the exact Top-K among the candidates (every key >= the row's threshold, chunk
+// by chunk in entry order).  Rows flagged by the scoring (a chunk held more than kCandCap),
+// or whose candidates number fewer than K or more than kCandList, are flagged here and left
+// to the exact path.
+// Two workgroups per CU (LDS under 80 KB, at most 64 VGPRs): each row's chain of
+// block-wide steps hides behind another row's.
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_cand_kernel(TopkParams p) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t s_lkey[kCandList];
+  __shared__ int32_t s_lidx[kCandList];
+  __shared__ uint32_t s_off[kTopkThreads + 1];
+  const int t = blockIdx.x;
+  const int n = p.n_vis[t];
+  const int K = p.K;
+  int32_t* out = p.idx_out + (int64_t)t * K;
+  const int tid = threadIdx.x;
+  if (n <= K) {
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  if (p.row_flags[t]) return;
+  const int nch = (n + kGemmChunk - 1) / kGemmChunk;   // chunks holding visible entries
+  // chunk offsets in the list: an exclusive scan of the counts (nch <= kTopkThreads chunks
+  // per thread pass)
+  uint32_t base = 0u;
+  for (int c0 = 0; c0 < nch; c0 += kTopkThreads) {
+    const int c = c0 + tid;
+    const uint32_t v = c < nch ? p.cand_cnt[(int64_t)t * p.n_chunks + c] : 0u;
+    const uint32_t incl = wave_incl_scan(v);
+    if ((tid & 63) == 63) sh.wave_tot[tid >> 6] = incl;
+    __syncthreads();
+    uint32_t woff = 0u, tot = 0u;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const uint32_t x = sh.wave_tot[w];
+      woff += (w < (tid >> 6)) ? x : 0u;
+      tot += x;
+    }
+    s_off[tid] = base + woff + incl - v;
+    if (tid == kTopkThreads - 1) s_off[kTopkThreads] = base + tot;
+    __syncthreads();
+    // copy this pass's chunks into the list: list position i -> (chunk, slot) by a binary
+    // search over the offsets, so that every thread issues all of its loads at once
+    const uint32_t L_end = s_off[kTopkThreads];
+    if (L_end <= (uint32_t)kCandList) {
+      const int ncc = min(kTopkThreads, nch - c0);
+      constexpr int kPer = kCandList / kTopkThreads;
+      uint32_t kk[kPer];
+      int32_t ii[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const uint32_t i = s_off[0] + (uint32_t)(tid + u * kTopkThreads);
+        if (i < L_end) {
+          int lo = 0, hi = ncc - 1;                  // last chunk whose offset <= i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
+          }
+          const int64_t src = ((int64_t)t * p.n_chunks + c0 + lo) * kCandCap + (i - s_off[lo]);
+          kk[u] = p.cand_key[src];
+          ii[u] = p.cand_idx[src];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const uint32_t i = s_off[0] + (uint32_t)(tid + u * kTopkThreads);
+        if (i < L_end) {
+          s_lkey[i] = kk[u];
+          s_lidx[i] = ii[u];
+        }
+      }
+    }
+    base += tot;
+    __syncthreads();
+  }
+  const uint32_t L = base;
+  if (L < (uint32_t)K || L > (uint32_t)kCandList) {
+    if (tid == 0) p.row_flags[t] = 1u;
+    return;
+  }
+  uint32_t tau, need_eq;
+  topk_list_select(sh, s_lkey, (int)L, (uint32_t)K, 3, tau, need_eq);
+  topk_emit_list(sh, s_lkey, s_lidx, (int)L, tau, need_eq, out);
+}
+
+hipError_t launch_topk_thr(const TopkParams& p, hipStream_t s) {
+  CSA2_LAUNCH(topk_thr_kernel, dim3((unsigned)p.T), dim3(kTopkThreads), s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_cand(const TopkParams& p, hipStream_t s) {
+  CSA2_LAUNCH(topk_cand_kernel, dim3((unsigned)p.T), dim3(kTopkThreads), s, p);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- chunked Top-K
@@ -1020,8 +1186,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_ck_select_kernel(TopkParams
 // (pages past the end reload the last one), so one counter value names the page to wait
 // for.  Rows of a tile that belong to different sequences are scored in one pass per
 // sequence.
-constexpr int kGemmChunk = 2048;     // entries per workgroup
 constexpr int kGemmRing = 4;
+// 16-pair MFMA row blocks per wave: 4 (not 8) leaves registers for three waves per SIMD,
+// which hide each other's barrier and epilogue time (prefill scoring 1332 -> 1093 us)
+constexpr int kGemmBlocks = 4;
+constexpr int kGemmWavesPerSimd = 3;
 constexpr int kGemmPageBytes = kPage * kDidx * 2;
 
 // Barrier with this wave's LDS accesses complete and no wait on vector memory (the key
@@ -1037,10 +1206,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int HP>
-__global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
+// MODE (kGemmKeys, kGemmSample, kGemmCand): see IdxScoreParams.  A workgroup's chunk is 32
+// pages of the "page space": page space page q is logical page q * G of the sequence (G =
+// page_gap in sample mode, else 1), and its keys go to columns 64 q .. 64 q + 63.
+template <int HP, int MODE>
+__global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxScoreParams p) {
   constexpr int RB = 16 / HP;            // rows per 16-pair MFMA block
-  constexpr int NRB = 8;                 // blocks per wave
+  constexpr int NRB = kGemmBlocks;       // blocks per wave
   constexpr int RW = RB * NRB;           // rows per wave
   constexpr int RT = 4 * RW;             // rows per workgroup
   constexpr int S = RW / 4;              // stores per wave and page
@@ -1052,20 +1224,29 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_pg3[kGemmPageBytes];
   __shared__ __attribute__((aligned(16))) float s_out[2][4][RW][kPage];
   __shared__ int s_seq[RT], s_nv[RT];
+  __shared__ uint32_t s_thr[MODE == kGemmCand ? RT : 1];
+  __shared__ int s_any;
 
   for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
     p.clear[i] = 0u;
+  const int G = (MODE == kGemmSample) ? p.page_gap : 1;
   const int nrt = (p.T + RT - 1) / RT;
   const int rt = (int)blockIdx.x % nrt, ch = (int)blockIdx.x / nrt;   // an XCD's blocks share ch
-  const int t0 = rt * RT, c0 = ch * kGemmChunk;
+  const int t0 = rt * RT, q0 = ch * (kGemmChunk / kPage);            // first page-space page
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
+  const bool filtered = MODE == kGemmKeys && p.row_flags != nullptr;
+  if (tid == 0) s_any = 0;
+  __syncthreads();
   for (int i = tid; i < RT; i += 256) {
     const int t = t0 + i;
     s_seq[i] = t < p.T ? p.seq_id[t] : -1;
     s_nv[i] = t < p.T ? p.n_vis[t] : 0;
+    if (MODE == kGemmCand) s_thr[i] = t < p.T ? p.thr[t] : 0xffffffffu;
+    if (filtered && t < p.T && p.row_flags[t]) s_any = 1;
   }
   __syncthreads();
+  if (filtered && !s_any) return;                    // no row of this tile needs the keys
 
   const int rw0 = wave * RW;                         // first tile row of the wave
   int prev = -1;
@@ -1082,8 +1263,12 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
       if (s_seq[i] == cur) nvmax = max(nvmax, s_nv[i]);
     cur = __builtin_amdgcn_readfirstlane(cur);
     prev = cur;
-    const int np = __builtin_amdgcn_readfirstlane(
-        min((max(min(nvmax, c0 + kGemmChunk) - c0, 0) + kPage - 1) / kPage, kGemmChunk / kPage));
+    // page-space pages holding visible entries of some row of this sequence, in this chunk
+    const int vq = ((nvmax + kPage - 1) / kPage + G - 1) / G;
+    const int np = __builtin_amdgcn_readfirstlane(min(max(vq - q0, 0), kGemmChunk / kPage));
+    uint32_t cnt[S];                                   // kGemmCand: candidates so far, per row
+#pragma unroll
+    for (int r4 = 0; r4 < S; ++r4) cnt[r4] = 0u;
     if (np == 0) continue;
 
     // operands of this wave's rows (zero for rows of other sequences and padded heads)
@@ -1108,7 +1293,8 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
     uint32_t* const sink = p.trash + 4 * lane;
     // physical pages of the range, one per lane (read once: a load in the page loop would
     // count among the operations the loop waits for)
-    const int my_page = lane < np ? p.page_table[(int64_t)cur * p.max_pages + c0 / kPage + lane] : 0;
+    const int my_page =
+        lane < np ? p.page_table[(int64_t)cur * p.max_pages + (int64_t)(q0 + lane) * G] : 0;
     // DMA of page pp (clamped to the last page) into ring slot `dst`: wave w moves keys
     // 16w .. 16w+15 (two 1 KB units)
     auto dma_page = [&](int pp, uint8_t* dst) {
@@ -1124,7 +1310,8 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
     // this wave's rows of page pp's scores (LDS buffer pp & 1), 256 bytes per row; masked
     // lanes store to the sink
     auto store_page = [&](int pp) {
-      const int e0 = c0 + kPage * pp + 4 * n;
+      const int col = kPage * (q0 + pp) + 4 * n;       // key column of the lane's first entry
+      const int e0 = kPage * (q0 + pp) * G + 4 * n;    // its entry
 #pragma unroll
       for (int r4 = 0; r4 < S; ++r4) {
         const int rl = 4 * r4 + g;
@@ -1133,9 +1320,41 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
         u32x4 kk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) kk[e] = float_key(v[e]);
-        const bool ok = s_seq[r] == cur && e0 < s_nv[r];
-        uint32_t* dst = ok ? p.keys + (int64_t)(t0 + r) * p.key_stride + e0 : sink;
-        *reinterpret_cast<u32x4*>(dst) = kk;
+        const bool row_ok = s_seq[r] == cur;
+        if (MODE == kGemmKeys) {
+          const bool ok = row_ok && e0 < s_nv[r];
+          uint32_t* dst = ok ? p.keys + (int64_t)(t0 + r) * p.key_stride + col : sink;
+          *reinterpret_cast<u32x4*>(dst) = kk;
+        } else if (MODE == kGemmSample) {            // masked entries read as 0
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[e] = (e0 + e < s_nv[r]) ? kk[e] : 0u;
+          uint32_t* dst = row_ok ? p.keys + (int64_t)(t0 + r) * p.key_stride + col : sink;
+          *reinterpret_cast<u32x4*>(dst) = kk;
+        } else {
+          // keys at or above the row's threshold, appended in entry order: the 16 lanes of
+          // lane group g hold the row's 64 entries of the page, four each
+          const uint32_t th = s_thr[r];
+          uint32_t f = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f |= (uint32_t)(row_ok && e0 + e < s_nv[r] && kk[e] >= th) << e;
+          const uint32_t c = (uint32_t)__popc(f);
+          const uint32_t incl = row16_incl_scan(c);
+          const uint32_t tot = (uint32_t)__shfl((int)incl, 16 * g + 15);
+          if (f) {
+            uint32_t pos = cnt[r4] + incl - c;
+            const int64_t base = ((int64_t)(t0 + r) * p.n_chunks + ch) * kCandCap;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (((f >> e) & 1u) && pos < (uint32_t)kCandCap) {
+                p.cand_key[base + pos] = kk[e];
+                p.cand_idx[base + pos] = e0 + e;
+              }
+              pos += (f >> e) & 1u;
+            }
+          }
+          cnt[r4] += tot;
+        }
       }
     };
     // One page: the stores of page pp-1, page pp's operands from slot `kp`, the DMA of page
@@ -1195,21 +1414,40 @@ __global__ __launch_bounds__(256, 2) void idx_gemm_kernel(IdxScoreParams p) {
       page_step(pp + 3, s_pg3, s_pg2);
     }
     store_page(np - 1);
+    if (MODE == kGemmCand && n == 0) {               // the rows' counts for this chunk
+#pragma unroll
+      for (int r4 = 0; r4 < S; ++r4) {
+        const int r = rw0 + 4 * r4 + g;
+        if (s_seq[r] == cur) {
+          p.cand_cnt[(int64_t)(t0 + r) * p.n_chunks + ch] = cnt[r4];
+          if (cnt[r4] > (uint32_t)kCandCap) p.row_flags[t0 + r] = 1u;
+        }
+      }
+    }
     wait_vmem<0>();
     dma_barrier(s_pg0);                                // ring free for the next pass
   }
 }
 
+template <int MODE>
+hipError_t launch_idx_gemm(const IdxScoreParams& p, unsigned blocks, hipStream_t s) {
+  const int hp = p.H_I <= 4 ? 4 : (p.H_I <= 8 ? 8 : 16);
+  if (hp == 4) CSA2_LAUNCH((idx_gemm_kernel<4, MODE>), dim3(blocks), dim3(256), s, p);
+  else if (hp == 8) CSA2_LAUNCH((idx_gemm_kernel<8, MODE>), dim3(blocks), dim3(256), s, p);
+  else CSA2_LAUNCH((idx_gemm_kernel<16, MODE>), dim3(blocks), dim3(256), s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
   if (p.T >= kIdxGemmMinRows && !p.pool_sel) {
+    // page-space columns: key_stride (every page, or the packed sample)
     const int64_t nch = (p.key_stride + kGemmChunk - 1) / kGemmChunk;
     const int hp = p.H_I <= 4 ? 4 : (p.H_I <= 8 ? 8 : 16);
-    const int rt = 4 * 8 * (16 / hp);                 // rows per workgroup
+    const int rt = 4 * kGemmBlocks * (16 / hp);       // rows per workgroup
     const unsigned blocks = (unsigned)(((int64_t)p.T + rt - 1) / rt * nch);
-    if (hp == 4) CSA2_LAUNCH(idx_gemm_kernel<4>, dim3(blocks), dim3(256), s, p);
-    else if (hp == 8) CSA2_LAUNCH(idx_gemm_kernel<8>, dim3(blocks), dim3(256), s, p);
-    else CSA2_LAUNCH(idx_gemm_kernel<16>, dim3(blocks), dim3(256), s, p);
-    return hipGetLastError();
+    if (p.gemm_mode == kGemmSample) return launch_idx_gemm<kGemmSample>(p, blocks, s);
+    if (p.gemm_mode == kGemmCand) return launch_idx_gemm<kGemmCand>(p, blocks, s);
+    return launch_idx_gemm<kGemmKeys>(p, blocks, s);
   }
   const int64_t blocks = (int64_t)p.T * p.chunks;
   if (p.pool_sel) CSA2_LAUNCH(idx_pool_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);

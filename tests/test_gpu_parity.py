@@ -478,6 +478,86 @@ def test_index_topk_rowtiled_parity(csa2, dev, name):
     _index_parity(csa2, dev, GEMM[name], name)
 
 
+# Row-tiled rows of at least 16384 keys select through sampled candidates: a threshold per
+# row from the keys of every page_gap-th page, the scoring keeping only the keys at or above
+# it (at most 128 per 2048-entry chunk, in entry order), the exact Top-K on those.  Rows
+# where that fails (too few or too many candidates, a chunk over its cap, K close to the row
+# length) go through the exact path again; clustered hot entries overflow chunks.
+def _cand_nvis(T, E, K, seed):
+    rng = np.random.default_rng(seed)
+    nv = rng.integers(K // 2, E + 1, T)
+    nv[:10] = [0, 1, K, K + 1, K + 64, 2 * K, E - 1, E, 2048, 2049]
+    return nv.astype(np.int32)
+
+
+CAND = {
+    "cand_t300_b3_e20480_k512": W(B=3, T=300, E=20480, H=16, H_I=8, K=512, H_kv=16,
+                                  seq_id_rows=_gemm_rows(300, [120, 60, 120], 21),
+                                  n_vis_rows=_cand_nvis(300, 20480, 512, 22)),
+    "cand_t260_b1_e16384_hi4_runs": W(B=1, T=260, E=16384, H=16, H_I=4, K=1024, H_kv=16,
+                                      hot="runs", n_hot=2048, hot_runs=4,
+                                      seq_id_rows=np.zeros(260, np.int32),
+                                      n_vis_rows=_cand_nvis(260, 16384, 1024, 23)),
+    "cand_t256_b2_e33024_hi16_k2048": W(B=2, T=256, E=33024, H=16, H_I=16, K=2048, H_kv=16,
+                                        seq_id_rows=(np.arange(256) % 2).astype(np.int32),
+                                        n_vis_rows=_cand_nvis(256, 33024, 2048, 24)),
+}
+
+
+@pytest.mark.parametrize("name", list(CAND))
+def test_index_topk_candidates_parity(csa2, dev, name):
+    _index_parity(csa2, dev, CAND[name], name)
+
+
+def _cand_direct(csa2, dev, kf, qf, K, T):
+    E = kf.shape[0]
+    kb = synth.f32_to_bf16_bits(kf)
+    qb = synth.f32_to_bf16_bits(qf.reshape(T, 1, 64))
+    wv = np.ones((T, 1), np.float32)
+    pt = np.arange(E // 64, dtype=np.int32)[None]
+    sid = np.zeros(T, np.int32)
+    nv = np.full(T, E, np.int32)
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    ti = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    idx = csa2.index_topk(t16(qb), ti(wv), t16(kb).view(E // 64, 64, 64), ti(pt), ti(sid),
+                          ti(nv), K).cpu().numpy()
+    return idx, (qb, wv, kb, pt, sid, nv)
+
+
+def test_topk_candidates_all_equal_scores(csa2, dev):
+    """Every key equal: every row's candidates overflow, the exact path keeps the lowest
+    indices."""
+    _say("topk_candidates_all_equal_scores")
+    E, K, T = 16384, 300, 260
+    kf = np.tile(synth.normal_f32(9, 1, 0, 64), (E, 1))
+    qf = synth.normal_f32(9, 2, 0, T * 64)
+    idx, _ = _cand_direct(csa2, dev, kf, qf, K, T)
+    for r in range(T):
+        np.testing.assert_array_equal(idx[r], np.arange(K))
+
+
+@pytest.mark.parametrize("boost", ["sampled", "unsampled"])
+def test_topk_candidates_sample_misses(csa2, dev, boost):
+    """Rows whose sample misleads the threshold: the keys of the sampled pages (every
+    ceil(pages / 64)-th page: every fourth at 16384 keys) scaled x8, so fewer than K keys
+    reach it, or the other pages' keys scaled x8, so that chunks overflow.  Both go through
+    the exact path and match the oracle."""
+    _say("topk_candidates_sample_misses", boost)
+    E, K, T = 16384, 512, 258
+    page = np.arange(E) // 64
+    gap = -(-(E // 64) // 64)
+    in_sample = page % gap == 0
+    kf = np.abs(synth.normal_f32(12, 1, 0, E * 64)).reshape(E, 64)
+    kf[in_sample if boost == "sampled" else ~in_sample] *= 8.0
+    qf = np.abs(synth.normal_f32(12, 2, 0, T * 64))
+    idx, (qb, wv, kb, pt, sid, nv) = _cand_direct(csa2, dev, kf, qf, K, T)
+    rows = np.array([0, 1, 129, 257])
+    _, s_ref = orc.index_topk(K, E // 64, qb, wv, kb, pt, sid, nv, rows=rows, want_scores=True)
+    tl.check_topk(idx[rows], s_ref, K, nv, rows=rows)
+    assert np.all(np.diff(idx, axis=1) > 0)
+
+
 def _swa_windows(T, L, seed):
     rng = np.random.default_rng(seed)
     ln = rng.choice([0, 1, 17, 64, 128, 200], T)
