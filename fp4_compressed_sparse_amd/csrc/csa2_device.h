@@ -28,6 +28,19 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// max(x, 0) in one integer max on the bits (a negative float, -0 included, is a negative
+// int32).  fmaxf (and its equivalents) costs two v_max_f32 here: the compiler first
+// canonicalizes a value it cannot prove canonical, such as an MFMA result.  Differs from
+// fmaxf only for NaN with the sign bit clear, which stays NaN.
+__device__ __forceinline__ float relu_f32(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// The inverse of float_key: the float whose key is k (key 0x80000000 -> +0).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // E8M0 scale byte -> fp32 2^(b - 127) (byte 0 -> the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __uint_as_float(b ? (b << 23) : 0x00400000u);
@@ -95,6 +108,25 @@ __device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
   return v;
+}
+
+// Lane 15 of each 16-lane row, broadcast to the row (DPP row_newbcast:15).
+__device__ __forceinline__ uint32_t row16_last(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x15f, 0xf, 0xf, false);
+}
+
+// x + x of lane ^ 16 (lane ^ 32) without the LDS crossbar: v_permlane16_swap exchanges the
+// odd 16-lane rows of one operand with the even rows of the other, so swapping x with
+// itself leaves each lane x of its row and of the paired row.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // max(a - b, 0) for unsigned values, written without a comparison-guarded subtraction:

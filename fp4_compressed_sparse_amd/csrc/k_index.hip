@@ -61,10 +61,10 @@ __device__ __forceinline__ float idx_score_64(const u32x4& qa0, const u32x4& qa1
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa0), as_bf16x8(kb[2 * u]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa1), as_bf16x8(kb[2 * u + 1]), acc, 0, 0, 0);
-    float s = w[0] * fmaxf(acc[0], 0.f);
-    s += w[1] * fmaxf(acc[1], 0.f);
-    s += w[2] * fmaxf(acc[2], 0.f);
-    s += w[3] * fmaxf(acc[3], 0.f);
+    float s = w[0] * relu_f32(acc[0]);
+    s += w[1] * relu_f32(acc[1]);
+    s += w[2] * relu_f32(acc[2]);
+    s += w[3] * relu_f32(acc[3]);
     su[u] = s;
   }
   // lanes 0..31 (g = 0, 1) gather groups u = 0, 1 from g + 2; lanes 32..63 gather u = 2, 3
@@ -1224,7 +1224,7 @@ __global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxSco
   __shared__ __attribute__((aligned(16))) uint8_t s_pg3[kGemmPageBytes];
   __shared__ __attribute__((aligned(16))) float s_out[2][4][RW][kPage];
   __shared__ int s_seq[RT], s_nv[RT];
-  __shared__ uint32_t s_thr[MODE == kGemmCand ? RT : 1];
+  __shared__ float s_thr[MODE == kGemmCand ? RT : 1];   // thresholds as scores
   __shared__ int s_any;
 
   for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
@@ -1242,7 +1242,7 @@ __global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxSco
     const int t = t0 + i;
     s_seq[i] = t < p.T ? p.seq_id[t] : -1;
     s_nv[i] = t < p.T ? p.n_vis[t] : 0;
-    if (MODE == kGemmCand) s_thr[i] = t < p.T ? p.thr[t] : 0xffffffffu;
+    if (MODE == kGemmCand) s_thr[i] = t < p.T ? key_float(p.thr[t]) : INFINITY;
     if (filtered && t < p.T && p.row_flags[t]) s_any = 1;
   }
   __syncthreads();
@@ -1318,8 +1318,10 @@ __global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxSco
         const int r = rw0 + rl;
         const f32x4 v = *reinterpret_cast<const f32x4*>(&s_out[pp & 1][wave][rl][4 * n]);
         u32x4 kk;
+        if (MODE != kGemmCand) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kk[e] = float_key(v[e]);
+          for (int e = 0; e < 4; ++e) kk[e] = float_key(v[e]);
+        }
         const bool row_ok = s_seq[r] == cur;
         if (MODE == kGemmKeys) {
           const bool ok = row_ok && e0 < s_nv[r];
@@ -1333,24 +1335,28 @@ __global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxSco
         } else {
           // keys at or above the row's threshold, appended in entry order: the 16 lanes of
           // lane group g hold the row's 64 entries of the page, four each
-          const uint32_t th = s_thr[r];
+          // !(score < threshold score) is key >= threshold key (the key map is monotone,
+          // -0 and +0 share a key and compare equal, and a NaN score, whose key is above
+          // every finite one, passes)
+          const float th = s_thr[r];
           uint32_t f = 0u;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            f |= (uint32_t)(row_ok && e0 + e < s_nv[r] && kk[e] >= th) << e;
+            f |= (uint32_t)(row_ok && e0 + e < s_nv[r] && !(v[e] < th)) << e;
           const uint32_t c = (uint32_t)__popc(f);
           const uint32_t incl = row16_incl_scan(c);
-          const uint32_t tot = (uint32_t)__shfl((int)incl, 16 * g + 15);
-          if (f) {
-            uint32_t pos = cnt[r4] + incl - c;
+          const uint32_t tot = row16_last(incl);
+          if (__ballot(f != 0u)) {                   // a wave-uniform test: mostly taken
             const int64_t base = ((int64_t)(t0 + r) * p.n_chunks + ch) * kCandCap;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (((f >> e) & 1u) && pos < (uint32_t)kCandCap) {
-                p.cand_key[base + pos] = kk[e];
+            uint32_t pos = cnt[r4] + incl - c;
+            while (f) {                              // the lane's candidates, in order
+              const int e = __builtin_ctz(f);
+              if (pos < (uint32_t)kCandCap) {
+                p.cand_key[base + pos] = float_key(v[e]);
                 p.cand_idx[base + pos] = e0 + e;
               }
-              pos += (f >> e) & 1u;
+              ++pos;
+              f &= f - 1u;
             }
           }
           cnt[r4] += tot;
@@ -1387,12 +1393,12 @@ __global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxSco
                                                             acc[rb], 0, 0, 0);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          float sc = wv[rb][0] * fmaxf(acc[rb][0], 0.f);
-          sc += wv[rb][1] * fmaxf(acc[rb][1], 0.f);
-          sc += wv[rb][2] * fmaxf(acc[rb][2], 0.f);
-          sc += wv[rb][3] * fmaxf(acc[rb][3], 0.f);
-          if (HP >= 8) sc += __shfl_xor(sc, 16);
-          if (HP >= 16) sc += __shfl_xor(sc, 32);
+          float sc = wv[rb][0] * relu_f32(acc[rb][0]);
+          sc += wv[rb][1] * relu_f32(acc[rb][1]);
+          sc += wv[rb][2] * relu_f32(acc[rb][2]);
+          sc += wv[rb][3] * relu_f32(acc[rb][3]);
+          if (HP >= 8) sc = xor16_sum(sc);
+          if (HP >= 16) sc = xor32_sum(sc);
           // lanes holding the same row write the same value
           const int rl = RB * rb + (HP == 4 ? g : (HP == 8 ? (g >> 1) : 0));
           s_out[pp & 1][wave][rl][k] = sc;
