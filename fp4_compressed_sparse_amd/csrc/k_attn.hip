@@ -326,45 +326,53 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
       for (int bb = 0; bb < kNPre; ++bb) {           // bb & 1 = i & 1: static buffer parity
         const int i = i0 + bb;
         if (active) {
-          // ---- S^T[entries 16mb + 4g + k][head n]: eight independent chains
+          // ---- S^T[entries 16mb + 4g + k][head n]: four chains, one per entry block; the
+          // MFMAs are ordered so that a chain's consecutive MFMAs have three others between
           const uint8_t* raw = s_raw[i & (kRing - 1)];
-          f32x4 ah[4], al[4];
+          f32x4 acc[4];
           u32x4 ksc[4];                              // the 16 block scales of entry e
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) {
-            ah[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            al[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (FMT == 0) ksc[mb] = *reinterpret_cast<const u32x4*>(raw + kRawScl + epos[mb]);
           }
           // A scale: block 4kk + g = byte g of dword kk, shifted down (op_sel 0); B scale:
-          // op_sel = kk picks byte kk of qscp
+          // op_sel = kk picks byte kk of qscp.  The hi and lo query parts accumulate into
+          // the same chain.
 #define CSA2_QK_CHUNK(kk)                                                                     \
-  _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                        \
-    const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
-        raw + kRawLat + 1024 * (4 * (kk) + g) + epos[mb]);                                  \
-    const i32x8 ka = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};          \
-    const int asc = (int)(ksc[mb][kk] >> (8 * g));                                          \
-    ah[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qhi[kk], ah[mb], 4, 0, 0,  \
-                                                               asc, kk, qscp);              \
-    al[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qlo[kk], al[mb], 4, 0, 0,  \
-                                                               asc, kk, qscp);              \
+  {                                                                                         \
+    i32x8 ka[4];                                                                            \
+    int asc[4];                                                                             \
+    _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                      \
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                     \
+          raw + kRawLat + 1024 * (4 * (kk) + g) + epos[mb]);                                \
+      ka[mb] = i32x8{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};           \
+      asc[mb] = (int)(ksc[mb][kk] >> (8 * g));                                              \
+      acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[mb], qhi[kk], acc[mb], 4, \
+                                                                  0, 0, asc[mb], kk, qscp); \
+    }                                                                                       \
+    _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                        \
+      acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[mb], qlo[kk], acc[mb], 4, \
+                                                                  0, 0, asc[mb], kk, qscp); \
   }
           // FMT 1: the lane dequantizes its 8 codes of step j (dword j of the slot of block
-          // 4kk + g, E4M3 group 8kk + 2g + j/2) into fp16; fp16 MFMA; steps alternate
-          // between the two accumulators
+          // 4kk + g, E4M3 group 8kk + 2g + j/2) into fp16; fp16 MFMA, steps outermost
 #define CSA2_QK_E4M3(kk)                                                                      \
-  _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                        \
-    const u32x4 w4 = *reinterpret_cast<const u32x4*>(                                       \
-        raw + kRawLat + 1024 * (4 * (kk) + g) + epos[mb]);                                  \
-    const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(                                \
-        raw + kRawScl + 1024 * ((kk) >> 1) + epos[mb] + ((8 * (kk) + 2 * g) & 15));          \
-    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {                                      \
-      uint32_t kv[4];                                                                       \
-      fp4x8_e4m3_to_f16_pairs(w4[jj], (sc2 >> (8 * (jj >> 1))) & 0xffu, kv);                \
-      const f16x8 ka = __builtin_bit_cast(f16x8, u32x4{kv[0], kv[1], kv[2], kv[3]});        \
-      if (jj & 1) al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][jj], al[mb], 0, 0, 0); \
-      else ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][jj], ah[mb], 0, 0, 0); \
+  {                                                                                         \
+    u32x4 w4[4];                                                                            \
+    uint32_t sc2[4];                                                                        \
+    _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                      \
+      w4[mb] = *reinterpret_cast<const u32x4*>(raw + kRawLat + 1024 * (4 * (kk) + g) + epos[mb]); \
+      sc2[mb] = *reinterpret_cast<const uint16_t*>(                                         \
+          raw + kRawScl + 1024 * ((kk) >> 1) + epos[mb] + ((8 * (kk) + 2 * g) & 15));       \
     }                                                                                       \
+    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj)                                        \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                    \
+        uint32_t kv[4];                                                                     \
+        fp4x8_e4m3_to_f16_pairs(w4[mb][jj], (sc2[mb] >> (8 * (jj >> 1))) & 0xffu, kv);      \
+        const f16x8 ka = __builtin_bit_cast(f16x8, u32x4{kv[0], kv[1], kv[2], kv[3]});      \
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][jj], acc[mb], 0, 0, 0); \
+      }                                                                                     \
   }
           if (FMT == 0) {
             CSA2_QK_CHUNK(0)
@@ -386,28 +394,32 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
             for (int mb = 0; mb < 4; ++mb) {
               const u32x4 rv = *reinterpret_cast<const u32x4*>(
                   raw + kRawRope + 1024 * (4 * s2 + g) + epos[mb]);
-              if (s2 == 0) ah[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, ah[mb], 0, 0, 0);
-              else al[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, al[mb], 0, 0, 0);
+              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(rv), qr, acc[mb], 0, 0, 0);
             }
           }
-          // ---- online softmax; masked slots get -inf (exp2 -> 0)
+          // ---- online softmax; masked slots get -inf (exp2 -> 0).  A tile whose every slot
+          // holds an entry (all but a split's last, mostly) skips the masking.
           const uint64_t tm = s_tmask[i];
           float x[16];
-          bool raise_lane = false;
+          if (tm == ~0ull) {                         // wave-uniform
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            const uint32_t bits = (uint32_t)(tm >> (16 * mb + 4 * g));
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float v = ((bits >> k) & 1u) ? (ah[mb][k] + al[mb][k]) * sc_log2 : -INFINITY;
-              x[4 * mb + k] = v;
-              raise_lane |= v > m_run + kRaise;
+              for (int k = 0; k < 4; ++k) x[4 * mb + k] = acc[mb][k] * sc_log2;
+          } else {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const uint32_t bits = (uint32_t)(tm >> (16 * mb + 4 * g));
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                x[4 * mb + k] = ((bits >> k) & 1u) ? acc[mb][k] * sc_log2 : -INFINITY;
             }
           }
-          if (__ballot(raise_lane)) {                // rare after the first tile
-            float tmax = x[0];
+          float lmax = x[0];                         // this lane's maximum of the tile
 #pragma unroll
-            for (int k = 1; k < 16; ++k) tmax = fmaxf(tmax, x[k]);
+          for (int k = 1; k < 16; ++k) lmax = fmaxf(lmax, x[k]);
+          if (__ballot(lmax > m_run + kRaise)) {     // rare after the first tile
+            float tmax = lmax;
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             float alpha = 1.f;
