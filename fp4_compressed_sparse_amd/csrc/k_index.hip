@@ -10,8 +10,9 @@
 //
 // Top-K: the K largest scores, ties to the lowest index, emitted in ascending index
 // order, -1 padded.  Radix select over order-preserving u32 keys (digits of 12, 12 and
-// 8 bits) finds the K-th key tau and how many keys equal to tau to keep; an ordered
-// block-wide scan then compacts the selected indices in index order.  Rows of up to 64K
+// 8 bits, or a 16-bit first digit in a window under the row maximum) finds the K-th key
+// tau and how many keys equal to tau to keep; an ordered block-wide scan then compacts
+// the selected indices in index order.  Rows of up to 64K
 // entries are read once into registers; few longer rows spread over many workgroups in
 // 4096-key chunks; many longer rows are streamed, one workgroup each, through a list of
 // candidates above a sampled threshold.
@@ -19,6 +20,8 @@
 // Pooled search (hierarchical indexer, [summary] item 3): the same scoring over the
 // aligned 8-entry blocks that hold a Full layer's selection, then the register Top-K over
 // those slots.
+#include <type_traits>
+
 #include "csa2_internal.h"
 #include "csa2_device.h"
 
@@ -342,9 +345,12 @@ __device__ __forceinline__ uint32_t wave_prefix_small(uint32_t v, uint32_t& tota
   return pre;
 }
 
+constexpr uint32_t kNoDigit = 0xffffffffu;
+
 // Wave 0 locates the digit holding the `remaining`-th key (from the top) in a 4096-bin
 // histogram: lane l first sums bins 64l .. 64l+63, a suffix scan over lanes picks the
 // lane whose range holds the rank, then the wave scans that lane's 64 bins in parallel.
+// A histogram of fewer than `remaining` keys yields kNoDigit.
 __device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_t remaining,
                                                    uint32_t* s_digit, uint32_t* s_rem) {
   const int lane = threadIdx.x & 63;
@@ -358,6 +364,10 @@ __device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_
   // suffix sums: keys in lanes >= l
   const uint32_t incl = wave_incl_scan(tot);
   const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if (all < remaining) {                                       // wave-uniform
+    if (lane == 0) *s_digit = kNoDigit;
+    return;
+  }
   const uint32_t suf = all - incl + tot;
   const uint32_t above = suf - tot;
   const uint64_t hit = __ballot(above < remaining && suf >= remaining);
@@ -375,30 +385,24 @@ __device__ __forceinline__ void topk_find_digit_w0(const uint32_t* hist, uint32_
   }
 }
 
-// Rows of at most 4096 * NR keys: thread t keeps keys [4NR t, 4NR (t+1)) in registers,
-// so the row is read from memory once and one block-wide scan orders the output.
-// POOL: the row is the 8 * pool_K key slots of the pooled scoring (0 = no candidate); when
-// at most K slots hold a candidate all of them are taken, and slots map back to entries.
-template <int NR, bool POOL>
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
+// Pooled rows: the row is the 8 * pool_K key slots of the pooled scoring (0 = no
+// candidate), at most 4096 * NR of them.  Thread t keeps slots [4NR t, 4NR (t+1)) in
+// registers, so the row is read from memory once and one block-wide scan orders the
+// output.  When at most K slots hold a candidate all of them are taken; slots map back to
+// entries.
+template <int NR>
+__global__ __launch_bounds__(kTopkThreads) void topk_pool_kernel(TopkParams p) {
   constexpr int KPT = 4 * NR;                        // keys per thread
   __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
   __shared__ uint32_t s_digit, s_rem;
   __shared__ uint32_t s_wtot[kTopkWaves];
   const int t = blockIdx.x;
-  if (!POOL && p.row_flags && !p.row_flags[t]) return;   // selected on the candidate path
-  const int n = POOL ? kPoolBlock * p.pool_K : p.n_vis[t];
+  const int n = kPoolBlock * p.pool_K;
   const int K = p.K;
   int32_t* out = p.idx_out + (int64_t)t * K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (!POOL && n <= K) {              // every visible entry is selected
-    for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
-    return;
-  }
-  const int32_t* psel = POOL ? p.pool_sel + (int64_t)t * p.pool_K : nullptr;
-  auto entry_of = [&](int slot) {
-    return POOL ? kPoolBlock * (psel[slot >> 3] >> 3) + (slot & 7) : slot;
-  };
+  const int32_t* psel = p.pool_sel + (int64_t)t * p.pool_K;
+  auto entry_of = [&](int slot) { return kPoolBlock * (psel[slot >> 3] >> 3) + (slot & 7); };
   // keys below n are >= float_key(-inf) > 0; 0 marks the slots past n
   const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
   const int i0 = KPT * tid;
@@ -438,16 +442,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
   }
   uint32_t ctot, nzt = 0u;
   (void)wave_prefix_small<7>(ctop, ctot);
-  if (POOL) (void)wave_prefix_small<7>(cnz, nzt);
+  (void)wave_prefix_small<7>(cnz, nzt);
   __syncthreads();                                   // everyone has read the maxima
   if (lane == 0) s_wtot[wave] = ctot | (nzt << 16);  // each part <= 64 * 64
   __syncthreads();
   uint32_t wsum = 0u;
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) wsum += s_wtot[w];
-  const uint32_t n_cand = POOL ? (wsum >> 16) : 0u;  // POOL: slots holding a candidate
-  ctop = POOL ? (wsum & 0xffffu) : wsum;             // (POOL rows hold <= 16384 slots)
-  const bool take_all = POOL && n_cand <= (uint32_t)K;
+  const uint32_t n_cand = wsum >> 16;                // slots holding a candidate
+  ctop = wsum & 0xffffu;                             // (rows hold <= 16384 slots)
+  const bool take_all = n_cand <= (uint32_t)K;
   const bool narrow = ctop >= (uint32_t)K;
   // take_all: tau = 0 with no ties to keep selects every candidate
   uint32_t prefix = (narrow && !take_all) ? (kmax & 0xf0000000u) : 0u;
@@ -520,6 +524,285 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkParams p) {
       sel &= sel - 1;
     }
     for (int i = n_out + tid; i < K; i += kTopkThreads) out[i] = -1;
+  }
+}
+
+// Maximum over the wave by DPP (row steps, then the row carries, as in wave_incl_scan).
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Exclusive prefix over the wave's lanes, and the wave total, of NG per-lane counts of at
+// most 4 each: three counts share one DPP scan in 10-bit fields (a field's total is at
+// most 256, so no carry crosses into the next).
+template <int NG>
+__device__ __forceinline__ void wave_group_prefix(const uint32_t (&c)[NG], uint32_t (&pre)[NG],
+                                                  uint32_t (&tot)[NG]) {
+#pragma unroll
+  for (int f = 0; f < NG; f += 3) {
+    uint32_t pk = 0u;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (f + j < NG) pk |= c[f + j] << (10 * j);
+    const uint32_t incl = wave_incl_scan(pk);
+    const uint32_t ex = incl - pk;
+    const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (f + j < NG) {
+        pre[f + j] = (ex >> (10 * j)) & 0x3ffu;
+        tot[f + j] = (all >> (10 * j)) & 0x3ffu;
+      }
+  }
+}
+
+// One digit pass over register-resident keys: keys whose bits above the digit equal
+// `prefix` are counted into h; the other buffer is cleared for the pass after.
+template <int KPT>
+__device__ __forceinline__ void topk_reg_pass(const uint32_t (&kv)[KPT], uint32_t* h,
+                                              uint32_t* h_next, int shift, int width,
+                                              uint32_t& prefix, uint32_t& remaining,
+                                              uint32_t* s_digit, uint32_t* s_rem) {
+  const int tid = threadIdx.x;
+  const uint32_t pmask = ~((2u << (shift + width - 1)) - 1u);   // bits above the digit
+  const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e)
+    if ((kv[e] & pmask) == prefix) atomicAdd(&h[(kv[e] >> shift) & dmask], 1u);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h_next[4 * tid + e] = 0u;
+  __syncthreads();
+  if (tid < 64) topk_find_digit_w0(h, remaining, s_digit, s_rem);
+  __syncthreads();
+  prefix |= *s_digit << shift;
+  remaining = *s_rem;
+}
+
+// Keys of the boundary bin after the first digit, gathered for the last two digits.
+constexpr int kRowList = 4096;
+
+// Rows of at most 4096 * NR keys, one workgroup per row, the row read once into registers.
+// Wave w holds keys [KPW w, KPW (w + 1)); its lane l holds the 4-key groups starting at
+// KPW w + 256 r + 4 l (r < NR), so every load instruction reads 1 KB of consecutive keys.
+// Digits: the first is bits 31..16 of the keys whose top 16 bits lie within 4095 of the
+// row maximum's (for float scores, about 32 octaves below the maximum, in bins of 1/128
+// octave).  When at least K keys fall in that window (the usual case) the K-th key is
+// among them; the keys of its bin are gathered into an LDS list, where one wave finds bits
+// 15..4 and 3..0.  Otherwise (or when the bin overflows the list) the remaining digits are
+// passes over the registers: bits 31..20, 19..8, 7..0, or 15..4, 3..0.
+// Slots past n_vis hold key 0, below every visible key (>= float_key(-inf) > 0); they can
+// only be counted when the maximum is within the window of 0, and there are always K
+// larger keys.
+template <int NR>
+__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
+  constexpr int KPT = 4 * NR;                        // keys per thread
+  constexpr int KPW = 64 * KPT;                      // keys per wave
+  typedef typename std::conditional<(KPT <= 32), uint32_t, uint64_t>::type Mask;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
+  __shared__ uint32_t s_list[kRowList];
+  __shared__ uint32_t s_digit, s_rem, s_cnt;
+  __shared__ uint32_t s_wtot[kTopkWaves];
+  const int t = blockIdx.x;
+  if (p.row_flags && !p.row_flags[t]) return;        // selected on the candidate path
+  const int n = p.n_vis[t];
+  const int K = p.K;
+  int32_t* out = p.idx_out + (int64_t)t * K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n <= K) {                                      // every visible entry is selected
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  const int wbase = KPW * wave;
+  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride + wbase + 4 * lane;
+  uint32_t kv[KPT];
+  if (wbase + KPW <= n) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(keys + 256 * r);
+      kv[4 * r] = v[0]; kv[4 * r + 1] = v[1]; kv[4 * r + 2] = v[2]; kv[4 * r + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        kv[4 * r + e] = (wbase + 256 * r + 4 * lane + e < n) ? keys[256 * r + e] : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hist[0][4 * tid + e] = 0u;
+    hist[1][4 * tid + e] = 0u;
+  }
+  if (tid == 0) s_cnt = 0u;
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) kmax = max(kmax, kv[e]);
+  kmax = wave_max_u32_dpp(kmax);
+  if (lane == 0) s_wtot[wave] = kmax;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) kmax = max(kmax, s_wtot[w]);
+
+  // first digit: bits 31..16 of the keys within 4095 below those of the maximum
+  const int lo = (int)(kmax >> 16) - (kHistBins - 1);
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const int b = (int)(kv[e] >> 16) - lo;
+    if (b >= 0) atomicAdd(&hist[0][b], 1u);
+  }
+  __syncthreads();
+  if (wave == 0) topk_find_digit_w0(hist[0], (uint32_t)K, &s_digit, &s_rem);
+  __syncthreads();
+  uint32_t prefix, remaining;
+  const uint32_t d0 = s_digit;
+  if (d0 == kNoDigit) {                              // block-uniform; hist[1] is clear
+    prefix = 0u;
+    remaining = (uint32_t)K;
+    topk_reg_pass(kv, hist[1], hist[0], 20, 12, prefix, remaining, &s_digit, &s_rem);
+    topk_reg_pass(kv, hist[0], hist[1], 8, 12, prefix, remaining, &s_digit, &s_rem);
+    topk_reg_pass(kv, hist[1], hist[0], 0, 8, prefix, remaining, &s_digit, &s_rem);
+  } else {
+    prefix = (uint32_t)(lo + (int)d0) << 16;
+    remaining = s_rem;
+    // gather the bin's keys (any order) into the list
+    Mask bm = 0u;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) bm |= (Mask)((kv[e] & 0xffff0000u) == prefix) << e;
+    const uint32_t c = (uint32_t)__builtin_popcountll((uint64_t)bm);
+    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t wt = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    uint32_t base = 0u;
+    if (lane == 0 && wt != 0u) base = atomicAdd(&s_cnt, wt);
+    uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + incl - c;
+    if (bm) {
+#pragma unroll
+      for (int e = 0; e < KPT; ++e)
+        if ((bm >> e) & 1u) {
+          if (at < (uint32_t)kRowList) s_list[at] = kv[e];
+          ++at;
+        }
+    }
+    __syncthreads();
+    const uint32_t L = s_cnt;
+    if (L > (uint32_t)kRowList) {                    // block-uniform; hist[1] is clear
+      topk_reg_pass(kv, hist[1], hist[0], 4, 12, prefix, remaining, &s_digit, &s_rem);
+      topk_reg_pass(kv, hist[0], hist[1], 0, 4, prefix, remaining, &s_digit, &s_rem);
+    } else {
+      if (wave == 0) {
+        // bits 15..4 over the list (hist[1] is clear)
+        for (uint32_t i = (uint32_t)lane; i < L; i += 64u)
+          atomicAdd(&hist[1][(s_list[i] >> 4) & 0xfffu], 1u);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        topk_find_digit_w0(hist[1], remaining, &s_digit, &s_rem);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        prefix |= s_digit << 4;
+        remaining = s_rem;
+        // bits 3..0: 16 bins, bin 15 - l read by lane l
+        if (lane < 16) hist[0][lane] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        for (uint32_t i = (uint32_t)lane; i < L; i += 64u) {
+          const uint32_t k = s_list[i];
+          if ((k & 0xfffffff0u) == prefix) atomicAdd(&hist[0][k & 0xfu], 1u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const uint32_t cb = lane < 16 ? hist[0][15 - lane] : 0u;
+        const uint32_t inc2 = wave_incl_scan(cb);   // keys in this bin and those above
+        const uint64_t hit = __ballot(lane < 16 && inc2 - cb < remaining && inc2 >= remaining);
+        const int l2 = (int)__builtin_ctzll(hit);
+        if (lane == l2) {
+          s_digit = prefix | (uint32_t)(15 - l2);
+          s_rem = remaining - (inc2 - cb);
+        }
+      }
+      __syncthreads();
+      prefix = s_digit;
+      remaining = s_rem;
+    }
+  }
+  const uint32_t tau = prefix, need_eq = remaining;
+
+  // ---- ordered compaction.  Entry order is (wave, group r, lane, key in group): wave
+  // offsets come from per-wave totals, the rest from per-group prefixes over the lanes.
+  Mask gtm = 0u, eqm = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    gtm |= (Mask)(kv[e] > tau) << e;
+    eqm |= (Mask)(kv[e] == tau) << e;
+  }
+  const uint32_t cg = (uint32_t)__builtin_popcountll((uint64_t)gtm);
+  const uint32_t ce = (uint32_t)__builtin_popcountll((uint64_t)eqm);
+  const uint32_t both = wave_incl_scan(cg | (ce << 16));   // each part <= 64 * KPT <= 4096
+  if (lane == 63) s_wtot[wave] = both;
+  __syncthreads();
+  uint32_t off_g = 0u, off_e = 0u, all_e = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t v = s_wtot[w];
+    if (w < wave) {
+      off_g += v & 0xffffu;
+      off_e += v >> 16;
+    }
+    all_e += v >> 16;
+  }
+  Mask sel = gtm;
+  if (all_e == need_eq) {                            // every key at tau is kept (usual)
+    sel |= eqm;
+  } else {                                           // the first need_eq keys at tau
+    uint32_t c[NR], pre[NR], tot[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) c[r] = (uint32_t)__builtin_popcount((uint32_t)(eqm >> (4 * r)) & 0xfu);
+    wave_group_prefix<NR>(c, pre, tot);
+    uint32_t acc = off_e;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      uint32_t rk = acc + pre[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((eqm >> (4 * r + e)) & 1u) {
+          if (rk < need_eq) sel |= (Mask)1 << (4 * r + e);
+          ++rk;
+        }
+      acc += tot[r];
+    }
+  }
+  uint32_t c[NR], pre[NR], tot[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) c[r] = (uint32_t)__builtin_popcount((uint32_t)(sel >> (4 * r)) & 0xfu);
+  wave_group_prefix<NR>(c, pre, tot);
+  uint32_t acc = off_g + min(off_e, need_eq);        // keys selected in the waves before
+  // Stage the ordered output in the (now free) histogram space when it fits, so that the
+  // row goes out in coalesced stores; else write it in place.
+  if (K <= 2 * kHistBins) {
+    int32_t* s_out = reinterpret_cast<int32_t*>(&hist[0][0]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      uint32_t at = acc + pre[r];
+      uint32_t nib = (uint32_t)(sel >> (4 * r)) & 0xfu;
+      while (nib) {
+        s_out[at++] = wbase + 256 * r + 4 * lane + (int)__builtin_ctz(nib);
+        nib &= nib - 1u;
+      }
+      acc += tot[r];
+    }
+    __syncthreads();
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = s_out[i];
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      uint32_t at = acc + pre[r];
+      uint32_t nib = (uint32_t)(sel >> (4 * r)) & 0xfu;
+      while (nib) {
+        out[at++] = wbase + 256 * r + 4 * lane + (int)__builtin_ctz(nib);
+        nib &= nib - 1u;
+      }
+      acc += tot[r];
+    }
   }
 }
 
@@ -1479,18 +1762,18 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   const dim3 grid((unsigned)p.T), block(kTopkThreads);
   if (p.pool_sel) {                                  // at most 8 * kPoolMaxSel slots
     const int slots = kPoolBlock * p.pool_K;
-    if (slots <= 4 * kTopkThreads) CSA2_LAUNCH((topk_reg_kernel<1, true>), grid, block, s, p);
-    else if (slots <= 8 * kTopkThreads) CSA2_LAUNCH((topk_reg_kernel<2, true>), grid, block, s, p);
-    else if (slots <= 16 * kTopkThreads) CSA2_LAUNCH((topk_reg_kernel<4, true>), grid, block, s, p);
+    if (slots <= 4 * kTopkThreads) CSA2_LAUNCH((topk_pool_kernel<1>), grid, block, s, p);
+    else if (slots <= 8 * kTopkThreads) CSA2_LAUNCH((topk_pool_kernel<2>), grid, block, s, p);
+    else if (slots <= 16 * kTopkThreads) CSA2_LAUNCH((topk_pool_kernel<4>), grid, block, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
   // key_stride bounds every row's n_vis; pick the register-resident variant that holds it
   const int64_t nr = (p.key_stride + 4 * kTopkThreads - 1) / (4 * kTopkThreads);
-  if (nr <= 2) CSA2_LAUNCH((topk_reg_kernel<2, false>), grid, block, s, p);
-  else if (nr <= 4) CSA2_LAUNCH((topk_reg_kernel<4, false>), grid, block, s, p);
-  else if (nr <= 8) CSA2_LAUNCH((topk_reg_kernel<8, false>), grid, block, s, p);
-  else if (nr <= 16) CSA2_LAUNCH((topk_reg_kernel<16, false>), grid, block, s, p);
+  if (nr <= 2) CSA2_LAUNCH((topk_row_kernel<2>), grid, block, s, p);
+  else if (nr <= 4) CSA2_LAUNCH((topk_row_kernel<4>), grid, block, s, p);
+  else if (nr <= 8) CSA2_LAUNCH((topk_row_kernel<8>), grid, block, s, p);
+  else if (nr <= 16) CSA2_LAUNCH((topk_row_kernel<16>), grid, block, s, p);
   else if (!topk_chunked(p.T, p.key_stride)) CSA2_LAUNCH(topk_stream_kernel, grid, block, s, p);
   else return hipErrorInvalidValue;                  // chunked rows go through launch_topk_chunked
   return hipGetLastError();

@@ -425,6 +425,52 @@ def test_topk_all_equal_scores(csa2, dev):
     np.testing.assert_array_equal(idx[1], np.arange(K))
 
 
+def _bf16_bits(x):
+    """float32 -> bf16 bit patterns by truncation (both sides then see the same values)."""
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_topk_row_paths(csa2, dev):
+    """The one-workgroup-per-row Top-K (rows of up to 64K keys) on exact scores (one head,
+    a unit query, keys whose first channel carries the score) that steer each of its
+    paths, compared with the oracle index for index: fewer than K keys within 32 octaves
+    of the row maximum (digit passes from bit 31), one bin larger than the LDS list
+    (digit passes over registers), ties at the K-th key inside the list, negative scores,
+    a row ending inside the last wave's keys, and a row that selects everything."""
+    _say("topk_row_paths")
+    rng = np.random.default_rng(2024)
+    P, K = 512, 2048
+    E = 64 * P
+    rows = []
+    v = (1.0 + rng.integers(0, 128, E) / 128.0).astype(np.float32)
+    v[rng.choice(E, 1000, replace=False)] = np.float32(2.0 ** 40)
+    rows.append((v, 1.0, E))
+    rows.append((np.full(E, 1.5, np.float32), 1.0, E))
+    rows.append((np.float32(1.0) + rng.integers(0, 16, E).astype(np.float32) / np.float32(16), 1.0, E))
+    rows.append((np.abs(rng.standard_normal(E)).astype(np.float32) + np.float32(0.01), -1.0, E))
+    rows.append((rng.standard_normal(E).astype(np.float32), 1.0, 20001))
+    rows.append((rng.standard_normal(E).astype(np.float32), 1.0, 1500))
+    T = len(rows)
+    k_bits = np.zeros((T * E, 64), np.uint16)
+    for b, (vals, _, _) in enumerate(rows):
+        k_bits[b * E:(b + 1) * E, 0] = _bf16_bits(vals)
+    q_bits = np.zeros((T, 1, 64), np.uint16)
+    q_bits[:, 0, 0] = _bf16_bits(1.0)
+    w = np.array([[r[1]] for r in rows], np.float32)
+    pt = (np.arange(T, dtype=np.int32)[:, None] * P + np.arange(P, dtype=np.int32)).astype(np.int32)
+    sid = np.arange(T, dtype=np.int32)
+    nv = np.array([r[2] for r in rows], np.int32)
+    ref = orc.index_topk(K, P, q_bits, w, k_bits, pt, sid, nv)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = csa2.index_topk(bf(q_bits), torch.from_numpy(w).to(dev),
+                          bf(k_bits).view(T * P, 64, 64), torch.from_numpy(pt).to(dev),
+                          torch.from_numpy(sid).to(dev), torch.from_numpy(nv).to(dev), K)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for t in range(T):
+        np.testing.assert_array_equal(got[t], ref[t], err_msg=f"row {t}")
+
+
 # Rows longer than 65536 keys, few of them: the chunked Top-K (4096-key chunks, one
 # workgroup each), with a ragged last chunk, chunks past a short row's end and a row that
 # selects everything.
