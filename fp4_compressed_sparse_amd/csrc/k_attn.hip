@@ -177,66 +177,44 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
   // barriers in the same order.
   const bool scorer_role = wave < 4;
 
-  // ---- the score waves' query loads
+  // ---- the score waves' query loads and conversion, and the value waves' row table.  The
+  // query work overlaps the value waves' index loads.  When the sequence's page table fits
+  // a raw tile slot (not written before the first loads below), the value waves fetch it
+  // together with the indices: one memory round trip instead of two dependent ones.
   const int hb = min(wave, NHB - 1);
-  const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
-  u32x4 qraw[4][2][2], qrope0, qrope1;
-  if (scorer_role && FMT == 1) {
-    // FMT 1: per 128-channel chunk kk and step j, B lane (g, n) carries query channels
-    // 32(4kk + g) + 8j .. +7, the channels A lane (g, n) dequantizes from the 16-byte code
-    // slot of block 4kk + g (dword j)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        qraw[kk][j >> 1][j & 1] = ld_global_16(qp + 32 * (4 * kk + g) + 8 * j);
-    qrope0 = ld_global_16(qp + kLat + 8 * g);
-    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
-  } else if (scorer_role) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
-#pragma unroll
-      for (int run = 0; run < 2; ++run) {
-        qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
-        qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
-      }
-    }
-    qrope0 = ld_global_16(qp + kLat + 8 * g);
-    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
-  } else {
-    // ---- value waves: resolve the split's physical rows (-1 = empty slot), all index
-    //      loads first, then all page-table loads; one validity bit per entry of a tile
-    const int b = p.seq_id[t];
-    const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-    const int32_t* idx = p.idx + (int64_t)t * p.K + k0;
-    const int tv = tid - 256;
-    constexpr int kPer = kMaxPerSplit / (64 * NV);   // slots per value thread
-    int j[kPer], row[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = tv + 64 * NV * r;
-      j[r] = (i < nslots) ? idx[i] : -1;
-    }
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) row[r] = (j[r] >= 0) ? pt[j[r] >> 6] * kPage + (j[r] & 63) : -1;
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = tv + 64 * NV * r;                // tile i / 64 = wave - 4 + 8r
-      if (i < ntiles2 * kTE) {
-        s_rows[i] = row[r];
-        const uint64_t bal = __ballot(row[r] >= 0);
-        if (lane == 0) s_tmask[i >> 6] = bal;
-      }
-    }
-    if (tid == 256) s_flag[0] = s_flag[1] = s_flag[2] = 0u;
-  }
-  __syncthreads();                                   // s_rows ready
-
-  const float sc_log2 = p.sm_scale_log2;
+  constexpr int kPtPer = 8;                          // page-table entries per value thread
+  const bool pt_lds = p.max_pages <= kPtPer * 64 * NV;   // block-uniform; <= 16 KB
+  i32x8 qhi[4], qlo[4];
+  int qscp = 0;                                      // byte kk: E8M0 scale of block 4kk + g
+  f16x8 qf[4][4];                                    // FMT 1: the query in fp16
+  u32x4 qrope0, qrope1;
+  constexpr int kPer = kMaxPerSplit / (64 * NV);     // slots per value thread
+  int jsl[kPer];
   if (scorer_role) {
-    // ======================================================== score waves
-    const bool active = wave < NHB;                  // score wave of heads 16hb..16hb+15
+    const uint16_t* qp = p.q + ((int64_t)t * p.H + h0 + 16 * hb + n) * kDq;
+    u32x4 qraw[4][2][2];
+    if (FMT == 1) {
+      // FMT 1: per 128-channel chunk kk and step j, B lane (g, n) carries query channels
+      // 32(4kk + g) + 8j .. +7, the channels A lane (g, n) dequantizes from the 16-byte code
+      // slot of block 4kk + g (dword j)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qraw[kk][j >> 1][j & 1] = ld_global_16(qp + 32 * (4 * kk + g) + 8 * j);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int c0 = 32 * (4 * kk + (g >> 1)) + 16 * (g & 1);
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+          qraw[kk][run][0] = ld_global_16(qp + c0 + 64 * run);
+          qraw[kk][run][1] = ld_global_16(qp + c0 + 64 * run + 8);
+        }
+      }
+    }
+    qrope0 = ld_global_16(qp + kLat + 8 * g);
+    qrope1 = ld_global_16(qp + kLat + 32 + 8 * g);
     // Query operands, per 128-channel chunk kk: the scaled MFMA pairs A lane group gA (one
     // 32-channel block 4kk + gA of an entry) with B lane group 2(gA&1) + (p >= 16), byte
     // p%16 + 16(gA>>1).  So B lane (g, n) carries channels 32(4kk + g/2) + 16(g&1) + [0,16)
@@ -244,9 +222,6 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
     // the E8M0 scale of block 4kk + g.  Each block is scaled by 2^X, X = floor(log2
     // max|q|) - 7, and split as hi = fp8(q 2^-X), lo = fp8(q 2^-X - hi): exact for every
     // bf16 value within 2^9 of the block maximum, and within 2^-16 of it below that.
-    i32x8 qhi[4], qlo[4];
-    int qscp = 0;                                    // byte kk: E8M0 scale of block 4kk + g
-    f16x8 qf[4][4];                                  // FMT 1: the query in fp16
     if (FMT == 1) {
       // bf16 -> fp16, to nearest: exact for magnitudes in [2^-14, 65504]
 #pragma unroll
@@ -312,6 +287,59 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
         }
       }
     }
+  } else {
+    // ---- value waves: the split's indices (and the page table when it fits)
+    const int b = p.seq_id[t];
+    const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+    const int32_t* idx = p.idx + (int64_t)t * p.K + k0;
+    const int tv = tid - 256;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tv + 64 * NV * r;
+      jsl[r] = (i < nslots) ? idx[i] : -1;
+    }
+    if (pt_lds) {                                    // all loads in flight at once
+      int32_t* s_pt = reinterpret_cast<int32_t*>(&s_raw[kRing - 1][0]);
+      int v[kPtPer];
+#pragma unroll
+      for (int u = 0; u < kPtPer; ++u) v[u] = (tv + 64 * NV * u < p.max_pages) ? pt[tv + 64 * NV * u] : 0;
+#pragma unroll
+      for (int u = 0; u < kPtPer; ++u)
+        if (tv + 64 * NV * u < p.max_pages) s_pt[tv + 64 * NV * u] = v[u];
+    }
+  }
+  if (pt_lds) __syncthreads();                       // page table in LDS
+  if (!scorer_role) {
+    // ---- value waves: resolve the split's physical rows (-1 = empty slot); one validity
+    //      bit per entry of a tile
+    const int tv = tid - 256;
+    int row[kPer];
+    if (pt_lds) {
+      const int32_t* s_pt = reinterpret_cast<const int32_t*>(&s_raw[kRing - 1][0]);
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) row[r] = (jsl[r] >= 0) ? s_pt[jsl[r] >> 6] * kPage + (jsl[r] & 63) : -1;
+    } else {
+      const int32_t* pt = p.page_table + (int64_t)p.seq_id[t] * p.max_pages;
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) row[r] = (jsl[r] >= 0) ? pt[jsl[r] >> 6] * kPage + (jsl[r] & 63) : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tv + 64 * NV * r;                // tile i / 64 = wave - 4 + 8r
+      if (i < ntiles2 * kTE) {
+        s_rows[i] = row[r];
+        const uint64_t bal = __ballot(row[r] >= 0);
+        if (lane == 0) s_tmask[i >> 6] = bal;
+      }
+    }
+    if (tid == 256) s_flag[0] = s_flag[1] = s_flag[2] = 0u;
+  }
+  __syncthreads();                                   // s_rows ready
+
+  const float sc_log2 = p.sm_scale_log2;
+  if (scorer_role) {
+    // ======================================================== score waves
+    const bool active = wave < NHB;                  // score wave of heads 16hb..16hb+15
     // this lane's entry positions in the staged columns: entry 16mb + n
     int epos[4];
 #pragma unroll
