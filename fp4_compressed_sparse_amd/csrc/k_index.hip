@@ -596,6 +596,10 @@ constexpr int kRowList = 4096;
 // among them; the keys of its bin are gathered into an LDS list, where one wave finds bits
 // 15..4 and 3..0.  Otherwise (or when the bin overflows the list) the remaining digits are
 // passes over the registers: bits 31..20, 19..8, 7..0, or 15..4, 3..0.
+// Compaction: when the list's last digit shows that every key equal to tau is kept (the
+// usual case), the selection is the keys >= tau, marked in an LDS bitmap in entry order
+// and compacted from it by contiguous runs per thread; otherwise from the lane-interleaved
+// registers, with the ties at tau ranked in entry order.
 // Slots past n_vis hold key 0, below every visible key (>= float_key(-inf) > 0); they can
 // only be counted when the maximum is within the window of 0, and there are always K
 // larger keys.
@@ -606,7 +610,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
   typedef typename std::conditional<(KPT <= 32), uint32_t, uint64_t>::type Mask;
   __shared__ __attribute__((aligned(16))) uint32_t hist[2][kHistBins];
   __shared__ uint32_t s_list[kRowList];
-  __shared__ uint32_t s_digit, s_rem, s_cnt;
+  __shared__ uint32_t s_bits[KPT * kTopkThreads / 32];   // selection bitmap (entry order)
+  __shared__ uint32_t s_digit, s_rem, s_cnt, s_eqc;
   __shared__ uint32_t s_wtot[kTopkWaves];
   const int t = blockIdx.x;
   if (p.row_flags && !p.row_flags[t]) return;        // selected on the candidate path
@@ -639,7 +644,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
     hist[0][4 * tid + e] = 0u;
     hist[1][4 * tid + e] = 0u;
   }
+#pragma unroll
+  for (int e = 0; e < KPT / 32 + (KPT < 32); ++e)
+    if (KPT >= 32 || tid < KPT * kTopkThreads / 32) s_bits[(KPT >= 32 ? KPT / 32 : 1) * tid + e] = 0u;
   if (tid == 0) s_cnt = 0u;
+  bool all_tied = false;                             // block-uniform: see the compaction
   uint32_t kmax = 0u;
 #pragma unroll
   for (int e = 0; e < KPT; ++e) kmax = max(kmax, kv[e]);
@@ -682,11 +691,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
     uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + incl - c;
     if (bm) {
 #pragma unroll
-      for (int e = 0; e < KPT; ++e)
-        if ((bm >> e) & 1u) {
-          if (at < (uint32_t)kRowList) s_list[at] = kv[e];
-          ++at;
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t nib = (uint32_t)(bm >> (4 * r)) & 0xfu;
+        if (nib) {                                   // the wave skips groups with no match
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((nib >> e) & 1u) {
+              if (at < (uint32_t)kRowList) s_list[at] = kv[4 * r + e];
+              ++at;
+            }
         }
+      }
     }
     __syncthreads();
     const uint32_t L = s_cnt;
@@ -718,14 +733,58 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
         if (lane == l2) {
           s_digit = prefix | (uint32_t)(15 - l2);
           s_rem = remaining - (inc2 - cb);
+          s_eqc = cb;                                // keys equal to tau
         }
       }
       __syncthreads();
       prefix = s_digit;
       remaining = s_rem;
+      all_tied = NR <= 8 && s_eqc == remaining;   // (the widest rows: register budget)
     }
   }
   const uint32_t tau = prefix, need_eq = remaining;
+
+  if (all_tied) {
+    // ---- every key at tau is kept, so the selection is the keys >= tau: marked in an LDS
+    // bitmap in entry order, then thread t compacts entries [KPT t, KPT (t + 1)).
+    Mask ge = 0u;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) ge |= (Mask)(kv[e] >= tau) << e;
+    while (ge) {
+      const int e = (int)__builtin_ctzll((uint64_t)ge);
+      const int j = wbase + 256 * (e >> 2) + 4 * lane + (e & 3);
+      atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+      ge &= ge - 1u;
+    }
+    __syncthreads();
+    const int i0 = KPT * tid;
+    uint64_t w;
+    if constexpr (KPT == 64) w = (uint64_t)s_bits[2 * tid] | ((uint64_t)s_bits[2 * tid + 1] << 32);
+    else if constexpr (KPT == 32) w = s_bits[tid];
+    else w = (s_bits[i0 >> 5] >> (i0 & 31)) & ((1u << KPT) - 1u);
+    const uint32_t c = (uint32_t)__builtin_popcountll(w);
+    const uint32_t incl = wave_incl_scan(c);
+    if (lane == 63) s_wtot[wave] = incl;
+    __syncthreads();
+    uint32_t at = incl - c;
+#pragma unroll
+    for (int v = 0; v < kTopkWaves; ++v) at += (v < wave) ? s_wtot[v] : 0u;
+    if (K <= 2 * kHistBins) {
+      int32_t* s_out = reinterpret_cast<int32_t*>(&hist[0][0]);
+      while (w) {
+        s_out[at++] = i0 + (int)__builtin_ctzll(w);
+        w &= w - 1u;
+      }
+      __syncthreads();
+      for (int i = tid; i < K; i += kTopkThreads) out[i] = s_out[i];
+    } else {
+      while (w) {
+        out[at++] = i0 + (int)__builtin_ctzll(w);
+        w &= w - 1u;
+      }
+    }
+    return;
+  }
 
   // ---- ordered compaction.  Entry order is (wave, group r, lane, key in group): wave
   // offsets come from per-wave totals, the rest from per-group prefixes over the lanes.
