@@ -322,7 +322,8 @@ def measure_append(dev, n, steps, flush_mb):
             "entries_per_s": round(n / (us * 1e-6), 1)}
 
 
-KERNEL_SOURCES = {"idx_score": "k_index.hip", "topk": "k_index.hip",
+KERNEL_SOURCES = {"idx_score": "k_index.hip", "topk": "k_index.hip", "idx_sample": "k_index.hip",
+                  "topk_thr": "k_index.hip", "idx_exact": "k_index.hip", "topk_exact": "k_index.hip",
                   "idx_pool_score": "k_index.hip", "topk_pool": "k_index.hip",
                   "topk_ck_hist": "k_index.hip", "topk_ck_compact": "k_index.hip",
                   "topk_ck_select": "k_index.hip", "sparse_attn": "k_attn.hip",
@@ -341,16 +342,24 @@ def kernel_source_sha(name):
 def library_kernel(device_name):
     """The library's timing name of a device kernel symbol (as rocprofv3 prints it)."""
     n = device_name
-    for pat, key in (("idx_score_kernel", "idx_score"), ("idx_gemm_kernel", "idx_score"),
-                     ("idx_pool_score_kernel", "idx_pool_score"), ("topk_stream_kernel", "topk"),
+    # the row-tiled scoring by mode (template argument 2): the sample, the candidate
+    # scoring, and the full-key scoring, which the benchmark workloads only run as the exact
+    # re-run of rows the candidates could not settle (as does the streamed Top-K)
+    if "idx_gemm_kernel" in n:
+        return {"1>": "idx_sample", "2>": "idx_score"}.get(n.split("(")[0][-2:], "idx_exact")
+    for pat, key in (("idx_score_kernel", "idx_score"), ("topk_thr_kernel", "topk_thr"),
+                     ("topk_cand_kernel", "topk"),
+                     ("idx_pool_score_kernel", "idx_pool_score"), ("topk_stream_kernel", "topk_exact"),
                      ("topk_ck_hist", "topk_ck_hist"), ("topk_ck_compact", "topk_ck_compact"),
                      ("topk_ck_select", "topk_ck_select"), ("sparse_attn_kernel", "sparse_attn"),
                      ("attn_merge_kernel", "attn_merge"), ("swa_", "swa"),
                      ("kv_append", "kv_append"), ("mxfp4_quantize", "mxfp4_quantize")):
         if pat in n:
             return key
-    if "topk_reg_kernel" in n:
-        return "topk_pool" if "true>" in n else "topk"
+    if "topk_pool_kernel" in n:
+        return "topk_pool"
+    if "topk_row_kernel" in n:
+        return "topk"
     return None
 
 
