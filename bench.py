@@ -70,6 +70,10 @@ def parse_args():
                     help="only measure this GPU's MFMA and LDS peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--graph-probe", action="store_true",
+                    help="only time the workload's step replayed from HIP graphs (one per "
+                         "input copy) beside the eager step, in this process (one-layer "
+                         "workloads)")
     return ap.parse_args()
 
 
@@ -155,6 +159,77 @@ def input_sets(w, dev, fmt=0):
     them, as in a model where the other layers' data passes through that cache between two
     steps of one layer."""
     return [Inputs(w, dev, fmt) for _ in range(input_copies(w, fmt))]
+
+
+def graph_probe(w, dev, steps, rounds=5):
+    """The step replayed from HIP graphs against the eager step, in one process: each input
+    copy's layer-group call (SWA side stream, fork and join included) is captured once
+    through torch's capture, and replays alternate over the copies like the eager clock.
+    Also checks that a replay reproduces the eager call's outputs bit for bit."""
+    import torch
+    ss = input_sets(w, dev, 0)
+    for s in ss:
+        s.step()
+    torch.cuda.synchronize()
+    keys = ("o", "lse", "o_swa", "lse_swa", "idx_out")
+    ref = {k: ss[0].layers[0][k].clone() for k in keys}
+
+    def clock(fn):
+        res = []
+        for _ in range(rounds):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                fn(i)
+            torch.cuda.synchronize()
+            res.append((time.perf_counter() - t0) * 1e3 / steps)
+        return min(res)
+
+    eager = clock(lambda i: ss[i % len(ss)].step())
+    graphs = []
+    for s in ss:
+        side = torch.cuda.Stream()                 # warm-up on a non-default stream first
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            s.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.step()
+        graphs.append(g)
+    same = True
+    for _ in range(2):
+        for k in keys:
+            ss[0].layers[0][k].zero_()
+        torch.cuda.synchronize()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(ss[0].layers[0][k], ref[k]) for k in keys)
+    graph = clock(lambda i: graphs[i % len(graphs)].replay())
+    return {"graph_ms_per_step": round(graph, 4), "eager_ms_per_step": round(eager, 4),
+            "replay_bit_identical": bool(same), "input_copies": len(ss)}
+
+
+def graph_probe_child(workload, steps):
+    """graph_probe in a child process (a fault there cannot take this process's line with
+    it); None for a workload of several layers, whose capture is not timed here."""
+    import subprocess
+    import synth
+    if len(synth.workload(workload).modes) != 1:
+        return None
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--graph-probe",
+                            "--workload", str(workload), "--steps", str(steps)],
+                           capture_output=True, text=True, timeout=300)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            return {"error": f"exit {r.returncode}: {r.stderr.strip()[-300:]}"}
+        return json.loads(lines[-1])
+    except Exception as e:                         # noqa: BLE001 - reported, not raised
+        return {"error": repr(e)[:300]}
 
 
 # ------------------------------------------------------------------ algorithmic bytes
@@ -581,6 +656,12 @@ def main():
 
     from fp4_compressed_sparse_amd import csa2
     w = synth.workload(args.workload)
+    if args.graph_probe:
+        if len(w.modes) != 1:
+            print("--graph-probe times one-layer workloads only", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(graph_probe(w, dev, args.steps)))
+        return
     if args.reindex_pool:
         w = dataclasses.replace(w, name=w.name.replace("reindex", "reindexpool"),
                                 modes=[3 if m == 1 else m for m in w.modes])
@@ -716,6 +797,13 @@ def main():
             result["extra"].append(measure_extra(wx, dev, steps, 2, args.flush_mb, fmt))
         print("[bench] extra: KV append", file=sys.stderr, flush=True)
         result["extra"].append(measure_append(dev, 32768, 20, args.flush_mb))
+        # the one-layer decode steps replayed from HIP graphs, beside the eager clock
+        if not args.kv_format and not args.reindex_pool:
+            print("[bench] graph replay", file=sys.stderr, flush=True)
+            result["graph_replay"] = graph_probe_child(args.workload, args.steps)
+            for e in result["extra"]:
+                if e.get("workload") == synth.workload(4).name:
+                    e["graph_replay"] = graph_probe_child(4, 20)
     if args.cpu_rows > 0:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_rows, w.T))
