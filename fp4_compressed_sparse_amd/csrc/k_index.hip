@@ -1116,21 +1116,22 @@ void topk_stream_kernel(TopkParams p) {
 }
 
 // ---------------------------------------------------------------- sampled candidates
-// Per row, from the packed sample of every page_gap-th page (zeros = masked): the
-// threshold, the r-th largest sampled key to 24 bits with r chosen so that about 1.5 K +
-// 16 page_gap 64 of the row's keys are expected at or above it.  Rows where that cannot
-// work (r above the sample) are flagged for the exact path; rows with at most K visible
-// entries need no threshold.
-__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
-void topk_thr_kernel(TopkParams p) {
-  __shared__ TopkShared sh;
-  __shared__ uint32_t s_lkey[kSamplePages * kPage];
-  __shared__ uint32_t s_cnt;
+// Per row: the threshold of the sampled-candidate path, the top 24 bits of the r-th
+// largest sampled key, r = 1.5 K nsv / n + 16 (nsv the row's valid samples).  One wave
+// per row and no block barrier: the wave holds the row's (at most 4096) samples in
+// registers, the first digit is bits 31..16 of the keys whose top 16 bits lie within 4095
+// of the sample maximum's, the second bits 15..8 of the keys in the chosen bin.  A row
+// with fewer than r valid samples, or fewer than r in the window, is flagged for the exact
+// path.  Rows that select everything (n <= K) get threshold ~0 and no flag.
+constexpr int kThrKeysPerLane = kSamplePages * kPage / 64;
+__global__ __launch_bounds__(64) void topk_thr_kernel(TopkParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
+  __shared__ uint32_t s_digit, s_rem;
   const int t = blockIdx.x;
+  const int lane = threadIdx.x;
   const int n = p.n_vis[t];
-  const int tid = threadIdx.x;
   if (n <= p.K) {
-    if (tid == 0) {
+    if (lane == 0) {
       p.thr[t] = 0xffffffffu;
       p.row_flags[t] = 0u;
     }
@@ -1138,34 +1139,60 @@ void topk_thr_kernel(TopkParams p) {
   }
   const int G = p.page_gap;
   const int nsp = ((n + kPage - 1) / kPage + G - 1) / G;   // sampled pages with visible keys
-  const int ns = min(nsp, kSamplePages) * kPage;
-  if (tid == 0) s_cnt = 0u;
-  __syncthreads();
-  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride;
-  uint32_t c = 0u;
-  for (int i = tid; i < ns; i += kTopkThreads) {
-    const uint32_t k = keys[i];
-    s_lkey[i] = k;
-    c += (k != 0u);
+  const int ns = min(nsp, kSamplePages) * kPage;            // a multiple of 64
+  // lane l holds keys 256 j + 4 l + e: 1 KB of consecutive keys per load instruction
+  const uint32_t* keys = p.keys + (int64_t)t * p.key_stride + 4 * lane;
+  uint32_t kv[kThrKeysPerLane];
+#pragma unroll
+  for (int j = 0; j < kThrKeysPerLane / 4; ++j) {
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (256 * j + 4 * lane < ns) v = *reinterpret_cast<const u32x4*>(keys + 256 * j);
+    kv[4 * j] = v[0]; kv[4 * j + 1] = v[1]; kv[4 * j + 2] = v[2]; kv[4 * j + 3] = v[3];
   }
-  c = wave_sum_u32(c);
-  if ((tid & 63) == 0) atomicAdd(&s_cnt, c);
-  __syncthreads();
-  const uint32_t nsv = s_cnt;                        // valid sampled keys
+  u32x4* h4 = reinterpret_cast<u32x4*>(s_hist);
+#pragma unroll
+  for (int q = 0; q < kHistBins / 256; ++q) h4[64 * q + lane] = u32x4{0u, 0u, 0u, 0u};
+  uint32_t c = 0u, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < kThrKeysPerLane; ++e) {
+    c += (kv[e] != 0u);
+    kmax = max(kmax, kv[e]);
+  }
+  const uint32_t nsv = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(c), 63);
+  kmax = wave_max_u32_dpp(kmax);
   const uint32_t r = (uint32_t)((1.5 * (double)p.K * nsv) / n) + 16u;
-  if (r > nsv) {
-    if (tid == 0) {
-      p.thr[t] = 0u;
-      p.row_flags[t] = 1u;
+  const int lo = (int)(kmax >> 16) - (kHistBins - 1);
+  bool flag = r > nsv;                               // wave-uniform
+  uint32_t thr = 0u;
+  if (!flag) {
+#pragma unroll
+    for (int e = 0; e < kThrKeysPerLane; ++e) {
+      const int b = (int)(kv[e] >> 16) - lo;
+      if (kv[e] != 0u && b >= 0) atomicAdd(&s_hist[b], 1u);
     }
-    return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    topk_find_digit_w0(s_hist, r, &s_digit, &s_rem);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const uint32_t d0 = s_digit;
+    flag = d0 == kNoDigit;
+    if (!flag) {
+      const uint32_t top = (uint32_t)(lo + (int)d0);  // the bin's top 16 bits
+      const uint32_t rem = s_rem;
+#pragma unroll
+      for (int q = 0; q < kHistBins / 256; ++q) h4[64 * q + lane] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int e = 0; e < kThrKeysPerLane; ++e)
+        if ((kv[e] >> 16) == top) atomicAdd(&s_hist[(kv[e] >> 8) & 0xffu], 1u);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      topk_find_digit_w0(s_hist, rem, &s_digit, &s_rem);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      thr = (top << 16) | (s_digit << 8);
+    }
   }
-  uint32_t thr, unused;
-  topk_list_select(sh, s_lkey, ns, r, 2, thr, unused);
-  (void)unused;
-  if (tid == 0) {
-    p.thr[t] = thr;
-    p.row_flags[t] = 0u;
+  if (lane == 0) {
+    p.thr[t] = flag ? 0u : thr;
+    p.row_flags[t] = flag ? 1u : 0u;
   }
 }
 
@@ -1256,7 +1283,7 @@ void topk_cand_kernel(TopkParams p) {
 }
 
 hipError_t launch_topk_thr(const TopkParams& p, hipStream_t s) {
-  CSA2_LAUNCH(topk_thr_kernel, dim3((unsigned)p.T), dim3(kTopkThreads), s, p);
+  CSA2_LAUNCH(topk_thr_kernel, dim3((unsigned)p.T), dim3(64), s, p);
   return hipGetLastError();
 }
 
