@@ -596,10 +596,11 @@ constexpr int kRowList = 4096;
 // among them; the keys of its bin are gathered into an LDS list, where one wave finds bits
 // 15..4 and 3..0.  Otherwise (or when the bin overflows the list) the remaining digits are
 // passes over the registers: bits 31..20, 19..8, 7..0, or 15..4, 3..0.
-// Compaction: when the list's last digit shows that every key equal to tau is kept (the
-// usual case), the selection is the keys >= tau, marked in an LDS bitmap in entry order
-// and compacted from it by contiguous runs per thread; otherwise from the lane-interleaved
-// registers, with the ties at tau ranked in entry order.
+// The list append also counts the second digit, so one wave finds it from the counts and
+// the last digit on the list.  Compaction: when the list's last digit shows that every key
+// equal to tau is kept (the usual case), the selection is the keys >= tau, marked in an
+// LDS bitmap in entry order and written from it by contiguous runs per thread; otherwise
+// from the lane-interleaved registers, with the ties at tau ranked in entry order.
 // Slots past n_vis hold key 0, below every visible key (>= float_key(-inf) > 0); they can
 // only be counted when the maximum is within the window of 0, and there are always K
 // larger keys.
@@ -679,7 +680,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
   } else {
     prefix = (uint32_t)(lo + (int)d0) << 16;
     remaining = s_rem;
-    // gather the bin's keys (any order) into the list
+    // gather the bin's keys (any order) into the list, counting their second digit (bits
+    // 15..4) on the way (hist[1] is clear)
     Mask bm = 0u;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) bm |= (Mask)((kv[e] & 0xffff0000u) == prefix) << e;
@@ -697,6 +699,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if ((nib >> e) & 1u) {
+              atomicAdd(&hist[1][(kv[4 * r + e] >> 4) & 0xfffu], 1u);
               if (at < (uint32_t)kRowList) s_list[at] = kv[4 * r + e];
               ++at;
             }
@@ -705,15 +708,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
     }
     __syncthreads();
     const uint32_t L = s_cnt;
-    if (L > (uint32_t)kRowList) {                    // block-uniform; hist[1] is clear
-      topk_reg_pass(kv, hist[1], hist[0], 4, 12, prefix, remaining, &s_digit, &s_rem);
+    if (L > (uint32_t)kRowList) {                    // block-uniform
+      // the second digit from its counts, the last over the registers
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hist[0][4 * tid + e] = 0u;
+      if (wave == 0) topk_find_digit_w0(hist[1], remaining, &s_digit, &s_rem);
+      __syncthreads();
+      prefix |= s_digit << 4;
+      remaining = s_rem;
       topk_reg_pass(kv, hist[0], hist[1], 0, 4, prefix, remaining, &s_digit, &s_rem);
     } else {
       if (wave == 0) {
-        // bits 15..4 over the list (hist[1] is clear)
-        for (uint32_t i = (uint32_t)lane; i < L; i += 64u)
-          atomicAdd(&hist[1][(s_list[i] >> 4) & 0xfffu], 1u);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        // bits 15..4 from their counts, bits 3..0 over the list
         topk_find_digit_w0(hist[1], remaining, &s_digit, &s_rem);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         prefix |= s_digit << 4;
@@ -769,19 +775,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkParams p) {
     uint32_t at = incl - c;
 #pragma unroll
     for (int v = 0; v < kTopkWaves; ++v) at += (v < wave) ? s_wtot[v] : 0u;
-    if (K <= 2 * kHistBins) {
-      int32_t* s_out = reinterpret_cast<int32_t*>(&hist[0][0]);
-      while (w) {
-        s_out[at++] = i0 + (int)__builtin_ctzll(w);
-        w &= w - 1u;
-      }
-      __syncthreads();
-      for (int i = tid; i < K; i += kTopkThreads) out[i] = s_out[i];
-    } else {
-      while (w) {
-        out[at++] = i0 + (int)__builtin_ctzll(w);
-        w &= w - 1u;
-      }
+    // each thread's picks are consecutive in the output, so the stores stay near-coalesced
+    while (w) {
+      out[at++] = i0 + (int)__builtin_ctzll(w);
+      w &= w - 1u;
     }
     return;
   }
