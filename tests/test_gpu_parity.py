@@ -604,6 +604,23 @@ def test_topk_candidates_sample_misses(csa2, dev, boost):
     assert np.all(np.diff(idx, axis=1) > 0)
 
 
+def test_topk_candidates_window_miss(csa2, dev):
+    """Rows whose sampled maximum sits more than 32 octaves above the rest: 200 keys scaled
+    by 2^36, so the threshold's first digit window holds fewer than its rank; the rows are
+    flagged, take the exact path and match the oracle (the 200 and the best of the rest)."""
+    _say("topk_candidates_window_miss")
+    E, K, T = 16384, 512, 258
+    rng = np.random.default_rng(31)
+    kf = np.abs(synth.normal_f32(13, 1, 0, E * 64)).reshape(E, 64)
+    kf[rng.choice(E, 200, replace=False)] *= np.float32(2.0 ** 36)
+    qf = np.abs(synth.normal_f32(13, 2, 0, T * 64))
+    idx, (qb, wv, kb, pt, sid, nv) = _cand_direct(csa2, dev, kf, qf, K, T)
+    rows = np.array([0, 1, 128, 257])
+    _, s_ref = orc.index_topk(K, E // 64, qb, wv, kb, pt, sid, nv, rows=rows, want_scores=True)
+    tl.check_topk(idx[rows], s_ref, K, nv, rows=rows)
+    assert np.all(np.diff(idx, axis=1) > 0)
+
+
 def _swa_windows(T, L, seed):
     rng = np.random.default_rng(seed)
     ln = rng.choice([0, 1, 17, 64, 128, 200], T)
