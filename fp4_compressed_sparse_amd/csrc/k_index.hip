@@ -1757,17 +1757,39 @@ __global__ __launch_bounds__(256, kGemmWavesPerSimd) void idx_gemm_kernel(IdxSco
         for (int rb = 0; rb < NRB; ++rb)
           acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rb][1]), as_bf16x8(kv[kb][1]),
                                                             acc[rb], 0, 0, 0);
+        float sc[NRB];                                 // this lane's heads, per block
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          float sc = wv[rb][0] * relu_f32(acc[rb][0]);
-          sc += wv[rb][1] * relu_f32(acc[rb][1]);
-          sc += wv[rb][2] * relu_f32(acc[rb][2]);
-          sc += wv[rb][3] * relu_f32(acc[rb][3]);
-          if (HP >= 8) sc = xor16_sum(sc);
-          if (HP >= 16) sc = xor32_sum(sc);
-          // lanes holding the same row write the same value
-          const int rl = RB * rb + (HP == 4 ? g : (HP == 8 ? (g >> 1) : 0));
-          s_out[pp & 1][wave][rl][k] = sc;
+          sc[rb] = wv[rb][0] * relu_f32(acc[rb][0]);
+          sc[rb] += wv[rb][1] * relu_f32(acc[rb][1]);
+          sc[rb] += wv[rb][2] * relu_f32(acc[rb][2]);
+          sc[rb] += wv[rb][3] * relu_f32(acc[rb][3]);
+        }
+        if (HP == 4) {                                 // lane group g is row g of the block
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) s_out[pp & 1][wave][RB * rb + g][k] = sc[rb];
+        } else if (HP == 8) {
+          // a row's heads sit in lane groups 2r and 2r + 1: one v_permlane16_swap of two
+          // blocks' sums leaves groups 0 and 2 with block 2j's rows 0 and 1, groups 1 and 3
+          // with block 2j + 1's (a reduce-scatter: no copy, every value written once)
+#pragma unroll
+          for (int j = 0; j < NRB / 2; ++j) {
+            const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(sc[2 * j]),
+                                                            __float_as_uint(sc[2 * j + 1]), false, false);
+            const float v = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+            s_out[pp & 1][wave][RB * (2 * j + (g & 1)) + (g >> 1)][k] = v;
+          }
+        } else {
+          // one row per block over all four lane groups: v_permlane32_swap pairs blocks 0, 2
+          // and 1, 3 across groups g and g + 2, then v_permlane16_swap leaves group g with
+          // block g's whole sum
+          static_assert(HP != 16 || NRB == 4, "four blocks per wave at 16 heads");
+          const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[0]), __float_as_uint(sc[2]), false, false);
+          const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[1]), __float_as_uint(sc[3]), false, false);
+          const float ha = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+          const float hb = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+          const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(ha), __float_as_uint(hb), false, false);
+          s_out[pp & 1][wave][g][k] = __uint_as_float(c[0]) + __uint_as_float(c[1]);
         }
       }
       wait_vmem<4>();                                  // page pp+1 in LDS
