@@ -115,46 +115,14 @@ __device__ __forceinline__ uint32_t row16_last(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x15f, 0xf, 0xf, false);
 }
 
-// x + x of lane ^ 16 (lane ^ 32) without the LDS crossbar: v_permlane16_swap exchanges the
-// odd 16-lane rows of one operand with the even rows of the other, so swapping x with
-// itself leaves each lane x of its row and of the paired row.
-__device__ __forceinline__ float xor16_sum(float x) {
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // max(a - b, 0) for unsigned values, written without a comparison-guarded subtraction:
 // this compiler has been seen to hoist the subtraction of `a > b ? f(a - b) : 0` with a
 // no-wrap flag and then treat b <= a as known elsewhere (dropping a later min(b, a)).
 __device__ __forceinline__ uint32_t sub_sat_u32(uint32_t a, uint32_t b) { return a - min(a, b); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 
