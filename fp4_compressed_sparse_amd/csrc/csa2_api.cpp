@@ -514,6 +514,7 @@ csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
   ap.max_pages = a->max_pages;
   ap.splits = S;
   ap.per_split = per;
+  ap.split_heads = attn_split_heads(a->T, a->H, S, cus - swa_wgs) ? 1 : 0;
   ap.fmt = a->kv_format;
   ap.sm_scale_log2 = a->sm_scale * 1.4426950408889634f;
   ap.q = static_cast<const uint16_t*>(a->q);

@@ -107,6 +107,7 @@ __host__ __device__ inline int64_t topk_chunks(int64_t key_stride) { return (key
 struct AttnParams {
   int T, H, K, max_pages, splits, per_split;   // per_split: idx slots per split
   int fmt = 0;                                  // 0: E8M0 per 32; 1: E4M3 per 16
+  int split_heads = 0;                          // H = 64 run as two 32-head workgroups
   float sm_scale_log2;                          // sm_scale * log2(e)
   const uint16_t* q;                            // [T, H, 576]
   const uint8_t* kv_lat;
@@ -217,6 +218,12 @@ inline int swa_persist_wgs(int T, int H, int H_kv, int cus) {
 }
 // 64-head workgroups per (row, split) of the sparse attention kernel
 inline int attn_head_groups(int H) { return H > 64 ? H / 64 : 1; }
+// With few rows the 64-head workgroups leave most CUs idle and each runs little more than
+// its fixed prologue and epilogue: 64 heads then run as two 32-head workgroups when the
+// doubled grid still fits the CUs in one round.
+inline bool attn_split_heads(int T, int H, int splits, int cus) {
+  return H == 64 && (int64_t)T * splits * 2 <= cus;
+}
 
 // ---------------------------------------------------------------- host-side runners
 // A side stream of the current device with its fork and join events (default priority;

@@ -766,7 +766,10 @@ hipError_t launch_sparse_attn_fmt(const AttnParams& p, hipStream_t s) {
   switch (p.H) {
     case 16: CSA2_LAUNCH((sparse_attn_kernel<1, FMT>), dim3(blocks), dim3(768), s, p); break;
     case 32: CSA2_LAUNCH((sparse_attn_kernel<2, FMT>), dim3(blocks), dim3(768), s, p); break;
-    case 64: CSA2_LAUNCH((sparse_attn_kernel<4, FMT>), dim3(blocks), dim3(768), s, p); break;
+    case 64:
+      if (p.split_heads) CSA2_LAUNCH((sparse_attn_kernel<2, FMT>), dim3(blocks, 2), dim3(768), s, p);
+      else CSA2_LAUNCH((sparse_attn_kernel<4, FMT>), dim3(blocks), dim3(768), s, p);
+      break;
     case 128: CSA2_LAUNCH((sparse_attn_kernel<4, FMT>), dim3(blocks, 2), dim3(768), s, p); break;
     default: return hipErrorInvalidValue;
   }
