@@ -430,16 +430,19 @@ def _bf16_bits(x):
     return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def test_topk_row_paths(csa2, dev):
+@pytest.mark.parametrize("P,K", [(512, 2048), (1024, 2048), (512, 9000)],
+                         ids=["32k_k2048", "64k_k2048", "32k_k9000"])
+def test_topk_row_paths(csa2, dev, P, K):
     """The one-workgroup-per-row Top-K (rows of up to 64K keys) on exact scores (one head,
     a unit query, keys whose first channel carries the score) that steer each of its
     paths, compared with the oracle index for index: fewer than K keys within 32 octaves
     of the row maximum (digit passes from bit 31), one bin larger than the LDS list
     (digit passes over registers), ties at the K-th key inside the list, negative scores,
-    a row ending inside the last wave's keys, and a row that selects everything."""
-    _say("topk_row_paths")
+    a row ending inside the last wave's keys, a row that selects everything, and one whose
+    ties at the K-th key are all kept.  Rows of 32K and 64K keys (32 and 64 keys per
+    thread), and K above the 8192 outputs that the staged compaction holds."""
+    _say("topk_row_paths", P, K)
     rng = np.random.default_rng(2024)
-    P, K = 512, 2048
     E = 64 * P
     rows = []
     v = (1.0 + rng.integers(0, 128, E) / 128.0).astype(np.float32)
@@ -448,8 +451,13 @@ def test_topk_row_paths(csa2, dev):
     rows.append((np.full(E, 1.5, np.float32), 1.0, E))
     rows.append((np.float32(1.0) + rng.integers(0, 16, E).astype(np.float32) / np.float32(16), 1.0, E))
     rows.append((np.abs(rng.standard_normal(E)).astype(np.float32) + np.float32(0.01), -1.0, E))
-    rows.append((rng.standard_normal(E).astype(np.float32), 1.0, 20001))
-    rows.append((rng.standard_normal(E).astype(np.float32), 1.0, 1500))
+    rows.append((rng.standard_normal(E).astype(np.float32), 1.0, min(20001, E - 7)))
+    rows.append((rng.standard_normal(E).astype(np.float32), 1.0, K - 548))
+    # every key at the K-th value kept (the bitmap compaction): the top keys come in groups
+    # of dup equal bf16 values, K a multiple of dup, spanning under 32 octaves
+    dup = 3 if K % 3 == 0 else 2
+    pat = np.maximum(0x7F00 - rng.permutation(E) // dup, 0x0080).astype(np.uint32)
+    rows.append(((pat << 16).view(np.float32), 1.0, E))
     T = len(rows)
     k_bits = np.zeros((T * E, 64), np.uint16)
     for b, (vals, _, _) in enumerate(rows):
