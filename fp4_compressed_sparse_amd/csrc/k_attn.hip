@@ -100,42 +100,28 @@ __device__ __forceinline__ int xcd_linear(int b, int n) {
   return (x < r8) ? x * (q8 + 1) + slot : r8 * (q8 + 1) + (x - r8) * q8 + slot;
 }
 
-// E4M3 scale byte -> (a power of two, for the conversions that apply a scale's exponent
-// only, and the remaining significand 1 + m/8, or m for the subnormals m 2^-9)
-__device__ __forceinline__ void e4m3_split(uint32_t b, float& pow2, _Float16& mant) {
-  const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
-  pow2 = __uint_as_float((uint32_t)((e ? e - 7 : -9) + 127) << 23);
-  mant = (_Float16)(e ? 1.f + 0.125f * (float)m : (float)m);
+// Two E4M3 scale bytes (bytes 0 and 1 of w, or 2 and 3 with HI) -> their values as packed
+// fp16, by the OCP 8-bit conversion (E4M3 variant: subnormals m 2^-9, S.1111.111 NaN, the
+// sign kept), scale 2^0.  Every E4M3 value is exact in fp16.
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HI);
 }
 
-// 8 E2M1 codes times an E4M3 scale -> 4 packed f16 pairs (exact: at most 6 significant bits,
-// magnitudes in [2^-10, 2688]).
-__device__ __forceinline__ void fp4x8_e4m3_to_f16_pairs(uint32_t w, uint32_t sbyte,
-                                                        uint32_t out[4]) {
-  float pow2;
-  _Float16 mant;
-  e4m3_split(sbyte, pow2, mant);
-  fp4x8_to_f16_pairs(w, pow2, out);
-  const f16x2 mm = {mant, mant};
+// 8 E2M1 codes times an fp16 scale -> 4 packed f16 pairs.  Exact for an E4M3 scale: at most
+// 6 significant bits, magnitudes in [2^-10, 2688].
+__device__ __forceinline__ void fp4x8_scaled_f16_pairs(uint32_t w, _Float16 sc, uint32_t out[4]) {
+  fp4x8_to_f16_pairs(w, 1.f, out);
+  const f16x2 mm = {sc, sc};
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     out[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, out[k]) * mm);
 }
 
-// Scale byte -> the fp16 bit pattern of the scale it encodes: E8M0 2^(b - 127) (FMT 0;
-// exponents below -24 give 0, above 15 give +inf, so that a value the fp16 product cannot
-// hold shows as a non-finite output rather than a wrong finite one), or the E4M3 value
-// (FMT 1; every E4M3 value is exact in fp16).
-template <int FMT>
-__device__ __forceinline__ uint32_t scale_f16_bits(uint32_t b) {
-  if (FMT == 1) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    if (e) return ((e + 8u) << 10) | (m << 7);       // 2^(e-7) (1 + m/8)
-    // m 2^-9: normal fp16 2^(j-9) (1 + (m - 2^j) / 2^j) with j = floor(log2 m)
-    if (m == 0u) return 0u;
-    const uint32_t j = 31u - (uint32_t)__builtin_clz(m);
-    return ((j + 6u) << 10) | (((m << (10u - j)) & 0x3ffu));
-  }
+// E8M0 scale byte -> the fp16 bit pattern of 2^(b - 127): exponents below -24 give 0, above
+// 15 give +inf, so that a value the fp16 product cannot hold shows as a non-finite output
+// rather than a wrong finite one.
+__device__ __forceinline__ uint32_t e8m0_f16_bits(uint32_t b) {
   const int k = (int)b - 127;
   if (k > 15) return 0x7c00u;
   if (k >= -14) return (uint32_t)(k + 15) << 10;
@@ -394,10 +380,12 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
       sc2[mb] = *reinterpret_cast<const uint16_t*>(                                         \
           raw + kRawScl + 1024 * ((kk) >> 1) + epos[mb] + ((8 * (kk) + 2 * g) & 15));       \
     }                                                                                       \
+    f16x2 s16[4];                                                                           \
+    _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) s16[mb] = e4m3x2_to_f16<false>(sc2[mb]); \
     _Pragma("unroll") for (int jj = 0; jj < 4; ++jj)                                        \
       _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) {                                    \
         uint32_t kv[4];                                                                     \
-        fp4x8_e4m3_to_f16_pairs(w4[mb][jj], (sc2[mb] >> (8 * (jj >> 1))) & 0xffu, kv);      \
+        fp4x8_scaled_f16_pairs(w4[mb][jj], s16[mb][jj >> 1], kv);                           \
         const f16x8 ka = __builtin_bit_cast(f16x8, u32x4{kv[0], kv[1], kv[2], kv[3]});      \
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[kk][jj], acc[mb], 0, 0, 0); \
       }                                                                                     \
@@ -569,14 +557,16 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
       const uint32_t b0 = raw[kRawScl + 16 * ent_pos(2 * ep) + cb];
       const uint32_t b1 = raw[kRawScl + 16 * ent_pos(2 * ep + 1) + cb];
       *reinterpret_cast<uint32_t*>(tb + cb * kTE + 2 * ep) =
-          scale_f16_bits<0>(b0) | (scale_f16_bits<0>(b1) << 16);
+          e8m0_f16_bits(b0) | (e8m0_f16_bits(b1) << 16);
     } else {
       const int cb = tv >> 4, eq = tv & 15;
-      uint32_t v[4];
+      uint32_t w = 0u;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        v[k] = scale_f16_bits<1>(raw[kRawScl + 1024 * (cb >> 4) + 16 * ent_pos(4 * eq + k) + (cb & 15)]);
-      *reinterpret_cast<u32x2*>(tb + cb * kTE + 4 * eq) = u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+        w |= (uint32_t)raw[kRawScl + 1024 * (cb >> 4) + 16 * ent_pos(4 * eq + k) + (cb & 15)] << (8 * k);
+      *reinterpret_cast<u32x2*>(tb + cb * kTE + 4 * eq) =
+          u32x2{__builtin_bit_cast(uint32_t, e4m3x2_to_f16<false>(w)),
+                __builtin_bit_cast(uint32_t, e4m3x2_to_f16<true>(w))};
     }
   };
 

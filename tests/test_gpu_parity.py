@@ -380,6 +380,53 @@ def test_attn_latent_scale_range(csa2, dev):
                               rows=np.array([t]), swa=False)
 
 
+def test_attn_e4m3_scale_bytes(csa2, dev):
+    """E4M3-per-16 latent planes written directly, with scale bytes over the whole format
+    but its NaNs: subnormals m 2^-9 and 0, the largest values (448), and negative scales
+    (the oracle decodes the sign bit; no quantizer writes one).  Every value code * scale is
+    exact in fp16, so each row meets the usual tolerances in units of its largest value."""
+    _say("attn_e4m3_scale_bytes")
+    w = W(B=1, T=4, E=512, K=128, H=64, seq_id_rows=[0, 0, 0, 0], shuffle=False)
+    d = tl.DeviceWorkload(w, dev, fmt=1)
+    h = tl.HostWorkload(w, fmt=1)
+    rng = np.random.default_rng(23)
+    lat = rng.integers(0, 256, size=(512, 256), dtype=np.uint8)
+    not_nan = np.r_[np.arange(0x00, 0x7f), np.arange(0x80, 0xff)]
+    scl = np.empty((512, 32), np.uint8)
+    scl[:128] = rng.integers(0x00, 0x18, size=(128, 32))        # subnormals, 0, smallest
+    scl[128:256] = rng.integers(0x60, 0x7f, size=(128, 32))     # 2^5 .. 448
+    scl[256:384] = rng.choice(not_nan, size=(128, 32))          # anything, sign included
+    scl[384:] = rng.integers(0x30, 0x41, size=(128, 32))        # 2^-1 .. 2
+    scl[5, :4] = np.arange(1, 5)                                # every subnormal step
+    scl[130, 0] = 0x7e
+    pt = w.page_table()
+    _, _, rope = h.kv[0]
+    lat_h = w.to_physical(lambda b: lat, pt)
+    scl_h = w.to_physical(lambda b: scl, pt)
+    L = d.layers[0]
+    L["kv_lat"].copy_(torch.from_numpy(lat_h.reshape(L["kv_lat"].shape)).to(dev))
+    L["kv_scl"].copy_(torch.from_numpy(scl_h.reshape(L["kv_scl"].shape)).to(dev))
+    idx = -np.ones((4, 128), np.int32)
+    idx[0] = np.arange(128)
+    idx[1] = np.arange(128, 256)
+    idx[2] = np.arange(256, 384)
+    idx[3, :96] = np.r_[np.arange(384, 448), np.arange(0, 128, 4)]   # ragged, mixed
+    e4 = np.array([orc.e4m3_decode(b) for b in range(256)])
+    unit = [6 * np.abs(e4[scl[idx[t][idx[t] >= 0]]]).max() for t in range(4)]
+    for sm, rows in ((1.0 / 24.0, [0, 3]), (1.0 / (24.0 * 512.0), [1, 2])):
+        o, lse = csa2.sparse_attn_fp4(L["q"], L["kv_lat"], L["kv_scl"], L["kv_rope"],
+                                      d.page_table, d.seq_id, torch.from_numpy(idx).to(dev),
+                                      sm_scale=sm, kv_format=1)
+        torch.cuda.synchronize()
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        ro, rl = orc.sparse_attn(w.P, w.q(), lat_h, scl_h, rope, pt, w.seq_id(), idx,
+                                 sm_scale=sm, rows=np.arange(4), fmt=1)
+        for t in rows:
+            u = unit[t]
+            tl.check_attn({"o": o / u, "lse": lse}, {"o": ro[[t]] / u, "lse": rl[[t]]},
+                          rows=np.array([t]), swa=False)
+
+
 def test_workspace_contents_do_not_matter(csa2, dev):
     """The layer group's outputs do not depend on what the workspace held before the call:
     a zeroed and an all-0xFF workspace give bit-identical outputs.  Rows longer than 65,536
