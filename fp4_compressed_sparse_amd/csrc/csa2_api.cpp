@@ -105,6 +105,9 @@ hipEvent_t timing_event() {
 // With kernel timing off: an event that the next launch records as it completes (set to
 // fork the side stream off a kernel without a separate event packet in the stream).
 thread_local hipEvent_t g_stop_next = nullptr;
+// Set with g_stop_next when the side stream is idle at the fork (the call's first): the
+// per-row scoring then forks off all but its last round (score_fork_blocks).
+thread_local bool g_fork_early = false;
 
 template <class F>
 csa2_status timed(const char* name, hipStream_t s, F&& fn) {
@@ -361,7 +364,18 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
     t6.row_flags = flags;
     return timed("topk_exact", s, [&] { return launch_topk(t6, s); });
   }
-  st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
+  const int64_t n1 = (g_stop_next && g_fork_early && sp.T < kIdxGemmMinRows)   // per-row kernel
+                         ? score_fork_blocks((int64_t)sp.T * sp.chunks, device_cus()) : 0;
+  if (n1 > 0) {
+    // the side branch's start latency overlaps the last round of the scoring
+    IdxScoreParams a1 = sp, a2 = sp;
+    a1.block_end = (int)n1;
+    a2.block0 = (int)n1;
+    st = timed("idx_score", s, [&] { return launch_idx_score(a1, s); });
+    if (!st) st = timed("idx_score", s, [&] { return launch_idx_score(a2, s); });
+  } else {
+    st = timed("idx_score", s, [&] { return launch_idx_score(sp, s); });
+  }
   if (st) return st;
   st = between();
   if (st) return st;
@@ -798,11 +812,21 @@ csa2_status layer_group_run(const csa2_layer_desc* L, int32_t n_layers,
       ia.idx_out = L[i].idx_out;
       armed = sd && !capturing;
       if (armed) g_stop_next = sd->fork;
+      // The scoring forks the side branch before its last round when that branch is idle
+      // and likely the longer one after the scoring: its K and V windows (at most L_swa
+      // positions, 128 bf16 channels per KV head) are at least as many bytes as the
+      // indexer keys the scoring reads (64 bf16 per entry).  (Measured: the 64 x 128K
+      // decode step -3%; a 32 x 256K group, whose side branch reads half the scoring's
+      // bytes, +1.5% with the early fork, so there it stays at the scoring's end.)
+      const int64_t swa_bytes = (int64_t)aa[i].T * aa[i].L_swa * aa[i].H_kv * 512;
+      const int64_t key_bytes = (int64_t)ia.T * ia.max_pages * CSA2_PAGE * 128;
+      g_fork_early = armed && !forked && aa[i].q_swa != nullptr && swa_bytes >= key_bytes;
       if (L[i].mode == CSA2_REINDEX_POOL)   // the pool of layer 0's (Full) selection
         st = run_index_pool_split(&ia, L[0].idx_out, g->K, ws, s, [&] { return swa_now(i, true); });
       else
         st = run_index_split(&ia, ws, s, [&] { return swa_now(i, true); });
       g_stop_next = nullptr;
+      g_fork_early = false;
     } else {
       st = swa_now(i, false);
     }

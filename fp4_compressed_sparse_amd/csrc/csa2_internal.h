@@ -40,6 +40,9 @@ struct IdxScoreParams {
   uint32_t* clear;                     // optional: words zeroed by the first blocks
   int clear_words;
   uint32_t* trash;                     // row-tiled scoring: 1 KB that masked stores hit
+  // per-row scoring: this launch runs workgroups [block0, block_end) of the T * chunks
+  // (block_end 0: to the last)
+  int block0 = 0, block_end = 0;
   // pooled scoring (hierarchical indexer): score the 8-entry blocks of the selections
   // pool_sel [T, pool_K] instead of every visible entry; key slot 8i + o = entry o of the
   // block of selection i (chunks then counts workgroups of kPoolSelPerBlock selections)
@@ -168,6 +171,17 @@ struct AppendParams {
 
 // ---------------------------------------------------------------- launch geometry
 constexpr int kIdxChunk = 2048;        // entries scored per workgroup (whole pages)
+// Per-row scoring that a side branch forks off: the first launch runs all but the last
+// kScoreForkTail rounds of one workgroup per CU (whole rounds, so that neither launch ends
+// on a partly filled round), and records the fork event; the rest follows in a second
+// launch while the side branch starts.  Only for grids of kScoreForkMinRounds rounds or
+// more; returns 0 (one launch) otherwise.
+constexpr int kScoreForkTail = 1;
+constexpr int kScoreForkMinRounds = 4;
+inline int64_t score_fork_blocks(int64_t nblk, int cus) {
+  if (cus <= 0 || nblk < (int64_t)kScoreForkMinRounds * cus) return 0;
+  return (nblk / cus - kScoreForkTail) * cus;
+}
 constexpr int kIdxGemmMinRows = 256;   // from this many rows, scoring runs row-tiled
 // Row-tiled rows of at least kCandMinKeys keys select through sampled candidates: the keys
 // of every page_gap-th page (at most kSamplePages pages) set a per-row threshold, the

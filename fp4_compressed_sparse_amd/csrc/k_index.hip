@@ -88,8 +88,9 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
   // zero a workspace area for the Top-K that follows
   for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
     p.clear[i] = 0u;
-  const int t = blockIdx.x / p.chunks;
-  const int c = blockIdx.x - t * p.chunks;
+  const int blk = (int)blockIdx.x + p.block0;
+  const int t = blk / p.chunks;
+  const int c = blk - t * p.chunks;
   const int nv = p.n_vis[t];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j_begin = c * kIdxChunk + wave * kIdxPerWave;
@@ -1843,7 +1844,8 @@ hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
     if (p.gemm_mode == kGemmCand) return launch_idx_gemm<kGemmCand>(p, blocks, s);
     return launch_idx_gemm<kGemmKeys>(p, blocks, s);
   }
-  const int64_t blocks = (int64_t)p.T * p.chunks;
+  const int64_t blocks = (p.block_end > 0 ? (int64_t)p.block_end : (int64_t)p.T * p.chunks) - p.block0;
+  if (blocks <= 0) return hipSuccess;
   if (p.pool_sel) CSA2_LAUNCH(idx_pool_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   else CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   return hipGetLastError();
