@@ -32,21 +32,40 @@ constexpr int kIdxPerWave = kIdxChunk / kIdxWaves;   // entries per wave (whole 
 constexpr int kIdxPagesPerWave = kIdxPerWave / kPage;
 static_assert(kIdxPagesPerWave <= 64, "one page-table entry per lane");
 
-// Keys of one 64-entry page for the MFMA B operand: group u (entries 16u .. 16u+15 of the
-// page), lane (g, n) holds entry 16u + n, channels [16g, 16g+8) and [16g+8, 16g+16).  The
-// keys are streamed once per step: non-temporal loads.
+// Keys of one 64-entry page for the MFMA B operands.  MFMA pair u covers entries 16u ..
+// 16u+15: in its first operand lane (g, n) holds entry 16u + n, channels [8g, 8g+8), in the
+// second the same entry, channels [32+8g, 40+8g) (the query operands use the same channel
+// order).  Loaded as is, every load instruction would read 64 bytes of each of 16 rows,
+// and the rows' halves would reach HBM as separate 64-byte requests (measured: the decode
+// scoring at 5.0 TB/s where a plain read of as many bytes runs at 6.6).  So each
+// instruction reads 8 whole rows instead, 1 KB contiguous: instruction 2u rows 16u + e,
+// 2u+1 rows 16u + 8 + e (e = n & 7), lane (g, n) taking the 16-byte piece g or 4 + g that
+// idx_key_operands needs; loads are masked per row.  Streamed once per step: non-temporal.
 __device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, int valid,
                                               int n, int g, u32x4 (&kb)[8]) {
+  const int e = n & 7;
+  const int cA = (n < 8) ? g : 4 + g, cB = (n < 8) ? 4 + g : g;
+  const uint16_t* pg = k_idx + (int64_t)page * kPage * kDidx;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (16 * u + n < valid) {
-      const uint16_t* kp = k_idx + ((int64_t)page * kPage + 16 * u + n) * kDidx + 16 * g;
-      kb[2 * u] = ld_global_16_nt(kp);
-      kb[2 * u + 1] = ld_global_16_nt(kp + 8);
-    } else {
-      kb[2 * u] = u32x4{0u, 0u, 0u, 0u};
-      kb[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int rA = 16 * u + e, rB = 16 * u + 8 + e;
+    kb[2 * u] = (rA < valid) ? ld_global_16_nt(pg + rA * kDidx + 8 * cA) : u32x4{0u, 0u, 0u, 0u};
+    kb[2 * u + 1] = (rB < valid) ? ld_global_16_nt(pg + rB * kDidx + 8 * cB) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// The loaded pieces of pair u -> its two MFMA operands.  Lane (g, n) holds, from
+// instruction A (rows 16u + e) the piece (row 16u + e, channels 8cA..), from B (row 16u + 8
+// + e, channels 8cB..).  First operand: lanes n < 8 keep A, lanes n >= 8 keep B.  Second:
+// lane n takes the other instruction's piece of lane n ^ 8 of its 16-lane row (a DPP
+// rotation by 8), which holds row 16u + n, channels 32 + 8g.
+__device__ __forceinline__ void idx_key_operands(bool lo, const u32x4& a, const u32x4& b,
+                                                 u32x4& k0, u32x4& k1) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    k0[d] = lo ? a[d] : b[d];
+    const uint32_t y = lo ? b[d] : a[d];
+    k1[d] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, 0x128, 0xf, 0xf, false);  // row_ror:8
   }
 }
 
@@ -57,13 +76,16 @@ __device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, i
 // lane (g, n) with the whole sum of entry 16g + n, so the page's 64 keys go out in one
 // store.
 __device__ __forceinline__ float idx_score_64(const u32x4& qa0, const u32x4& qa1,
-                                              const float (&w)[4], const u32x4 (&kb)[8]) {
+                                              const float (&w)[4], const u32x4 (&kb)[8],
+                                              int n) {
   float su[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
+    u32x4 k0, k1;
+    idx_key_operands(n < 8, kb[2 * u], kb[2 * u + 1], k0, k1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa0), as_bf16x8(kb[2 * u]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa1), as_bf16x8(kb[2 * u + 1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa0), as_bf16x8(k0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa1), as_bf16x8(k1), acc, 0, 0, 0);
     float s = w[0] * relu_f32(acc[0]);
     s += w[1] * relu_f32(acc[1]);
     s += w[2] * relu_f32(acc[2]);
@@ -105,9 +127,9 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
 
   u32x4 qa0 = {0u, 0u, 0u, 0u}, qa1 = {0u, 0u, 0u, 0u};
   if (n < p.H_I) {
-    const uint16_t* qp = p.q_idx + ((int64_t)t * p.H_I + n) * kDidx + 16 * g;
+    const uint16_t* qp = p.q_idx + ((int64_t)t * p.H_I + n) * kDidx + 8 * g;
     qa0 = ld_global_16(qp);
-    qa1 = ld_global_16(qp + 8);
+    qa1 = ld_global_16(qp + 32);
   }
   float w[4];
 #pragma unroll
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
     if (pi < npages) {                        // wave-uniform
       if (pi + 1 < npages)
         idx_load_page(p.k_idx, __shfl(my_page, pi + 1), valid_in(pi + 1), n, g, buf[(pi + 1) & 1]);
-      sc[pi] = idx_score_64(qa0, qa1, w, buf[pi & 1]);
+      sc[pi] = idx_score_64(qa0, qa1, w, buf[pi & 1], n);
     }
   }
 #pragma unroll
@@ -175,9 +197,9 @@ __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
 
   u32x4 qa0 = {0u, 0u, 0u, 0u}, qa1 = {0u, 0u, 0u, 0u};
   if (n < p.H_I) {
-    const uint16_t* qp = p.q_idx + ((int64_t)t * p.H_I + n) * kDidx + 16 * g;
+    const uint16_t* qp = p.q_idx + ((int64_t)t * p.H_I + n) * kDidx + 8 * g;
     qa0 = ld_global_16(qp);
-    qa1 = ld_global_16(qp + 8);
+    qa1 = ld_global_16(qp + 32);
   }
   float w[4];
 #pragma unroll
@@ -188,21 +210,21 @@ __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
   uint32_t* keys = p.keys + (int64_t)t * p.key_stride + kPoolBlock * (int64_t)i0;
   const int ngroups = min(kPoolSelPerWave / 8, (p.pool_K - i0 + 7) / 8);
 
-  // group v, MFMA column block u: lane (g, n) loads entry n & 7 of the block of
-  // selection 8v + 2u + (n >> 3) of this wave
+  // group v, MFMA pair u: column n is entry n & 7 of the block of selection 8v + 2u +
+  // (n >> 3) of this wave; as in idx_load_page, instruction 2u reads the block of selection
+  // 8v + 2u whole (1 KB) and 2u+1 that of 8v + 2u + 1, idx_key_operands then forms the
+  // operands
   auto load_group = [&](int v, u32x4 (&kb)[8]) {
+    const int e = n & 7;
+    const int cA = (n < 8) ? g : 4 + g, cB = (n < 8) ? 4 + g : g;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int src = 8 * v + 2 * u + (n >> 3);
-      const int row = __shfl(brow, src) + (n & 7);
-      if ((n & 7) < __shfl(bvis, src)) {
-        const uint16_t* kp = p.k_idx + (int64_t)row * kDidx + 16 * g;
-        kb[2 * u] = ld_global_16(kp);
-        kb[2 * u + 1] = ld_global_16(kp + 8);
-      } else {
-        kb[2 * u] = u32x4{0u, 0u, 0u, 0u};
-        kb[2 * u + 1] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int sA = 8 * v + 2 * u, sB = sA + 1;
+      const int rowA = __shfl(brow, sA) + e, rowB = __shfl(brow, sB) + e;
+      kb[2 * u] = (e < __shfl(bvis, sA)) ? ld_global_16(p.k_idx + (int64_t)rowA * kDidx + 8 * cA)
+                                         : u32x4{0u, 0u, 0u, 0u};
+      kb[2 * u + 1] = (e < __shfl(bvis, sB)) ? ld_global_16(p.k_idx + (int64_t)rowB * kDidx + 8 * cB)
+                                             : u32x4{0u, 0u, 0u, 0u};
     }
   };
   // lane (g, n) holds slot 16g + n of the group: entry n & 7 of selection 8v + 2g + (n >> 3);
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
     sc[v] = 0.f;
     if (v < ngroups) {                               // wave-uniform
       if (v + 1 < ngroups) load_group(v + 1, buf[(v + 1) & 1]);
-      sc[v] = idx_score_64(qa0, qa1, w, buf[v & 1]);
+      sc[v] = idx_score_64(qa0, qa1, w, buf[v & 1], n);
     }
   }
 #pragma unroll
