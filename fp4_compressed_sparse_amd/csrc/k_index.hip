@@ -40,17 +40,20 @@ static_assert(kIdxPagesPerWave <= 64, "one page-table entry per lane");
 // scoring at 5.0 TB/s where a plain read of as many bytes runs at 6.6).  So each
 // instruction reads 8 whole rows instead, 1 KB contiguous: instruction 2u rows 16u + e,
 // 2u+1 rows 16u + 8 + e (e = n & 7), lane (g, n) taking the 16-byte piece g or 4 + g that
-// idx_key_operands needs; loads are masked per row.  Streamed once per step: non-temporal.
-__device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, int valid,
-                                              int n, int g, u32x4 (&kb)[8]) {
+// idx_key_operands needs.  Every row of the page is read, visible or not (a page is whole
+// in memory): the scores of rows past the visible count are never stored, and loads
+// without a per-lane condition keep the loop free of branches, so that the wait for a page
+// leaves the next page's loads in flight (with masked loads the compiler waited for all).
+// Streamed once per step: non-temporal.
+__device__ __forceinline__ void idx_load_page(const uint16_t* k_idx, int page, int n, int g,
+                                              u32x4 (&kb)[8]) {
   const int e = n & 7;
   const int cA = (n < 8) ? g : 4 + g, cB = (n < 8) ? 4 + g : g;
   const uint16_t* pg = k_idx + (int64_t)page * kPage * kDidx;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int rA = 16 * u + e, rB = 16 * u + 8 + e;
-    kb[2 * u] = (rA < valid) ? ld_global_16_nt(pg + rA * kDidx + 8 * cA) : u32x4{0u, 0u, 0u, 0u};
-    kb[2 * u + 1] = (rB < valid) ? ld_global_16_nt(pg + rB * kDidx + 8 * cB) : u32x4{0u, 0u, 0u, 0u};
+    kb[2 * u] = ld_global_16_nt(pg + (16 * u + e) * kDidx + 8 * cA);
+    kb[2 * u + 1] = ld_global_16_nt(pg + (16 * u + 8 + e) * kDidx + 8 * cB);
   }
 }
 
@@ -144,17 +147,18 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
   // The scores stay in registers until the last page: a store inside the loop would sit
   // among the memory operations that each page's wait counts, so every page would also
   // wait for the previous page's store to be acknowledged.
+  // Every wave runs all kIdxPagesPerWave pages, its last page again in place of those past
+  // its run (scores not stored): straight-line code, so each page's wait leaves the next
+  // page's loads in flight.
   float sc[kIdxPagesPerWave];
   u32x4 buf[2][8];
-  idx_load_page(p.k_idx, __shfl(my_page, 0), valid_in(0), n, g, buf[0]);
+  const int last = npages - 1;
+  idx_load_page(p.k_idx, __shfl(my_page, 0), n, g, buf[0]);
 #pragma unroll
   for (int pi = 0; pi < kIdxPagesPerWave; ++pi) {
-    sc[pi] = 0.f;
-    if (pi < npages) {                        // wave-uniform
-      if (pi + 1 < npages)
-        idx_load_page(p.k_idx, __shfl(my_page, pi + 1), valid_in(pi + 1), n, g, buf[(pi + 1) & 1]);
-      sc[pi] = idx_score_64(qa0, qa1, w, buf[pi & 1], n);
-    }
+    if (pi + 1 < kIdxPagesPerWave)
+      idx_load_page(p.k_idx, __shfl(my_page, min(pi + 1, last)), n, g, buf[(pi + 1) & 1]);
+    sc[pi] = idx_score_64(qa0, qa1, w, buf[pi & 1], n);
   }
 #pragma unroll
   for (int pi = 0; pi < kIdxPagesPerWave; ++pi)
@@ -221,10 +225,8 @@ __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
     for (int u = 0; u < 4; ++u) {
       const int sA = 8 * v + 2 * u, sB = sA + 1;
       const int rowA = __shfl(brow, sA) + e, rowB = __shfl(brow, sB) + e;
-      kb[2 * u] = (e < __shfl(bvis, sA)) ? ld_global_16(p.k_idx + (int64_t)rowA * kDidx + 8 * cA)
-                                         : u32x4{0u, 0u, 0u, 0u};
-      kb[2 * u + 1] = (e < __shfl(bvis, sB)) ? ld_global_16(p.k_idx + (int64_t)rowB * kDidx + 8 * cB)
-                                             : u32x4{0u, 0u, 0u, 0u};
+      kb[2 * u] = ld_global_16(p.k_idx + (int64_t)rowA * kDidx + 8 * cA);
+      kb[2 * u + 1] = ld_global_16(p.k_idx + (int64_t)rowB * kDidx + 8 * cB);
     }
   };
   // lane (g, n) holds slot 16g + n of the group: entry n & 7 of selection 8v + 2g + (n >> 3);
@@ -232,14 +234,13 @@ __global__ __launch_bounds__(256) void idx_pool_score_kernel(IdxScoreParams p) {
   constexpr int kGroups = kPoolSelPerWave / 8;
   float sc[kGroups];
   u32x4 buf[2][8];
+  // all kGroups groups, straight-line (a group past the wave's selections reads rows 0..7
+  // and is not stored), so that each group's wait leaves the next group's loads in flight
   load_group(0, buf[0]);
 #pragma unroll
   for (int v = 0; v < kGroups; ++v) {
-    sc[v] = 0.f;
-    if (v < ngroups) {                               // wave-uniform
-      if (v + 1 < ngroups) load_group(v + 1, buf[(v + 1) & 1]);
-      sc[v] = idx_score_64(qa0, qa1, w, buf[v & 1], n);
-    }
+    if (v + 1 < kGroups) load_group(v + 1, buf[(v + 1) & 1]);
+    sc[v] = idx_score_64(qa0, qa1, w, buf[v & 1], n);
   }
 #pragma unroll
   for (int v = 0; v < kGroups; ++v) {
