@@ -155,26 +155,44 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   constexpr int D = kLat + kRope;                    // channels per token
   const float* c = p.c + e * 4 * D;
   const float* z = p.z + e * 4 * D;
-  float cl[4][8], zl[4][8], cr[4], zr[4];
+  // Latent loads read whole lines: each instruction 1 KB contiguous, lane l channels 4l ..
+  // 4l+3 (h = 0) or 256 + 4l .. (h = 1).  (Eight channels per lane straight from memory put
+  // 16-byte pieces 32 bytes apart, so every line reached HBM in 64-byte halves.)
+  float cl[4][2][4], zl[4][2][4], cr[4], zr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f32x4* cp = reinterpret_cast<const f32x4*>(c + i * D + 8 * lane);
-    const f32x4* zp = reinterpret_cast<const f32x4*>(z + i * D + 8 * lane);
-    const f32x4 c0 = cp[0], c1 = cp[1], z0 = zp[0], z1 = zp[1];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      cl[i][k] = c0[k]; cl[i][4 + k] = c1[k];
-      zl[i][k] = z0[k]; zl[i][4 + k] = z1[k];
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 c4 = *reinterpret_cast<const f32x4*>(c + i * D + 256 * h + 4 * lane);
+      const f32x4 z4 = *reinterpret_cast<const f32x4*>(z + i * D + 256 * h + 4 * lane);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cl[i][h][k] = c4[k];
+        zl[i][h][k] = z4[k];
+      }
     }
     cr[i] = c[i * D + kLat + lane];
     zr[i] = z[i * D + kLat + lane];
   }
+  float yh[2][4];                                    // pooled channels 256h + 4l + k
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float zk[4] = {zl[0][h][k], zl[1][h][k], zl[2][h][k], zl[3][h][k]};
+      const float ck[4] = {cl[0][h][k], cl[1][h][k], cl[2][h][k], cl[3][h][k]};
+      yh[h][k] = pool4(zk, ck);
+    }
+  // the encoder's layout, lane l channels 8l .. 8l+7: lanes 2l' and 2l'+1 (l' = l mod 32)
+  // of half l / 32
+  const bool hi = lane >= 32;
+  const int s0 = (2 * lane) & 63;
   float y[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float zk[4] = {zl[0][k], zl[1][k], zl[2][k], zl[3][k]};
-    const float ck[4] = {cl[0][k], cl[1][k], cl[2][k], cl[3][k]};
-    y[k] = pool4(zk, ck);
+    const int src = s0 + (k >> 2);
+    const float a = __shfl(yh[0][k & 3], src), b = __shfl(yh[1][k & 3], src);
+    y[k] = hi ? b : a;
   }
   int X;
   const uint32_t word = mxfp4_encode_lane(y, X);
