@@ -922,6 +922,39 @@ def test_layer_group_pooled_reindex(csa2, dev):
     np.testing.assert_array_equal(res[2]["idx"], res[1]["idx"])
 
 
+def test_index_ignores_keys_past_visible(csa2, dev):
+    """The scoring reads whole pages (and, pooled, whole 8-entry blocks), visible or not:
+    key rows past a sequence's visible count may hold anything, NaN and huge values
+    included, and the selections do not change.  Visible counts end inside a page, inside
+    an 8-entry block and at a page edge."""
+    _say("index_ignores_keys_past_visible")
+    w = W(name="tailpoison", B=3, T=3, E=1536, K=300, H_I=8, seq_id_rows=[0, 1, 2],
+          n_vis_rows=[1003, 704, 33], shuffle=True, modes=[0, 3])
+    d = tl.DeviceWorkload(w, dev)
+    L = d.layers[1]
+    sel = torch.from_numpy(w.selection(256)).to(dev)
+    args = (L["q_idx"], L["w_idx"], L["k_idx"], d.page_table, d.seq_id, d.n_vis, w.K)
+
+    def run():
+        a = csa2.index_topk(*args)
+        b = csa2.index_topk_pool(*args, sel)
+        torch.cuda.synchronize()
+        return a.cpu().numpy(), b.cpu().numpy()
+
+    before = run()
+    pt = w.page_table()
+    kv = L["k_idx"].view(-1, 64).view(torch.int16)
+    rng = np.random.default_rng(5)
+    for b, nv in enumerate(w.n_vis()):
+        rows = w.physical_rows(b, pt)[int(nv):]
+        junk = rng.choice(np.array([0x7fc0, 0xffc0, 0x7f7f, 0xff7f, 0x7f80], np.uint16),
+                          size=(rows.size, 64)).view(np.int16)
+        kv[torch.from_numpy(rows).to(dev)] = torch.from_numpy(junk).to(dev)
+    after = run()
+    np.testing.assert_array_equal(after[0], before[0])
+    np.testing.assert_array_equal(after[1], before[1])
+
+
 def test_determinism(csa2, dev):
     _say("determinism")
     w = W(B=4, T=8, E=4096, K=1024, H=64, seq_id_rows=[0, 1, 2, 3, 3, 2, 1, 0])
