@@ -262,8 +262,11 @@ csa2_status validate_index(const csa2_index_args* a) {
 }
 
 // Indexer scoring, then Top-K; `between` runs after the scoring launch.
+// fuse_swa: a small SWA branch of the same rows, run inside the per-row scoring's launch
+// (swa_blocks workgroups) instead of on the side stream.
 template <class Between>
-csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, Between&& between) {
+csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, Between&& between,
+                            const SwaParams* fuse_swa = nullptr, int swa_blocks = 0) {
   if (a->T == 0) return between();
   const int64_t E = (int64_t)a->max_pages * CSA2_PAGE;
   IdxScoreParams sp;
@@ -366,7 +369,9 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   }
   const int64_t n1 = (g_stop_next && g_fork_early && sp.T < kIdxGemmMinRows)   // per-row kernel
                          ? score_fork_blocks((int64_t)sp.T * sp.chunks, device_cus()) : 0;
-  if (n1 > 0) {
+  if (fuse_swa && sp.T < kIdxGemmMinRows) {
+    st = timed("idx_score", s, [&] { return launch_idx_score_swa(sp, *fuse_swa, swa_blocks, s); });
+  } else if (n1 > 0) {
     // the side branch's start latency overlaps the last round of the scoring
     IdxScoreParams a1 = sp, a2 = sp;
     a1.block_end = (int)n1;
@@ -520,11 +525,11 @@ csa2_status validate_attn(const csa2_attn_args* a) {
   return CSA2_OK;
 }
 
-csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
+csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s, bool swa_beside = true) {
   if (a->T == 0) return CSA2_OK;
   // with an SWA branch on persistent workgroups beside it, plan for the CUs they leave
   const int cus = device_cus();
-  const int swa_wgs = a->q_swa ? swa_persist_wgs(a->T, a->H, a->H_kv, cus) : 0;
+  const int swa_wgs = (a->q_swa && swa_beside) ? swa_persist_wgs(a->T, a->H, a->H_kv, cus) : 0;
   int S, per;
   attn_plan(a->T, a->H, a->K, &S, &per, cus - swa_wgs);
   AttnParams ap;
@@ -564,29 +569,29 @@ csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s) {
   return CSA2_OK;
 }
 
+SwaParams swa_params(const csa2_attn_args* a) {
+  SwaParams wp;
+  wp.T = a->T;
+  wp.H = a->H;
+  wp.H_kv = a->H_kv;
+  wp.L_swa = a->L_swa;
+  wp.sm_scale_log2 = a->sm_scale_swa * 1.4426950408889634f;
+  wp.q_swa = static_cast<const uint16_t*>(a->q_swa);
+  wp.k = static_cast<const uint16_t*>(a->swa_k);
+  wp.v = static_cast<const uint16_t*>(a->swa_v);
+  wp.seq_id = a->seq_id;
+  wp.start = a->swa_start;
+  wp.len = a->swa_len;
+  wp.o = a->o_swa;
+  wp.lse = a->lse_swa;
+  wp.wgs = swa_persist_wgs(a->T, a->H, a->H_kv, device_cus());
+  return wp;
+}
+
 csa2_status run_swa(const csa2_attn_args* a, hipStream_t s) {
   if (a->T == 0 || !a->q_swa) return CSA2_OK;
-  csa2_status st;
-  {
-    SwaParams wp;
-    wp.T = a->T;
-    wp.H = a->H;
-    wp.H_kv = a->H_kv;
-    wp.L_swa = a->L_swa;
-    wp.sm_scale_log2 = a->sm_scale_swa * 1.4426950408889634f;
-    wp.q_swa = static_cast<const uint16_t*>(a->q_swa);
-    wp.k = static_cast<const uint16_t*>(a->swa_k);
-    wp.v = static_cast<const uint16_t*>(a->swa_v);
-    wp.seq_id = a->seq_id;
-    wp.start = a->swa_start;
-    wp.len = a->swa_len;
-    wp.o = a->o_swa;
-    wp.lse = a->lse_swa;
-    wp.wgs = swa_persist_wgs(a->T, a->H, a->H_kv, device_cus());
-    st = timed("swa", s, [&] { return launch_swa(wp, s); });
-    if (st) return st;
-  }
-  return CSA2_OK;
+  const SwaParams wp = swa_params(a);
+  return timed("swa", s, [&] { return launch_swa(wp, s); });
 }
 
 // The global branch on `s` and the SWA branches of `a[0..n)` on the side stream (on `s`
@@ -804,40 +809,56 @@ csa2_status layer_group_run(const csa2_layer_desc* L, int32_t n_layers,
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   const bool capturing =
       sd && hipStreamIsCapturing(s, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
+  bool fused[kMaxGroupLayers] = {};
   for (int i = 0; i < n_layers && !st; ++i) {
     if (L[i].mode != CSA2_REUSE) {
       ia.q_idx = L[i].q_idx;
       ia.w_idx = L[i].w_idx;
       ia.k_idx = L[i].k_idx;
       ia.idx_out = L[i].idx_out;
-      armed = sd && !capturing;
-      if (armed) g_stop_next = sd->fork;
-      // The scoring forks the side branch before its last round when that branch is idle
-      // and likely the longer one after the scoring: its K and V windows (at most L_swa
-      // positions, 128 bf16 channels per KV head) are at least as many bytes as the
-      // indexer keys the scoring reads (64 bf16 per entry).  (Measured: the 64 x 128K
-      // decode step -3%; a 32 x 256K group, whose side branch reads half the scoring's
-      // bytes, +1.5% with the early fork, so there it stays at the scoring's end.)
+      // The SWA branch reads its K and V windows (at most L_swa positions, 128 bf16
+      // channels per KV head), the scoring 64 bf16 of indexer key per entry.
       const int64_t swa_bytes = (int64_t)aa[i].T * aa[i].L_swa * aa[i].H_kv * 512;
       const int64_t key_bytes = (int64_t)ia.T * ia.max_pages * CSA2_PAGE * 128;
+      // A branch of at most a quarter of the scoring's bytes runs inside the per-row
+      // scoring's launch: the scoring's own time then covers most of it, and the fork and
+      // join events (about 6 us a step) go away (4 x 1M decode 0.0765 -> 0.0723 ms).  Not
+      // while kernels are timed one by one.
+      fused[i] = !g_timing.on && L[i].mode != CSA2_REINDEX_POOL && aa[i].q_swa != nullptr &&
+                 aa[i].T > 0 && aa[i].T < kIdxGemmMinRows && aa[i].H == aa[i].H_kv &&
+                 swa_persist_wgs(aa[i].T, aa[i].H, aa[i].H_kv, device_cus()) > 0 &&
+                 4 * swa_bytes <= key_bytes;
+      armed = sd && !capturing && !fused[i];
+      if (armed) g_stop_next = sd->fork;
+      // The scoring forks the side branch before its last round when that branch is idle
+      // and likely the longer one after the scoring: at least the scoring's bytes.
+      // (Measured: the 64 x 128K decode step -3%; a 32 x 256K group, whose side branch
+      // reads half the scoring's bytes, +1.5% with the early fork, so there it stays at
+      // the scoring's end.)
       g_fork_early = armed && !forked && aa[i].q_swa != nullptr && swa_bytes >= key_bytes;
-      if (L[i].mode == CSA2_REINDEX_POOL)   // the pool of layer 0's (Full) selection
+      if (fused[i]) {
+        const SwaParams wp = swa_params(&aa[i]);
+        const int blocks = (int)std::min<int64_t>(((int64_t)aa[i].T * aa[i].H_kv + 3) / 4, 1024);
+        st = run_index_split(&ia, ws, s, [] { return CSA2_OK; }, &wp, blocks);
+      } else if (L[i].mode == CSA2_REINDEX_POOL) {   // the pool of layer 0's (Full) selection
         st = run_index_pool_split(&ia, L[0].idx_out, g->K, ws, s, [&] { return swa_now(i, true); });
-      else
+      } else {
         st = run_index_split(&ia, ws, s, [&] { return swa_now(i, true); });
+      }
       g_stop_next = nullptr;
       g_fork_early = false;
     } else {
       st = swa_now(i, false);
     }
-    if (!st) st = run_attn(&aa[i], ws, s);
+    if (!st) st = run_attn(&aa[i], ws, s, !fused[i]);
   }
   if (forked) {
     csa2_status sj = join_from(sd, s);
     if (!st) st = sj;
   }
   if (!sd)
-    for (int i = 0; i < n_layers && !st; ++i) st = run_swa(&aa[i], s);
+    for (int i = 0; i < n_layers && !st; ++i)
+      if (!fused[i]) st = run_swa(&aa[i], s);
   return st ? st : st_swa;
 }
 

@@ -264,6 +264,8 @@ csa2_status set_error(csa2_status st, const char* msg);
 // ---------------------------------------------------------------- launchers
 // Each launcher enqueues one kernel on `s` and returns hipGetLastError().
 hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s);
+hipError_t launch_idx_score_swa(const IdxScoreParams& p, const SwaParams& w, int swa_blocks,
+                                hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_topk_thr(const TopkParams& p, hipStream_t s);
 hipError_t launch_topk_cand(const TopkParams& p, hipStream_t s);

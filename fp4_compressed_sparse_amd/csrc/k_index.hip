@@ -24,6 +24,7 @@
 
 #include "csa2_internal.h"
 #include "csa2_device.h"
+#include "csa2_swa_wave.h"
 
 namespace csa2 {
 
@@ -109,11 +110,7 @@ __device__ __forceinline__ float idx_score_64(const u32x4& qa0, const u32x4& qa1
 // pages.  The wave resolves its pages' physical numbers once (one page-table entry per
 // lane, broadcast by shuffle) and keeps the next page's 8 KB of keys in flight while it
 // scores the current one; the run's keys are stored at its end.
-__global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
-  // zero a workspace area for the Top-K that follows
-  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
-    p.clear[i] = 0u;
-  const int blk = (int)blockIdx.x + p.block0;
+__device__ __forceinline__ void idx_score_block(const IdxScoreParams& p, int blk) {
   const int t = blk / p.chunks;
   const int c = blk - t * p.chunks;
   const int nv = p.n_vis[t];
@@ -163,6 +160,31 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
 #pragma unroll
   for (int pi = 0; pi < kIdxPagesPerWave; ++pi)
     if (pi < npages && 16 * g + n < valid_in(pi)) keys[kPage * pi + 16 * g + n] = float_key(sc[pi]);
+}
+
+// zero a workspace area for the Top-K that follows (every workgroup of the launch takes part)
+__device__ __forceinline__ void idx_clear(const IdxScoreParams& p) {
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < p.clear_words; i += (int)gridDim.x * 256)
+    p.clear[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
+  idx_clear(p);
+  idx_score_block(p, (int)blockIdx.x + p.block0);
+}
+
+// The same scoring with a small SWA branch of the same rows in one launch (no second stream,
+// so no fork and join events): workgroups 0 .. swa_blocks-1 run the window attention, one
+// (row, KV head) unit per wave in turn, and the rest score.  The branch's bytes are a small
+// share of the scoring's, so it costs the launch little.
+__global__ __launch_bounds__(256) void idx_score_swa_kernel(IdxScoreParams p, SwaParams w,
+                                                           int swa_blocks) {
+  idx_clear(p);
+  if ((int)blockIdx.x < swa_blocks) {                // workgroup-uniform
+    swa_wave_units<1>(w, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), swa_blocks * 4);
+    return;
+  }
+  idx_score_block(p, (int)blockIdx.x - swa_blocks + p.block0);
 }
 
 // ---------------------------------------------------------------- pooled scoring
@@ -1871,6 +1893,13 @@ hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (p.pool_sel) CSA2_LAUNCH(idx_pool_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
   else CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_idx_score_swa(const IdxScoreParams& p, const SwaParams& w, int swa_blocks,
+                                hipStream_t s) {
+  const int64_t blocks = (int64_t)p.T * p.chunks + swa_blocks;
+  CSA2_LAUNCH(idx_score_swa_kernel, dim3((unsigned)blocks), dim3(256), s, p, w, swa_blocks);
   return hipGetLastError();
 }
 

@@ -1051,6 +1051,16 @@ def test_layer_group_e4m3_group_small(csa2, dev):
     _group_case(csa2, dev, w, np.arange(4), "group_small_e4m3", fmt=1)
 
 
+def test_layer_group_swa_in_scoring_launch(csa2, dev):
+    """A small SWA branch (at most a quarter of the scoring's bytes) runs inside the per-row
+    scoring's launch: the Full and Reindex layers' branches that way, the Reuse layer's on
+    the side stream; ragged windows, an empty window, ragged visible counts."""
+    w = W(name="swa_fused", B=3, T=4, E=8192, K=256, H=16, H_I=8, H_kv=16, L_swa=32,
+          seq_id_rows=[0, 1, 2, 1], n_vis_rows=[8192, 5000, 777, 6001],
+          swa_start_rows=[0, 3, 31, 10], swa_len_rows=[32, 29, 1, 0], modes=[0, 1, 2])
+    _group_case(csa2, dev, w, np.arange(4), "swa_fused")
+
+
 def test_full_size_decode_4x1m(csa2, dev):
     w = synth.workload(4)
     _group_case(csa2, dev, w, np.arange(4), w.name)
