@@ -54,6 +54,9 @@ def parse_args():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra lines for the 1M-context decode and the chunked "
                          "prefill workloads")
+    ap.add_argument("--kv-layout", default="planes", choices=("packed", "planes"),
+                    help="main-KV cache rows: three dense planes (the default) or packed "
+                         "(one 400-byte row per entry, 416 with E4M3 scales)")
     ap.add_argument("--kv-format", type=int, default=0, choices=(0, 1),
                     help="main-KV cache format of the timed workload: 0 = MXFP4 (E8M0 per 32), "
                          "1 = E2M1 with an E4M3 scale per 16 channels")
@@ -86,6 +89,7 @@ class Inputs:
         import numpy as np
         import torch
         from fp4_compressed_sparse_amd import csa2
+        row_bytes = 0
         self.w, self.dev, self.csa2 = w, dev, csa2
         pt = w.page_table()
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -118,6 +122,14 @@ class Inputs:
                     quant(t(w.latent_seq(b, li)), lat, scl, dst)
                     rope.view(-1, 64)[dst] = b16(w.rope_seq(b, li))
                 L["kv_lat"], L["kv_scl"], L["kv_rope"] = lat, scl, rope
+                if KV_LAYOUT == "packed":         # one row per entry: codes | rope | scales
+                    buf, plat, pscl, prope, row_bytes = csa2.kv_packed(w.n_pages, fmt, dev)
+                    plat.copy_(lat)
+                    pscl.copy_(scl)
+                    prope.copy_(rope)
+                    del lat, scl, rope
+                    L["kv_buf"] = buf
+                    L["kv_lat"], L["kv_scl"], L["kv_rope"] = plat, pscl, prope
             L["o"] = torch.empty((w.T, w.H, 512), dtype=torch.float32, device=dev)
             L["lse"] = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
             L["o_swa"] = torch.empty((w.T, w.H, 128), dtype=torch.float32, device=dev)
@@ -125,7 +137,7 @@ class Inputs:
             self.layers.append(L)
         self.g = csa2.group_args(w.T, w.B, w.H, w.H_I, w.K, w.H_kv, w.L_swa, w.P, w.n_pages,
                                  self.page_table, self.seq_id, self.n_vis, self.swa_start,
-                                 self.swa_len, kv_format=fmt)
+                                 self.swa_len, kv_format=fmt, kv_row_bytes=row_bytes)
         self.descs = [csa2.layer_desc(
             L["mode"], L["q"], L["o"], L["lse"], q_swa=L["q_swa"], q_idx=L.get("q_idx"),
             w_idx=L.get("w_idx"), k_idx=L.get("k_idx"), kv_lat=L.get("kv_lat"),
@@ -141,6 +153,7 @@ class Inputs:
 
 
 LLC_BYTES = 256 << 20                        # MI355X last-level cache (Infinity Cache)
+KV_LAYOUT = "planes"                         # main-KV rows of the timed inputs (--kv-layout)
 
 
 def input_copies(w, fmt=0):
@@ -222,7 +235,8 @@ def graph_probe_child(workload, steps):
         return None
     try:
         r = subprocess.run([sys.executable, os.path.abspath(__file__), "--graph-probe",
-                            "--workload", str(workload), "--steps", str(steps)],
+                            "--workload", str(workload), "--steps", str(steps),
+                            "--kv-layout", KV_LAYOUT],
                            capture_output=True, text=True, timeout=300)
         lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
         if r.returncode != 0 or not lines:
@@ -334,6 +348,7 @@ def measure_extra(w, dev, steps, warmup, flush_mb, fmt=0):
     out = {"workload": w.name, "query_rows": w.T, "entries_per_seq": w.E, "top_k": w.K,
            "input_copies": len(sets),
            "kv_format": "E2M1 + E4M3 per 16" if fmt else "MXFP4 (E2M1 + E8M0 per 32)",
+           "kv_layout": KV_LAYOUT,
            "layers": [["full", "reindex", "reuse", "reindex_pool"][m] for m in w.modes],
            "steps": steps, "ms_per_step": round(ms, 4),
            "query_tokens_per_s": round(w.T / (ms * 1e-3), 1),
@@ -622,6 +637,8 @@ def measure_peaks():
 # ------------------------------------------------------------------ main
 def main():
     args = parse_args()
+    global KV_LAYOUT
+    KV_LAYOUT = args.kv_layout
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the hot path shards by sequence with no "
               f"exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -794,6 +811,7 @@ def main():
                    "indexer_heads": w.H_I, "swa_window": w.n_win, "swa_kv_heads": w.H_kv,
                    "kv_format": ("E2M1 + E4M3 per 16" if args.kv_format else
                                  "MXFP4 (E2M1, E8M0 per 32)") + " latent 512 + bf16 rope 64",
+                   "kv_layout": KV_LAYOUT,
                    "layers": [["full", "reindex", "reuse", "reindex_pool"][m] for m in w.modes],
                    "parallelism": "single GPU"},
         "step_algo_bytes": step_bytes,

@@ -41,7 +41,7 @@ class PoolArgs(ctypes.Structure):
 class AppendArgs(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("c", _vp), ("z", _vp), ("c_idx", _vp), ("z_idx", _vp),
                 ("dst_row", _vp), ("kv_lat", _vp), ("kv_scl", _vp), ("kv_rope", _vp),
-                ("k_idx", _vp)]
+                ("k_idx", _vp), ("kv_row_bytes", _i32)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -51,7 +51,7 @@ class AttnArgs(ctypes.Structure):
                 ("sm_scale", _f32), ("o", _vp), ("lse", _vp), ("H_kv", _i32), ("L_swa", _i32),
                 ("q_swa", _vp), ("swa_k", _vp), ("swa_v", _vp), ("swa_start", _vp),
                 ("swa_len", _vp), ("sm_scale_swa", _f32), ("o_swa", _vp), ("lse_swa", _vp),
-                ("kv_format", _i32)]
+                ("kv_format", _i32), ("kv_row_bytes", _i32)]
 
 
 class LayerDesc(ctypes.Structure):
@@ -66,7 +66,7 @@ class GroupArgs(ctypes.Structure):
                 ("H_kv", _i32), ("L_swa", _i32), ("max_pages", _i32), ("n_pages", _i32),
                 ("page_table", _vp), ("seq_id", _vp), ("n_vis", _vp), ("swa_start", _vp),
                 ("swa_len", _vp), ("sm_scale", _f32), ("sm_scale_swa", _f32),
-                ("kv_format", _i32)]
+                ("kv_format", _i32), ("kv_row_bytes", _i32)]
 
 
 EXPORTS = ["csa2_index_topk", "csa2_index_topk_pool", "csa2_sparse_attn_fp4", "csa2_layer_group", "csa2_layer_group_noalloc", "csa2_mxfp4_quantize", "csa2_kv_append", "csa2_fp4e4m3_quantize",
@@ -91,11 +91,11 @@ def _load():
     L.csa2_layer_group_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _i32,
                                            ctypes.POINTER(GroupArgs), _vp]
     L.csa2_fp4e4m3_quantize.restype = _i32
-    L.csa2_fp4e4m3_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]
+    L.csa2_fp4e4m3_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _i32, _vp]
     L.csa2_kv_append.restype = _i32
     L.csa2_kv_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
     L.csa2_mxfp4_quantize.restype = _i32
-    L.csa2_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]
+    L.csa2_mxfp4_quantize.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp, _i32, _vp]
     L.csa2_workspace_bytes.restype = ctypes.c_size_t
     L.csa2_workspace_bytes.argtypes = [_i32, _vp]
     L.csa2_last_error.restype = ctypes.c_char_p
@@ -192,7 +192,7 @@ def index_topk_pool(q_idx, w_idx, k_idx, page_table, seq_id, n_vis, K, sel, idx_
 
 def attn_args(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, o, lse, sm_scale=None,
               q_swa=None, swa_k=None, swa_v=None, swa_start=None, swa_len=None,
-              sm_scale_swa=None, o_swa=None, lse_swa=None, kv_format=KV_MXFP4):
+              sm_scale_swa=None, o_swa=None, lse_swa=None, kv_format=KV_MXFP4, kv_row_bytes=0):
     T, H = q.shape[0], q.shape[1]
     K = idx.shape[1]
     if sm_scale is None:
@@ -205,14 +205,16 @@ def attn_args(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, o, lse, sm_sc
                     _p(q), _p(kv_lat), _p(kv_scl), _p(kv_rope), _p(page_table), _p(seq_id),
                     _p(idx), sm_scale, _p(o), _p(lse), H_kv, L_swa, _p(q_swa), _p(swa_k),
                     _p(swa_v), _p(swa_start), _p(swa_len), sm_scale_swa, _p(o_swa), _p(lse_swa),
-                    kv_format)
+                    kv_format, kv_row_bytes)
 
 
 def sparse_attn_fp4(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, sm_scale=None,
                     q_swa=None, swa_k=None, swa_v=None, swa_start=None, swa_len=None,
-                    sm_scale_swa=None, stream=None, out=None, kv_format=KV_MXFP4):
+                    sm_scale_swa=None, stream=None, out=None, kv_format=KV_MXFP4,
+                    kv_row_bytes=0):
     """Sparse FP4 global attention (+ SWA when q_swa is given).
-    kv_lat u8 [n_pages, 64, 256]; kv_scl u8 [n_pages, 64, 16]; kv_rope bf16 [n_pages, 64, 64].
+    kv_lat u8 [n_pages, 64, 256]; kv_scl u8 [n_pages, 64, 16]; kv_rope bf16 [n_pages, 64, 64]:
+    dense planes (kv_row_bytes 0) or views of one packed buffer (see kv_packed).
     Returns (o, lse) or (o, lse, o_swa, lse_swa)."""
     T, H = q.shape[0], q.shape[1]
     dev = q.device
@@ -224,7 +226,7 @@ def sparse_attn_fp4(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, sm_scal
             out["lse_swa"] = torch.empty((T, H), dtype=torch.float32, device=dev)
     a = attn_args(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, out["o"], out["lse"],
                   sm_scale, q_swa, swa_k, swa_v, swa_start, swa_len, sm_scale_swa,
-                  out.get("o_swa"), out.get("lse_swa"), kv_format)
+                  out.get("o_swa"), out.get("lse_swa"), kv_format, kv_row_bytes)
     need = lib.csa2_workspace_bytes(OP_SPARSE_ATTN, ctypes.byref(a))
     ws = _ws(need, dev)
     _check(lib.csa2_sparse_attn_fp4(ctypes.byref(a), _p(ws), need, _stream(stream)))
@@ -234,14 +236,15 @@ def sparse_attn_fp4(q, kv_lat, kv_scl, kv_rope, page_table, seq_id, idx, sm_scal
 
 
 def group_args(T, B, H, H_I, K, H_kv, L_swa, max_pages, n_pages, page_table, seq_id, n_vis,
-               swa_start, swa_len, sm_scale=None, sm_scale_swa=None, kv_format=KV_MXFP4):
+               swa_start, swa_len, sm_scale=None, sm_scale_swa=None, kv_format=KV_MXFP4,
+               kv_row_bytes=0):
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D_Q)
     if sm_scale_swa is None:
         sm_scale_swa = 1.0 / math.sqrt(D_SWA)
     return GroupArgs(T, B, H, H_I, K, H_kv, L_swa, max_pages, n_pages, _p(page_table),
                      _p(seq_id), _p(n_vis), _p(swa_start), _p(swa_len), sm_scale, sm_scale_swa,
-                     kv_format)
+                     kv_format, kv_row_bytes)
 
 
 def layer_desc(mode, q, o, lse, q_swa=None, q_idx=None, w_idx=None, k_idx=None, kv_lat=None,
@@ -273,28 +276,43 @@ def layer_group_noalloc(descs, g: GroupArgs, stream=None):
     _check(lib.csa2_layer_group_noalloc(arr, n, ctypes.byref(g), _stream(stream)))
 
 
-def mxfp4_quantize(x, lat, scl, dst_row=None, stream=None):
-    """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 16] at rows dst_row (int64) or 0..rows-1."""
+def mxfp4_quantize(x, lat, scl, dst_row=None, stream=None, row_bytes=0):
+    """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 16] at rows dst_row (int64) or
+    0..rows-1; row_bytes: the planes' row layout (0 = dense)."""
     rows = x.shape[0]
-    _check(lib.csa2_mxfp4_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row), _stream(stream)))
+    _check(lib.csa2_mxfp4_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row), row_bytes,
+                                   _stream(stream)))
 
 
-def fp4e4m3_quantize(x, lat, scl, dst_row=None, stream=None):
+def fp4e4m3_quantize(x, lat, scl, dst_row=None, stream=None, row_bytes=0):
     """x f32 [rows, 512] -> lat u8 [*, 256], scl u8 [*, 32] (E4M3 per 16 channels) at rows
-    dst_row (int64) or 0..rows-1."""
+    dst_row (int64) or 0..rows-1; row_bytes: the planes' row layout (0 = dense)."""
     rows = x.shape[0]
-    _check(lib.csa2_fp4e4m3_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row),
+    _check(lib.csa2_fp4e4m3_quantize(_p(x), rows, _p(lat), _p(scl), _p(dst_row), row_bytes,
                                      _stream(stream)))
 
 
 def kv_append(c, z, kv_lat, kv_scl, kv_rope, dst_row=None, c_idx=None, z_idx=None,
-              k_idx=None, stream=None):
+              k_idx=None, stream=None, kv_row_bytes=0):
     """KV append: entries pooled from blocks of 4 raw tokens.  c, z f32 [n, 4, 576];
     c_idx, z_idx f32 [n, 4, 64] (optional, with k_idx); writes rows dst_row (int64) or
     0..n-1 of kv_lat u8 [*, 256], kv_scl u8 [*, 16], kv_rope bf16 [*, 64], k_idx bf16 [*, 64]."""
     a = AppendArgs(c.shape[0], _p(c), _p(z), _p(c_idx), _p(z_idx), _p(dst_row), _p(kv_lat),
-                   _p(kv_scl), _p(kv_rope), _p(k_idx))
+                   _p(kv_scl), _p(kv_rope), _p(k_idx), kv_row_bytes)
     _check(lib.csa2_kv_append(ctypes.byref(a), _stream(stream)))
+
+
+def kv_packed(n_pages, kv_format=KV_MXFP4, device=None, row_bytes=None):
+    """One buffer of packed main-KV rows (codes | rope | scales, 400 bytes per entry, 416 with
+    E4M3 scales, unless row_bytes says more) and its three plane views, for the
+    kv_row_bytes layout.  Returns (buf, kv_lat, kv_scl, kv_rope, row_bytes)."""
+    scl_b = 32 if kv_format == KV_FP4_E4M3 else 16
+    rb = row_bytes or (256 + 128 + scl_b)
+    buf = torch.zeros((n_pages, 64, rb), dtype=torch.uint8, device=device)
+    lat = buf[..., 0:256]
+    rope = buf[..., 256:384].view(torch.bfloat16)
+    scl = buf[..., 384:384 + scl_b]
+    return buf, lat, scl, rope, rb
 
 
 def workspace_bytes(op: int, args) -> int:

@@ -186,6 +186,17 @@ csa2_status join_from(Side* sd, hipStream_t s) {
 
 constexpr int64_t kMaxPagesTotal = (int64_t(1) << 25) - 1;   // physical rows fit in int32
 
+// Main-KV row layout: 0 (dense planes) or a multiple of 16 that holds the entry's codes,
+// rope and scales (400 bytes, 416 with E4M3 scales), at most CSA2_MAX_ROW_BYTES.
+csa2_status check_row_bytes(const char* fn, int32_t row_bytes, int32_t fmt) {
+  if (row_bytes == 0) return CSA2_OK;
+  const int need = kLatBytes + 2 * kRope + (fmt == CSA2_KV_FP4_E4M3 ? 2 * kScl : kScl);
+  if (row_bytes < need || row_bytes > CSA2_MAX_ROW_BYTES || row_bytes % 16 != 0)
+    return fail(CSA2_ERR_SHAPE, "%s: row bytes %d must be 0 or a multiple of 16 in [%d, %d]",
+                fn, row_bytes, need, CSA2_MAX_ROW_BYTES);
+  return CSA2_OK;
+}
+
 csa2_status check_paging(const char* fn, int32_t B, int32_t max_pages, int32_t n_pages) {
   if (B < 1) return fail(CSA2_ERR_SHAPE, "%s: B=%d must be >= 1", fn, B);
   if (max_pages < 1 || (int64_t)max_pages * CSA2_PAGE > INT32_MAX)
@@ -486,6 +497,8 @@ csa2_status validate_attn(const csa2_attn_args* a) {
   if (a->kv_format != CSA2_KV_MXFP4 && a->kv_format != CSA2_KV_FP4_E4M3)
     return fail(CSA2_ERR_UNSUPPORTED, "%s: kv_format=%d is not a known format", fn,
                 a->kv_format);
+  st = check_row_bytes(fn, a->kv_row_bytes, a->kv_format);
+  if (st) return st;
   const bool swa = a->q_swa != nullptr;
   if (swa) {
     if (a->H_kv < 1 || a->H % a->H_kv != 0)
@@ -546,6 +559,10 @@ csa2_status run_attn(const csa2_attn_args* a, void* ws, hipStream_t s, bool swa_
   ap.kv_lat = a->kv_lat;
   ap.kv_scl = a->kv_scl;
   ap.kv_rope = static_cast<const uint16_t*>(a->kv_rope);
+  const KvStrides ks = kv_strides(a->kv_format, a->kv_row_bytes);
+  ap.lat_stride = ks.lat;
+  ap.rope_stride = ks.rope;
+  ap.scl_stride = ks.scl;
   ap.page_table = a->page_table;
   ap.seq_id = a->seq_id;
   ap.idx = a->idx;
@@ -690,6 +707,7 @@ csa2_status validate_group(const csa2_layer_desc* L, int32_t n_layers, const csa
     aa[i].seq_id = g->seq_id;
     aa[i].sm_scale = g->sm_scale;
     aa[i].kv_format = g->kv_format;
+    aa[i].kv_row_bytes = g->kv_row_bytes;
     aa[i].o = L[i].o;
     aa[i].lse = L[i].lse;
     aa[i].H_kv = g->H_kv;
@@ -879,8 +897,10 @@ csa2_status csa2_layer_group(const csa2_layer_desc* L, int32_t n_layers,
 }
 
 csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
-                                const int64_t* dst_row, void* stream) {
+                                const int64_t* dst_row, int32_t row_bytes, void* stream) {
   const char* fn = "csa2_mxfp4_quantize";
+  csa2_status st = check_row_bytes(fn, row_bytes, CSA2_KV_MXFP4);
+  if (st) return st;
   if (rows < 0) return fail(CSA2_ERR_SHAPE, "%s: rows=%lld < 0", fn, (long long)rows);
   if (rows > (int64_t)0xffffffff * 4)
     return fail(CSA2_ERR_SHAPE, "%s: rows=%lld too large", fn, (long long)rows);
@@ -890,7 +910,8 @@ csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint
   REQ(scl, "scl");
   if (dst_row && misaligned(dst_row))
     return fail(CSA2_ERR_ALIGN, "%s: dst_row is not 16-byte aligned", fn);
-  QuantParams p{rows, x, lat, scl, dst_row};
+  const KvStrides ks = kv_strides(CSA2_KV_MXFP4, row_bytes);
+  QuantParams p{rows, x, lat, scl, dst_row, ks.lat, ks.scl};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed("mxfp4_quantize", s, [&] { return launch_quantize(p, s); });
 }
@@ -904,6 +925,8 @@ csa2_status csa2_kv_append(const csa2_append_args* a, void* stream) {
   if ((a->c_idx != nullptr) != (a->z_idx != nullptr) ||
       (a->c_idx != nullptr) != (a->k_idx != nullptr))
     return fail(CSA2_ERR_MODE, "%s: c_idx, z_idx and k_idx must be all set or all NULL", fn);
+  csa2_status st = check_row_bytes(fn, a->kv_row_bytes, CSA2_KV_MXFP4);
+  if (st) return st;
   if (a->n == 0) return CSA2_OK;
   REQ(a->c, "c");
   REQ(a->z, "z");
@@ -917,15 +940,19 @@ csa2_status csa2_kv_append(const csa2_append_args* a, void* stream) {
   }
   if (a->dst_row && misaligned(a->dst_row))
     return fail(CSA2_ERR_ALIGN, "%s: dst_row is not 16-byte aligned", fn);
+  const KvStrides ks = kv_strides(CSA2_KV_MXFP4, a->kv_row_bytes);
   AppendParams p{a->n, a->c, a->z, a->c_idx, a->z_idx, a->dst_row, a->kv_lat, a->kv_scl,
-                 static_cast<uint16_t*>(a->kv_rope), static_cast<uint16_t*>(a->k_idx)};
+                 static_cast<uint16_t*>(a->kv_rope), static_cast<uint16_t*>(a->k_idx),
+                 ks.lat, ks.scl, ks.rope};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed("kv_append", s, [&] { return launch_kv_append(p, s); });
 }
 
 csa2_status csa2_fp4e4m3_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
-                                  const int64_t* dst_row, void* stream) {
+                                  const int64_t* dst_row, int32_t row_bytes, void* stream) {
   const char* fn = "csa2_fp4e4m3_quantize";
+  csa2_status st = check_row_bytes(fn, row_bytes, CSA2_KV_FP4_E4M3);
+  if (st) return st;
   if (rows < 0) return fail(CSA2_ERR_SHAPE, "%s: rows=%lld < 0", fn, (long long)rows);
   if (rows > (int64_t)0xffffffff * 4)
     return fail(CSA2_ERR_SHAPE, "%s: rows=%lld too large", fn, (long long)rows);
@@ -935,7 +962,8 @@ csa2_status csa2_fp4e4m3_quantize(const float* x, int64_t rows, uint8_t* lat, ui
   REQ(scl, "scl");
   if (dst_row && misaligned(dst_row))
     return fail(CSA2_ERR_ALIGN, "%s: dst_row is not 16-byte aligned", fn);
-  QuantParams p{rows, x, lat, scl, dst_row};
+  const KvStrides ks = kv_strides(CSA2_KV_FP4_E4M3, row_bytes);
+  QuantParams p{rows, x, lat, scl, dst_row, ks.lat, ks.scl};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed("fp4e4m3_quantize", s, [&] { return launch_fp4e4m3_quantize(p, s); });
 }

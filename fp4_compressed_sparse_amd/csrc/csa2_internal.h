@@ -25,6 +25,15 @@ constexpr int kDq = 576;
 constexpr int kDidx = 64;
 constexpr int kDswa = 128;
 constexpr int kPage = 64;
+// Bytes between consecutive rows of each main-KV plane: dense planes (row_bytes 0), or one
+// row of row_bytes holding all three parts of an entry.
+struct KvStrides {
+  int lat, rope, scl;
+};
+inline KvStrides kv_strides(int fmt, int row_bytes) {
+  if (row_bytes > 0) return KvStrides{row_bytes, row_bytes, row_bytes};
+  return KvStrides{kLatBytes, 2 * kRope, fmt == 1 ? 2 * kScl : kScl};
+}
 
 // ---------------------------------------------------------------- parameter blocks
 struct IdxScoreParams {
@@ -116,6 +125,7 @@ struct AttnParams {
   const uint8_t* kv_lat;
   const uint8_t* kv_scl;
   const uint16_t* kv_rope;
+  int lat_stride, rope_stride, scl_stride;      // bytes between the planes' rows
   const int32_t* page_table;
   const int32_t* seq_id;
   const int32_t* idx;                           // [T, K]
@@ -154,6 +164,7 @@ struct QuantParams {
   uint8_t* lat;
   uint8_t* scl;
   const int64_t* dst_row;              // may be null
+  int64_t lat_stride, scl_stride;      // bytes between rows
 };
 
 struct AppendParams {
@@ -167,6 +178,7 @@ struct AppendParams {
   uint8_t* scl;                        // [*, 16]
   uint16_t* rope;                      // [*, 64] bf16
   uint16_t* k_idx;                     // [*, 64] bf16, or null
+  int64_t lat_stride, scl_stride, rope_stride;   // bytes between rows of the main-KV planes
 };
 
 // ---------------------------------------------------------------- launch geometry

@@ -497,15 +497,15 @@ __global__ __launch_bounds__(768) void sparse_attn_kernel(AttnParams p) {   // p
   for (int c = 0; c < kMaxUnits; ++c) {
     if (c < 2) {                                     // code column 2rid + c
       u_base[c] = p.kv_lat + 16 * (2 * rid + c);
-      u_stride[c] = kLatBytes;
+      u_stride[c] = p.lat_stride;
       u_dst[c] = kRawLat + 1024 * (2 * rid + c);
     } else if (c == 2) {                             // rope column rid
       u_base[c] = reinterpret_cast<const uint8_t*>(p.kv_rope) + 16 * rid;
-      u_stride[c] = 2 * kRope;
+      u_stride[c] = p.rope_stride;
       u_dst[c] = kRawRope + 1024 * rid;
     } else {                                         // scale unit rid (0, or 1 for E4M3)
       u_base[c] = p.kv_scl + 16 * rid;
-      u_stride[c] = FMT == 1 ? 2 * kScl : kScl;
+      u_stride[c] = p.scl_stride;
       u_dst[c] = kRawScl + 1024 * rid;
     }
   }

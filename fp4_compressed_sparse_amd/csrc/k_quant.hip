@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(QuantParams p) {
   int X;
   const uint32_t word = mxfp4_encode_lane(x, X);
   const int64_t dst = p.dst_row ? p.dst_row[r] : r;
-  *reinterpret_cast<uint32_t*>(p.lat + dst * kLatBytes + 4 * lane) = word;
-  if ((lane & 3) == 0) p.scl[dst * kScl + (lane >> 2)] = (uint8_t)(X + 127);
+  *reinterpret_cast<uint32_t*>(p.lat + dst * p.lat_stride + 4 * lane) = word;
+  if ((lane & 3) == 0) p.scl[dst * p.scl_stride + (lane >> 2)] = (uint8_t)(X + 127);
 }
 
 // ---------------------------------------------------------------- E4M3 scales per 16
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void fp4e4m3_quantize_kernel(QuantParams p) {
     word |= code << (4 * e);
   }
   const int64_t dst = p.dst_row ? p.dst_row[r] : r;
-  *reinterpret_cast<uint32_t*>(p.lat + dst * kLatBytes + 4 * lane) = word;
-  if ((lane & 1) == 0) p.scl[dst * 2 * kScl + (lane >> 1)] = (uint8_t)sb;
+  *reinterpret_cast<uint32_t*>(p.lat + dst * p.lat_stride + 4 * lane) = word;
+  if ((lane & 1) == 0) p.scl[dst * p.scl_stride + (lane >> 1)] = (uint8_t)sb;
 }
 
 hipError_t launch_fp4e4m3_quantize(const QuantParams& p, hipStream_t s) {
@@ -197,9 +197,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   int X;
   const uint32_t word = mxfp4_encode_lane(y, X);
   const int64_t dst = p.dst_row ? p.dst_row[e] : e;
-  *reinterpret_cast<uint32_t*>(p.lat + dst * kLatBytes + 4 * lane) = word;
-  if ((lane & 3) == 0) p.scl[dst * kScl + (lane >> 2)] = (uint8_t)(X + 127);
-  p.rope[dst * kRope + lane] = bf16_rne(pool4(zr, cr));
+  *reinterpret_cast<uint32_t*>(p.lat + dst * p.lat_stride + 4 * lane) = word;
+  if ((lane & 3) == 0) p.scl[dst * p.scl_stride + (lane >> 2)] = (uint8_t)(X + 127);
+  uint16_t* rope_row = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(p.rope) + dst * p.rope_stride);
+  rope_row[lane] = bf16_rne(pool4(zr, cr));
   if (p.c_idx) {
     float ci[4], zi[4];
 #pragma unroll

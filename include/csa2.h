@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 #define CSA2_D_LAT 512   /* latent channels per entry (MXFP4) */
 #define CSA2_D_ROPE 64   /* rope channels per entry (bf16) */
@@ -67,6 +67,19 @@ extern "C" {
  *                      format of [summary] item 5 (largest magnitude 6 x 448 = 2688). */
 #define CSA2_KV_MXFP4 0
 #define CSA2_KV_FP4_E4M3 1
+/* Main-KV row layout (kv_row_bytes, row_bytes): the byte distance between consecutive cache
+ * rows, the same in all three planes (codes, rope, scales).
+ *   0: dense planes, each its own array: codes 256 B, rope 128 B, scales 16 B (E8M0) or
+ *      32 B (E4M3) per row;
+ *   otherwise a multiple of 16, at least the entry's bytes (400 with E8M0 scales, 416 with
+ *      E4M3 scales), at most CSA2_MAX_ROW_BYTES: the planes interleave, every entry's three
+ *      parts in one row, e.g. kv_lat = base, kv_rope = base + 256, kv_scl = base + 384 with
+ *      row bytes 400 (the packed row layout).  The plane pointers must then be 16-byte
+ *      aligned, and the caller keeps the three parts of a row apart.
+ * With packed rows the attention gathers each selected entry from one row instead of three
+ * arrays (one DRAM page rather than three): faster when the picks are scattered and the
+ * attention has the whole device, no faster when it shares the memory with other work. */
+#define CSA2_MAX_ROW_BYTES 4096
 
 typedef enum {
   CSA2_OK = 0,
@@ -184,6 +197,8 @@ typedef struct csa2_attn_args {
   float* lse_swa;              /* device f32 [T, H]      (output) */
   int32_t kv_format;           /* CSA2_KV_MXFP4 (kv_scl [n_pages, 64, 16]) or
                                   CSA2_KV_FP4_E4M3 (kv_scl [n_pages, 64, 32]) */
+  int32_t kv_row_bytes;        /* main-KV row layout: 0 = dense planes, else the bytes
+                                  between rows of every plane (see CSA2_MAX_ROW_BYTES) */
 } csa2_attn_args;
 
 /* One layer of a Full / Reindex / Reuse group ([summary] Architecture Components,
@@ -223,6 +238,8 @@ typedef struct csa2_group_args {
   const int32_t* swa_len;      /* [T] */
   float sm_scale, sm_scale_swa;
   int32_t kv_format;           /* format of every Full layer's main-KV planes */
+  int32_t kv_row_bytes;        /* row layout of every Full layer's main-KV planes (as in
+                                  csa2_attn_args) */
 } csa2_group_args;
 
 /* Indexer scoring + Top-K.  Workspace: csa2_workspace_bytes(CSA2_OP_INDEX_TOPK, a).
@@ -267,9 +284,10 @@ csa2_status csa2_layer_group_noalloc(const csa2_layer_desc* L, int32_t n_layers,
  * lat [*, 256] and scl [*, 16] (OCP MX: shared exponent floor(log2 max|x|) - 2 over each
  * 32-channel block, clamped to [-127, 127]; elements rounded to E2M1 to nearest, ties to
  * the even code, saturating at 6; sign kept on zeros).  dst_row NULL = rows 0..rows-1.
- * Inputs must be finite. */
+ * row_bytes: the row layout of lat and scl (0 = dense planes; see CSA2_MAX_ROW_BYTES);
+ * only the codes and scale bytes of the written rows change.  Inputs must be finite. */
 csa2_status csa2_mxfp4_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
-                                const int64_t* dst_row, void* stream);
+                                const int64_t* dst_row, int32_t row_bytes, void* stream);
 
 /* KV append: one compressed cache entry from each block of CSA2_APPEND_TOKENS raw tokens,
  * written straight into the paged cache planes (a Full layer computing its own KV:
@@ -295,6 +313,8 @@ typedef struct csa2_append_args {
   uint8_t* kv_scl;             /* device u8   [rows, 16]  (output) */
   void* kv_rope;               /* device bf16 [rows, 64]  (output) */
   void* k_idx;                 /* device bf16 [rows, 64]  (output); NULL iff c_idx is */
+  int32_t kv_row_bytes;        /* row layout of kv_lat, kv_scl and kv_rope (as in
+                                  csa2_attn_args; MXFP4 scales) */
 } csa2_append_args;
 csa2_status csa2_kv_append(const csa2_append_args* a, void* stream);
 /* Cache write in the CSA2_KV_FP4_E4M3 format ([summary] item 5, literal reading): rows
@@ -302,9 +322,10 @@ csa2_status csa2_kv_append(const csa2_append_args* a, void* stream);
  * 16 channels: s = E4M3(max|x| / 6), to nearest with ties to the even significand,
  * saturating at 448; each element |x| / s rounded to E2M1 (ties to the even code,
  * saturating at 6), sign kept; a scale that rounds to 0 gives (signed) zero codes.
- * dst_row as for csa2_mxfp4_quantize.  Inputs must be finite. */
+ * dst_row and row_bytes (at least 416 when not 0) as for csa2_mxfp4_quantize.  Inputs
+ * must be finite. */
 csa2_status csa2_fp4e4m3_quantize(const float* x, int64_t rows, uint8_t* lat, uint8_t* scl,
-                                  const int64_t* dst_row, void* stream);
+                                  const int64_t* dst_row, int32_t row_bytes, void* stream);
 /* Workspace bytes for an operation; args points to the op's argument struct
  * (csa2_index_args, csa2_attn_args, csa2_group_args or csa2_pool_args).  Returns 0 for
  * NULL args. */

@@ -66,7 +66,7 @@ def test_plan_cus_without_a_device(c):
 
 
 def test_version_and_strings(c):
-    assert c.abi_version() == 2
+    assert c.abi_version() == 3
     for st, name in c.STATUS.items():
         assert c.lib.csa2_status_string(st).decode() == name
 
@@ -201,10 +201,13 @@ def test_attn_kv_format(c):
     assert st == 6 and "kv_format" in msg
     assert call_attn(c, good_attn(c, kv_format=1))[0] == 5       # valid: reaches workspace
     q = c.lib.csa2_fp4e4m3_quantize
-    assert q(None, 4, fake(1), fake(2), None, None) == 1
-    assert q(fake(0), -1, fake(1), fake(2), None, None) == 2
-    assert q(fake(0), 4, fake(1), ctypes.c_void_p(FAKE + 4), None, None) == 3
-    assert q(None, 0, None, None, None, None) == 0
+    assert q(None, 4, fake(1), fake(2), None, 0, None) == 1
+    assert q(fake(0), -1, fake(1), fake(2), None, 0, None) == 2
+    assert q(fake(0), 4, fake(1), ctypes.c_void_p(FAKE + 4), None, 0, None) == 3
+    assert q(None, 0, None, None, None, 0, None) == 0
+    # E4M3 rows hold 32 scale bytes: packed rows need at least 416 bytes
+    assert q(fake(0), 4, fake(1), fake(2), None, 400, None) == 2
+    assert q(None, 0, None, None, None, 416, None) == 0
 
 
 def test_attn_swa_disabled_must_be_consistent(c):
@@ -222,6 +225,19 @@ def test_attn_swa_disabled_must_be_consistent(c):
 def test_attn_misaligned(c):
     a = good_attn(c, kv_rope=ctypes.c_void_p(FAKE + 2))
     assert call_attn(c, a)[0] == 3
+
+
+@pytest.mark.parametrize("fmt,row_bytes,status", [
+    (0, 0, 5), (0, 400, 5), (0, 512, 5), (0, 4096, 5), (1, 416, 5), (1, 1024, 5),
+    (0, 384, 2), (0, 408, 2), (1, 400, 2), (0, 4112, 2), (0, -400, 2),
+])
+def test_attn_row_layout(c, fmt, row_bytes, status):
+    """kv_row_bytes: 0 (dense planes) or a multiple of 16 holding the whole entry (400 bytes,
+    416 with E4M3 scales), up to 4096; valid layouts reach the workspace check."""
+    st, msg = call_attn(c, good_attn(c, kv_format=fmt, kv_row_bytes=row_bytes))
+    assert st == status, msg
+    if status == 2:
+        assert "row bytes" in msg
 
 
 def layer(c, mode, full=True, **kw):
@@ -283,6 +299,9 @@ def test_group_mode_rules(c):
     assert call_group(c, [layer(c, F), layer(c, c.REINDEX_POOL, kv_lat=fake(50))], g)[0] == 4
     # shapes are validated per op
     assert call_group(c, ok, group(c, H=40))[0] == 2
+    assert call_group(c, ok, group(c, kv_row_bytes=400))[0] == 5
+    st, msg = call_group(c, ok, group(c, kv_row_bytes=200))
+    assert st == 2 and "row bytes" in msg
     assert call_group(c, ok, group(c, H_I=99))[0] == 2
     assert c.lib.csa2_layer_group(None, 1, ctypes.byref(g), None, 0, None) == 1
 
@@ -310,11 +329,15 @@ def test_noalloc_group_validation_and_limit(c):
 
 def test_quantize_validation(c):
     q = c.lib.csa2_mxfp4_quantize
-    assert q(None, 4, fake(1), fake(2), None, None) == 1
-    assert q(fake(0), -1, fake(1), fake(2), None, None) == 2
-    assert q(ctypes.c_void_p(FAKE + 4), 4, fake(1), fake(2), None, None) == 3
-    assert q(fake(0), 4, fake(1), fake(2), ctypes.c_void_p(FAKE + 8), None) == 3
-    assert q(None, 0, None, None, None, None) == 0
+    assert q(None, 4, fake(1), fake(2), None, 0, None) == 1
+    assert q(fake(0), -1, fake(1), fake(2), None, 0, None) == 2
+    assert q(ctypes.c_void_p(FAKE + 4), 4, fake(1), fake(2), None, 0, None) == 3
+    assert q(fake(0), 4, fake(1), fake(2), ctypes.c_void_p(FAKE + 8), 0, None) == 3
+    assert q(None, 0, None, None, None, 0, None) == 0
+    for rb in (16, 392, 408, 4112, -16):                 # short, unaligned or too long rows
+        st = q(fake(0), 4, fake(1), fake(2), None, rb, None)
+        assert st == 2, rb
+        assert "row bytes" in c.lib.csa2_last_error().decode()
 
 
 def test_kv_append_validation(c):
@@ -333,6 +356,8 @@ def test_kv_append_validation(c):
     assert call(kv_rope=None)[0] == 1
     assert call(kv_scl=ctypes.c_void_p(FAKE + 4))[0] == 3
     assert call(dst_row=ctypes.c_void_p(FAKE + 8))[0] == 3
+    assert call(kv_row_bytes=392)[0] == 2
+    assert call(kv_row_bytes=400, kv_lat=None)[0] == 1      # row layout valid, then buffers
     assert call(n=0, c=None, z=None)[0] == 0                 # nothing to write
     assert c.lib.csa2_kv_append(None, None) == 1
 

@@ -304,6 +304,124 @@ def test_attn_arbitrary_index_lists(csa2, dev):
     assert np.all(res["o"][1] == 0) and np.all(np.isneginf(res["lse"][1]))
 
 
+def _packed_copy(csa2, L, fmt, row_bytes=None):
+    """The layer's dense main-KV planes copied into one buffer of packed rows."""
+    buf, lat, scl, rope, rb = csa2.kv_packed(L["kv_lat"].shape[0], fmt, L["kv_lat"].device,
+                                             row_bytes)
+    lat.copy_(L["kv_lat"])
+    scl.copy_(L["kv_scl"])
+    rope.copy_(L["kv_rope"])
+    return buf, lat, scl, rope, rb
+
+
+PACKED = ["ragged_b3_t5_h64_gqa4", "k_not_tile_multiple_h32_gqa8", "h16_shuffled_b4_k2048",
+          "many_splits_b1_k2048_h64"]
+
+
+@pytest.mark.parametrize("name", PACKED)
+@pytest.mark.parametrize("fmt,row_bytes", [(0, None), (0, 512), (1, None), (1, 448)])
+def test_attn_packed_rows_match_planes(csa2, dev, name, fmt, row_bytes):
+    """The attention over packed main-KV rows (kv_row_bytes: codes, rope and scales of an
+    entry in one row) gives the dense-plane call's outputs bit for bit: the same bytes reach
+    the same arithmetic.  Index lists with holes and an empty row."""
+    _say("attn_packed_rows", name, fmt, row_bytes)
+    w = SMALL[name]
+    d = tl.DeviceWorkload(w, dev, modes=[0], fmt=fmt)
+    L = d.layers[0]
+    rng = np.random.default_rng(11)
+    idx = np.sort(rng.integers(0, w.E, size=(w.T, w.K)), axis=1).astype(np.int32)
+    idx[0, ::5] = -1
+    if w.T > 1:
+        idx[1, :] = -1
+    idx = torch.from_numpy(idx).to(dev)
+    args = (d.page_table, d.seq_id, idx)
+    kw = dict(q_swa=L["q_swa"], swa_k=L["swa_k"], swa_v=L["swa_v"], swa_start=d.swa_start,
+              swa_len=d.swa_len, kv_format=fmt)
+    ref = csa2.sparse_attn_fp4(L["q"], L["kv_lat"], L["kv_scl"], L["kv_rope"], *args, **kw)
+    buf, lat, scl, rope, rb = _packed_copy(csa2, L, fmt, row_bytes)
+    got = csa2.sparse_attn_fp4(L["q"], lat, scl, rope, *args, kv_row_bytes=rb, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_layer_group_packed_rows_match_planes(csa2, dev, fmt):
+    """A Full -> Reindex -> Reuse group over packed main-KV rows: selections and outputs
+    equal the dense-plane group's bit for bit."""
+    _say("layer_group_packed_rows", fmt)
+    w = W(name="group_packed", B=3, T=3, E=2048, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
+          seq_id_rows=[0, 1, 2], n_vis_rows=[2048, 1500, 700], modes=[0, 1, 2])
+    d = tl.DeviceWorkload(w, dev, fmt=fmt)
+    ref = d.run_layer_group()
+    L = d.layers[0]
+    buf, lat, scl, rope, rb = _packed_copy(csa2, L, fmt)
+    L["kv_lat"], L["kv_scl"], L["kv_rope"] = lat, scl, rope
+    for Li in d.layers:
+        for k in ("o", "lse", "o_swa", "lse_swa"):
+            Li[k].fill_(float("nan"))
+        if "idx_out" in Li:
+            Li["idx_out"].fill_(-7)
+    g = d.group_args()
+    g.kv_row_bytes = rb
+    csa2.layer_group(d.descs(), g, device=dev)
+    torch.cuda.synchronize()
+    for li, Li in enumerate(d.layers):
+        for k in ("o", "lse", "o_swa", "lse_swa"):
+            np.testing.assert_array_equal(Li[k].cpu().numpy(), ref[li][k])
+        if "idx_out" in Li:
+            np.testing.assert_array_equal(Li["idx_out"].cpu().numpy(), ref[li]["idx"])
+
+
+@pytest.mark.parametrize("row_bytes", [None, 512])
+def test_cache_writes_into_packed_rows(csa2, dev, row_bytes):
+    """The quantizers and the KV append write the same bytes into packed rows as into dense
+    planes (rows dst_row, in any order), and nothing else: the other parts of a written row
+    and the rows not written keep their contents."""
+    _say("cache_writes_packed", row_bytes)
+    n_pages, n = 20, 1000
+    R = 64 * n_pages
+    rows = np.random.default_rng(5).permutation(R)[:n].astype(np.int64)
+    dst = torch.from_numpy(rows).to(dev)
+    x = torch.from_numpy(synth.normal_f32(21, 1, 0, n * 512).reshape(n, 512)).to(dev)
+    for fmt, quant in ((0, csa2.mxfp4_quantize), (1, csa2.fp4e4m3_quantize)):
+        sb = 32 if fmt == 1 else 16
+        lat = torch.zeros((R, 256), dtype=torch.uint8, device=dev)
+        scl = torch.zeros((R, sb), dtype=torch.uint8, device=dev)
+        quant(x, lat, scl, dst)
+        buf, plat, pscl, _, rb = csa2.kv_packed(n_pages, fmt, dev, row_bytes)
+        buf.fill_(0xA5)
+        quant(x, plat, pscl, dst, row_bytes=rb)
+        torch.cuda.synchronize()
+        b = buf.cpu().numpy().reshape(R, rb)
+        np.testing.assert_array_equal(b[rows, 0:256], lat.cpu().numpy()[rows])
+        np.testing.assert_array_equal(b[rows, 384:384 + sb], scl.cpu().numpy()[rows])
+        rest = np.ones(rb, bool)
+        rest[0:256] = rest[384:384 + sb] = False
+        assert np.all(b[rows][:, rest] == 0xA5)
+        assert np.all(np.delete(b, rows, axis=0) == 0xA5)
+    c, z, ci, zi, _ = _append_case(n, 31, with_idx=True, dst=False)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    lat = torch.zeros((R, 256), dtype=torch.uint8, device=dev)
+    scl = torch.zeros((R, 16), dtype=torch.uint8, device=dev)
+    rope = torch.zeros((R, 64), dtype=torch.int16, device=dev)
+    kidx = torch.zeros((R, 64), dtype=torch.int16, device=dev)
+    csa2.kv_append(t(c), t(z), lat, scl, rope, dst_row=dst, c_idx=t(ci), z_idx=t(zi), k_idx=kidx)
+    buf, plat, pscl, prope, rb = csa2.kv_packed(n_pages, 0, dev, row_bytes)
+    buf.fill_(0x5A)
+    kidx2 = torch.zeros_like(kidx)
+    csa2.kv_append(t(c), t(z), plat, pscl, prope, dst_row=dst, c_idx=t(ci), z_idx=t(zi),
+                   k_idx=kidx2, kv_row_bytes=rb)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy().reshape(R, rb)
+    np.testing.assert_array_equal(b[rows, 0:256], lat.cpu().numpy()[rows])
+    np.testing.assert_array_equal(b[rows, 256:384], rope.cpu().numpy().view(np.uint8)[rows])
+    np.testing.assert_array_equal(b[rows, 384:400], scl.cpu().numpy()[rows])
+    np.testing.assert_array_equal(kidx2.cpu().numpy(), kidx.cpu().numpy())
+    assert np.all(b[rows, 400:] == 0x5A)
+    assert np.all(np.delete(b, rows, axis=0) == 0x5A)
+
+
 def _planes_from(csa2, dev, w, x, h, d):
     """Quantize latent rows x [E, 512] of the single sequence of w on both sides (library
     quantizer on the GPU, oracle quantizer on the host) into each side's planes."""
