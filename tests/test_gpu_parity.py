@@ -345,13 +345,17 @@ def test_attn_packed_rows_match_planes(csa2, dev, name, fmt, row_bytes):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
-def test_layer_group_packed_rows_match_planes(csa2, dev, fmt):
+@pytest.mark.parametrize("fmt,full", [(0, False), (1, False), (0, True)])
+def test_layer_group_packed_rows_match_planes(csa2, dev, fmt, full):
     """A Full -> Reindex -> Reuse group over packed main-KV rows: selections and outputs
-    equal the dense-plane group's bit for bit."""
-    _say("layer_group_packed_rows", fmt)
-    w = W(name="group_packed", B=3, T=3, E=2048, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
-          seq_id_rows=[0, 1, 2], n_vis_rows=[2048, 1500, 700], modes=[0, 1, 2])
+    equal the dense-plane group's bit for bit; also the headline decode layer (64 rows over
+    32,768 entries, K = 2048) in the step's launch configuration."""
+    _say("layer_group_packed_rows", fmt, "full" if full else "small")
+    if full:
+        w = synth.workload(2)
+    else:
+        w = W(name="group_packed", B=3, T=3, E=2048, K=256, H=64, H_I=8, H_kv=64, n_hot=20,
+              seq_id_rows=[0, 1, 2], n_vis_rows=[2048, 1500, 700], modes=[0, 1, 2])
     d = tl.DeviceWorkload(w, dev, fmt=fmt)
     ref = d.run_layer_group()
     L = d.layers[0]
