@@ -284,7 +284,12 @@ csa2_status run_index_split(const csa2_index_args* a, void* ws, hipStream_t s, B
   sp.T = a->T;
   sp.H_I = a->H_I;
   sp.max_pages = a->max_pages;
-  sp.chunks = (int)((E + kIdxChunk - 1) / kIdxChunk);
+  // per-row scoring: 8 pages per wave, or 4 when the rows' 2048-entry chunks would leave
+  // the CUs short of four workgroups each (few long rows: twice the waves, each with its
+  // next page in flight)
+  const int64_t full_blocks = (int64_t)a->T * ((E + kIdxChunk - 1) / kIdxChunk);
+  sp.ppw = (full_blocks < 4 * (int64_t)device_cus()) ? 4 : 8;
+  sp.chunks = (int)((E + 256 * sp.ppw - 1) / (256 * sp.ppw));
   sp.key_stride = E;
   sp.q_idx = static_cast<const uint16_t*>(a->q_idx);
   sp.w_idx = a->w_idx;

@@ -38,6 +38,7 @@ inline KvStrides kv_strides(int fmt, int row_bytes) {
 // ---------------------------------------------------------------- parameter blocks
 struct IdxScoreParams {
   int T, H_I, max_pages, chunks;       // chunks = blocks per row
+  int ppw = 8;                         // per-row scoring: pages per wave (8 or 4)
   int64_t key_stride;                  // u32 keys per row in the workspace
   const uint16_t* q_idx;               // [T, H_I, 64]
   const float* w_idx;                  // [T, H_I]

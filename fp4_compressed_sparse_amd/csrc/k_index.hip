@@ -29,9 +29,8 @@
 namespace csa2 {
 
 constexpr int kIdxWaves = 4;
-constexpr int kIdxPerWave = kIdxChunk / kIdxWaves;   // entries per wave (whole pages)
-constexpr int kIdxPagesPerWave = kIdxPerWave / kPage;
-static_assert(kIdxPagesPerWave <= 64, "one page-table entry per lane");
+constexpr int kIdxPagesPerWave = kIdxChunk / kIdxWaves / kPage;   // pooled scoring, and the
+static_assert(kIdxPagesPerWave <= 64, "one page-table entry per lane");   // most per wave
 
 // Keys of one 64-entry page for the MFMA B operands.  MFMA pair u covers entries 16u ..
 // 16u+15: in its first operand lane (g, n) holds entry 16u + n, channels [8g, 8g+8), in the
@@ -106,18 +105,22 @@ __device__ __forceinline__ float idx_score_64(const u32x4& qa0, const u32x4& qa1
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// One workgroup scores kIdxChunk consecutive entries of one row, each wave a run of whole
+// One workgroup scores 4 PPW consecutive pages of one row, each wave a run of PPW whole
 // pages.  The wave resolves its pages' physical numbers once (one page-table entry per
 // lane, broadcast by shuffle) and keeps the next page's 8 KB of keys in flight while it
 // scores the current one; the run's keys are stored at its end.
+// PPW pages per wave (8, or 4 when a row set too small to fill the CUs needs more waves).
+template <int PPW>
 __device__ __forceinline__ void idx_score_block(const IdxScoreParams& p, int blk) {
+  constexpr int kPerWave = PPW * kPage;
+  static_assert(PPW <= kIdxPagesPerWave, "register budget");
   const int t = blk / p.chunks;
   const int c = blk - t * p.chunks;
   const int nv = p.n_vis[t];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j_begin = c * kIdxChunk + wave * kIdxPerWave;
+  const int j_begin = (c * kIdxWaves + wave) * kPerWave;
   if (j_begin >= nv) return;                 // wave-uniform; no block barriers below
-  const int j_end = min(j_begin + kIdxPerWave, nv);
+  const int j_end = min(j_begin + kPerWave, nv);
   const int npages = (j_end - j_begin + kPage - 1) / kPage;
   const int b = p.seq_id[t];
   const int n = lane & 15, g = lane >> 4;
@@ -144,21 +147,21 @@ __device__ __forceinline__ void idx_score_block(const IdxScoreParams& p, int blk
   // The scores stay in registers until the last page: a store inside the loop would sit
   // among the memory operations that each page's wait counts, so every page would also
   // wait for the previous page's store to be acknowledged.
-  // Every wave runs all kIdxPagesPerWave pages, its last page again in place of those past
-  // its run (scores not stored): straight-line code, so each page's wait leaves the next
-  // page's loads in flight.
-  float sc[kIdxPagesPerWave];
+  // Every wave runs all PPW pages, its last page again in place of those past its run
+  // (scores not stored): straight-line code, so each page's wait leaves the next page's
+  // loads in flight.
+  float sc[PPW];
   u32x4 buf[2][8];
   const int last = npages - 1;
   idx_load_page(p.k_idx, __shfl(my_page, 0), n, g, buf[0]);
 #pragma unroll
-  for (int pi = 0; pi < kIdxPagesPerWave; ++pi) {
-    if (pi + 1 < kIdxPagesPerWave)
+  for (int pi = 0; pi < PPW; ++pi) {
+    if (pi + 1 < PPW)
       idx_load_page(p.k_idx, __shfl(my_page, min(pi + 1, last)), n, g, buf[(pi + 1) & 1]);
     sc[pi] = idx_score_64(qa0, qa1, w, buf[pi & 1], n);
   }
 #pragma unroll
-  for (int pi = 0; pi < kIdxPagesPerWave; ++pi)
+  for (int pi = 0; pi < PPW; ++pi)
     if (pi < npages && 16 * g + n < valid_in(pi)) keys[kPage * pi + 16 * g + n] = float_key(sc[pi]);
 }
 
@@ -168,15 +171,17 @@ __device__ __forceinline__ void idx_clear(const IdxScoreParams& p) {
     p.clear[i] = 0u;
 }
 
+template <int PPW>
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxScoreParams p) {
   idx_clear(p);
-  idx_score_block(p, (int)blockIdx.x + p.block0);
+  idx_score_block<PPW>(p, (int)blockIdx.x + p.block0);
 }
 
 // The same scoring with a small SWA branch of the same rows in one launch (no second stream,
 // so no fork and join events): workgroups 0 .. swa_blocks-1 run the window attention, one
 // (row, KV head) unit per wave in turn, and the rest score.  The branch's bytes are a small
 // share of the scoring's, so it costs the launch little.
+template <int PPW>
 __global__ __launch_bounds__(256) void idx_score_swa_kernel(IdxScoreParams p, SwaParams w,
                                                            int swa_blocks) {
   idx_clear(p);
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(256) void idx_score_swa_kernel(IdxScoreParams p, Sw
     swa_wave_units<1>(w, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), swa_blocks * 4);
     return;
   }
-  idx_score_block(p, (int)blockIdx.x - swa_blocks + p.block0);
+  idx_score_block<PPW>(p, (int)blockIdx.x - swa_blocks + p.block0);
 }
 
 // ---------------------------------------------------------------- pooled scoring
@@ -1892,14 +1897,16 @@ hipError_t launch_idx_score(const IdxScoreParams& p, hipStream_t s) {
   const int64_t blocks = (p.block_end > 0 ? (int64_t)p.block_end : (int64_t)p.T * p.chunks) - p.block0;
   if (blocks <= 0) return hipSuccess;
   if (p.pool_sel) CSA2_LAUNCH(idx_pool_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
-  else CSA2_LAUNCH(idx_score_kernel, dim3((unsigned)blocks), dim3(256), s, p);
+  else if (p.ppw == 4) CSA2_LAUNCH(idx_score_kernel<4>, dim3((unsigned)blocks), dim3(256), s, p);
+  else CSA2_LAUNCH(idx_score_kernel<8>, dim3((unsigned)blocks), dim3(256), s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_idx_score_swa(const IdxScoreParams& p, const SwaParams& w, int swa_blocks,
                                 hipStream_t s) {
   const int64_t blocks = (int64_t)p.T * p.chunks + swa_blocks;
-  CSA2_LAUNCH(idx_score_swa_kernel, dim3((unsigned)blocks), dim3(256), s, p, w, swa_blocks);
+  if (p.ppw == 4) CSA2_LAUNCH(idx_score_swa_kernel<4>, dim3((unsigned)blocks), dim3(256), s, p, w, swa_blocks);
+  else CSA2_LAUNCH(idx_score_swa_kernel<8>, dim3((unsigned)blocks), dim3(256), s, p, w, swa_blocks);
   return hipGetLastError();
 }
 
